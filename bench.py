@@ -1,0 +1,261 @@
+"""Benchmark: KDA chunked prefill tokens/s and decode-step state GB/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
+
+One step = one chunked prefill (chunk index + chunk prep + chunked recurrence)
+of the single-sequence workload T=8192, H=32, d_k=d_v=128, bf16 I/O, fp32
+state, with seeded synthetic inputs resident in HBM.  Four copies of the inputs
+are rotated so a step never finds its inputs in the 256 MB MALL.  K steps are
+timed between device synchronisations; each call is also bracketed by HIP
+events on the stream the library launches on, which gives the per-call
+duration behind the roofline figure.  In the same run the decode step is timed
+on 256 sequences x 32 heads (512 MiB fp32 state, advanced in place), and the
+fp64 oracle is timed on the host cores on the full prefill workload
+(repeated to ~10 s of CPU work).
+
+Prints one JSON line (rank 0, N = 1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked-prefill tokens/s and decode-step state HBM GB/s on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk
+D = 128
+PREFILL_T, PREFILL_H = 8192, 32
+DECODE_N, DECODE_H = 256, 32
+
+
+def prefill_algorithmic_bytes(T, H, d, n_seqs=1):
+    """q, k, v, g (4 x 2d B), beta (2 B) in, o (2d B) out per token-head, plus the
+    fp32 state read and written once per (sequence, head)."""
+    return (10 * d + 2) * T * H + 2 * 4 * d * d * n_seqs * H
+
+
+def prefill_executed_flops(T, H, d, C=64):
+    """MFMA work per token-head as executed (full tiles): 6 d^2 + 10 C d + C^2 / 3."""
+    return (6 * d * d + 10 * C * d + C * C / 3) * T * H
+
+
+def decode_state_bytes(n, h, d):
+    return 2 * 4 * d * d * n * h
+
+
+def decode_token_bytes(n, h, d):
+    return (10 * d + 2) * n * h
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_recurrence_06_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kind: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, or None
+    when it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash() or kind not in t:
+        return None
+    return t[kind].get("hbm_bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for profilers: few steps, no CPU baseline, one 1 GiB "
+                         "device copy as a traffic calibration")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the KDA path shards by head and sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.profile:
+        args.steps, args.warmup, args.decode_steps = 5, 2, 10
+        args.no_cpu_baseline = True
+
+    import numpy as np
+    import torch
+
+    import linear_attention_recurrence_06_amd as kda
+    from kda_inputs import CONFIGS, make_config_decode, make_config_prefill
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ------------------------------------------------------------------ prefill
+    base = make_config_prefill(1, device=dev)
+    T, H = PREFILL_T, PREFILL_H
+    sets = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                     for _ in range(3)]
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    dims = kda.make_dims(T, 1, H, D, D, 0)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+
+    def prefill(i):
+        s = sets[i % len(sets)]
+        kda.kda_chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["initial_state"],
+                              None, out, fin, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        prefill(i)
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_avg_s = float(np.mean(call_ms)) * 1e-3
+    tokens_per_s = T / (wall / args.steps)
+    p_bytes = prefill_algorithmic_bytes(T, H, D)
+    p_achieved = p_bytes / call_avg_s / 1e9
+    p_traffic = counter_traffic("prefill")
+
+    # ------------------------------------------------------------------ decode
+    dw = make_config_decode(3, device=dev, steps=args.decode_steps)
+    state = dw["state"]
+    dout = torch.empty((DECODE_N, DECODE_H, D), dtype=torch.bfloat16, device=dev)
+
+    def decode(s):
+        kda.kda_decode_step(dw["q"][s], dw["k"][s], dw["v"][s], dw["g"][s], dw["beta"][s],
+                            state, dout, stream=stream)
+
+    for s in range(min(3, args.decode_steps)):
+        decode(s)
+    torch.cuda.synchronize(dev)
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.decode_steps)]
+    t1 = time.perf_counter()
+    for s in range(args.decode_steps):
+        dev_ev[s][0].record(stream)
+        decode(s)
+        dev_ev[s][1].record(stream)
+    torch.cuda.synchronize(dev)
+    d_wall = time.perf_counter() - t1
+    d_ms = [a.elapsed_time(b) for a, b in dev_ev]
+    d_avg_s = float(np.mean(d_ms)) * 1e-3
+    sb = decode_state_bytes(DECODE_N, DECODE_H, D)
+    tb = decode_token_bytes(DECODE_N, DECODE_H, D)
+    d_traffic = counter_traffic("decode")
+
+    if args.profile:
+        # plain device copy of known size: scales the HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+
+    # ------------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import kda_oracle
+        kda_oracle.build(force=False)
+        host = lambda t: t.detach().float().cpu().numpy()
+        hq, hk, hv, hg, hb = (host(base[x]) for x in ("q", "k", "v", "g", "beta"))
+        hs0 = host(base["initial_state"])
+        threads = kda_oracle.default_threads()
+        reps, spent = 0, 0.0
+        while spent < 10.0 and reps < 50:
+            c0 = time.perf_counter()
+            kda_oracle.prefill(hq, hk, hv, hg, hb, initial_state=hs0, threads=threads)
+            spent += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": T * reps / spent, "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the full prefill workload (T=8192, all 32 heads, fp64 "
+                         f"token-by-token recurrence) run {reps} times, {spent:.1f} s, "
+                         f"one (sequence, head) chain per thread"}
+
+    cfg = CONFIGS[1]
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
+                "g -softplus(N(0,1))*0.5, S0 N(0,0.02^2))",
+        "config": {"workload": cfg.name, "seq_len": T, "num_seqs": 1, "heads": H,
+                   "d_k": D, "d_v": D, "chunk": 64, "io": "bf16", "state": "fp32"},
+        "roofline": {
+            "kernel": "kda_chunk_prefill call (chunk_index + prep + recur kernels)",
+            "bound": "hbm",
+            "achieved": p_achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": p_achieved / HBM_PEAK_GBPS,
+            "traffic": p_traffic,
+            "algorithmic_bytes_per_call": p_bytes,
+            "avg_call_us": call_avg_s * 1e6,
+            "mfma_view_tflops": prefill_executed_flops(T, H, D) / call_avg_s / 1e12,
+            "mfma_view_frac": prefill_executed_flops(T, H, D) / call_avg_s / 1e12 / BF16_PEAK_TFLOPS,
+        },
+        "cpu_baseline": cpu,
+        "decode": {
+            "workload": CONFIGS[3].name.replace(", 100 steps", ""),
+            "steps": args.decode_steps,
+            "us_per_step": d_wall * 1e6 / args.decode_steps,
+            "tokens_per_s": DECODE_N * args.decode_steps / d_wall,
+            "state_GBps": sb / d_avg_s / 1e9,
+            "roofline": {
+                "kernel": "decode_kernel<bf16,128>",
+                "bound": "hbm",
+                "achieved": (sb + tb) / d_avg_s / 1e9,
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": (sb + tb) / d_avg_s / 1e9 / HBM_PEAK_GBPS,
+                "traffic": d_traffic,
+                "algorithmic_bytes_per_call": sb + tb,
+                "avg_call_us": d_avg_s * 1e6,
+            },
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

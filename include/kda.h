@@ -1,0 +1,154 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operation.  Kimi Delta Attention (KDA) keeps, per sequence and head, one
+ * fixed-size state matrix S (d_k x d_v, fp32) instead of a growing key/value
+ * list ("one matrix replaced the KV cache", post body).  Each token first
+ * predicts from the memory, then writes only the difference between the
+ * incoming value and the prediction; a learned retention alpha (per key
+ * channel, so channels forget on different timescales) and an update strength
+ * beta control it ("From KV Cache to Depth Attention: The Bottlenecks Kimi K3
+ * Had to Break", Technical Details, Kimi Delta Attention bullet; "Kimi K3: The
+ * Manos, The Mythos, The Legendos", bullet on KDA as online learning with a
+ * diagonal gate).  Queries and keys are L2-normalised (same page, bullet on
+ * stability details).  Written out, with alpha_t = exp(g_t), g_t <= 0:
+ *
+ *     q_t <- scale * q_t / sqrt(|q_t|^2 + eps),  k_t <- k_t / sqrt(|k_t|^2 + eps)
+ *     S_t  = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t  = S_t^T q_t
+ *
+ * with eps = 1e-6.  Prefill runs this over whole (optionally packed) sequences
+ * with linear cost, decode advances one token per sequence at a cost that does
+ * not depend on the position ("Kimi K3: The Manos, The Mythos, The Legendos",
+ * bullet on chunked prefill and constant-cost decode).
+ *
+ * Layouts (all row-major, contiguous, token-major):
+ *   q, k, g : [T_total, H, d_k]      v, out : [T_total, H, d_v]
+ *   beta    : [T_total, H]
+ *   states  : [N, H, d_k, d_v] fp32; S[i][j], i = key channel, j = value
+ *             channel (fastest)
+ *   cu_seqlens : int32 [N + 1], cu[0] = 0, non-decreasing, cu[N] = T_total
+ * q, k, v, g, beta and out share one element type (kda_dims.io_dtype): bf16
+ * (raw 16-bit bfloat16 bit patterns) or fp32.  States are always fp32.
+ *
+ * Ownership: the caller allocates and owns every buffer (device memory).  The
+ * library keeps no device memory between calls.
+ *
+ * Asynchrony: every call only enqueues work on `stream` (a hipStream_t, or
+ * NULL for the null stream) and returns without synchronising.  A fault in a
+ * kernel surfaces at the caller's next synchronisation.
+ *
+ * Errors: every call returns a kda_status and never throws.  Validation uses
+ * only the descriptor and pointer values (no device reads, no sync):
+ * NULL required pointers, unsupported sizes or dtypes, misaligned pointers,
+ * undersized workspace, forbidden overlaps.  Alignment: prefill q, k, v, g and
+ * the workspace 16 bytes; the decode state 16 bytes; every other pointer its
+ * element size.  The contents of
+ * cu_seqlens and the value ranges (g <= 0, 0 <= beta <= 1) are preconditions
+ * the library does not check.  For full prefill accuracy, per-token decay
+ * should also satisfy g >= -5 in every channel; see kda_chunk_prefill.
+ *
+ * Thread safety and determinism: the library is stateless and reentrant.  The
+ * kernels use no atomics, so identical inputs and sizes give bitwise identical
+ * results.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, bad count, bad overlap   */
+    KDA_ERR_UNSUPPORTED = 2, /* head size, chunk size or dtype not implemented  */
+    KDA_ERR_MISALIGNED = 3,  /* a pointer is not aligned as its access needs    */
+    KDA_ERR_WORKSPACE = 4,   /* workspace smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed       */
+} kda_status;
+
+typedef enum {
+    KDA_BF16 = 0, /* bfloat16 inputs and outputs, fp32 state, bf16 MFMA with fp32 accumulation */
+    KDA_FP32 = 1  /* fp32 inputs and outputs, fp32 state, fp32 MFMA                            */
+} kda_dtype;
+
+/* Problem descriptor (host memory, read during the call only). */
+typedef struct {
+    int64_t total_tokens; /* T_total: length of the packed token axis (decode: = num_seqs) */
+    int32_t num_seqs;     /* N >= 1; without cu_seqlens, N equal-length sequences back to back */
+    int32_t num_heads;    /* H >= 1                                                       */
+    int32_t d_k, d_v;     /* supported: (64, 64) and (128, 128)                            */
+    int32_t chunk;        /* prefill chunk length: 0 (default) or 64                      */
+    int32_t io_dtype;     /* kda_dtype                                                    */
+    float scale;          /* multiplies q after its L2 normalisation (1.0 for plain KDA)  */
+    int32_t qk_l2norm;    /* 1: the library L2-normalises q and k; 0: used as given        */
+} kda_dims;
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes (0 on a
+ * descriptor the library would reject).  The workspace holds the per-chunk
+ * factors the chunk-prep kernel hands to the recurrence kernel. */
+size_t kda_prefill_workspace_bytes(const kda_dims* dims);
+
+/* Chunked prefill over packed sequences.
+ *
+ * Sequence n is tokens cu_seqlens[n] <= t < cu_seqlens[n+1] (cu_seqlens NULL:
+ * T_total / num_seqs tokens each, T_total must divide evenly).  Each sequence
+ * starts from initial_state[n] (NULL: zero state), writes out[t] for each of
+ * its tokens, and ends with final_state[n] (NULL: not written).
+ *
+ *   q, k, v, g, beta : device, read-only, io_dtype, layouts above
+ *   initial_state    : device fp32 [N,H,d_k,d_v] or NULL
+ *   cu_seqlens       : device int32 [N+1] or NULL
+ *   out              : device io_dtype [T_total,H,d_v]; must not overlap any input
+ *   final_state      : device fp32 [N,H,d_k,d_v] or NULL; may be the very same
+ *                      pointer as initial_state (each sequence-head reads its
+ *                      slot before writing it), any other overlap is rejected
+ *   workspace        : device, at least kda_prefill_workspace_bytes(dims) bytes,
+ *                      16-byte aligned, required (NULL -> KDA_ERR_WORKSPACE);
+ *                      contents on entry are ignored and on return are
+ *                      unspecified
+ *   stream           : hipStream_t (as void*), NULL for the null stream
+ *
+ * Supported: d_k = d_v = 128 with bf16 I/O; d_k = d_v = 64 with bf16 or fp32
+ * I/O (fp32 I/O at d = 128 returns KDA_ERR_UNSUPPORTED); T_total < 2^31.
+ *
+ * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
+ * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Inside a 64-token chunk the
+ * decay ratios are factored around 16-token block boundaries; every factor
+ * stays within exp(+-40) when g >= -5 in every channel of every token (per-token
+ * retention alpha >= 0.0067).  Below that the diagonal 16-token blocks may
+ * under- or overflow and lose accuracy.
+ */
+kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
+                             const void* v, const void* g, const void* beta,
+                             const float* initial_state, const int32_t* cu_seqlens,
+                             void* out, float* final_state, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* One decode step: one new token for each of N sequences.
+ *
+ * dims->total_tokens must equal dims->num_seqs.  q, k, g [N,H,d_k], v [N,H,d_v],
+ * beta [N,H] (io_dtype); state_inout fp32 [N,H,d_k,d_v] is advanced in place by
+ * one token; out [N,H,d_v] (io_dtype) receives o = S_t^T q_t.  Each
+ * (sequence, head) state is read once and written once.  out must not overlap
+ * any input or the state.
+ */
+kda_status kda_decode_step(const kda_dims* dims, const void* q, const void* k,
+                           const void* v, const void* g, const void* beta,
+                           float* state_inout, void* out, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill and decode step.
+
+The computation lives in libkda.so (hand-written HIP, C ABI in include/kda.h);
+this package holds its sources (csrc/), the in-tree build script and a thin
+ctypes binding whose functions carry the C ABI's names.
+"""
+
+from .kda import (KDAError, kda_chunk_prefill, kda_decode_step, kda_dims,
+                  kda_prefill_workspace_bytes, load_library, make_dims, status_string)
+
+__all__ = ["KDAError", "kda_chunk_prefill", "kda_decode_step", "kda_dims",
+           "kda_prefill_workspace_bytes", "load_library", "make_dims", "status_string"]

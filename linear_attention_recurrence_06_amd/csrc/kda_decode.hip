@@ -1,0 +1,160 @@
+// KDA decode step on gfx950: one token per sequence, state advanced in place.
+//
+// Per (sequence, head) the step is, with qb, kb the L2-normalised q, k and
+// alpha = exp(g) (retention per key channel):
+//     S' = Diag(alpha) S;  vh = S'^T kb;  y = S'^T qb       (one pass over S)
+//     delta = beta (v - vh);  S = S' + kb delta^T;  o = y + (qb . kb) delta
+// The second form of o follows from o = (S' + kb delta^T)^T qb, so the state
+// is read once and written once ("Kimi K3: The Manos, The Mythos, The
+// Legendos", bullet on decode cost constant in sequence length; the update is
+// the delta rule with a diagonal gate of "From KV Cache to Depth Attention:
+// The Bottlenecks Kimi K3 Had to Break", Technical Details, KDA bullet).
+//
+// Work split: one 256-thread workgroup per (sequence, head).  Thread t owns
+// value columns 4*(t % (D/4)) .. +3 of rows (t / (D/4)) + (256/(D/4)) * m, so
+// each wave reads and writes whole 512-byte (D=128) state rows with 16-byte
+// accesses, every lane keeps its D*D/256 state values in registers between the
+// read and the write, and the read-outs reduce over row groups with one
+// cross-lane step inside the wave and one LDS exchange across the four waves.
+// The kernel is bound by HBM: 2 * 4 * D*D bytes of state per unit.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
+                                                     const T* __restrict__ k,
+                                                     const T* __restrict__ v,
+                                                     const T* __restrict__ g,
+                                                     const T* __restrict__ beta,
+                                                     float* __restrict__ S,
+                                                     T* __restrict__ out, float scale,
+                                                     int l2norm) {
+    constexpr int TPR = D / 4;       // threads per state row
+    constexpr int RG = 256 / TPR;    // row groups
+    constexpr int RPT = D / RG;      // rows per thread
+    constexpr int EPL = D / kWave;   // vector elements per lane in the norm pass
+    static_assert(RPT * RG == D && EPL * kWave == D, "bad decode tiling");
+
+    const int64_t unit = blockIdx.x;  // = n * H + h
+    const int t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const int cq = t % TPR, rg = t / TPR;
+
+    __shared__ float s_q[D], s_k[D], s_a[D];
+    __shared__ float s_red[4][TPR][8];
+
+    // 1. stream the state in (all loads in flight before any arithmetic)
+    float* Su = S + unit * (int64_t)(D * D);
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(Su + (int64_t)(rg + RG * m) * D + 4 * cq));
+
+    // 2. token vectors: every wave computes the norms itself (no barrier needed for them)
+    const T* qu = q + unit * D;
+    const T* ku = k + unit * D;
+    float qv[EPL], kv[EPL];
+    float ssq = 0.f, ssk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        qv[e] = to_f32(qu[lane + kWave * e]);
+        kv[e] = to_f32(ku[lane + kWave * e]);
+        ssq += qv[e] * qv[e];
+        ssk += kv[e] * kv[e];
+        sqk += qv[e] * kv[e];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        ssq += xor_shfl(ssq, m);
+        ssk += xor_shfl(ssk, m);
+        sqk += xor_shfl(sqk, m);
+    }
+    const float rq = l2norm ? 1.0f / sqrtf(ssq + kL2Eps) : 1.0f;
+    const float rk = l2norm ? 1.0f / sqrtf(ssk + kL2Eps) : 1.0f;
+    const float qk = sqk * rq * rk * scale;   // (scale * qb) . kb
+    if (wave == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int i = lane + kWave * e;
+            s_q[i] = qv[e] * rq * scale;
+            s_k[i] = kv[e] * rk;
+            s_a[i] = __expf(to_f32(g[unit * D + i]));
+        }
+    }
+    const float b = to_f32(beta[unit]);
+    float vj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vj[j] = to_f32(v[unit * D + 4 * cq + j]);
+    __syncthreads();
+
+    // 3. decay the rows and accumulate both read-outs
+    f32x4 vh = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        s[m] *= s_a[i];
+        vh += s_k[i] * s[m];
+        y += s_q[i] * s[m];
+    }
+    // 4. reduce over the row groups: inside the wave, then across waves
+#pragma unroll
+    for (int off = TPR; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            vh[j] += xor_shfl(vh[j], off);
+            y[j] += xor_shfl(y[j], off);
+        }
+    }
+    if (lane < TPR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s_red[wave][cq][j] = vh[j];
+            s_red[wave][cq][4 + j] = y[j];
+        }
+    }
+    __syncthreads();
+    float d[4], o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float vhat = (s_red[0][cq][j] + s_red[1][cq][j]) + (s_red[2][cq][j] + s_red[3][cq][j]);
+        const float yy = (s_red[0][cq][4 + j] + s_red[1][cq][4 + j]) +
+                         (s_red[2][cq][4 + j] + s_red[3][cq][4 + j]);
+        d[j] = b * (vj[j] - vhat);
+        o[j] = yy + qk * d[j];
+    }
+    // 5. write the difference and stream the state out
+    const f32x4 dv = {d[0], d[1], d[2], d[3]};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        s[m] += s_k[i] * dv;
+        __builtin_nontemporal_store(
+            s[m], reinterpret_cast<f32x4*>(Su + (int64_t)(rg + RG * m) * D + 4 * cq));
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[unit * D + 4 * cq + j] = from_f32<T>(o[j]);
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.n_seqs * a.n_heads;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)units), dim3(256), 0, stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                       (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    if (a.bf16) {
+        return a.d == 128 ? launch<bf16, 128>(a, stream) : launch<bf16, 64>(a, stream);
+    }
+    return a.d == 128 ? launch<float, 128>(a, stream) : launch<float, 64>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,86 @@
+// Host-side interface between the C ABI (kda_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// epsilon inside the L2-norm square root: x / sqrt(sum x^2 + eps)
+constexpr float kL2Eps = 1e-6f;
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float* state;
+    void* out;
+    int32_t n_seqs, n_heads, d;
+    bool bf16;
+    float scale;
+    int l2norm;
+};
+
+// Workspace for one prefill call: a chunk index (first chunk slot of each
+// sequence, int32 [N+1]) followed by one record per (chunk slot, head) with
+// the factors the recurrence kernel consumes.  Record layout, E = element size
+// of the I/O type, all matrices in MFMA fragment order:
+//   W    64 x D   (A order)   W = T Diag(beta) Khat
+//   Qh   64 x D   (A order)   Qhat = q * exp(gamma)
+//   M    64 x 64  (A order)   inclusive-lower Q K decay products
+//   Kt   D  x 64  (A order)   Kprime^T, Kprime = k * exp(gamma_C - gamma)
+//   U    64 x D   (C order)   U = T Diag(beta) V
+//   gC   D fp32               exp(gamma_C)
+struct PrefillLayout {
+    int d;
+    int elt;               // bytes per I/O element
+    int64_t slots;         // chunk slots (upper bound on the chunk count)
+    int64_t heads;
+    size_t index_bytes;    // chunk index, padded to 256 B
+    size_t rec_bytes;      // bytes per (slot, head) record
+    size_t off_w, off_q, off_m, off_kt, off_u, off_gc;
+    size_t total() const { return index_bytes + rec_bytes * (size_t)slots * (size_t)heads; }
+};
+
+inline PrefillLayout make_layout(int d, int elt, int64_t total_tokens, int64_t n_seqs,
+                                 int64_t heads, bool varlen) {
+    PrefillLayout L;
+    L.d = d;
+    L.elt = elt;
+    L.heads = heads;
+    if (varlen || n_seqs == 0) {
+        L.slots = (total_tokens + 63) / 64 + n_seqs;
+    } else {
+        const int64_t len = total_tokens / n_seqs;
+        L.slots = n_seqs * ((len + 63) / 64);
+    }
+    L.index_bytes = (((size_t)(n_seqs + 1) * 4 + 255) / 256) * 256;
+    size_t o = 0;
+    L.off_w = o;  o += (size_t)64 * d * elt;
+    L.off_q = o;  o += (size_t)64 * d * elt;
+    L.off_m = o;  o += (size_t)64 * 64 * elt;
+    L.off_kt = o; o += (size_t)d * 64 * elt;
+    L.off_u = o;  o += (size_t)64 * d * elt;
+    L.off_gc = o; o += (size_t)d * 4;
+    L.rec_bytes = o;
+    return L;
+}
+
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float* initial_state;
+    const int32_t* cu_seqlens;   // may be null: equal lengths
+    void* out;
+    float* final_state;          // may be null
+    unsigned char* workspace;
+    int64_t total_tokens;
+    int32_t n_seqs, n_heads, d;
+    bool bf16;
+    float scale;
+    int l2norm;
+    PrefillLayout layout;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,203 @@
+"""Python binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the stream; there
+is no CPU path.  If libkda.so is missing or fails to load, every call raises.
+
+    out, final = kda_chunk_prefill(q, k, v, g, beta, initial_state, cu_seqlens)
+    out = kda_decode_step(q, k, v, g, beta, state)        # state updated in place
+
+Layouts (contiguous, token-major): q, k, g ``[T, H, d_k]``; v, out ``[T, H, d_v]``;
+beta ``[T, H]``; states ``[N, H, d_k, d_v]`` float32; cu_seqlens int32 ``[N+1]``.
+q, k, v, g, beta share one dtype (bfloat16 or float32), which is also out's.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED, \
+    KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(6)
+KDA_BF16, KDA_FP32 = 0, 1
+
+#: every symbol include/kda.h declares
+EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
+            "kda_status_string", "kda_version")
+
+
+class kda_dims(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64),
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("qk_l2norm", ctypes.c_int32),
+    ]
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -m linear_attention_recurrence_06_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(kda_dims)
+    lib.kda_prefill_workspace_bytes.argtypes = [D]
+    lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"unsupported I/O dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_dims(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
+              io_dtype: int, scale: float = 1.0, qk_l2norm: bool = True,
+              chunk: int = 64) -> kda_dims:
+    return kda_dims(int(total_tokens), int(num_seqs), int(num_heads), int(d_k), int(d_v),
+                    int(chunk), int(io_dtype), float(scale), 1 if qk_l2norm else 0)
+
+
+def kda_prefill_workspace_bytes(dims: kda_dims) -> int:
+    return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None, *,
+                      num_seqs: Optional[int] = None, scale: float = 1.0,
+                      qk_l2norm: bool = True, workspace: Optional[torch.Tensor] = None,
+                      output_final_state: bool = True,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill over packed sequences (see include/kda.h).
+
+    Returns ``(out, final_state)``; ``final_state`` is None when
+    ``output_final_state`` is False and none was passed.  Without
+    ``cu_seqlens`` the T tokens form ``num_seqs`` (default 1) equal sequences.
+    """
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("g", g, (T, H, dk)),
+                         ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
+        _check_tensor(name, t, shp, dt, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (T, H, dv), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    need = kda_prefill_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
+                               _ptr(final_state), _ptr(workspace), workspace.numel(),
+                               _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_prefill")
+    return out, final_state
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, *, scale: float = 1.0,
+                    qk_l2norm: bool = True, stream=None) -> torch.Tensor:
+    """One KDA decode step (one token per sequence); ``state`` [N,H,d_k,d_v]
+    float32 is advanced in place.  Returns ``out`` [N,H,d_v]."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("g", g, (N, H, dk)),
+                         ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (N, H, dv), dt, dev)
+    dims = make_dims(N, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    rc = lib.kda_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                             _ptr(beta), _ptr(state), _ptr(out), _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_step")
+    return out
