@@ -21,8 +21,9 @@ struct DecodeArgs {
 };
 
 // Workspace for one prefill call: a chunk index (first chunk slot of each
-// sequence, int32 [N+1]) followed by one record per (chunk slot, head) with
-// the factors the recurrence kernel consumes.  Record layout, E = element size
+// sequence, int32 [N+1]), one descriptor per chunk slot (first token and
+// length, int32 x 2; length 0 marks an unused slot), then one record per
+// (chunk slot, head) with the factors the recurrence kernel consumes.  Record layout, E = element size
 // of the I/O type, all matrices in MFMA fragment order:
 //   W    64 x D   (A order)   W = T Diag(beta) Khat
 //   Qh   64 x D   (A order)   Qhat = q * exp(gamma)
@@ -36,9 +37,11 @@ struct PrefillLayout {
     int64_t slots;         // chunk slots (upper bound on the chunk count)
     int64_t heads;
     size_t index_bytes;    // chunk index, padded to 256 B
+    size_t desc_bytes;     // chunk-slot descriptors, padded to 256 B
     size_t rec_bytes;      // bytes per (slot, head) record
     size_t off_w, off_q, off_m, off_kt, off_u, off_gc;
-    size_t total() const { return index_bytes + rec_bytes * (size_t)slots * (size_t)heads; }
+    __host__ __device__ size_t records_offset() const { return index_bytes + desc_bytes; }
+    size_t total() const { return records_offset() + rec_bytes * (size_t)slots * (size_t)heads; }
 };
 
 inline PrefillLayout make_layout(int d, int elt, int64_t total_tokens, int64_t n_seqs,
@@ -54,6 +57,7 @@ inline PrefillLayout make_layout(int d, int elt, int64_t total_tokens, int64_t n
         L.slots = n_seqs * ((len + 63) / 64);
     }
     L.index_bytes = (((size_t)(n_seqs + 1) * 4 + 255) / 256) * 256;
+    L.desc_bytes = (((size_t)L.slots * 8 + 255) / 256) * 256;
     size_t o = 0;
     L.off_w = o;  o += (size_t)64 * d * elt;
     L.off_q = o;  o += (size_t)64 * d * elt;
@@ -77,6 +81,7 @@ struct PrefillArgs {
     bool bf16;
     float scale;
     int l2norm;
+    int cu_count;                // compute units of the device (persistent grids)
     PrefillLayout layout;
 };
 

@@ -26,15 +26,23 @@
 // F-scaled).  On diagonal blocks the factors stay within e^(+-40) when every
 // g >= -5, the documented accuracy range.
 //
-// Steps (256 threads = 4 waves; wave w owns tokens 16w..16w+15 = block w):
-//   P0 load q, k, v, g, beta; L2-normalise q, k; cumulative sum of g per block
-//      (in-thread, then across the wave), block totals exchanged through LDS;
-//   P1 decay factors; E/F-scaled tiles to LDS; Qhat, Kprime^T, Gamma_C out;
+// Work split: a persistent grid (one workgroup per CU) walks the (chunk slot,
+// head) items; each workgroup loads the next item's raw rows while it computes
+// the current one, and the item after that's descriptor one step earlier, so
+// global-memory latency overlaps the arithmetic.
+//
+// Steps per item (256 threads = 4 waves; wave w owns tokens 16w..16w+15 = block w):
+//   P0 L2-normalise q, k; cumulative sum of g per block (in-thread, then across
+//      the wave); block totals through LDS, then a per-channel table of every
+//      block-level decay factor (16 x d_k exponentials per chunk);
+//   P1 element decay factors; E/F-scaled tiles to LDS; Qhat, Kprime^T, Gamma_C out;
 //   P2 A and M blocks on MFMA (A row block w, M row block 3-w per wave);
 //   P3 T = (I + A)^-1: the four 16x16 diagonal inverses by forward substitution
 //      (one lane per column), then block rows 1..3 by T_RJ = -T_RR sum_K A_RK T_KJ
 //      on fp32 MFMA;
 //   P4 W and U on MFMA; U, M, W out.
+#include <algorithm>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -72,9 +80,13 @@ __device__ __forceinline__ void mm16_lds(f32x4& acc, const float* A, int lda, co
 template <typename T, int D>
 struct PrepSmem {
     static constexpr int P = 16 / sizeof(T);  // 16-byte row padding
-    float A[64][65];          // beta-scaled strictly-lower A
+    float A[64][68];          // beta-scaled strictly-lower A (16-byte aligned rows)
     T M[64][64 + P];          // inclusive-lower Q K decay products
     float tau[4][D];          // per-block total log-decay
+    // per-channel decay factors, rows: 0-3 e^(-tau_R/2); 4 e^(tau_1); 5 e^(tau_1+tau_2);
+    // 6 e^(tau_2); 7-10 e^(rho_{R-1}) (chunk start -> block R start); 11-14
+    // e^(rho_3 - rho_R) (block R end -> chunk end); 15 e^(rho_3) = Gamma_C
+    float fac[16][D];
     float beta[64];
     union {
         struct {
@@ -95,6 +107,55 @@ struct PrepSmem {
     } u;
 };
 
+// One 16x16 block (R, J) of A (IS_A: rows from KE, beta-scaled, strictly lower)
+// or of M (rows from QE, inclusive lower), from the decayed tiles in LDS.
+template <typename T, int D, bool IS_A>
+__device__ __forceinline__ void decay_block(PrepSmem<T, D>& sm, int R, int J, int lane) {
+    constexpr int NKS = D / 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (J <= R) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 8 * (lane >> 4);
+            Frag<T> a = load_frag<T>(IS_A ? &sm.u.a.KE[16 * R + (lane & 15)][c0]
+                                          : &sm.u.a.QE[16 * R + (lane & 15)][c0]);
+            Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
+            if (J == R) {
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0 + 4]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float f = j < 4 ? f0[j] : f1[j - 4];
+                    a.v[j] = from_f32<T>(to_f32(a.v[j]) * f);
+                    b.v[j] = from_f32<T>(to_f32(b.v[j]) * f);
+                }
+            } else if (J < R - 1) {
+                const int row = (R == 2) ? 4 : 5 + J;  // e^(rho_{R-1} - rho_J)
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0 + 4]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    b.v[j] = from_f32<T>(to_f32(b.v[j]) * (j < 4 ? f0[j] : f1[j - 4]));
+            }
+            mma(acc, a, b);
+        }
+    }
+    const int col = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 4 * (lane >> 4) + e;
+        float val = acc[e];
+        if (IS_A) {
+            val *= sm.beta[16 * R + row];
+            if (J > R || (J == R && col >= row)) val = 0.f;
+            sm.A[16 * R + row][16 * J + col] = val;
+        } else {
+            if (J > R || (J == R && col > row)) val = 0.f;
+            sm.M[16 * R + row][16 * J + col] = from_f32<T>(val);
+        }
+    }
+}
+
 struct PrepParams {
     const void *q, *k, *v, *g, *beta;
     const int32_t* cu;
@@ -106,62 +167,68 @@ struct PrepParams {
     PrefillLayout L;
 };
 
+// (first token, length) of a chunk slot; length 0 marks an unused slot.
+__device__ __forceinline__ int2 slot_desc(const PrepParams& p, int64_t slot) {
+    if (p.cu) return reinterpret_cast<const int2*>(p.ws + p.L.index_bytes)[slot];
+    const int64_t N = p.n_seqs;
+    const int64_t each = p.total_tokens / N;
+    const int64_t per = (each + 63) / 64;
+    if (per == 0 || slot >= per * N) return make_int2(0, 0);
+    const int64_t n = slot / per, kc = slot - n * per;
+    return make_int2((int)(n * each + 64 * kc), (int)min((int64_t)64, each - 64 * kc));
+}
+
+// One thread's share of a chunk's raw input rows (rows 4*rg..4*rg+3, channels
+// CPT*cg..+CPT-1), kept in the I/O type so the next item's rows can be in
+// flight while the current item computes.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
-    constexpr int CPT = D / 16;  // channels per thread in the row layout
-    constexpr int NKS = D / 32;  // 32-deep k-steps over the channels
-    __shared__ PrepSmem<T, D> sm;
+struct RawRows {
+    static constexpr int CPT = D / 16;
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    V q[4], k[4], g[4], v[4];
+    T b[4];
 
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int rg = t >> 4, cg = t & 15, grp = lane >> 4;
-    const int64_t slot = blockIdx.x;
-    const int h = blockIdx.y;
-    const int64_t H = p.n_heads;
-    const int32_t* cf = reinterpret_cast<const int32_t*>(p.ws);
-    const int N = p.n_seqs;
-    if (slot >= cf[N]) return;
-    // sequence owning this chunk slot: largest n with cf[n] <= slot
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cf[mid] <= slot) lo = mid; else hi = mid - 1;
-    }
-    const int n = lo;
-    const int64_t each = N ? p.total_tokens / N : 0;
-    const int64_t s_begin = p.cu ? (int64_t)p.cu[n] : (int64_t)n * each;
-    const int64_t s_end = p.cu ? (int64_t)p.cu[n + 1] : s_begin + each;
-    const int64_t t0 = s_begin + 64 * (slot - cf[n]);
-    const int Lc = (int)min((int64_t)64, s_end - t0);
-
-    unsigned char* rec = p.ws + p.L.index_bytes + (size_t)(slot * H + h) * p.L.rec_bytes;
-
-    // ---------------------------------------------------------------- P0
-    const T* qg = (const T*)p.q;
-    const T* kg = (const T*)p.k;
-    const T* vg = (const T*)p.v;
-    const T* gg = (const T*)p.g;
-    float qf[4][CPT], kf[4][CPT], gf[4][CPT], vf[4][CPT];
+    __device__ __forceinline__ void load(const PrepParams& p, int2 d, int h, int rg, int cg) {
+        const int64_t H = p.n_heads;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * rg + i;
-        if (r < Lc) {
-            const int64_t off = ((t0 + r) * H + h) * D + CPT * cg;
-            load_n<T, CPT>(qg + off, qf[i]);
-            load_n<T, CPT>(kg + off, kf[i]);
-            load_n<T, CPT>(gg + off, gf[i]);
-            load_n<T, CPT>(vg + off, vf[i]);
-        } else {
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            if (r < d.y) {
+                const int64_t row = (int64_t)d.x + r;
+                const int64_t off = (row * H + h) * D + CPT * cg;
+                q[i] = *reinterpret_cast<const V*>((const T*)p.q + off);
+                k[i] = *reinterpret_cast<const V*>((const T*)p.k + off);
+                g[i] = *reinterpret_cast<const V*>((const T*)p.g + off);
+                v[i] = *reinterpret_cast<const V*>((const T*)p.v + off);
+                b[i] = ((const T*)p.beta)[row * H + h];
+            } else {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) qf[i][c] = kf[i][c] = gf[i][c] = vf[i][c] = 0.f;
+                for (int c = 0; c < CPT; ++c) q[i][c] = k[i][c] = g[i][c] = v[i][c] = from_f32<T>(0.f);
+                b[i] = from_f32<T>(0.f);
+            }
         }
     }
-    float bt[4];
+};
+
+// Everything for one (chunk slot, head) item whose raw rows are already in
+// registers (converted to fp32).  Ends with a barrier so the next item may
+// reuse the shared memory.
+template <typename T, int D>
+__device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
+                                          int h, float (&qf)[4][D / 16], float (&kf)[4][D / 16],
+                                          float (&gf)[4][D / 16], const float (&vf)[4][D / 16],
+                                          const float (&bt)[4]) {
+    constexpr int CPT = D / 16;  // channels per thread in the row layout
+    constexpr int NKS = D / 32;  // 32-deep k-steps over the channels
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int rg = t >> 4, cg = t & 15, grp = lane >> 4;
+    const int64_t H = p.n_heads;
+    unsigned char* rec = p.ws + p.L.records_offset() + (size_t)(slot * H + h) * p.L.rec_bytes;
+
+    // ---------------------------------------------------------------- P0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * rg + i;
-        bt[i] = (r < Lc) ? to_f32(((const T*)p.beta)[(t0 + r) * H + h]) : 0.f;
-        if (cg == 0) sm.beta[r] = bt[i];
-    }
+    for (int i = 0; i < 4; ++i)
+        if (cg == 0) sm.beta[4 * rg + i] = bt[i];
     // L2 norms over the 16 lanes that share a row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -191,8 +258,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
         gf[1][c] += gf[0][c];
         gf[2][c] += gf[1][c];
         gf[3][c] += gf[2][c];
-        const float tot = gf[3][c];
-        float incl = tot;
+        float incl = gf[3][c];
         float x = __shfl_up(incl, 16, kWave);
         if (grp >= 1) incl += x;
         x = __shfl_up(incl, 32, kWave);
@@ -205,35 +271,47 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
         if (grp == 0) sm.tau[w][CPT * cg + c] = tau;
     }
     __syncthreads();
+    // per-channel table of the block-level decay factors (16 x D exponentials)
+    for (int e = t; e < 16 * D; e += 256) {
+        const int row = e / D, c = e % D;
+        const float t0 = sm.tau[0][c], t1 = sm.tau[1][c], t2 = sm.tau[2][c], t3 = sm.tau[3][c];
+        const float tv[4] = {t0, t1, t2, t3};
+        float x;
+        if (row < 4) {
+            x = -0.5f * tv[row];
+        } else if (row == 4) {
+            x = t1;
+        } else if (row == 5) {
+            x = t1 + t2;
+        } else if (row == 6) {
+            x = t2;
+        } else if (row < 11) {
+            const int R = row - 7;
+            x = 0.f;
+            for (int m = 0; m < R; ++m) x += tv[m];
+        } else if (row < 15) {
+            const int R = row - 11;
+            x = 0.f;
+            for (int m = R + 1; m < 4; ++m) x += tv[m];
+        } else {
+            x = ((t0 + t1) + t2) + t3;
+        }
+        sm.fac[row][c] = __expf(x);
+    }
+    __syncthreads();
 
     // ---------------------------------------------------------------- P1
-    float tauR[CPT], rho_prev[CPT], rho_after[CPT], gamC[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        float tv[4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R) tv[R] = sm.tau[R][CPT * cg + c];
-        tauR[c] = tv[w];
-        float before = 0.f, after = 0.f;
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            if (R < w) before += tv[R];
-            if (R > w) after += tv[R];
-        }
-        rho_prev[c] = before;   // log-decay from the chunk start to this block's start
-        rho_after[c] = after;   // log-decay from this block's end to the chunk end
-        gamC[c] = ((tv[0] + tv[1]) + tv[2]) + tv[3];
-    }
-    float Gs[CPT], Kp[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        Gs[c] = __expf(rho_prev[c]);
-        Kp[c] = __expf(rho_after[c]);
-    }
     T* Qg = reinterpret_cast<T*>(rec + p.L.off_q);
     T* Ktg = reinterpret_cast<T*>(rec + p.L.off_kt);
     float bK[4][CPT], bV[4][CPT];
     float kpT[CPT][4];
+    float tauR[CPT], Gs[CPT], Kp[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        tauR[c] = sm.tau[w][CPT * cg + c];
+        Gs[c] = sm.fac[7 + w][CPT * cg + c];
+        Kp[c] = sm.fac[11 + w][CPT * cg + c];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
@@ -260,56 +338,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     if (rg == 0) {
         float* gC = reinterpret_cast<float*>(rec + p.L.off_gc);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) gC[CPT * cg + c] = __expf(gamC[c]);
+        for (int c = 0; c < CPT; ++c) gC[CPT * cg + c] = sm.fac[15][CPT * cg + c];
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- P2
-    // block (R, J): isA -> A (rows from KE, beta-scaled, strict), else M (rows from QE, inclusive)
-    auto block = [&](bool isA, int R, int J) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (J <= R) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int c0 = 32 * ks + 8 * (lane >> 4);
-                Frag<T> a = load_frag<T>(isA ? &sm.u.a.KE[16 * R + (lane & 15)][c0]
-                                             : &sm.u.a.QE[16 * R + (lane & 15)][c0]);
-                Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
-                if (J == R) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float f = __expf(-0.5f * sm.tau[R][c0 + j]);
-                        a.v[j] = from_f32<T>(to_f32(a.v[j]) * f);
-                        b.v[j] = from_f32<T>(to_f32(b.v[j]) * f);
-                    }
-                } else if (J < R - 1) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        float s = 0.f;
-                        for (int m = J + 1; m < R; ++m) s += sm.tau[m][c0 + j];
-                        b.v[j] = from_f32<T>(to_f32(b.v[j]) * __expf(s));
-                    }
-                }
-                mma(acc, a, b);
-            }
-        }
-        const int col = lane & 15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 4 * (lane >> 4) + e;
-            float val = acc[e];
-            if (isA) {
-                val *= sm.beta[16 * R + row];
-                if (J > R || (J == R && col >= row)) val = 0.f;
-                sm.A[16 * R + row][16 * J + col] = val;
-            } else {
-                if (J > R || (J == R && col > row)) val = 0.f;
-                sm.M[16 * R + row][16 * J + col] = from_f32<T>(val);
-            }
-        }
-    };
-    for (int J = 0; J < 4; ++J) block(true, w, J);
-    for (int J = 0; J < 4; ++J) block(false, 3 - w, J);
+    for (int J = 0; J < 4; ++J) decay_block<T, D, true>(sm, w, J, lane);
+    for (int J = 0; J < 4; ++J) decay_block<T, D, false>(sm, 3 - w, J, lane);
     __syncthreads();
 
     // ---------------------------------------------------------------- P3
@@ -326,14 +361,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
         store_n<T, 4>(&sm.u.b.BV[CPT * cg + c][4 * rg], xv);
     }
     if (w == 0) {
-        // diagonal 16x16 blocks of (I + A)^-1: lane = (block, column), forward substitution
+        // diagonal 16x16 blocks of (I + A)^-1: lane = (block, column), forward
+        // substitution; every row of A_RR is read with 16-byte loads up front
         const int R = lane >> 4, j = lane & 15;
+        float arow[16][16];
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < (i + 3) / 4; ++q4) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.A[16 * R + i][16 * R + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[i][4 * q4 + e] = a4[e];
+            }
         float colv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float acc = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < i; ++kk) acc += sm.A[16 * R + i][16 * R + kk] * colv[kk];
+            for (int kk = 0; kk < i; ++kk) acc += arow[i][kk] * colv[kk];
             colv[i] = (i == j) ? 1.f : ((i < j) ? 0.f : -acc);
         }
 #pragma unroll
@@ -345,7 +390,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
             const int J = w;
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
             for (int K = J; K < R; ++K)
-                mm16_lds(x, &sm.A[16 * R][16 * K], 65, &sm.u.b.Tf[16 * K][16 * J], 65);
+                mm16_lds(x, &sm.A[16 * R][16 * K], 68, &sm.u.b.Tf[16 * K][16 * J], 65);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.u.b.X[w][4 * (lane >> 4) + e][lane & 15] = -x[e];
         }
@@ -411,6 +456,47 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
             store_frag<T>(Wg + ((int64_t)(w * NKS + ks) * kWave + lane) * 8, f);
         }
     }
+    __syncthreads();  // the next item overwrites the shared tiles
+}
+
+// Persistent driver: item = slot * H + head; workgroup b takes items b, b + G, ...
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
+    constexpr int CPT = D / 16;
+    __shared__ PrepSmem<T, D> sm;
+    const int t = threadIdx.x;
+    const int rg = t >> 4, cg = t & 15;
+    const int64_t H = p.n_heads;
+    const int64_t items = p.L.slots * H;
+    const int64_t G = gridDim.x;
+    int64_t item = blockIdx.x;
+    if (item >= items) return;
+
+    RawRows<T, D> raw;
+    int2 d_cur = slot_desc(p, item / H);
+    int2 d_nxt = item + G < items ? slot_desc(p, (item + G) / H) : make_int2(0, 0);
+    raw.load(p, d_cur, (int)(item % H), rg, cg);
+    for (; item < items; item += G) {
+        const int2 d = d_cur;
+        float qf[4][CPT], kf[4][CPT], gf[4][CPT], vf[4][CPT], bt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                qf[i][c] = to_f32(raw.q[i][c]);
+                kf[i][c] = to_f32(raw.k[i][c]);
+                gf[i][c] = to_f32(raw.g[i][c]);
+                vf[i][c] = to_f32(raw.v[i][c]);
+            }
+            bt[i] = to_f32(raw.b[i]);
+        }
+        // next item's rows go in flight now; the descriptor after it one step earlier
+        if (item + G < items) raw.load(p, d_nxt, (int)((item + G) % H), rg, cg);
+        const int2 d_nn = item + 2 * G < items ? slot_desc(p, (item + 2 * G) / H) : make_int2(0, 0);
+        if (d.y > 0) prep_item<T, D>(p, sm, item / H, (int)(item % H), qf, kf, gf, vf, bt);
+        d_cur = d_nxt;
+        d_nxt = d_nn;
+    }
 }
 
 // Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks.
@@ -444,6 +530,27 @@ __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t* __restr
     if (t == 0) cf[n_seqs] = carry;
 }
 
+// Chunk-slot descriptors for packed sequences: desc[s] = (first token, length)
+// of chunk slot s (length 0 for slots past the last chunk).
+__global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restrict__ cu,
+                                                         int32_t n_seqs,
+                                                         const int32_t* __restrict__ cf,
+                                                         int64_t slots, int2* __restrict__ desc) {
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (s >= slots) return;
+    if (s >= cf[n_seqs]) {
+        desc[s] = make_int2(0, 0);
+        return;
+    }
+    int lo = 0, hi = n_seqs - 1;  // largest n with cf[n] <= s
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cf[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    const int64_t t0 = (int64_t)cu[lo] + 64 * (s - cf[lo]);
+    desc[s] = make_int2((int)t0, (int)min((int64_t)64, (int64_t)cu[lo + 1] - t0));
+}
+
 template <typename T, int D>
 hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     PrepParams p;
@@ -456,13 +563,22 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     p.L = a.layout;
+    int32_t* cf = reinterpret_cast<int32_t*>(a.workspace);
     hipLaunchKernelGGL((chunk_index_kernel), dim3(1), dim3(256), 0, stream, a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, reinterpret_cast<int32_t*>(a.workspace));
+                       a.n_seqs, a.total_tokens, cf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.total_tokens == 0) return hipSuccess;
-    hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)a.layout.slots, (unsigned)a.n_heads),
-                       dim3(256), 0, stream, p);
+    if (a.cu_seqlens) {
+        const unsigned nb = (unsigned)((a.layout.slots + 255) / 256);
+        hipLaunchKernelGGL((chunk_desc_kernel), dim3(nb), dim3(256), 0, stream, a.cu_seqlens,
+                           a.n_seqs, cf, a.layout.slots,
+                           reinterpret_cast<int2*>(a.workspace + a.layout.index_bytes));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t items = a.layout.slots * a.n_heads;
+    const int64_t grid = std::min<int64_t>(items, (int64_t)a.cu_count);
+    hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

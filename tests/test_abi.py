@@ -50,10 +50,13 @@ def test_status_strings(kda):
 def test_workspace_bytes(kda):
     d = kda.make_dims(8192, 1, 32, 128, 128, kda.KDA_BF16)
     ws = kda.kda_prefill_workspace_bytes(d)
-    # per (chunk slot, head): W, Qhat, U (64x128), Kprime^T (128x64), M (64x64) bf16 + 128 fp32
+    # chunk index (N+1 int32) and one (token, length) descriptor per chunk slot,
+    # each padded to 256 B, then per (chunk slot, head): W, Qhat, U (64x128),
+    # Kprime^T (128x64), M (64x64) bf16 and 128 fp32
     rec = (4 * 64 * 128 + 64 * 64) * 2 + 128 * 4
     slots = 8192 // 64 + 1
-    assert ws == 256 + rec * slots * 32
+    desc = -(-slots * 8 // 256) * 256
+    assert ws == 256 + desc + rec * slots * 32
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 128, 128, kda.KDA_FP32)) == 0
