@@ -111,6 +111,21 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+// DPP move within each 16-lane row (ctrl: quad_perm 0x00-0xff, row_ror:n = 0x120 + n).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of each DPP row, result in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x124>(x);  // row_ror:4
+    x += dpp<0x128>(x);  // row_ror:8
+    return x;
+}
+
 // Fragment-ordered storage ("A order"): a rows x kdim matrix stored as 16x32
 // tiles, each tile as 64 lanes x 8 elements in A-operand lane order, so one
 // wave loads a whole MFMA operand with one contiguous 16-byte (bf16) or

@@ -23,7 +23,9 @@ struct DecodeArgs {
 // Workspace for one prefill call: a chunk index (first chunk slot of each
 // sequence, int32 [N+1]), one descriptor per chunk slot (first token and
 // length, int32 x 2; length 0 marks an unused slot), then one record per
-// (chunk slot, head) with the factors the recurrence kernel consumes.  Record layout, E = element size
+// (chunk slot, head) with the factors the recurrence kernel consumes, stored head-major
+// (all chunk slots of head 0, then head 1, ...) so that one head's chain of
+// chunks is one contiguous stream.  Record layout, E = element size
 // of the I/O type, all matrices in MFMA fragment order:
 //   W    64 x D   (A order)   W = T Diag(beta) Khat
 //   Qh   64 x D   (A order)   Qhat = q * exp(gamma)

@@ -21,10 +21,10 @@
 // a non-positive number except on the diagonal blocks:
 //     E_r = e^(gamma_r - rho_{R-1}),  F_r = e^(rho_R - gamma_r)        (both <= 1)
 //     block (R, J<R):  e^(gamma_r - gamma_j) = E_r * e^(rho_{R-1} - rho_J) * F_j
-//     block (R, R):    e^(gamma_r - gamma_j) = (E_r / sqrt(D_R)) (F_j / sqrt(D_R)),  D_R = e^(rho_R - rho_{R-1})
+//     block (R, R):    e^(gamma_r - gamma_j) = (E_r / D_R) F_j,  D_R = e^(rho_R - rho_{R-1})
 // so the products run on MFMA from three decayed copies of q and k (E-, E- and
-// F-scaled).  On diagonal blocks the factors stay within e^(+-40) when every
-// g >= -5, the documented accuracy range.
+// F-scaled).  On diagonal blocks 1/D_R stays below e^80 (and F_j above e^-80)
+// when every g >= -5, the documented accuracy range.
 //
 // Work split: a persistent grid (one workgroup per CU) walks the (chunk slot,
 // head) items; each workgroup loads the next item's raw rows while it computes
@@ -36,7 +36,7 @@
 //      the wave); block totals through LDS, then a per-channel table of every
 //      block-level decay factor (16 x d_k exponentials per chunk);
 //   P1 element decay factors; E/F-scaled tiles to LDS; Qhat, Kprime^T, Gamma_C out;
-//   P2 A and M blocks on MFMA (A row block w, M row block 3-w per wave);
+//   P2 A and M blocks on MFMA (row block w of both per wave);
 //   P3 T = (I + A)^-1: the four 16x16 diagonal inverses by forward substitution
 //      (one lane per column), then block rows 1..3 by T_RJ = -T_RR sum_K A_RK T_KJ
 //      on fp32 MFMA;
@@ -83,7 +83,7 @@ struct PrepSmem {
     float A[64][68];          // beta-scaled strictly-lower A (16-byte aligned rows)
     T M[64][64 + P];          // inclusive-lower Q K decay products
     float tau[4][D];          // per-block total log-decay
-    // per-channel decay factors, rows: 0-3 e^(-tau_R/2); 4 e^(tau_1); 5 e^(tau_1+tau_2);
+    // per-channel decay factors, rows: 0-3 e^(-tau_R); 4 e^(tau_1); 5 e^(tau_1+tau_2);
     // 6 e^(tau_2); 7-10 e^(rho_{R-1}) (chunk start -> block R start); 11-14
     // e^(rho_3 - rho_R) (block R end -> chunk end); 15 e^(rho_3) = Gamma_C
     float fac[16][D];
@@ -107,51 +107,61 @@ struct PrepSmem {
     } u;
 };
 
-// One 16x16 block (R, J) of A (IS_A: rows from KE, beta-scaled, strictly lower)
-// or of M (rows from QE, inclusive lower), from the decayed tiles in LDS.
-template <typename T, int D, bool IS_A>
-__device__ __forceinline__ void decay_block(PrepSmem<T, D>& sm, int R, int J, int lane) {
+// Row block R of A (beta-scaled, strictly lower) and of M (inclusive lower):
+// for every column block J <= R the K-side operand (KF rows of block J) is
+// loaded once and feeds both products, so each wave runs two independent MFMA
+// chains; blocks J > R are zero.
+template <typename T, int D>
+__device__ __forceinline__ void decay_row_block(PrepSmem<T, D>& sm, int R, int lane) {
     constexpr int NKS = D / 32;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (J <= R) {
+    Frag<T> ke[NKS], qe[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = 32 * ks + 8 * (lane >> 4);
-            Frag<T> a = load_frag<T>(IS_A ? &sm.u.a.KE[16 * R + (lane & 15)][c0]
-                                          : &sm.u.a.QE[16 * R + (lane & 15)][c0]);
-            Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
-            if (J == R) {
-                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0]);
-                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0 + 4]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float f = j < 4 ? f0[j] : f1[j - 4];
-                    a.v[j] = from_f32<T>(to_f32(a.v[j]) * f);
-                    b.v[j] = from_f32<T>(to_f32(b.v[j]) * f);
-                }
-            } else if (J < R - 1) {
-                const int row = (R == 2) ? 4 : 5 + J;  // e^(rho_{R-1} - rho_J)
-                const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0]);
-                const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0 + 4]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    b.v[j] = from_f32<T>(to_f32(b.v[j]) * (j < 4 ? f0[j] : f1[j - 4]));
-            }
-            mma(acc, a, b);
-        }
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * (lane >> 4);
+        ke[ks] = load_frag<T>(&sm.u.a.KE[16 * R + (lane & 15)][c0]);
+        qe[ks] = load_frag<T>(&sm.u.a.QE[16 * R + (lane & 15)][c0]);
     }
-    const int col = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int row = 4 * (lane >> 4) + e;
-        float val = acc[e];
-        if (IS_A) {
-            val *= sm.beta[16 * R + row];
-            if (J > R || (J == R && col >= row)) val = 0.f;
-            sm.A[16 * R + row][16 * J + col] = val;
-        } else {
-            if (J > R || (J == R && col > row)) val = 0.f;
-            sm.M[16 * R + row][16 * J + col] = from_f32<T>(val);
+    for (int J = 0; J < 4; ++J) {
+        f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_m = {0.f, 0.f, 0.f, 0.f};
+        if (J <= R) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int c0 = 32 * ks + 8 * (lane >> 4);
+                Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
+                Frag<T> a = ke[ks], q = qe[ks];
+                if (J == R) {
+                    // diagonal block: e^(gamma_r - gamma_j) = E_r F_j / D_R, on the row side
+                    const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0]);
+                    const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0 + 4]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float f = j < 4 ? f0[j] : f1[j - 4];
+                        a.v[j] = from_f32<T>(to_f32(a.v[j]) * f);
+                        q.v[j] = from_f32<T>(to_f32(q.v[j]) * f);
+                    }
+                } else if (J < R - 1) {
+                    const int row = (R == 2) ? 4 : 5 + J;  // e^(rho_{R-1} - rho_J)
+                    const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0]);
+                    const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0 + 4]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        b.v[j] = from_f32<T>(to_f32(b.v[j]) * (j < 4 ? f0[j] : f1[j - 4]));
+                }
+                mma(acc_a, a, b);
+                mma(acc_m, q, b);
+            }
+        }
+        const int col = lane & 15;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 4 * (lane >> 4) + e;
+            float va = acc_a[e] * sm.beta[16 * R + row];
+            float vm = acc_m[e];
+            if (J > R || (J == R && col >= row)) va = 0.f;
+            if (J > R || (J == R && col > row)) vm = 0.f;
+            sm.A[16 * R + row][16 * J + col] = va;
+            sm.M[16 * R + row][16 * J + col] = from_f32<T>(vm);
         }
     }
 }
@@ -188,24 +198,21 @@ struct RawRows {
     V q[4], k[4], g[4], v[4];
     T b[4];
 
+    // Rows past the chunk's length are loaded from its first row (always a
+    // valid token) and zeroed by the caller, so the loads are never predicated
+    // and the compiler can keep the next item's rows in flight.
     __device__ __forceinline__ void load(const PrepParams& p, int2 d, int h, int rg, int cg) {
         const int64_t H = p.n_heads;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
-            if (r < d.y) {
-                const int64_t row = (int64_t)d.x + r;
-                const int64_t off = (row * H + h) * D + CPT * cg;
-                q[i] = *reinterpret_cast<const V*>((const T*)p.q + off);
-                k[i] = *reinterpret_cast<const V*>((const T*)p.k + off);
-                g[i] = *reinterpret_cast<const V*>((const T*)p.g + off);
-                v[i] = *reinterpret_cast<const V*>((const T*)p.v + off);
-                b[i] = ((const T*)p.beta)[row * H + h];
-            } else {
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) q[i][c] = k[i][c] = g[i][c] = v[i][c] = from_f32<T>(0.f);
-                b[i] = from_f32<T>(0.f);
-            }
+            const int64_t row = (int64_t)d.x + (r < d.y ? r : 0);
+            const int64_t off = (row * H + h) * D + CPT * cg;
+            q[i] = *reinterpret_cast<const V*>((const T*)p.q + off);
+            k[i] = *reinterpret_cast<const V*>((const T*)p.k + off);
+            g[i] = *reinterpret_cast<const V*>((const T*)p.g + off);
+            v[i] = *reinterpret_cast<const V*>((const T*)p.v + off);
+            b[i] = ((const T*)p.beta)[row * H + h];
         }
     }
 };
@@ -222,8 +229,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     constexpr int NKS = D / 32;  // 32-deep k-steps over the channels
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int rg = t >> 4, cg = t & 15, grp = lane >> 4;
-    const int64_t H = p.n_heads;
-    unsigned char* rec = p.ws + p.L.records_offset() + (size_t)(slot * H + h) * p.L.rec_bytes;
+    unsigned char* rec = p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot) * p.L.rec_bytes;
 
     // ---------------------------------------------------------------- P0
 #pragma unroll
@@ -238,11 +244,8 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
             sq += qf[i][c] * qf[i][c];
             sk += kf[i][c] * kf[i][c];
         }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-            sq += xor_shfl(sq, m);
-            sk += xor_shfl(sk, m);
-        }
+        sq = row16_sum(sq);
+        sk = row16_sum(sk);
         const float rq = (p.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f) * p.scale;
         const float rk = p.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
 #pragma unroll
@@ -271,32 +274,25 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         if (grp == 0) sm.tau[w][CPT * cg + c] = tau;
     }
     __syncthreads();
-    // per-channel table of the block-level decay factors (16 x D exponentials)
-    for (int e = t; e < 16 * D; e += 256) {
-        const int row = e / D, c = e % D;
+    // per-channel table of the block-level decay factors (16 x D exponentials):
+    // thread t owns channel t % D and rows t / D + (256 / D) * i
+    {
+        constexpr int RSTEP = 256 / D;
+        const int c = t % D, r0 = t / D;
         const float t0 = sm.tau[0][c], t1 = sm.tau[1][c], t2 = sm.tau[2][c], t3 = sm.tau[3][c];
-        const float tv[4] = {t0, t1, t2, t3};
-        float x;
-        if (row < 4) {
-            x = -0.5f * tv[row];
-        } else if (row == 4) {
-            x = t1;
-        } else if (row == 5) {
-            x = t1 + t2;
-        } else if (row == 6) {
-            x = t2;
-        } else if (row < 11) {
-            const int R = row - 7;
-            x = 0.f;
-            for (int m = 0; m < R; ++m) x += tv[m];
-        } else if (row < 15) {
-            const int R = row - 11;
-            x = 0.f;
-            for (int m = R + 1; m < 4; ++m) x += tv[m];
-        } else {
-            x = ((t0 + t1) + t2) + t3;
+        const float x[16] = {-t0, -t1, -t2, -t3,
+                             t1, t1 + t2, t2,
+                             0.f, t0, t0 + t1, (t0 + t1) + t2,
+                             (t1 + t2) + t3, t2 + t3, t3, 0.f,
+                             ((t0 + t1) + t2) + t3};
+#pragma unroll
+        for (int i = 0; i < 16 / RSTEP; ++i) {
+            const int row = r0 + RSTEP * i;
+            float v = x[0];
+#pragma unroll
+            for (int k = 1; k < 16; ++k) v = (row == k) ? x[k] : v;
+            sm.fac[row][c] = __expf(v);
         }
-        sm.fac[row][c] = __expf(x);
     }
     __syncthreads();
 
@@ -343,22 +339,47 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     __syncthreads();
 
     // ---------------------------------------------------------------- P2
-    for (int J = 0; J < 4; ++J) decay_block<T, D, true>(sm, w, J, lane);
-    for (int J = 0; J < 4; ++J) decay_block<T, D, false>(sm, 3 - w, J, lane);
+    decay_row_block<T, D>(sm, w, lane);
     __syncthreads();
 
     // ---------------------------------------------------------------- P3
-    // transposed beta*Khat and beta*V tiles (the B operands of W and U)
+    // transposed beta*Khat and beta*V tiles (the B operands of W and U).  Lane
+    // (rg, cg) holds 4 tokens x CPT channels; at write step j it stores channel
+    // (j + cg) % CPT, so the 16 lanes of a token group spread over the banks
+    // (a plain channel order puts them on two bank positions).  The rotation is
+    // a barrel shift of packed token quadruples across the channel index.
+    {
+        typedef T V4 __attribute__((ext_vector_type(4)));
+        V4 rk[CPT], rv[CPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        float xk[4], xv[4];
+        for (int c = 0; c < CPT; ++c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xk[i] = bK[i][c];
-            xv[i] = bV[i][c];
+            for (int i = 0; i < 4; ++i) {
+                rk[c][i] = from_f32<T>(bK[i][c]);
+                rv[c][i] = from_f32<T>(bV[i][c]);
+            }
         }
-        store_n<T, 4>(&sm.u.b.BK[CPT * cg + c][4 * rg], xk);
-        store_n<T, 4>(&sm.u.b.BV[CPT * cg + c][4 * rg], xv);
+#pragma unroll
+        for (int sh = 1; sh < CPT; sh <<= 1) {
+            const bool on = (cg & sh) != 0;
+            V4 tk[CPT], tv[CPT];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                tk[j] = on ? rk[(j + sh) % CPT] : rk[j];
+                tv[j] = on ? rv[(j + sh) % CPT] : rv[j];
+            }
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                rk[j] = tk[j];
+                rv[j] = tv[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = CPT * cg + ((j + cg) % CPT);
+            *reinterpret_cast<V4*>(&sm.u.b.BK[c][4 * rg]) = rk[j];
+            *reinterpret_cast<V4*>(&sm.u.b.BV[c][4 * rg]) = rv[j];
+        }
     }
     if (w == 0) {
         // diagonal 16x16 blocks of (I + A)^-1: lane = (block, column), forward
@@ -404,9 +425,20 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         }
         __syncthreads();
     }
-    for (int idx = t; idx < 64 * 64; idx += 256) {
-        const int r = idx >> 6, c = idx & 63;
-        sm.u.b.Tb[r][c] = from_f32<T>(c <= r ? sm.u.b.Tf[r][c] : 0.f);
+    {
+        // thread t converts row t / 4, columns 16 * (t % 4) .. +15 (zero above the diagonal)
+        const int r = t >> 2, c0 = 16 * (t & 3);
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (c0 + j <= r) ? sm.u.b.Tf[r][c0 + j] : 0.f;
+        float lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo[j] = x[j];
+            hi[j] = x[8 + j];
+        }
+        store_frag<T>(&sm.u.b.Tb[r][c0], make_frag<T>(lo));
+        store_frag<T>(&sm.u.b.Tb[r][c0 + 8], make_frag<T>(hi));
     }
     __syncthreads();
 
@@ -471,31 +503,56 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     const int64_t G = gridDim.x;
     int64_t item = blockIdx.x;
     if (item >= items) return;
+    // (slot, head) of item, item + G, item + 2G, stepped without 64-bit divisions
+    const int gh = (int)(G % H);
+    const int64_t gs = G / H;
+    auto advance = [&](int64_t& s, int& hh) {
+        s += gs;
+        hh += gh;
+        if (hh >= H) {
+            hh -= (int)H;
+            s += 1;
+        }
+    };
+    int64_t s0 = item / H;
+    int h0 = (int)(item % H);
+    int64_t s1 = s0, s2;
+    int h1 = h0, h2;
+    advance(s1, h1);
+    s2 = s1;
+    h2 = h1;
+    advance(s2, h2);
 
     RawRows<T, D> raw;
-    int2 d_cur = slot_desc(p, item / H);
-    int2 d_nxt = item + G < items ? slot_desc(p, (item + G) / H) : make_int2(0, 0);
-    raw.load(p, d_cur, (int)(item % H), rg, cg);
+    int2 d_cur = slot_desc(p, s0);
+    int2 d_nxt = item + G < items ? slot_desc(p, s1) : make_int2(0, 0);
+    raw.load(p, d_cur, h0, rg, cg);
     for (; item < items; item += G) {
         const int2 d = d_cur;
         float qf[4][CPT], kf[4][CPT], gf[4][CPT], vf[4][CPT], bt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const bool ok = 4 * rg + i < d.y;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                qf[i][c] = to_f32(raw.q[i][c]);
-                kf[i][c] = to_f32(raw.k[i][c]);
-                gf[i][c] = to_f32(raw.g[i][c]);
-                vf[i][c] = to_f32(raw.v[i][c]);
+                qf[i][c] = ok ? to_f32(raw.q[i][c]) : 0.f;
+                kf[i][c] = ok ? to_f32(raw.k[i][c]) : 0.f;
+                gf[i][c] = ok ? to_f32(raw.g[i][c]) : 0.f;
+                vf[i][c] = ok ? to_f32(raw.v[i][c]) : 0.f;
             }
-            bt[i] = to_f32(raw.b[i]);
+            bt[i] = ok ? to_f32(raw.b[i]) : 0.f;
         }
-        // next item's rows go in flight now; the descriptor after it one step earlier
-        if (item + G < items) raw.load(p, d_nxt, (int)((item + G) % H), rg, cg);
-        const int2 d_nn = item + 2 * G < items ? slot_desc(p, (item + 2 * G) / H) : make_int2(0, 0);
-        if (d.y > 0) prep_item<T, D>(p, sm, item / H, (int)(item % H), qf, kf, gf, vf, bt);
+        // next item's rows go in flight now (past the last item: the current one
+        // again, never used); the descriptor after it one step earlier
+        const bool more = item + G < items;
+        raw.load(p, more ? d_nxt : d, more ? h1 : h0, rg, cg);
+        const int2 d_nn = item + 2 * G < items ? slot_desc(p, s2) : make_int2(0, 0);
+        if (d.y > 0) prep_item<T, D>(p, sm, s0, h0, qf, kf, gf, vf, bt);
         d_cur = d_nxt;
         d_nxt = d_nn;
+        s0 = s1; h0 = h1;
+        s1 = s2; h1 = h2;
+        advance(s2, h2);
     }
 }
 

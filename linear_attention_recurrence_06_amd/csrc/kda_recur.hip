@@ -31,8 +31,16 @@ namespace kda {
 template <typename T, int D, int NT>
 struct RecurSmem {
     static constexpr int P = 16 / sizeof(T);
+    static constexpr int E = sizeof(T);
+    static constexpr int NB = NT / 16;
+    // one chunk's operands, laid out as in the workspace record:
+    // W | Qhat | M | Kprime^T (contiguous), this tile's U, Gamma_C
+    static constexpr int CORE = (192 * D + 64 * 64) * E;
+    static constexpr int UBYTES = 4 * NB * 256 * E;
+    static constexpr int SLOT = CORE + UBYTES + D * 4;
     T ST[NT][D + P];   // S tile, transposed: [value column][key row]
     T UT[NT][64 + P];  // u tile, transposed: [value column][token]
+    alignas(16) unsigned char slot[2][SLOT];
 };
 
 struct RecurParams {
@@ -46,49 +54,51 @@ struct RecurParams {
     PrefillLayout L;
 };
 
-// One chunk's operands for one wave: token block w (16 tokens) for u and O,
-// key rows 64/4*w.. (D/4 rows) for the state update.
+// Loader side: one chunk's operands staged in the loader waves' registers
+// (16-byte vectors; every loader thread always issues the same loads, so the
+// compiler can count outstanding loads exactly).
 template <typename T, int D, int NT>
-struct ChunkOperands {
-    static constexpr int NKS = D / 32;
-    static constexpr int NB = NT / 16;
-    static constexpr int RBW = D / 64;
-    typedef T V4 __attribute__((ext_vector_type(4)));
-    Frag<T> W[NKS];      // W rows of token block w
-    Frag<T> Q[NKS];      // Qhat rows of token block w
-    Frag<T> Mf[2];       // M rows of token block w
-    Frag<T> Kt[RBW][2];  // Kprime^T rows owned by this wave
-    V4 U[NB];            // U, token block w, this tile's columns (accumulator layout)
-    f32x4 gC[RBW];       // Gamma_C for this wave's key rows
+struct Staging {
+    typedef RecurSmem<T, D, NT> SM;
+    static constexpr int NCORE = SM::CORE / 16 / 256;
+    static constexpr int NU = SM::UBYTES / 16;        // U vectors (this tile)
+    static constexpr int NG = D / 4;                   // Gamma_C vectors
+    static constexpr int NX = (NU + NG + 255) / 256;   // extra vectors per loader
+    static_assert(NCORE * 16 * 256 == SM::CORE, "core must split evenly over 256 loaders");
+    u32x4 core[NCORE];
+    u32x4 extra[NX];
 
-    __device__ __forceinline__ void load(const unsigned char* rec, const PrefillLayout& L, int w,
-                                         int lane, int col0) {
-        const T* Wg = reinterpret_cast<const T*>(rec + L.off_w);
-        const T* Qg = reinterpret_cast<const T*>(rec + L.off_q);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            W[ks] = load_frag<T>(Wg + ((int64_t)(w * NKS + ks) * kWave + lane) * 8);
-            Q[ks] = load_frag<T>(Qg + ((int64_t)(w * NKS + ks) * kWave + lane) * 8);
+    // source / destination byte offsets of extra vector x (index x < NU + NG)
+    __device__ __forceinline__ static void extra_offsets(const PrefillLayout& L, int x, int tile,
+                                                         int& src, int& dst) {
+        constexpr int E = SM::E;
+        constexpr int NB = SM::NB;
+        constexpr int per_rb = NB * 256 * E / 16;  // vectors of one 16-row block of this tile's U
+        if (x < NU) {
+            const int rb = x / per_rb, v = x % per_rb;
+            src = (int)L.off_u + ((rb * (D / 16) + tile * NB) * 256) * E + v * 16;
+            dst = SM::CORE + rb * NB * 256 * E + v * 16;
+        } else {
+            const int v = min(x - NU, NG - 1);
+            src = (int)L.off_gc + v * 16;
+            dst = SM::CORE + SM::UBYTES + v * 16;
         }
-        const T* Mg = reinterpret_cast<const T*>(rec + L.off_m);
+    }
+    __device__ __forceinline__ void load(const unsigned char* rec, int lt, const int (&src)[NX]) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            Mf[ks] = load_frag<T>(Mg + ((int64_t)(w * 2 + ks) * kWave + lane) * 8);
-        const T* Kg = reinterpret_cast<const T*>(rec + L.off_kt);
+        for (int i = 0; i < NCORE; ++i)
+            core[i] = *reinterpret_cast<const u32x4*>(rec + (size_t)(i * 256 + lt) * 16);
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
+        for (int i = 0; i < NX; ++i) extra[i] = *reinterpret_cast<const u32x4*>(rec + src[i]);
+    }
+    __device__ __forceinline__ void store(unsigned char* slot, int lt, const int (&dst)[NX],
+                                          const bool (&has)[NX]) const {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                Kt[rb][ks] = load_frag<T>(Kg + ((int64_t)((RBW * w + rb) * 2 + ks) * kWave + lane) * 8);
-        const T* Ug = reinterpret_cast<const T*>(rec + L.off_u);
+        for (int i = 0; i < NCORE; ++i)
+            *reinterpret_cast<u32x4*>(slot + (i * 256 + lt) * 16) = core[i];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            U[nb] = *reinterpret_cast<const V4*>(
-                Ug + corder_index(16 * w + 4 * (lane >> 4), col0 + 16 * nb + (lane & 15), D));
-        const float* gcg = reinterpret_cast<const float*>(rec + L.off_gc);
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-            gC[rb] = *reinterpret_cast<const f32x4*>(gcg + 16 * (RBW * w + rb) + 4 * (lane >> 4));
+        for (int i = 0; i < NX; ++i)
+            if (has[i]) *reinterpret_cast<u32x4*>(slot + dst[i]) = extra[i];
     }
 };
 
@@ -109,16 +119,26 @@ __device__ __forceinline__ void put_state(RecurSmem<T, D, NT>& sm,
         }
 }
 
-// One chunk: u = U - W S, O = Qhat S + M u, S <- Diag(Gamma_C) S + Kprime^T u.
+// One chunk for compute wave w (token block w; key rows D/4*w..):
+// u = U - W S, O = Qhat S + M u, S <- Diag(Gamma_C) S + Kprime^T u,
+// with every operand read from the chunk's LDS slot.
 template <typename T, int D, int NT>
 __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[D / 64][NT / 16],
-                                           const ChunkOperands<T, D, NT>& c, T* outp,
-                                           int64_t tok0, int Lc, int64_t H, int h, int col0,
-                                           int w, int lane) {
+                                           const unsigned char* slot, T* outp, int64_t tok0,
+                                           int Lc, int64_t H, int h, int col0, int w, int lane) {
+    typedef RecurSmem<T, D, NT> SM;
     constexpr int NKS = D / 32;
     constexpr int NB = NT / 16;
     constexpr int RBW = D / 64;
+    constexpr int E = SM::E;
     typedef T V4 __attribute__((ext_vector_type(4)));
+    const T* Wl = reinterpret_cast<const T*>(slot);
+    const T* Ql = reinterpret_cast<const T*>(slot + 64 * D * E);
+    const T* Ml = reinterpret_cast<const T*>(slot + 128 * D * E);
+    const T* Kl = reinterpret_cast<const T*>(slot + (128 * D + 64 * 64) * E);
+    const T* Ul = reinterpret_cast<const T*>(slot + SM::CORE);
+    const float* Gl = reinterpret_cast<const float*>(slot + SM::CORE + SM::UBYTES);
+
     Frag<T> Sb[NKS][NB];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -126,19 +146,28 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[D
         for (int nb = 0; nb < NB; ++nb)
             Sb[ks][nb] = load_frag<T>(&sm.ST[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
     f32x4 accO[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        f32x4 au = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+    {
+        Frag<T> Wf[NKS], Qf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            mma(au, c.W[ks], Sb[ks][nb]);
-            mma(ao, c.Q[ks], Sb[ks][nb]);
+            Wf[ks] = load_frag<T>(Wl + ((w * NKS + ks) * kWave + lane) * 8);
+            Qf[ks] = load_frag<T>(Ql + ((w * NKS + ks) * kWave + lane) * 8);
         }
-        accO[nb] = ao;
-        V4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(to_f32(c.U[nb][e]) - au[e]);
-        *reinterpret_cast<V4*>(&sm.UT[16 * nb + (lane & 15)][16 * w + 4 * (lane >> 4)]) = x;
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4 au = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                mma(au, Wf[ks], Sb[ks][nb]);
+                mma(ao, Qf[ks], Sb[ks][nb]);
+            }
+            accO[nb] = ao;
+            const V4 U = *reinterpret_cast<const V4*>(Ul + ((w * NB + nb) * kWave + lane) * 4);
+            V4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(to_f32(U[e]) - au[e]);
+            *reinterpret_cast<V4*>(&sm.UT[16 * nb + (lane & 15)][16 * w + 4 * (lane >> 4)]) = x;
+        }
     }
     __syncthreads();
     Frag<T> Ub[2][NB];
@@ -148,17 +177,23 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[D
         for (int nb = 0; nb < NB; ++nb)
             Ub[ks][nb] = load_frag<T>(&sm.UT[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+    for (int rb = 0; rb < RBW; ++rb) {
+        const Frag<T> k0 = load_frag<T>(Kl + (((RBW * w + rb) * 2 + 0) * kWave + lane) * 8);
+        const Frag<T> k1 = load_frag<T>(Kl + (((RBW * w + rb) * 2 + 1) * kWave + lane) * 8);
+        const f32x4 g = *reinterpret_cast<const f32x4*>(Gl + 16 * (RBW * w + rb) + 4 * (lane >> 4));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            S[rb][nb] *= c.gC[rb];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) mma(S[rb][nb], c.Kt[rb][ks], Ub[ks][nb]);
+            S[rb][nb] *= g;
+            mma(S[rb][nb], k0, Ub[0][nb]);
+            mma(S[rb][nb], k1, Ub[1][nb]);
         }
+    }
+    const Frag<T> m0 = load_frag<T>(Ml + ((w * 2 + 0) * kWave + lane) * 8);
+    const Frag<T> m1 = load_frag<T>(Ml + ((w * 2 + 1) * kWave + lane) * 8);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) mma(accO[nb], c.Mf[ks], Ub[ks][nb]);
+        mma(accO[nb], m0, Ub[0][nb]);
+        mma(accO[nb], m1, Ub[1][nb]);
         const int col = col0 + 16 * nb + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -170,8 +205,12 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[D
     __syncthreads();
 }
 
+// 512 threads: waves 0-3 compute, waves 4-7 load.  Both sides pass the same
+// 1 + 2 * nch barriers.  Chunk kc's operands sit in LDS slot kc % 2; the
+// loaders write slot (kc+1) % 2 while the compute waves work on chunk kc, and
+// keep chunks kc+2 and kc+3 in flight in their registers.
 template <typename T, int D, int NT>
-__global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
+__global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     constexpr int NB = NT / 16;
     constexpr int RBW = D / 64;
     __shared__ RecurSmem<T, D, NT> sm;
@@ -190,8 +229,50 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
     const int64_t slot0 = cf[n];
     const int64_t nch = (s_len + 63) / 64;
     const int col0 = tile * NT;
+    const int64_t last = nch > 0 ? nch - 1 : 0;
+    const unsigned char* rec0 =
+        p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot0) * p.L.rec_bytes;
+    auto rec = [&](int64_t kc) { return rec0 + (size_t)min(kc, last) * p.L.rec_bytes; };
 
-    // initial state slice -> registers (fp32) and LDS (operand copy)
+    if (w >= 4) {
+        // ------------------------------------------------------------ loaders
+        typedef Staging<T, D, NT> ST_;
+        const int lt = t - 256;
+        int src_x[ST_::NX], dst_x[ST_::NX];
+        bool has_x[ST_::NX];
+#pragma unroll
+        for (int i = 0; i < ST_::NX; ++i) {
+            const int x = lt + 256 * i;
+            has_x[i] = x < ST_::NU + ST_::NG;
+            ST_::extra_offsets(p.L, has_x[i] ? x : ST_::NU, tile, src_x[i], dst_x[i]);
+        }
+        ST_ s0, s1;
+        if (nch > 0) {
+            s0.load(rec(0), lt, src_x);
+            s0.store(sm.slot[0], lt, dst_x, has_x);
+            s1.load(rec(1), lt, src_x);
+            s0.load(rec(2), lt, src_x);
+        }
+        __syncthreads();
+        int64_t kc = 0;
+        for (; kc + 2 <= nch; kc += 2) {
+            s1.store(sm.slot[1], lt, dst_x, has_x);  // chunk kc+1
+            s1.load(rec(kc + 3), lt, src_x);
+            __syncthreads();
+            __syncthreads();
+            s0.store(sm.slot[0], lt, dst_x, has_x);  // chunk kc+2
+            s0.load(rec(kc + 4), lt, src_x);
+            __syncthreads();
+            __syncthreads();
+        }
+        if (kc < nch) {
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- compute
     f32x4 S[RBW][NB];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 #pragma unroll
@@ -206,31 +287,11 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
             }
         }
     put_state<T, D, NT>(sm, S, w, lane);
-
-    const size_t rec_stride = p.L.rec_bytes * (size_t)H;
-    const unsigned char* rec0 =
-        p.ws + p.L.records_offset() + (size_t)(slot0 * H + h) * p.L.rec_bytes;
-    T* outp = reinterpret_cast<T*>(p.out);
-    // three operand buffers in rotation: chunk kc's operands are requested at
-    // the start of chunk kc-2, so two chunks of compute cover their latency
-    ChunkOperands<T, D, NT> b0, b1, b2;
-    if (nch > 0) b0.load(rec0, p.L, w, lane, col0);
-    if (nch > 1) b1.load(rec0 + rec_stride, p.L, w, lane, col0);
     __syncthreads();
-    auto tok = [&](int64_t kc) { return s_begin + 64 * kc; };
-    auto len = [&](int64_t kc) { return (int)min((int64_t)64, s_len - 64 * kc); };
-    for (int64_t kc = 0; kc < nch; kc += 3) {
-        if (kc + 2 < nch) b2.load(rec0 + (size_t)(kc + 2) * rec_stride, p.L, w, lane, col0);
-        recur_step<T, D, NT>(sm, S, b0, outp, tok(kc), len(kc), H, h, col0, w, lane);
-        if (kc + 1 < nch) {
-            if (kc + 3 < nch) b0.load(rec0 + (size_t)(kc + 3) * rec_stride, p.L, w, lane, col0);
-            recur_step<T, D, NT>(sm, S, b1, outp, tok(kc + 1), len(kc + 1), H, h, col0, w, lane);
-        }
-        if (kc + 2 < nch) {
-            if (kc + 4 < nch) b1.load(rec0 + (size_t)(kc + 4) * rec_stride, p.L, w, lane, col0);
-            recur_step<T, D, NT>(sm, S, b2, outp, tok(kc + 2), len(kc + 2), H, h, col0, w, lane);
-        }
-    }
+    T* outp = reinterpret_cast<T*>(p.out);
+    for (int64_t kc = 0; kc < nch; ++kc)
+        recur_step<T, D, NT>(sm, S, sm.slot[kc & 1], outp, s_begin + 64 * kc,
+                             (int)min((int64_t)64, s_len - 64 * kc), H, h, col0, w, lane);
 
     if (p.fin) {
 #pragma unroll
@@ -249,8 +310,8 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
 
 // Column-tile width: the widest tile that still gives at least ~2 workgroups
 // per CU; 16 otherwise (fewest columns per chain, most chains).
-static int pick_tile(int64_t chains, int d) {
-    if (chains * (d / 32) >= 512) return 32;
+static int pick_tile(int64_t chains, int d, bool wide_ok) {
+    if (wide_ok && chains * (d / 32) >= 512) return 32;
     return 16;
 }
 
@@ -270,7 +331,7 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t groups = (chains + 7) / 8;
     const int64_t grid = 8 * p.ntiles * groups;
-    hipLaunchKernelGGL((recur_kernel<T, D, NT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((recur_kernel<T, D, NT>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -278,7 +339,9 @@ template <typename T, int D>
 hipError_t launch_recur(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     if (chains == 0) return hipSuccess;
-    if (pick_tile(chains, D) == 32) return launch_nt<T, D, 32>(a, stream);
+    // fp32 operands fill LDS at 16 columns already
+    if constexpr (sizeof(T) == 2)
+        if (pick_tile(chains, D, true) == 32) return launch_nt<T, D, 32>(a, stream);
     return launch_nt<T, D, 16>(a, stream);
 }
 
