@@ -1,0 +1,255 @@
+"""GPU properties of the HIP path that hold at any size, and option coverage.
+
+* determinism: the same call twice gives the same bytes;
+* a NULL initial state is the zero state, bit for bit;
+* final_state may alias initial_state (in-place resume) with the same result;
+* splitting a sequence at a chunk boundary and resuming from the final state
+  reproduces the unsplit run bit for bit (the chunk partition is the same); a
+  split inside a chunk agrees within the parity tolerance;
+* the prefill of T tokens and T decode steps agree (two independent kernels);
+* a non-finite value in one sequence leaves every other sequence untouched;
+* scale != 1 and qk_l2norm = 0, odd head counts, many short sequences, against
+  the fp64 oracle.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def maxerr(a, b):
+    a = np.asarray(a, np.float64)
+    return float(np.max(np.abs(a - np.asarray(b, np.float64)))) if a.size else 0.0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_recurrence_06_amd as kda
+    kda.load_library()
+    return kda
+
+
+def prefill(lib, inp, **kw):
+    out, fin = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     inp.get("initial_state"), inp.get("cu_seqlens"),
+                                     num_seqs=len(inp["lens"]), **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def oracle_prefill(oracle, inp, **kw):
+    s0 = inp.get("initial_state")
+    cu = inp.get("cu_seqlens")
+    return oracle.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]),
+                          host(inp["beta"]), cu_seqlens=None if cu is None else cu.cpu().numpy(),
+                          initial_state=None if s0 is None else host(s0),
+                          n_seqs=len(inp["lens"]), **kw)
+
+
+def slice_tokens(inp, t0, t1, s0):
+    """One sequence made of tokens [t0, t1) of a single-sequence batch."""
+    return dict(q=inp["q"][t0:t1].contiguous(), k=inp["k"][t0:t1].contiguous(),
+                v=inp["v"][t0:t1].contiguous(), g=inp["g"][t0:t1].contiguous(),
+                beta=inp["beta"][t0:t1].contiguous(), initial_state=s0, cu_seqlens=None,
+                lens=[t1 - t0])
+
+
+# ----------------------------------------------------------------------------- bitwise properties
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_prefill_deterministic(lib, io, d):
+    from kda_inputs import make_prefill
+    say(f"determinism io={io} d={d}")
+    inp = make_prefill([1000, 700, 64, 3], 4, d, io, g_scale=0.5, s0_std=0.02, seed=31,
+                       device="cuda")
+    o1, f1 = prefill(lib, inp)
+    o2, f2 = prefill(lib, inp)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_decode_deterministic(lib):
+    from kda_inputs import make_decode
+    w = make_decode(7, 5, 128, "bf16", steps=2, seed=32, device="cuda")
+    outs = []
+    for _ in range(2):
+        st = w["state"].clone()
+        o = [lib.kda_decode_step(w["q"][s], w["k"][s], w["v"][s], w["g"][s], w["beta"][s], st)
+             for s in range(2)]
+        torch.cuda.synchronize()
+        outs.append((torch.stack(o), st))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_null_initial_state_is_zero_state(lib):
+    from kda_inputs import make_prefill
+    inp = make_prefill([300, 65], 3, 128, "bf16", g_scale=0.5, s0_std=None, seed=33,
+                       device="cuda")
+    assert inp["initial_state"] is None
+    o_null, f_null = prefill(lib, inp)
+    inp["initial_state"] = torch.zeros(2, 3, 128, 128, device="cuda")
+    o_zero, f_zero = prefill(lib, inp)
+    assert torch.equal(o_null, o_zero) and torch.equal(f_null, f_zero)
+
+
+def test_final_state_may_alias_initial_state(lib):
+    from kda_inputs import make_prefill
+    inp = make_prefill([257, 64, 1], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=34,
+                       device="cuda")
+    o_ref, f_ref = prefill(lib, inp)
+    st = inp["initial_state"].clone()
+    inp["initial_state"] = st
+    o, f = prefill(lib, inp, final_state=st)
+    assert f.data_ptr() == st.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(st, f_ref)
+
+
+def test_split_at_chunk_boundary_is_exact(lib):
+    """Tokens [0, 128) then [128, 300) resumed from the first part's final
+    state equal one pass over [0, 300), bit for bit."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([300], 4, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=35, device="cuda")
+    o_full, f_full = prefill(lib, inp)
+    a = slice_tokens(inp, 0, 128, inp["initial_state"])
+    o_a, f_a = prefill(lib, a)
+    b = slice_tokens(inp, 128, 300, f_a)
+    o_b, f_b = prefill(lib, b)
+    assert torch.equal(torch.cat([o_a, o_b]), o_full)
+    assert torch.equal(f_b, f_full)
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_split_inside_chunk_resumes(lib, oracle, io, d):
+    """A split at token 130 (inside a chunk) changes the chunk partition; both
+    halves, chained through the final state, agree with the oracle's one pass."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([300], 3, d, io, g_scale=0.5, s0_std=0.02, seed=36, device="cuda")
+    a = slice_tokens(inp, 0, 130, inp["initial_state"])
+    o_a, f_a = prefill(lib, a)
+    b = slice_tokens(inp, 130, 300, f_a)
+    o_b, f_b = prefill(lib, b)
+    o_ref, f_ref = oracle_prefill(oracle, inp)
+    eo = maxerr(host(torch.cat([o_a, o_b])), o_ref)
+    ef = maxerr(host(f_b), f_ref)
+    say(f"split at 130 {io} d={d}: err_out={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL[io] and ef <= TOL[io]
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_prefill_matches_decode_steps(lib, io, d):
+    """The chunked prefill over T tokens and T single-token decode steps (the
+    token-by-token form, a separate kernel) reach the same outputs and state."""
+    from kda_inputs import make_prefill
+    lens = [150, 64, 1]
+    inp = make_prefill(lens, 3, d, io, g_scale=0.5, s0_std=0.02, seed=37, device="cuda")
+    o_p, f_p = prefill(lib, inp)
+    o_d = torch.empty_like(o_p)
+    starts = np.cumsum([0] + lens)
+    for n, L in enumerate(lens):
+        st = inp["initial_state"][n:n + 1].clone()
+        for t in range(starts[n], starts[n] + L):
+            sl = lambda x: x[t:t + 1].contiguous()
+            o_d[t:t + 1] = lib.kda_decode_step(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
+                                               sl(inp["g"]), sl(inp["beta"]), st)
+        torch.cuda.synchronize()
+        ef = maxerr(host(st[0]), host(f_p[n]))
+        assert ef <= TOL[io], f"sequence {n}: state differs by {ef}"
+    eo = maxerr(host(o_d), host(o_p))
+    say(f"prefill vs decode {io} d={d}: out diff {eo:.3e}")
+    assert eo <= TOL[io]
+
+
+def test_nonfinite_input_stays_in_its_sequence(lib):
+    """A NaN in one sequence's values and a +inf in another's keys leave every
+    other sequence's outputs and states exactly as in the clean run."""
+    from kda_inputs import make_prefill
+    lens = [200, 130, 64, 77]
+    inp = make_prefill(lens, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=38, device="cuda")
+    o_ref, f_ref = prefill(lib, inp)
+    bad = dict(inp)
+    bad["v"] = inp["v"].clone()
+    bad["k"] = inp["k"].clone()
+    bad["v"][200 + 70, 1, 5] = float("nan")       # sequence 1
+    bad["k"][330 + 10, 0, 0] = float("inf")       # sequence 2
+    o, f = prefill(lib, bad)
+    for n, (t0, t1) in enumerate([(0, 200), (394, 471)]):
+        assert torch.equal(o[t0:t1], o_ref[t0:t1])
+    assert torch.equal(f[0], f_ref[0]) and torch.equal(f[3], f_ref[3])
+    # heads are independent too: sequence 1's head 0 never saw the NaN
+    assert torch.equal(o[200:330, 0], o_ref[200:330, 0])
+
+
+# ----------------------------------------------------------------------------- options vs oracle
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_scale_and_no_l2norm(lib, oracle, io, d):
+    """scale = 0.25 on q̄ and qk_l2norm = 0 (q, k used as given: the recipe
+    already draws unit rows, so the recurrence stays contractive)."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([190, 64], 2, d, io, g_scale=0.5, s0_std=0.02, seed=39, device="cuda")
+    for scale, l2 in ((0.25, True), (1.0, False), (0.5, False)):
+        o, f = prefill(lib, inp, scale=scale, qk_l2norm=l2)
+        o_ref, f_ref = oracle_prefill(oracle, inp, scale=scale, l2norm=l2)
+        eo, ef = maxerr(host(o), o_ref), maxerr(host(f), f_ref)
+        say(f"scale={scale} l2norm={l2} {io} d={d}: err_out={eo:.3e} err_state={ef:.3e}")
+        assert eo <= TOL[io] and ef <= TOL[io]
+
+
+def test_decode_scale_and_no_l2norm(lib, oracle):
+    from kda_inputs import make_decode
+    w = make_decode(4, 3, 128, "bf16", steps=3, seed=40, device="cuda")
+    for scale, l2 in ((0.25, True), (0.5, False)):
+        st = w["state"].clone()
+        st_ref = host(w["state"]).astype(np.float64)
+        for s in range(3):
+            o = lib.kda_decode_step(w["q"][s], w["k"][s], w["v"][s], w["g"][s], w["beta"][s],
+                                    st, scale=scale, qk_l2norm=l2)
+            torch.cuda.synchronize()
+            o_ref = oracle.decode_step(host(w["q"][s]), host(w["k"][s]), host(w["v"][s]),
+                                       host(w["g"][s]), host(w["beta"][s]), st_ref,
+                                       scale=scale, l2norm=l2)
+            assert maxerr(host(o), o_ref) <= TOL["bf16"]
+        assert maxerr(host(st), st_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("heads", [1, 5])
+def test_odd_head_counts(lib, oracle, heads):
+    from kda_inputs import make_prefill
+    inp = make_prefill([129, 260], heads, 128, "bf16", g_scale=0.5, s0_std=0.02,
+                       seed=41 + heads, device="cuda")
+    o, f = prefill(lib, inp)
+    o_ref, f_ref = oracle_prefill(oracle, inp)
+    assert maxerr(host(o), o_ref) <= TOL["bf16"] and maxerr(host(f), f_ref) <= TOL["bf16"]
+
+
+def test_many_short_sequences(lib, oracle):
+    """300 packed sequences of 0..130 tokens (many single-chunk and empty
+    sequences, more sequences than compute units)."""
+    from kda_inputs import make_prefill
+    rng = np.random.default_rng(43)
+    lens = rng.integers(0, 131, size=300).tolist()
+    lens[5] = 0
+    lens[6] = 1
+    inp = make_prefill(lens, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=43, device="cuda")
+    o, f = prefill(lib, inp)
+    o_ref, f_ref = oracle_prefill(oracle, inp)
+    eo, ef = maxerr(host(o), o_ref), maxerr(host(f), f_ref)
+    say(f"300 short sequences ({sum(lens)} tokens): err_out={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    # the empty sequence returns its initial state unchanged
+    assert torch.equal(f[5], inp["initial_state"][5])
