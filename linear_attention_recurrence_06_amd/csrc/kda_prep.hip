@@ -21,26 +21,29 @@
 // a non-positive number except on the diagonal blocks:
 //     E_r = e^(gamma_r - rho_{R-1}),  F_r = e^(rho_R - gamma_r)        (both <= 1)
 //     block (R, J<R):  e^(gamma_r - gamma_j) = E_r * e^(rho_{R-1} - rho_J) * F_j
-//     block (R, R):    e^(gamma_r - gamma_j) = (E_r / D_R) F_j,  D_R = e^(rho_R - rho_{R-1})
+//     block (R, R):    e^(gamma_r - gamma_j) = E_r (F_j / D_R),  D_R = e^(rho_R - rho_{R-1})
 // so the products run on MFMA from three decayed copies of q and k (E-, E- and
-// F-scaled).  On diagonal blocks 1/D_R stays below e^80 (and F_j above e^-80)
-// when every g >= -5, the documented accuracy range.
+// F-scaled), the middle factor and 1/D_R applied per channel to the F-scaled
+// operand.  On diagonal blocks F_j / D_R stays below e^80 when every g >= -5,
+// the documented accuracy range.
 //
-// Work split: a persistent grid (one workgroup per CU) walks the (chunk slot,
-// head) items; each workgroup loads the next item's raw rows while it computes
-// the current one, and the item after that's descriptor one step earlier, so
-// global-memory latency overlaps the arithmetic.
-//
-// Steps per item (256 threads = 4 waves; wave w owns tokens 16w..16w+15 = block w):
-//   P0 L2-normalise q, k; cumulative sum of g per block (in-thread, then across
-//      the wave); block totals through LDS, then a per-channel table of every
-//      block-level decay factor (16 x d_k exponentials per chunk);
+// Work split: one workgroup of 512 threads (8 waves) per (chunk slot, head);
+// the shared tiles fit in 80 KB, so two workgroups share a CU and one's
+// arithmetic covers the other's memory and barrier waits.
+// Thread t holds tokens 2*(t/16), +1 and channels (d_k/16)*(t%16).. of the
+// chunk's rows; wave w holds tokens 8w..8w+7 (half of 16-token block w/2).
+//   P0 L2-normalise q, k; cumulative sum of g inside each 16-token block (in
+//      thread, across the wave's four lane rows, then across the two waves of a
+//      block through LDS); a per-channel table of every block-level decay
+//      factor (16 x d_k exponentials per chunk);
 //   P1 element decay factors; E/F-scaled tiles to LDS; Qhat, Kprime^T, Gamma_C out;
-//   P2 A and M blocks on MFMA (row block w of both per wave);
-//   P3 T = (I + A)^-1: the four 16x16 diagonal inverses by forward substitution
-//      (one lane per column), then block rows 1..3 by T_RJ = -T_RR sum_K A_RK T_KJ
-//      on fp32 MFMA;
-//   P4 W and U on MFMA; U, M, W out.
+//   P2 the ten lower 16x16 blocks of A and M on MFMA, spread over the waves;
+//      A stays in LDS, M goes out;
+//   P3 T = (I + A)^-1 in place of A: the four 16x16 diagonal inverses by forward
+//      substitution (one lane per column), then block rows 1..3 by
+//      T_RJ = -T_RR sum_K A_RK T_KJ on fp32 MFMA;
+//   P4 U = T Diag(beta) V and W^T = (Diag(beta) Khat)^T T^T on MFMA, each
+//      written straight from the accumulators in the layout the recurrence reads.
 #include <algorithm>
 
 #include "kda_common.hpp"
@@ -80,15 +83,15 @@ __device__ __forceinline__ void mm16_lds(f32x4& acc, const float* A, int lda, co
 template <typename T, int D>
 struct PrepSmem {
     static constexpr int P = 16 / sizeof(T);  // 16-byte row padding
-    float A[64][68];          // beta-scaled strictly-lower A (16-byte aligned rows)
-    T M[64][64 + P];          // inclusive-lower Q K decay products
-    float tau[4][D];          // per-block total log-decay
+    float A[64][68];  // beta-scaled strictly-lower A, then T = (I + A)^-1 in place
+    float tau[4][D];  // per-block total log-decay
     // per-channel decay factors, rows: 0-3 e^(-tau_R); 4 e^(tau_1); 5 e^(tau_1+tau_2);
     // 6 e^(tau_2); 7-10 e^(rho_{R-1}) (chunk start -> block R start); 11-14
     // e^(rho_3 - rho_R) (block R end -> chunk end); 15 e^(rho_3) = Gamma_C
     float fac[16][D];
     float beta[64];
     union {
+        float wsum[8][D];  // P0: per-wave sums of g
         struct {
             T KE[64][D + P];
             T QE[64][D + P];
@@ -97,73 +100,53 @@ struct PrepSmem {
         struct {
             T BK[D][64 + P];  // (Diag(beta) Khat)^T
             T BV[D][64 + P];  // (Diag(beta) V)^T
-            float Tf[64][65];
             T Tb[64][64 + P];
             float X[4][16][17];
         } b;
-        struct {
-            T Wst[64][D + P]; // W staging (aliases BK after its last use)
-        } c;
     } u;
 };
 
-// Row block R of A (beta-scaled, strictly lower) and of M (inclusive lower):
-// for every column block J <= R the K-side operand (KF rows of block J) is
-// loaded once and feeds both products, so each wave runs two independent MFMA
-// chains; blocks J > R are zero.
+// Block (R, J), J <= R, of A (beta-scaled, strictly lower; to LDS) and of M
+// (inclusive lower; to the record).  Both products share the K-side operand,
+// the F-scaled rows of block J, scaled per channel by 1/D_R on the diagonal and
+// by e^(rho_{R-1} - rho_J) when J < R - 1.  M is formed transposed, so each lane
+// ends with four consecutive columns of one row and writes them in A order.
 template <typename T, int D>
-__device__ __forceinline__ void decay_row_block(PrepSmem<T, D>& sm, int R, int lane) {
+__device__ __forceinline__ void decay_block(PrepSmem<T, D>& sm, T* Mg, int R, int J, int lane) {
     constexpr int NKS = D / 32;
-    Frag<T> ke[NKS], qe[NKS];
+    const int frow = (J == R) ? R : (J < R - 1 ? (R == 2 ? 4 : 5 + J) : -1);
+    f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         const int c0 = 32 * ks + 8 * (lane >> 4);
-        ke[ks] = load_frag<T>(&sm.u.a.KE[16 * R + (lane & 15)][c0]);
-        qe[ks] = load_frag<T>(&sm.u.a.QE[16 * R + (lane & 15)][c0]);
-    }
+        const Frag<T> ke = load_frag<T>(&sm.u.a.KE[16 * R + (lane & 15)][c0]);
+        const Frag<T> qe = load_frag<T>(&sm.u.a.QE[16 * R + (lane & 15)][c0]);
+        Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
+        if (frow >= 0) {
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[frow][c0]);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[frow][c0 + 4]);
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_m = {0.f, 0.f, 0.f, 0.f};
-        if (J <= R) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int c0 = 32 * ks + 8 * (lane >> 4);
-                Frag<T> b = load_frag<T>(&sm.u.a.KF[16 * J + (lane & 15)][c0]);
-                Frag<T> a = ke[ks], q = qe[ks];
-                if (J == R) {
-                    // diagonal block: e^(gamma_r - gamma_j) = E_r F_j / D_R, on the row side
-                    const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0]);
-                    const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[R][c0 + 4]);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float f = j < 4 ? f0[j] : f1[j - 4];
-                        a.v[j] = from_f32<T>(to_f32(a.v[j]) * f);
-                        q.v[j] = from_f32<T>(to_f32(q.v[j]) * f);
-                    }
-                } else if (J < R - 1) {
-                    const int row = (R == 2) ? 4 : 5 + J;  // e^(rho_{R-1} - rho_J)
-                    const f32x4 f0 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0]);
-                    const f32x4 f1 = *reinterpret_cast<const f32x4*>(&sm.fac[row][c0 + 4]);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        b.v[j] = from_f32<T>(to_f32(b.v[j]) * (j < 4 ? f0[j] : f1[j - 4]));
-                }
-                mma(acc_a, a, b);
-                mma(acc_m, q, b);
-            }
+            for (int j = 0; j < 8; ++j)
+                b.v[j] = from_f32<T>(to_f32(b.v[j]) * (j < 4 ? f0[j] : f1[j - 4]));
         }
-        const int col = lane & 15;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 4 * (lane >> 4) + e;
-            float va = acc_a[e] * sm.beta[16 * R + row];
-            float vm = acc_m[e];
-            if (J > R || (J == R && col >= row)) va = 0.f;
-            if (J > R || (J == R && col > row)) vm = 0.f;
-            sm.A[16 * R + row][16 * J + col] = va;
-            sm.M[16 * R + row][16 * J + col] = from_f32<T>(vm);
-        }
+        mma(acc_a, ke, b);  // A[r][j]: r in block R (rows), j in block J (columns)
+        mma(acc_m, b, qe);  // M^T[j][r]
     }
+    const int col = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 4 * (lane >> 4) + e;
+        float va = acc_a[e] * sm.beta[16 * R + row];
+        if (J == R && col >= row) va = 0.f;
+        sm.A[16 * R + row][16 * J + col] = va;
+    }
+    float m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * (lane >> 4) + i;
+        m[i] = (J == R && j > col) ? 0.f : acc_m[i];
+    }
+    store_n<T, 4>(Mg + aorder_index(16 * R + col, 16 * J + 4 * (lane >> 4), 64), m);
 }
 
 struct PrepParams {
@@ -188,56 +171,67 @@ __device__ __forceinline__ int2 slot_desc(const PrepParams& p, int64_t slot) {
     return make_int2((int)(n * each + 64 * kc), (int)min((int64_t)64, each - 64 * kc));
 }
 
-// One thread's share of a chunk's raw input rows (rows 4*rg..4*rg+3, channels
-// CPT*cg..+CPT-1), kept in the I/O type so the next item's rows can be in
-// flight while the current item computes.
-template <typename T, int D>
-struct RawRows {
-    static constexpr int CPT = D / 16;
-    typedef T V __attribute__((ext_vector_type(CPT)));
-    V q[4], k[4], g[4], v[4];
-    T b[4];
+// Exclusive prefix over the four 16-lane rows of a wave of x (lanes in the same
+// column of different rows), and the wave total, with cross-row lane swaps.
+__device__ __forceinline__ void wave_rows_scan(float x, int row, float& excl, float& total) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s1 = x + ((row & 1) ? __uint_as_float(a[0]) : 0.f);  // rows (0,1), (2,3) inclusive
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s1), __float_as_uint(s1), false, false);
+    const float pt = (row & 1) ? s1 : __uint_as_float(b[1]);          // pair total
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(pt), __float_as_uint(pt), false, false);
+    const float incl = s1 + (row >= 2 ? __uint_as_float(c[0]) : 0.f);
+    total = pt + (row >= 2 ? __uint_as_float(c[0]) : __uint_as_float(c[1]));
+    excl = incl - x;
+}
 
-    // Rows past the chunk's length are loaded from its first row (always a
-    // valid token) and zeroed by the caller, so the loads are never predicated
-    // and the compiler can keep the next item's rows in flight.
-    __device__ __forceinline__ void load(const PrepParams& p, int2 d, int h, int rg, int cg) {
-        const int64_t H = p.n_heads;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * rg + i;
-            const int64_t row = (int64_t)d.x + (r < d.y ? r : 0);
-            const int64_t off = (row * H + h) * D + CPT * cg;
-            q[i] = *reinterpret_cast<const V*>((const T*)p.q + off);
-            k[i] = *reinterpret_cast<const V*>((const T*)p.k + off);
-            g[i] = *reinterpret_cast<const V*>((const T*)p.g + off);
-            v[i] = *reinterpret_cast<const V*>((const T*)p.v + off);
-            b[i] = ((const T*)p.beta)[row * H + h];
-        }
-    }
-};
-
-// Everything for one (chunk slot, head) item whose raw rows are already in
-// registers (converted to fp32).  Ends with a barrier so the next item may
-// reuse the shared memory.
+// One (chunk slot, head) item per workgroup of 512 threads.
 template <typename T, int D>
-__device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
-                                          int h, float (&qf)[4][D / 16], float (&kf)[4][D / 16],
-                                          float (&gf)[4][D / 16], const float (&vf)[4][D / 16],
-                                          const float (&bt)[4]) {
+__global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
     constexpr int CPT = D / 16;  // channels per thread in the row layout
-    constexpr int NKS = D / 32;  // 32-deep k-steps over the channels
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    typedef T V2 __attribute__((ext_vector_type(2)));
+    __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int rg = t >> 4, cg = t & 15, grp = lane >> 4;
+    const int rg = t >> 4, cg = t & 15, lrow = lane >> 4;
+    const int Rb = w >> 1;  // 16-token block of this thread's rows
+    const int64_t H = p.n_heads;
+    const int64_t item = blockIdx.x;
+    const int64_t slot = item / H;
+    const int h = (int)(item - slot * H);
+    const int2 d = slot_desc(p, slot);
+    if (d.y <= 0) return;
     unsigned char* rec = p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot) * p.L.rec_bytes;
+
+    // rows 2rg, 2rg+1 (rows past the chunk's length read its first row, then zeroed)
+    float qf[2][CPT], kf[2][CPT], gf[2][CPT], vf[2][CPT], bt[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 2 * rg + i;
+        const bool ok = r < d.y;
+        const int64_t row = (int64_t)d.x + (ok ? r : 0);
+        const int64_t off = (row * H + h) * D + CPT * cg;
+        const V q = *reinterpret_cast<const V*>((const T*)p.q + off);
+        const V k = *reinterpret_cast<const V*>((const T*)p.k + off);
+        const V g = *reinterpret_cast<const V*>((const T*)p.g + off);
+        const V v = *reinterpret_cast<const V*>((const T*)p.v + off);
+        const T b = ((const T*)p.beta)[row * H + h];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            qf[i][c] = ok ? to_f32(q[c]) : 0.f;
+            kf[i][c] = ok ? to_f32(k[c]) : 0.f;
+            gf[i][c] = ok ? to_f32(g[c]) : 0.f;
+            vf[i][c] = ok ? to_f32(v[c]) : 0.f;
+        }
+        bt[i] = ok ? to_f32(b) : 0.f;
+    }
 
     // ---------------------------------------------------------------- P0
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (cg == 0) sm.beta[4 * rg + i] = bt[i];
+    for (int i = 0; i < 2; ++i)
+        if (cg == 0) sm.beta[2 * rg + i] = bt[i];
     // L2 norms over the 16 lanes that share a row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
@@ -254,32 +248,36 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
             kf[i][c] *= rk;
         }
     }
-    // cumulative log-decay inside the 16-token block: in-thread, then across
-    // the four 4-row groups of the wave (inclusive scan, then shift by one group)
+    // cumulative log-decay inside the 16-token block: in-thread over the two
+    // rows, across the wave's four lane rows, then across the block's two waves
+    float excl[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         gf[1][c] += gf[0][c];
-        gf[2][c] += gf[1][c];
-        gf[3][c] += gf[2][c];
-        float incl = gf[3][c];
-        float x = __shfl_up(incl, 16, kWave);
-        if (grp >= 1) incl += x;
-        x = __shfl_up(incl, 32, kWave);
-        if (grp >= 2) incl += x;
-        float ex = __shfl_up(incl, 16, kWave);
-        if (grp == 0) ex = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gf[i][c] += ex;
-        const float tau = __shfl(gf[3][c], 48 + cg, kWave);  // block total = last row
-        if (grp == 0) sm.tau[w][CPT * cg + c] = tau;
+        float total;
+        wave_rows_scan(gf[1][c], lrow, excl[c], total);
+        if (lrow == 0) sm.u.wsum[w][CPT * cg + c] = total;
     }
     __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const float add = excl[c] + ((w & 1) ? sm.u.wsum[w - 1][CPT * cg + c] : 0.f);
+        gf[0][c] += add;
+        gf[1][c] += add;
+    }
     // per-channel table of the block-level decay factors (16 x D exponentials):
-    // thread t owns channel t % D and rows t / D + (256 / D) * i
+    // thread t owns channel t % D and rows t / D + (512 / D) * i
     {
-        constexpr int RSTEP = 256 / D;
+        constexpr int RSTEP = 512 / D;
         const int c = t % D, r0 = t / D;
-        const float t0 = sm.tau[0][c], t1 = sm.tau[1][c], t2 = sm.tau[2][c], t3 = sm.tau[3][c];
+        float tb[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) tb[R] = sm.u.wsum[2 * R][c] + sm.u.wsum[2 * R + 1][c];
+        if (r0 == 0) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) sm.tau[R][c] = tb[R];
+        }
+        const float t0 = tb[0], t1 = tb[1], t2 = tb[2], t3 = tb[3];
         const float x[16] = {-t0, -t1, -t2, -t3,
                              t1, t1 + t2, t2,
                              0.f, t0, t0 + t1, (t0 + t1) + t2,
@@ -299,18 +297,18 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     // ---------------------------------------------------------------- P1
     T* Qg = reinterpret_cast<T*>(rec + p.L.off_q);
     T* Ktg = reinterpret_cast<T*>(rec + p.L.off_kt);
-    float bK[4][CPT], bV[4][CPT];
-    float kpT[CPT][4];
+    V2 rk[CPT], rv[CPT];  // beta Khat and beta V of the two rows, per channel
+    float kpT[CPT][2];
     float tauR[CPT], Gs[CPT], Kp[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-        tauR[c] = sm.tau[w][CPT * cg + c];
-        Gs[c] = sm.fac[7 + w][CPT * cg + c];
-        Kp[c] = sm.fac[11 + w][CPT * cg + c];
+        tauR[c] = sm.tau[Rb][CPT * cg + c];
+        Gs[c] = sm.fac[7 + Rb][CPT * cg + c];
+        Kp[c] = sm.fac[11 + Rb][CPT * cg + c];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * rg + i;
+    for (int i = 0; i < 2; ++i) {
+        const int r = 2 * rg + i;
         float ke[CPT], qe[CPT], kfv[CPT], qh[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
@@ -320,8 +318,8 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
             qe[c] = qf[i][c] * E;
             kfv[c] = kf[i][c] * F;
             qh[c] = qe[c] * Gs[c];
-            bK[i][c] = bt[i] * ke[c] * Gs[c];
-            bV[i][c] = bt[i] * vf[i][c];
+            rk[c][i] = from_f32<T>(bt[i] * ke[c] * Gs[c]);
+            rv[c][i] = from_f32<T>(bt[i] * vf[i][c]);
             kpT[c][i] = kfv[c] * Kp[c];
         }
         store_n<T, CPT>(&sm.u.a.KE[r][CPT * cg], ke);
@@ -330,7 +328,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         store_n<T, CPT>(Qg + aorder_index(r, CPT * cg, D), qh);
     }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) store_n<T, 4>(Ktg + aorder_index(CPT * cg + c, 4 * rg, 64), kpT[c]);
+    for (int c = 0; c < CPT; ++c) store_n<T, 2>(Ktg + aorder_index(CPT * cg + c, 2 * rg, 64), kpT[c]);
     if (rg == 0) {
         float* gC = reinterpret_cast<float*>(rec + p.L.off_gc);
 #pragma unroll
@@ -339,30 +337,38 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     __syncthreads();
 
     // ---------------------------------------------------------------- P2
-    decay_row_block<T, D>(sm, w, lane);
+    {
+        T* Mg = reinterpret_cast<T*>(rec + p.L.off_m);
+        // waves 0-6: blocks (0,0) (1,1) (2,2) (3,3) (2,0) (3,0) (3,1), which all
+        // scale their K-side operand; wave 7: (1,0) (2,1) (3,2), which do not.
+        // Waves 0-5 also write the six zero blocks of M above the diagonal.
+        if (w < 7) {
+            const int R = (0x3323210 >> (4 * w)) & 15;
+            const int J = (0x1003210 >> (4 * w)) & 15;
+            decay_block<T, D>(sm, Mg, R, J, lane);
+            if (w < 6) {
+                const int zR = (0x211000 >> (4 * w)) & 15;
+                const int zJ = (0x332321 >> (4 * w)) & 15;
+                const float z[4] = {0.f, 0.f, 0.f, 0.f};
+                store_n<T, 4>(Mg + aorder_index(16 * zR + (lane & 15), 16 * zJ + 4 * (lane >> 4), 64), z);
+            }
+        } else {
+            for (int R = 1; R < 4; ++R) decay_block<T, D>(sm, Mg, R, R - 1, lane);
+        }
+    }
     __syncthreads();
 
     // ---------------------------------------------------------------- P3
-    // transposed beta*Khat and beta*V tiles (the B operands of W and U).  Lane
-    // (rg, cg) holds 4 tokens x CPT channels; at write step j it stores channel
+    // transposed beta*Khat and beta*V tiles (the operands of W^T and U).  Lane
+    // (rg, cg) holds 2 tokens x CPT channels; at write step j it stores channel
     // (j + cg) % CPT, so the 16 lanes of a token group spread over the banks
-    // (a plain channel order puts them on two bank positions).  The rotation is
-    // a barrel shift of packed token quadruples across the channel index.
+    // (a plain channel order puts them on one bank).  The rotation is a barrel
+    // shift of packed token pairs across the channel index.
     {
-        typedef T V4 __attribute__((ext_vector_type(4)));
-        V4 rk[CPT], rv[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                rk[c][i] = from_f32<T>(bK[i][c]);
-                rv[c][i] = from_f32<T>(bV[i][c]);
-            }
-        }
 #pragma unroll
         for (int sh = 1; sh < CPT; sh <<= 1) {
             const bool on = (cg & sh) != 0;
-            V4 tk[CPT], tv[CPT];
+            V2 tk[CPT], tv[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 tk[j] = on ? rk[(j + sh) % CPT] : rk[j];
@@ -377,13 +383,14 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = CPT * cg + ((j + cg) % CPT);
-            *reinterpret_cast<V4*>(&sm.u.b.BK[c][4 * rg]) = rk[j];
-            *reinterpret_cast<V4*>(&sm.u.b.BV[c][4 * rg]) = rv[j];
+            *reinterpret_cast<V2*>(&sm.u.b.BK[c][2 * rg]) = rk[j];
+            *reinterpret_cast<V2*>(&sm.u.b.BV[c][2 * rg]) = rv[j];
         }
     }
     if (w == 0) {
-        // diagonal 16x16 blocks of (I + A)^-1: lane = (block, column), forward
-        // substitution; every row of A_RR is read with 16-byte loads up front
+        // diagonal 16x16 blocks of (I + A)^-1, in place: lane = (block, column),
+        // forward substitution; every row of A_RR is read (16-byte loads) before
+        // the wave writes any column of T_RR
         const int R = lane >> 4, j = lane & 15;
         float arow[16][16];
 #pragma unroll
@@ -403,15 +410,17 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
             colv[i] = (i == j) ? 1.f : ((i < j) ? 0.f : -acc);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.u.b.Tf[16 * R + i][16 * R + j] = colv[i];
+        for (int i = 0; i < 16; ++i) sm.A[16 * R + i][16 * R + j] = colv[i];
     }
     __syncthreads();
+    // block rows 1..3: wave J forms T_RJ = -T_RR sum_{K=J}^{R-1} A_RK T_KJ; the
+    // sums are taken before any T_RJ replaces A_RJ
     for (int R = 1; R < 4; ++R) {
         if (w < R) {
             const int J = w;
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
             for (int K = J; K < R; ++K)
-                mm16_lds(x, &sm.A[16 * R][16 * K], 68, &sm.u.b.Tf[16 * K][16 * J], 65);
+                mm16_lds(x, &sm.A[16 * R][16 * K], 68, &sm.A[16 * K][16 * J], 68);
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm.u.b.X[w][4 * (lane >> 4) + e][lane & 15] = -x[e];
         }
@@ -419,140 +428,52 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         if (w < R) {
             const int J = w;
             f32x4 tt = {0.f, 0.f, 0.f, 0.f};
-            mm16_lds(tt, &sm.u.b.Tf[16 * R][16 * R], 65, &sm.u.b.X[w][0][0], 17);
+            mm16_lds(tt, &sm.A[16 * R][16 * R], 68, &sm.u.b.X[w][0][0], 17);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.u.b.Tf[16 * R + 4 * (lane >> 4) + e][16 * J + (lane & 15)] = tt[e];
+            for (int e = 0; e < 4; ++e) sm.A[16 * R + 4 * (lane >> 4) + e][16 * J + (lane & 15)] = tt[e];
         }
         __syncthreads();
     }
     {
-        // thread t converts row t / 4, columns 16 * (t % 4) .. +15 (zero above the diagonal)
-        const int r = t >> 2, c0 = 16 * (t & 3);
-        float x[16];
+        // thread t converts row t / 8, columns 8 * (t % 8) .. +7 (zero above the diagonal)
+        const int r = t >> 3, c0 = 8 * (t & 7);
+        float x[8];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = (c0 + j <= r) ? sm.u.b.Tf[r][c0 + j] : 0.f;
-        float lo[8], hi[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            lo[j] = x[j];
-            hi[j] = x[8 + j];
-        }
-        store_frag<T>(&sm.u.b.Tb[r][c0], make_frag<T>(lo));
-        store_frag<T>(&sm.u.b.Tb[r][c0 + 8], make_frag<T>(hi));
+        for (int j = 0; j < 8; ++j) x[j] = (c0 + j <= r) ? sm.A[r][c0 + j] : 0.f;
+        store_frag<T>(&sm.u.b.Tb[r][c0], make_frag<T>(x));
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- P4
     {
-        const int R = w;
-        const int nks = (R >= 2) ? 2 : 1;  // T[R][J] = 0 for blocks J > R
+        const int R = w & 3;
+        const int nks = (R >= 2) ? 2 : 1;  // T[r][j] = 0 for j in blocks past R
         Frag<T> ta[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             if (ks < nks) ta[ks] = load_frag<T>(&sm.u.b.Tb[16 * R + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-        f32x4 accW[D / 16];
         T* Ug = reinterpret_cast<T*>(rec + p.L.off_u);
+        T* Wg = reinterpret_cast<T*>(rec + p.L.off_w);
+        constexpr int NBW = D / 32;  // column tiles per wave
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
+        for (int i = 0; i < NBW; ++i) {
+            const int nb = (w >> 2) * NBW + i;
             f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks < nks) {
-                    const Frag<T> bk = load_frag<T>(&sm.u.b.BK[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-                    const Frag<T> bv = load_frag<T>(&sm.u.b.BV[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-                    mma(aw, ta[ks], bk);
-                    mma(au, ta[ks], bv);
+                    const int c0 = 32 * ks + 8 * (lane >> 4);
+                    const Frag<T> bk = load_frag<T>(&sm.u.b.BK[16 * nb + (lane & 15)][c0]);
+                    const Frag<T> bv = load_frag<T>(&sm.u.b.BV[16 * nb + (lane & 15)][c0]);
+                    mma(aw, bk, ta[ks]);  // W^T[n][r]
+                    mma(au, ta[ks], bv);  // U[r][n]
                 }
             }
-            accW[nb] = aw;
-            float uv[4] = {au[0], au[1], au[2], au[3]};
+            const float uv[4] = {au[0], au[1], au[2], au[3]};
             store_n<T, 4>(Ug + corder_index(16 * R + 4 * (lane >> 4), 16 * nb + (lane & 15), D), uv);
+            const float wv[4] = {aw[0], aw[1], aw[2], aw[3]};
+            store_n<T, 4>(Wg + aorder_index(16 * R + (lane & 15), 16 * nb + 4 * (lane >> 4), D), wv);
         }
-        T* Mg = reinterpret_cast<T*>(rec + p.L.off_m);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const Frag<T> f = load_frag<T>(&sm.M[16 * w + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-            store_frag<T>(Mg + ((int64_t)(w * 2 + ks) * kWave + lane) * 8, f);
-        }
-        __syncthreads();  // every wave is done with BK / BV
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sm.u.c.Wst[16 * R + 4 * (lane >> 4) + e][16 * nb + (lane & 15)] = from_f32<T>(accW[nb][e]);
-        __syncthreads();
-        T* Wg = reinterpret_cast<T*>(rec + p.L.off_w);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const Frag<T> f = load_frag<T>(&sm.u.c.Wst[16 * w + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-            store_frag<T>(Wg + ((int64_t)(w * NKS + ks) * kWave + lane) * 8, f);
-        }
-    }
-    __syncthreads();  // the next item overwrites the shared tiles
-}
-
-// Persistent driver: item = slot * H + head; workgroup b takes items b, b + G, ...
-template <typename T, int D>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
-    constexpr int CPT = D / 16;
-    __shared__ PrepSmem<T, D> sm;
-    const int t = threadIdx.x;
-    const int rg = t >> 4, cg = t & 15;
-    const int64_t H = p.n_heads;
-    const int64_t items = p.L.slots * H;
-    const int64_t G = gridDim.x;
-    int64_t item = blockIdx.x;
-    if (item >= items) return;
-    // (slot, head) of item, item + G, item + 2G, stepped without 64-bit divisions
-    const int gh = (int)(G % H);
-    const int64_t gs = G / H;
-    auto advance = [&](int64_t& s, int& hh) {
-        s += gs;
-        hh += gh;
-        if (hh >= H) {
-            hh -= (int)H;
-            s += 1;
-        }
-    };
-    int64_t s0 = item / H;
-    int h0 = (int)(item % H);
-    int64_t s1 = s0, s2;
-    int h1 = h0, h2;
-    advance(s1, h1);
-    s2 = s1;
-    h2 = h1;
-    advance(s2, h2);
-
-    RawRows<T, D> raw;
-    int2 d_cur = slot_desc(p, s0);
-    int2 d_nxt = item + G < items ? slot_desc(p, s1) : make_int2(0, 0);
-    raw.load(p, d_cur, h0, rg, cg);
-    for (; item < items; item += G) {
-        const int2 d = d_cur;
-        float qf[4][CPT], kf[4][CPT], gf[4][CPT], vf[4][CPT], bt[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = 4 * rg + i < d.y;
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                qf[i][c] = ok ? to_f32(raw.q[i][c]) : 0.f;
-                kf[i][c] = ok ? to_f32(raw.k[i][c]) : 0.f;
-                gf[i][c] = ok ? to_f32(raw.g[i][c]) : 0.f;
-                vf[i][c] = ok ? to_f32(raw.v[i][c]) : 0.f;
-            }
-            bt[i] = ok ? to_f32(raw.b[i]) : 0.f;
-        }
-        // next item's rows go in flight now (past the last item: the current one
-        // again, never used); the descriptor after it one step earlier
-        const bool more = item + G < items;
-        raw.load(p, more ? d_nxt : d, more ? h1 : h0, rg, cg);
-        const int2 d_nn = item + 2 * G < items ? slot_desc(p, s2) : make_int2(0, 0);
-        if (d.y > 0) prep_item<T, D>(p, sm, s0, h0, qf, kf, gf, vf, bt);
-        d_cur = d_nxt;
-        d_nxt = d_nn;
-        s0 = s1; h0 = h1;
-        s1 = s2; h1 = h2;
-        advance(s2, h2);
     }
 }
 
@@ -634,8 +555,7 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t items = a.layout.slots * a.n_heads;
-    const int64_t grid = std::min<int64_t>(items, (int64_t)a.cu_count);
-    hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)items), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

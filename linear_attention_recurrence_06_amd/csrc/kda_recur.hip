@@ -17,12 +17,23 @@
 // the same XCD (blockIdx % 8 selects the XCD) so the W / Qhat / M / Kprime^T
 // they all read come from one L2.
 //
-// Per chunk, wave w computes u and Qhat S for the 16 tokens of block w; u goes
-// through LDS (transposed, as MFMA B operand); then every wave advances its 32
-// (d_k = 128) or 16 (d_k = 64) state rows and adds M u to its outputs.  The
-// fp32 master state never leaves registers; the I/O-typed copy used as MFMA
-// operand is rewritten to LDS once per chunk.  Operands are requested two
-// chunks ahead (three register buffers in rotation).
+// Eight waves, two per SIMD.  Wave w works on token block b = w % 4:
+//   waves 0-3 compute u = U - W S for block b and publish it (transposed) in LDS;
+//   waves 4-7 compute Qhat S for block b and, once u is published, add M u and
+//   write the outputs;
+//   the state rows are split in 16-row blocks over waves 0..d_k/16-1, each
+//   applying Diag(Gamma_C) and adding Kprime^T u to its rows, then publishing
+//   the I/O-typed copy of its rows (the MFMA operand of the next chunk).
+// No operand of a chunk is used by two waves, so every wave streams its own
+// operands from the workspace straight into registers, three chunks ahead (three
+// register buffers in rotation; loads are never predicated, so the compiler
+// counts the outstanding loads exactly).  Two barriers per chunk.
+//
+// The eight tiles of a head read the same records at about the same time, so
+// each record would arrive from HBM with every tile waiting on it.  Each
+// workgroup therefore also touches its eighth (1/ntiles) of the record one chunk
+// beyond those in flight, one 128-byte line per lane, which brings the record
+// into L2 before the full loads ask for it.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -31,16 +42,8 @@ namespace kda {
 template <typename T, int D, int NT>
 struct RecurSmem {
     static constexpr int P = 16 / sizeof(T);
-    static constexpr int E = sizeof(T);
-    static constexpr int NB = NT / 16;
-    // one chunk's operands, laid out as in the workspace record:
-    // W | Qhat | M | Kprime^T (contiguous), this tile's U, Gamma_C
-    static constexpr int CORE = (192 * D + 64 * 64) * E;
-    static constexpr int UBYTES = 4 * NB * 256 * E;
-    static constexpr int SLOT = CORE + UBYTES + D * 4;
-    T ST[NT][D + P];   // S tile, transposed: [value column][key row]
-    T UT[NT][64 + P];  // u tile, transposed: [value column][token]
-    alignas(16) unsigned char slot[2][SLOT];
+    T ST[NT][D + P];   // I/O-typed copy of S, transposed: [value column][key row]
+    T UT[NT][64 + P];  // u, transposed: [value column][token]
 };
 
 struct RecurParams {
@@ -54,259 +57,268 @@ struct RecurParams {
     PrefillLayout L;
 };
 
-// Loader side: one chunk's operands staged in the loader waves' registers
-// (16-byte vectors; every loader thread always issues the same loads, so the
-// compiler can count outstanding loads exactly).
+// One chunk's operands as held by one wave.
 template <typename T, int D, int NT>
-struct Staging {
-    typedef RecurSmem<T, D, NT> SM;
-    static constexpr int NCORE = SM::CORE / 16 / 256;
-    static constexpr int NU = SM::UBYTES / 16;        // U vectors (this tile)
-    static constexpr int NG = D / 4;                   // Gamma_C vectors
-    static constexpr int NX = (NU + NG + 255) / 256;   // extra vectors per loader
-    static_assert(NCORE * 16 * 256 == SM::CORE, "core must split evenly over 256 loaders");
-    u32x4 core[NCORE];
-    u32x4 extra[NX];
+struct WaveOps {
+    static constexpr int NKS = D / 32;  // 32-deep steps over d_k
+    static constexpr int NB = NT / 16;
+    typedef T V4 __attribute__((ext_vector_type(4)));
+    Frag<T> A[NKS];   // W (waves 0-3) or Qhat (waves 4-7) rows of token block b
+    Frag<T> Mf[2];    // M rows of token block b (waves 4-7)
+    V4 U[NB];         // U of token block b, this tile (waves 0-3)
+    Frag<T> Kt[2];    // Kprime^T rows of this wave's state row block
+    f32x4 gc;         // Gamma_C of this wave's state rows (4 per lane)
+    uint32_t pf;      // one word of a later chunk's record (L2 prefetch; never used)
 
-    // source / destination byte offsets of extra vector x (index x < NU + NG)
-    __device__ __forceinline__ static void extra_offsets(const PrefillLayout& L, int x, int tile,
-                                                         int& src, int& dst) {
-        constexpr int E = SM::E;
-        constexpr int NB = SM::NB;
-        constexpr int per_rb = NB * 256 * E / 16;  // vectors of one 16-row block of this tile's U
-        if (x < NU) {
-            const int rb = x / per_rb, v = x % per_rb;
-            src = (int)L.off_u + ((rb * (D / 16) + tile * NB) * 256) * E + v * 16;
-            dst = SM::CORE + rb * NB * 256 * E + v * 16;
-        } else {
-            const int v = min(x - NU, NG - 1);
-            src = (int)L.off_gc + v * 16;
-            dst = SM::CORE + SM::UBYTES + v * 16;
+    // Loads for the phase-one operands (A, and U or M) of record `rec`.
+    __device__ __forceinline__ void load_front(const unsigned char* rec, const PrefillLayout& L,
+                                               bool uwave, int b, int tile, int lane) {
+        const T* a = reinterpret_cast<const T*>(rec + (uwave ? L.off_w : L.off_q));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) A[ks] = load_frag<T>(a + ((b * NKS + ks) * kWave + lane) * 8);
+        if (uwave) {
+            const T* u = reinterpret_cast<const T*>(rec + L.off_u);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                U[nb] = *reinterpret_cast<const V4*>(
+                    u + ((b * (D / 16) + tile * NB + nb) * kWave + lane) * 4);
         }
     }
-    __device__ __forceinline__ void load(const unsigned char* rec, int lt, const int (&src)[NX]) {
+    // Loads for the phase-two operands: Kprime^T and Gamma_C of state row block
+    // rb, and M (waves 4-7).
+    __device__ __forceinline__ void load_back(const unsigned char* rec, const PrefillLayout& L,
+                                              bool uwave, int b, int rb, int lane) {
+        const T* k = reinterpret_cast<const T*>(rec + L.off_kt);
 #pragma unroll
-        for (int i = 0; i < NCORE; ++i)
-            core[i] = *reinterpret_cast<const u32x4*>(rec + (size_t)(i * 256 + lt) * 16);
+        for (int ks = 0; ks < 2; ++ks) Kt[ks] = load_frag<T>(k + ((rb * 2 + ks) * kWave + lane) * 8);
+        gc = *reinterpret_cast<const f32x4*>(rec + L.off_gc + (16 * rb + 4 * (lane >> 4)) * 4);
+        if (!uwave) {
+            const T* m = reinterpret_cast<const T*>(rec + L.off_m);
 #pragma unroll
-        for (int i = 0; i < NX; ++i) extra[i] = *reinterpret_cast<const u32x4*>(rec + src[i]);
-    }
-    __device__ __forceinline__ void store(unsigned char* slot, int lt, const int (&dst)[NX],
-                                          const bool (&has)[NX]) const {
-#pragma unroll
-        for (int i = 0; i < NCORE; ++i)
-            *reinterpret_cast<u32x4*>(slot + (i * 256 + lt) * 16) = core[i];
-#pragma unroll
-        for (int i = 0; i < NX; ++i)
-            if (has[i]) *reinterpret_cast<u32x4*>(slot + dst[i]) = extra[i];
+            for (int ks = 0; ks < 2; ++ks) Mf[ks] = load_frag<T>(m + ((b * 2 + ks) * kWave + lane) * 8);
+        }
     }
 };
 
-// Write the I/O-typed copy of this wave's state rows into the LDS operand tile.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void put_state(RecurSmem<T, D, NT>& sm,
-                                          const f32x4 (&S)[D / 64][NT / 16], int w, int lane) {
-    typedef T V4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int rb = 0; rb < D / 64; ++rb)
-#pragma unroll
-        for (int nb = 0; nb < NT / 16; ++nb) {
-            V4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(S[rb][nb][e]);
-            *reinterpret_cast<V4*>(
-                &sm.ST[16 * nb + (lane & 15)][16 * ((D / 64) * w + rb) + 4 * (lane >> 4)]) = x;
-        }
-}
+// Per-wave constants of one chain.
+struct WaveCtx {
+    const unsigned char* rec0;  // record of the chain's first chunk
+    size_t rec_bytes;
+    int64_t last;               // index of the last chunk
+    int64_t s_begin;            // first token of the sequence
+    int64_t s_len;
+    int64_t H;
+    int h, col0, tile, w, lane, b, rb;
+    uint32_t pf_off;            // byte offset of this lane's prefetch line in a record
+    bool uwave, has_rows;
+    __device__ __forceinline__ const unsigned char* rec(int64_t kc) const {
+        return rec0 + (size_t)min(kc, last) * rec_bytes;
+    }
+};
 
-// One chunk for compute wave w (token block w; key rows D/4*w..):
-// u = U - W S, O = Qhat S + M u, S <- Diag(Gamma_C) S + Kprime^T u,
-// with every operand read from the chunk's LDS slot.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[D / 64][NT / 16],
-                                           const unsigned char* slot, T* outp, int64_t tok0,
-                                           int Lc, int64_t H, int h, int col0, int w, int lane) {
-    typedef RecurSmem<T, D, NT> SM;
+// One chunk: consume `ops` (chunk kc), then refill it with chunk kc + NBUF.
+template <typename T, int D, int NT, int NBUF, int PF>
+__device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[NT / 16],
+                                           WaveOps<T, D, NT>& ops, const RecurParams& p,
+                                           const WaveCtx& c, int64_t kc) {
     constexpr int NKS = D / 32;
     constexpr int NB = NT / 16;
-    constexpr int RBW = D / 64;
-    constexpr int E = SM::E;
     typedef T V4 __attribute__((ext_vector_type(4)));
-    const T* Wl = reinterpret_cast<const T*>(slot);
-    const T* Ql = reinterpret_cast<const T*>(slot + 64 * D * E);
-    const T* Ml = reinterpret_cast<const T*>(slot + 128 * D * E);
-    const T* Kl = reinterpret_cast<const T*>(slot + (128 * D + 64 * 64) * E);
-    const T* Ul = reinterpret_cast<const T*>(slot + SM::CORE);
-    const float* Gl = reinterpret_cast<const float*>(slot + SM::CORE + SM::UBYTES);
+    const int lane = c.lane;
 
+    // ---- phase one: A S for token block b (A = W or Qhat)
     Frag<T> Sb[NKS][NB];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             Sb[ks][nb] = load_frag<T>(&sm.ST[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-    f32x4 accO[NB];
-    {
-        Frag<T> Wf[NKS], Qf[NKS];
+    f32x4 acc[NB];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            Wf[ks] = load_frag<T>(Wl + ((w * NKS + ks) * kWave + lane) * 8);
-            Qf[ks] = load_frag<T>(Ql + ((w * NKS + ks) * kWave + lane) * 8);
-        }
+    for (int nb = 0; nb < NB; ++nb) {
+        acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma(acc[nb], ops.A[ks], Sb[ks][nb]);
+    }
+    if (c.uwave) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            f32x4 au = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                mma(au, Wf[ks], Sb[ks][nb]);
-                mma(ao, Qf[ks], Sb[ks][nb]);
-            }
-            accO[nb] = ao;
-            const V4 U = *reinterpret_cast<const V4*>(Ul + ((w * NB + nb) * kWave + lane) * 4);
             V4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(to_f32(U[e]) - au[e]);
-            *reinterpret_cast<V4*>(&sm.UT[16 * nb + (lane & 15)][16 * w + 4 * (lane >> 4)]) = x;
+            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(to_f32(ops.U[nb][e]) - acc[nb][e]);
+            *reinterpret_cast<V4*>(&sm.UT[16 * nb + (lane & 15)][16 * c.b + 4 * (lane >> 4)]) = x;
         }
     }
+    ops.load_front(c.rec(kc + NBUF), p.L, c.uwave, c.b, c.tile, lane);
     __syncthreads();
+
+    // ---- phase two: state rows, then M u and the outputs
     Frag<T> Ub[2][NB];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             Ub[ks][nb] = load_frag<T>(&sm.UT[16 * nb + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-        const Frag<T> k0 = load_frag<T>(Kl + (((RBW * w + rb) * 2 + 0) * kWave + lane) * 8);
-        const Frag<T> k1 = load_frag<T>(Kl + (((RBW * w + rb) * 2 + 1) * kWave + lane) * 8);
-        const f32x4 g = *reinterpret_cast<const f32x4*>(Gl + 16 * (RBW * w + rb) + 4 * (lane >> 4));
+    if (c.has_rows) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            S[rb][nb] *= g;
-            mma(S[rb][nb], k0, Ub[0][nb]);
-            mma(S[rb][nb], k1, Ub[1][nb]);
+            S[nb] *= ops.gc;
+            mma(S[nb], ops.Kt[0], Ub[0][nb]);
+            mma(S[nb], ops.Kt[1], Ub[1][nb]);
+            V4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(S[nb][e]);
+            *reinterpret_cast<V4*>(&sm.ST[16 * nb + (lane & 15)][16 * c.rb + 4 * (lane >> 4)]) = x;
         }
     }
-    const Frag<T> m0 = load_frag<T>(Ml + ((w * 2 + 0) * kWave + lane) * 8);
-    const Frag<T> m1 = load_frag<T>(Ml + ((w * 2 + 1) * kWave + lane) * 8);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        mma(accO[nb], m0, Ub[0][nb]);
-        mma(accO[nb], m1, Ub[1][nb]);
-        const int col = col0 + 16 * nb + (lane & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * w + 4 * (lane >> 4) + e;
-            if (row < Lc) outp[((tok0 + row) * H + h) * D + col] = from_f32<T>(accO[nb][e]);
-        }
-    }
-    put_state<T, D, NT>(sm, S, w, lane);
-    __syncthreads();
-}
-
-// 512 threads: waves 0-3 compute, waves 4-7 load.  Both sides pass the same
-// 1 + 2 * nch barriers.  Chunk kc's operands sit in LDS slot kc % 2; the
-// loaders write slot (kc+1) % 2 while the compute waves work on chunk kc, and
-// keep chunks kc+2 and kc+3 in flight in their registers.
-template <typename T, int D, int NT>
-__global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
-    constexpr int NB = NT / 16;
-    constexpr int RBW = D / 64;
-    __shared__ RecurSmem<T, D, NT> sm;
-
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    const int b = blockIdx.x;
-    const int chain = 8 * ((b >> 3) / p.ntiles) + (b & 7);
-    const int tile = (b >> 3) % p.ntiles;
-    const int64_t H = p.n_heads;
-    if (chain >= p.n_seqs * p.n_heads) return;
-    const int n = chain / p.n_heads, h = chain % p.n_heads;
-    const int64_t each = p.n_seqs ? p.total_tokens / p.n_seqs : 0;
-    const int64_t s_begin = p.cu ? (int64_t)p.cu[n] : (int64_t)n * each;
-    const int64_t s_len = p.cu ? (int64_t)p.cu[n + 1] - s_begin : each;
-    const int32_t* cf = reinterpret_cast<const int32_t*>(p.ws);
-    const int64_t slot0 = cf[n];
-    const int64_t nch = (s_len + 63) / 64;
-    const int col0 = tile * NT;
-    const int64_t last = nch > 0 ? nch - 1 : 0;
-    const unsigned char* rec0 =
-        p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot0) * p.L.rec_bytes;
-    auto rec = [&](int64_t kc) { return rec0 + (size_t)min(kc, last) * p.L.rec_bytes; };
-
-    if (w >= 4) {
-        // ------------------------------------------------------------ loaders
-        typedef Staging<T, D, NT> ST_;
-        const int lt = t - 256;
-        int src_x[ST_::NX], dst_x[ST_::NX];
-        bool has_x[ST_::NX];
-#pragma unroll
-        for (int i = 0; i < ST_::NX; ++i) {
-            const int x = lt + 256 * i;
-            has_x[i] = x < ST_::NU + ST_::NG;
-            ST_::extra_offsets(p.L, has_x[i] ? x : ST_::NU, tile, src_x[i], dst_x[i]);
-        }
-        ST_ s0, s1;
-        if (nch > 0) {
-            s0.load(rec(0), lt, src_x);
-            s0.store(sm.slot[0], lt, dst_x, has_x);
-            s1.load(rec(1), lt, src_x);
-            s0.load(rec(2), lt, src_x);
-        }
-        __syncthreads();
-        int64_t kc = 0;
-        for (; kc + 2 <= nch; kc += 2) {
-            s1.store(sm.slot[1], lt, dst_x, has_x);  // chunk kc+1
-            s1.load(rec(kc + 3), lt, src_x);
-            __syncthreads();
-            __syncthreads();
-            s0.store(sm.slot[0], lt, dst_x, has_x);  // chunk kc+2
-            s0.load(rec(kc + 4), lt, src_x);
-            __syncthreads();
-            __syncthreads();
-        }
-        if (kc < nch) {
-            __syncthreads();
-            __syncthreads();
-        }
-        return;
-    }
-
-    // ---------------------------------------------------------------- compute
-    f32x4 S[RBW][NB];
-    const int64_t sbase = ((int64_t)n * H + h) * D * D;
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+    if (!c.uwave) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int col = col0 + 16 * nb + (lane & 15);
+            mma(acc[nb], ops.Mf[0], Ub[0][nb]);
+            mma(acc[nb], ops.Mf[1], Ub[1][nb]);
+        }
+    }
+    ops.load_back(c.rec(kc + NBUF), p.L, c.uwave, c.b, c.rb, lane);
+    if constexpr (PF > 0) {
+        // touch this workgroup's share of the record PF chunks beyond the
+        // last one requested, so that its lines are in L2 when all tiles ask
+        asm volatile("" ::"v"(ops.pf));
+        ops.pf = *reinterpret_cast<const uint32_t*>(c.rec(kc + NBUF + PF) + c.pf_off);
+    }
+    if (!c.uwave) {
+        const int Lc = (int)min((int64_t)64, c.s_len - 64 * kc);
+        T* outp = reinterpret_cast<T*>(p.out);
+        const int64_t tok0 = c.s_begin + 64 * kc;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int col = c.col0 + 16 * nb + (lane & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = 16 * (RBW * w + rb) + 4 * (lane >> 4) + e;
-                S[rb][nb][e] = p.init ? p.init[sbase + (int64_t)row * D + col] : 0.f;
+                const int row = 16 * c.b + 4 * (lane >> 4) + e;
+                if (row < Lc) outp[((tok0 + row) * c.H + c.h) * D + col] = from_f32<T>(acc[nb][e]);
             }
         }
-    put_state<T, D, NT>(sm, S, w, lane);
+    }
     __syncthreads();
-    T* outp = reinterpret_cast<T*>(p.out);
-    for (int64_t kc = 0; kc < nch; ++kc)
-        recur_step<T, D, NT>(sm, S, sm.slot[kc & 1], outp, s_begin + 64 * kc,
-                             (int)min((int64_t)64, s_len - 64 * kc), H, h, col0, w, lane);
+}
 
-    if (p.fin) {
+template <typename T, int D, int NT, int NBUF, int PF>
+__global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
+    constexpr int NB = NT / 16;
+    __shared__ RecurSmem<T, D, NT> sm;
+
+    const int t = threadIdx.x;
+    const int bid = blockIdx.x;
+    const int chain = 8 * ((bid >> 3) / p.ntiles) + (bid & 7);
+    const int tile = (bid >> 3) % p.ntiles;
+    if (chain >= p.n_seqs * p.n_heads) return;
+
+    WaveCtx c;
+    c.w = t >> 6;
+    c.lane = t & 63;
+    c.b = c.w & 3;
+    c.uwave = c.w < 4;
+    c.rb = c.w;
+    c.has_rows = c.w < D / 16;
+    c.tile = tile;
+    c.col0 = tile * NT;
+    c.H = p.n_heads;
+    const int n = chain / p.n_heads;
+    c.h = chain % p.n_heads;
+    const int64_t each = p.n_seqs ? p.total_tokens / p.n_seqs : 0;
+    c.s_begin = p.cu ? (int64_t)p.cu[n] : (int64_t)n * each;
+    c.s_len = p.cu ? (int64_t)p.cu[n + 1] - c.s_begin : each;
+    const int32_t* cf = reinterpret_cast<const int32_t*>(p.ws);
+    const int64_t nch = (c.s_len + 63) / 64;
+    c.last = nch > 0 ? nch - 1 : 0;
+    c.rec_bytes = p.L.rec_bytes;
+    c.rec0 = p.ws + p.L.records_offset() + ((size_t)c.h * p.L.slots + cf[n]) * p.L.rec_bytes;
+    const int lane = c.lane;
+    {
+        // prefetch share: lines [tile * per, (tile + 1) * per) of each record,
+        // one 128-byte line per lane (lanes past the share repeat its first line)
+        const uint32_t lines = (uint32_t)((p.L.rec_bytes + 127) / 128);
+        const uint32_t per = (lines + p.ntiles - 1) / p.ntiles;
+        const uint32_t i = (uint32_t)t < per ? (uint32_t)t : 0u;
+        const uint32_t line = min((uint32_t)tile * per + i, lines - 1);
+        c.pf_off = line * 128;
+    }
+    // waves without state rows (d_k = 64) read the rows of block 0 in load_back
+    // and never use them
+    if (!c.has_rows) c.rb = 0;
+
+    // state rows 16*rb .. 16*rb+15 of this tile's columns (waves with rows only)
+    f32x4 S[NB];
+    const int64_t sbase = ((int64_t)n * c.H + c.h) * D * D;
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = c.col0 + 16 * nb + (lane & 15);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int col = col0 + 16 * nb + (lane & 15);
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * c.rb + 4 * (lane >> 4) + e;
+            S[nb][e] = (p.init && c.has_rows) ? p.init[sbase + (int64_t)row * D + col] : 0.f;
+        }
+    }
+    if (c.has_rows) {
+        typedef T V4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * (RBW * w + rb) + 4 * (lane >> 4) + e;
-                    p.fin[sbase + (int64_t)row * D + col] = S[rb][nb][e];
-                }
+        for (int nb = 0; nb < NB; ++nb) {
+            V4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(S[nb][e]);
+            *reinterpret_cast<V4*>(&sm.ST[16 * nb + (lane & 15)][16 * c.rb + 4 * (lane >> 4)]) = x;
+        }
+    }
+    __syncthreads();
+
+    if (nch > 0) {
+        // NBUF named register buffers (an array of them defeats register
+        // promotion); chunk kc is consumed from buffer kc % NBUF
+        static_assert(NBUF >= 3 && NBUF <= 5, "prefetch depth");
+        WaveOps<T, D, NT> b0, b1, b2, b3, b4;
+        auto prime = [&](WaveOps<T, D, NT>& b, int64_t k) {
+            b.load_front(c.rec(k), p.L, c.uwave, c.b, tile, lane);
+            b.load_back(c.rec(k), p.L, c.uwave, c.b, c.rb, lane);
+            if constexpr (PF > 0) b.pf = *reinterpret_cast<const uint32_t*>(c.rec(k + NBUF) + c.pf_off);
+        };
+        prime(b0, 0);
+        prime(b1, 1);
+        prime(b2, 2);
+        if constexpr (NBUF > 3) prime(b3, 3);
+        if constexpr (NBUF > 4) prime(b4, 4);
+        int64_t kc = 0;
+        for (; kc + NBUF <= nch; kc += NBUF) {
+            recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
+            recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
+            recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
+            if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF>(sm, S, b3, p, c, kc + 3);
+            if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF>(sm, S, b4, p, c, kc + 4);
+        }
+        if (kc < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
+        if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
+        if constexpr (NBUF > 3)
+            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
+        if constexpr (NBUF > 4)
+            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b3, p, c, kc + 3);
+    }
+
+    if (p.fin && c.has_rows) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int col = c.col0 + 16 * nb + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * c.rb + 4 * (lane >> 4) + e;
+                p.fin[sbase + (int64_t)row * D + col] = S[nb][e];
             }
+        }
     }
 }
+
+// Chunks whose operands are in flight ahead of the one being consumed.
+constexpr int kRecurDepth = 3;
+// Chunks beyond those in flight whose records are touched early (L2 prefetch).
+constexpr int kRecurPrefetch = 1;
 
 // Column-tile width: the widest tile that still gives at least ~2 workgroups
 // per CU; 16 otherwise (fewest columns per chain, most chains).
@@ -331,7 +343,7 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t groups = (chains + 7) / 8;
     const int64_t grid = 8 * p.ntiles * groups;
-    hipLaunchKernelGGL((recur_kernel<T, D, NT>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch>), dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -339,7 +351,6 @@ template <typename T, int D>
 hipError_t launch_recur(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     if (chains == 0) return hipSuccess;
-    // fp32 operands fill LDS at 16 columns already
     if constexpr (sizeof(T) == 2)
         if (pick_tile(chains, D, true) == 32) return launch_nt<T, D, 32>(a, stream);
     return launch_nt<T, D, 16>(a, stream);
