@@ -126,6 +126,32 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// ---------------------------------------------------------------- buffer access
+// Raw buffer resource over [base, base + bytes): the hardware range check makes
+// a load at a byte offset at or past `bytes` return zeros (no memory access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Load a V (8 or 16 bytes, or one 2- or 4-byte element) at byte offset `off`.
+template <typename V>
+__device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (sizeof(V) == 16) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    } else if constexpr (sizeof(V) == 8) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    } else if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    } else {
+        static_assert(sizeof(V) == 2, "buffer_load: 2, 4, 8 or 16 bytes");
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+    }
+}
+
+// 2^x on the hardware exponential unit.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Fragment-ordered storage ("A order"): a rows x kdim matrix stored as 16x32
 // tiles, each tile as 64 lanes x 8 elements in A-operand lane order, so one
 // wave loads a whole MFMA operand with one contiguous 16-byte (bf16) or

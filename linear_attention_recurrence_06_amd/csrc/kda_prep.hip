@@ -42,9 +42,10 @@
 //   P3 T = (I + A)^-1 in place of A: the four 16x16 diagonal inverses by forward
 //      substitution (one lane per column), then block rows 1..3 by
 //      T_RJ = -T_RR sum_K A_RK T_KJ on fp32 MFMA;
-//   P4 U = T Diag(beta) V and W^T = (Diag(beta) Khat)^T T^T on MFMA, each
+//   P4 U = (T Diag(beta)) V and W^T = Khat^T (T Diag(beta))^T on MFMA, each
 //      written straight from the accumulators in the layout the recurrence reads.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
@@ -98,9 +99,9 @@ struct PrepSmem {
             T KF[64][D + P];
         } a;
         struct {
-            T BK[D][64 + P];  // (Diag(beta) Khat)^T
-            T BV[D][64 + P];  // (Diag(beta) V)^T
-            T Tb[64][64 + P];
+            T BK[D][64 + P];  // Khat^T
+            T BV[D][64 + P];  // V^T
+            T Tb[64][64 + P];  // T Diag(beta)
             float X[4][16][17];
         } b;
     } u;
@@ -163,12 +164,14 @@ struct PrepParams {
 // (first token, length) of a chunk slot; length 0 marks an unused slot.
 __device__ __forceinline__ int2 slot_desc(const PrepParams& p, int64_t slot) {
     if (p.cu) return reinterpret_cast<const int2*>(p.ws + p.L.index_bytes)[slot];
-    const int64_t N = p.n_seqs;
-    const int64_t each = p.total_tokens / N;
-    const int64_t per = (each + 63) / 64;
-    if (per == 0 || slot >= per * N) return make_int2(0, 0);
-    const int64_t n = slot / per, kc = slot - n * per;
-    return make_int2((int)(n * each + 64 * kc), (int)min((int64_t)64, each - 64 * kc));
+    // equal lengths: T < 2^31, so every quantity here fits 32 bits
+    const uint32_t N = (uint32_t)p.n_seqs;
+    const uint32_t each = (uint32_t)(p.total_tokens / N);
+    const uint32_t per = (each + 63) / 64;
+    const uint32_t s = (uint32_t)slot;
+    if (per == 0 || s >= per * N) return make_int2(0, 0);
+    const uint32_t n = s / per, kc = s - n * per;
+    return make_int2((int)(n * each + 64 * kc), (int)min(64u, each - 64 * kc));
 }
 
 // Exclusive prefix over the four 16-lane rows of a wave of x (lanes in the same
@@ -184,45 +187,68 @@ __device__ __forceinline__ void wave_rows_scan(float x, int row, float& excl, fl
     excl = incl - x;
 }
 
-// One (chunk slot, head) item per workgroup of 512 threads.
+// One thread's share of a chunk's raw rows: tokens 2rg, 2rg+1, channels
+// (d_k/16) cg.. of q, k, g, v, and beta, in the I/O type.  Rows past the chunk's
+// length read as zeros (buffer range check), so the loads are never predicated.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
+struct RawRows {
+    static constexpr int CPT = D / 16;
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    V q[2], k[2], g[2], v[2];
+    T b[2];
+    __device__ __forceinline__ void load(const PrepParams& p, int2 d, int h, int rg, int cg) {
+        const int64_t H = p.n_heads;
+        const uint32_t E = sizeof(T);
+        const uint32_t rstride = (uint32_t)(H * D) * E;  // bytes between tokens
+        const uint32_t span = (uint32_t)(d.y - 1) * rstride + D * E;
+        const int64_t first = ((int64_t)d.x * H + h) * D;
+        const auto rq = make_rsrc((const T*)p.q + first, span);
+        const auto rk = make_rsrc((const T*)p.k + first, span);
+        const auto rgg = make_rsrc((const T*)p.g + first, span);
+        const auto rv = make_rsrc((const T*)p.v + first, span);
+        const auto rb = make_rsrc((const T*)p.beta + (int64_t)d.x * H + h,
+                                  (uint32_t)((d.y - 1) * H + 1) * E);
+        // v is issued last: it is first used after the other rows, so waiting
+        // for them does not wait for it
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t r = 2 * rg + i;
+            const uint32_t off = r * rstride + CPT * cg * E;
+            q[i] = buffer_load<V>(rq, off);
+            k[i] = buffer_load<V>(rk, off);
+            g[i] = buffer_load<V>(rgg, off);
+            b[i] = buffer_load<T>(rb, r * (uint32_t)H * E);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the v loads behind the others
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            v[i] = buffer_load<V>(rv, (2 * rg + i) * rstride + CPT * cg * E);
+    }
+};
+
+// Everything for one (chunk slot, head) item whose raw rows are in `raw`.
+template <typename T, int D>
+__device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
+                                          int h, const RawRows<T, D>& raw) {
     constexpr int CPT = D / 16;  // channels per thread in the row layout
     typedef T V __attribute__((ext_vector_type(CPT)));
     typedef T V2 __attribute__((ext_vector_type(2)));
-    __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int rg = t >> 4, cg = t & 15, lrow = lane >> 4;
     const int Rb = w >> 1;  // 16-token block of this thread's rows
-    const int64_t H = p.n_heads;
-    const int64_t item = blockIdx.x;
-    const int64_t slot = item / H;
-    const int h = (int)(item - slot * H);
-    const int2 d = slot_desc(p, slot);
-    if (d.y <= 0) return;
     unsigned char* rec = p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot) * p.L.rec_bytes;
 
-    // rows 2rg, 2rg+1 (rows past the chunk's length read its first row, then zeroed)
-    float qf[2][CPT], kf[2][CPT], gf[2][CPT], vf[2][CPT], bt[2];
+    // g is taken in base-2 units (g log2 e) from here on
+    float qf[2][CPT], kf[2][CPT], gf[2][CPT], bt[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r = 2 * rg + i;
-        const bool ok = r < d.y;
-        const int64_t row = (int64_t)d.x + (ok ? r : 0);
-        const int64_t off = (row * H + h) * D + CPT * cg;
-        const V q = *reinterpret_cast<const V*>((const T*)p.q + off);
-        const V k = *reinterpret_cast<const V*>((const T*)p.k + off);
-        const V g = *reinterpret_cast<const V*>((const T*)p.g + off);
-        const V v = *reinterpret_cast<const V*>((const T*)p.v + off);
-        const T b = ((const T*)p.beta)[row * H + h];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            qf[i][c] = ok ? to_f32(q[c]) : 0.f;
-            kf[i][c] = ok ? to_f32(k[c]) : 0.f;
-            gf[i][c] = ok ? to_f32(g[c]) : 0.f;
-            vf[i][c] = ok ? to_f32(v[c]) : 0.f;
+            qf[i][c] = to_f32(raw.q[i][c]);
+            kf[i][c] = to_f32(raw.k[i][c]);
+            gf[i][c] = to_f32(raw.g[i][c]) * 1.4426950408889634f;
         }
-        bt[i] = ok ? to_f32(b) : 0.f;
+        bt[i] = to_f32(raw.b[i]);
     }
 
     // ---------------------------------------------------------------- P0
@@ -240,8 +266,8 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
         }
         sq = row16_sum(sq);
         sk = row16_sum(sk);
-        const float rq = (p.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f) * p.scale;
-        const float rk = p.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
+        const float rq = (p.l2norm ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.0f) * p.scale;
+        const float rk = p.l2norm ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.0f;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             qf[i][c] *= rq;
@@ -266,30 +292,34 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
         gf[1][c] += add;
     }
     // per-channel table of the block-level decay factors (16 x D exponentials):
-    // thread t owns channel t % D and rows t / D + (512 / D) * i
+    // thread t owns channel t % D and rows t / D + (512 / D) * i, one row per wave
+    // and step, so each exponent is a signed sum of a run of block totals with
+    // coefficients known to the whole wave
     {
         constexpr int RSTEP = 512 / D;
-        const int c = t % D, r0 = t / D;
+        const int c = t % D;
+        const int rbase = __builtin_amdgcn_readfirstlane(t / D);
         float tb[4];
 #pragma unroll
         for (int R = 0; R < 4; ++R) tb[R] = sm.u.wsum[2 * R][c] + sm.u.wsum[2 * R + 1][c];
-        if (r0 == 0) {
+        if (rbase == 0) {
 #pragma unroll
             for (int R = 0; R < 4; ++R) sm.tau[R][c] = tb[R];
         }
-        const float t0 = tb[0], t1 = tb[1], t2 = tb[2], t3 = tb[3];
-        const float x[16] = {-t0, -t1, -t2, -t3,
-                             t1, t1 + t2, t2,
-                             0.f, t0, t0 + t1, (t0 + t1) + t2,
-                             (t1 + t2) + t3, t2 + t3, t3, 0.f,
-                             ((t0 + t1) + t2) + t3};
 #pragma unroll
         for (int i = 0; i < 16 / RSTEP; ++i) {
-            const int row = r0 + RSTEP * i;
-            float v = x[0];
+            const int row = rbase + RSTEP * i;
+            int lo, hi;  // the run of blocks summed; empty when lo > hi
+            if (row < 4) { lo = row; hi = row; }                  // e^(-tau_R)
+            else if (row < 7) { lo = row == 6 ? 2 : 1; hi = row == 4 ? 1 : 2; }
+            else if (row < 11) { lo = 0; hi = row - 8; }          // e^(rho_{R-1})
+            else if (row < 15) { lo = row - 10; hi = 3; }         // e^(rho_3 - rho_R)
+            else { lo = 0; hi = 3; }                              // Gamma_C
+            const float sg = row < 4 ? -1.f : 1.f;
+            float arg = 0.f;
 #pragma unroll
-            for (int k = 1; k < 16; ++k) v = (row == k) ? x[k] : v;
-            sm.fac[row][c] = __expf(v);
+            for (int R = 0; R < 4; ++R) arg += (lo <= R && R <= hi ? sg : 0.f) * tb[R];
+            sm.fac[row][c] = exp2_hw(arg);
         }
     }
     __syncthreads();
@@ -297,7 +327,10 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
     // ---------------------------------------------------------------- P1
     T* Qg = reinterpret_cast<T*>(rec + p.L.off_q);
     T* Ktg = reinterpret_cast<T*>(rec + p.L.off_kt);
-    V2 rk[CPT], rv[CPT];  // beta Khat and beta V of the two rows, per channel
+    // Khat and V of the two rows, per channel, as packed words (the rotation
+    // below moves whole words)
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, uint64_t>::type W2;
+    W2 rk[CPT], rv[CPT];
     float kpT[CPT][2];
     float tauR[CPT], Gs[CPT], Kp[CPT];
 #pragma unroll
@@ -306,20 +339,20 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
         Gs[c] = sm.fac[7 + Rb][CPT * cg + c];
         Kp[c] = sm.fac[11 + Rb][CPT * cg + c];
     }
+    V2 kh[CPT];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = 2 * rg + i;
         float ke[CPT], qe[CPT], kfv[CPT], qh[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const float E = __expf(gf[i][c]);
-            const float F = __expf(tauR[c] - gf[i][c]);
+            const float E = exp2_hw(gf[i][c]);
+            const float F = exp2_hw(tauR[c] - gf[i][c]);
             ke[c] = kf[i][c] * E;
             qe[c] = qf[i][c] * E;
             kfv[c] = kf[i][c] * F;
             qh[c] = qe[c] * Gs[c];
-            rk[c][i] = from_f32<T>(bt[i] * ke[c] * Gs[c]);
-            rv[c][i] = from_f32<T>(bt[i] * vf[i][c]);
+            kh[c][i] = from_f32<T>(ke[c] * Gs[c]);
             kpT[c][i] = kfv[c] * Kp[c];
         }
         store_n<T, CPT>(&sm.u.a.KE[r][CPT * cg], ke);
@@ -327,6 +360,8 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
         store_n<T, CPT>(&sm.u.a.KF[r][CPT * cg], kfv);
         store_n<T, CPT>(Qg + aorder_index(r, CPT * cg, D), qh);
     }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) rk[c] = __builtin_bit_cast(W2, kh[c]);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) store_n<T, 2>(Ktg + aorder_index(CPT * cg + c, 2 * rg, 64), kpT[c]);
     if (rg == 0) {
@@ -359,16 +394,19 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
     __syncthreads();
 
     // ---------------------------------------------------------------- P3
-    // transposed beta*Khat and beta*V tiles (the operands of W^T and U).  Lane
+    // transposed Khat and V tiles (the operands of W^T and U).  Lane
     // (rg, cg) holds 2 tokens x CPT channels; at write step j it stores channel
     // (j + cg) % CPT, so the 16 lanes of a token group spread over the banks
     // (a plain channel order puts them on one bank).  The rotation is a barrel
-    // shift of packed token pairs across the channel index.
+    // shift of packed token pairs across the channel index.  V is first used
+    // here, so its loads have had P0-P2 to arrive.
     {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) rv[c] = __builtin_bit_cast(W2, V2{raw.v[0][c], raw.v[1][c]});
 #pragma unroll
         for (int sh = 1; sh < CPT; sh <<= 1) {
             const bool on = (cg & sh) != 0;
-            V2 tk[CPT], tv[CPT];
+            W2 tk[CPT], tv[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 tk[j] = on ? rk[(j + sh) % CPT] : rk[j];
@@ -383,8 +421,8 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = CPT * cg + ((j + cg) % CPT);
-            *reinterpret_cast<V2*>(&sm.u.b.BK[c][2 * rg]) = rk[j];
-            *reinterpret_cast<V2*>(&sm.u.b.BV[c][2 * rg]) = rv[j];
+            *reinterpret_cast<W2*>(&sm.u.b.BK[c][2 * rg]) = rk[j];
+            *reinterpret_cast<W2*>(&sm.u.b.BV[c][2 * rg]) = rv[j];
         }
     }
     if (w == 0) {
@@ -435,11 +473,12 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
         __syncthreads();
     }
     {
-        // thread t converts row t / 8, columns 8 * (t % 8) .. +7 (zero above the diagonal)
+        // thread t converts row t / 8, columns 8 * (t % 8) .. +7 of T Diag(beta)
+        // (zero above the diagonal)
         const int r = t >> 3, c0 = 8 * (t & 7);
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = (c0 + j <= r) ? sm.A[r][c0 + j] : 0.f;
+        for (int j = 0; j < 8; ++j) x[j] = (c0 + j <= r) ? sm.A[r][c0 + j] * sm.beta[c0 + j] : 0.f;
         store_frag<T>(&sm.u.b.Tb[r][c0], make_frag<T>(x));
     }
     __syncthreads();
@@ -475,6 +514,23 @@ __global__ __launch_bounds__(512, 2) void prep_kernel(PrepParams p) {
             store_n<T, 4>(Wg + aorder_index(16 * R + (lane & 15), 16 * nb + 4 * (lane >> 4), D), wv);
         }
     }
+}
+
+// One (chunk slot, head) item per workgroup; two workgroups share a CU (80 KB
+// of LDS and at most 128 VGPRs each).
+template <typename T, int D>
+__global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
+    __shared__ PrepSmem<T, D> sm;
+    const int t = threadIdx.x;
+    const uint32_t H = (uint32_t)p.n_heads;
+    const uint32_t item = blockIdx.x;  // the grid is one workgroup per item
+    const uint32_t slot = item / H;
+    const int h = (int)(item - slot * H);
+    const int2 d = slot_desc(p, slot);
+    if (d.y <= 0) return;
+    RawRows<T, D> raw;
+    raw.load(p, d, h, t >> 4, t & 15);
+    prep_item<T, D>(p, sm, slot, h, raw);
 }
 
 // Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks.

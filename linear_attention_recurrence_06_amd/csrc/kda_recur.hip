@@ -274,7 +274,7 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     if (nch > 0) {
         // NBUF named register buffers (an array of them defeats register
         // promotion); chunk kc is consumed from buffer kc % NBUF
-        static_assert(NBUF >= 3 && NBUF <= 5, "prefetch depth");
+        static_assert(NBUF >= 2 && NBUF <= 5, "prefetch depth");
         WaveOps<T, D, NT> b0, b1, b2, b3, b4;
         auto prime = [&](WaveOps<T, D, NT>& b, int64_t k) {
             b.load_front(c.rec(k), p.L, c.uwave, c.b, tile, lane);
@@ -283,19 +283,20 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
         };
         prime(b0, 0);
         prime(b1, 1);
-        prime(b2, 2);
+        if constexpr (NBUF > 2) prime(b2, 2);
         if constexpr (NBUF > 3) prime(b3, 3);
         if constexpr (NBUF > 4) prime(b4, 4);
         int64_t kc = 0;
         for (; kc + NBUF <= nch; kc += NBUF) {
             recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
             recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
-            recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
+            if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
             if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF>(sm, S, b3, p, c, kc + 3);
             if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF>(sm, S, b4, p, c, kc + 4);
         }
         if (kc < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
-        if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
+        if constexpr (NBUF > 2)
+            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
         if constexpr (NBUF > 3)
             if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
         if constexpr (NBUF > 4)
