@@ -176,12 +176,20 @@ def main():
     tb = decode_token_bytes(DECODE_N, DECODE_H, D)
     d_traffic = counter_traffic("decode")
 
-    if args.profile:
-        # plain device copy of known size: scales the HBM byte counters
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+    # plain 1 GiB device-to-device copy: the practical HBM ceiling on this machine
+    # (and, in --profile runs, the known-size transfer that scales the counters)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for i in range(1 if args.profile else 4):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
         dst.copy_(src)
+        c1.record(stream)
         torch.cuda.synchronize(dev)
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_GBps = 2 * (1 << 30) / (min(copy_ms[1:] or copy_ms) * 1e-3) / 1e9
+    del src, dst
 
     # ------------------------------------------------------------------ CPU baseline
     cpu = None
@@ -198,8 +206,18 @@ def main():
             kda_oracle.prefill(hq, hk, hv, hg, hb, initial_state=hs0, threads=threads)
             spent += time.perf_counter() - c0
             reps += 1
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         cpu = {"value": T * reps / spent, "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "token_heads_per_s": T * H * reps / spent,
+               "cpu_model": cpu_model,
                "sample": f"the full prefill workload (T=8192, all 32 heads, fp64 "
                          f"token-by-token recurrence) run {reps} times, {spent:.1f} s, "
                          f"one (sequence, head) chain per thread"}
@@ -231,6 +249,10 @@ def main():
             "traffic": p_traffic,
             "algorithmic_bytes_per_call": p_bytes,
             "avg_call_us": call_avg_s * 1e6,
+            "median_call_us": float(np.median(call_ms)) * 1e3,
+            "min_call_us": float(np.min(call_ms)) * 1e3,
+            "practical_hbm_GBps": copy_GBps,
+            "frac_of_practical": p_achieved / copy_GBps,
             "mfma_view_tflops": prefill_executed_flops(T, H, D) / call_avg_s / 1e12,
             "mfma_view_frac": prefill_executed_flops(T, H, D) / call_avg_s / 1e12 / BF16_PEAK_TFLOPS,
         },
@@ -251,6 +273,10 @@ def main():
                 "traffic": d_traffic,
                 "algorithmic_bytes_per_call": sb + tb,
                 "avg_call_us": d_avg_s * 1e6,
+                "median_call_us": float(np.median(d_ms)) * 1e3,
+                "total_ms": float(np.sum(d_ms)),
+                "practical_hbm_GBps": copy_GBps,
+                "frac_of_practical": (sb + tb) / d_avg_s / 1e9 / copy_GBps,
             },
         },
     }
