@@ -149,6 +149,35 @@ def main():
     p_achieved = p_bytes / call_avg_s / 1e9
     p_traffic = counter_traffic("prefill")
 
+    # checkpointed prefill (intermediate states every `interval` chunks)
+    ckpt = {}
+    for interval in (16, 1):
+        n_ck = kda.kda_checkpoint_count(dims, None, interval)
+        ck_buf = torch.empty((n_ck, H, D, D), dtype=torch.float32, device=dev)
+        reps = max(3, args.steps // 4)
+        for i in range(2):
+            kda.kda_chunk_prefill_checkpoints(
+                sets[i]["q"], sets[i]["k"], sets[i]["v"], sets[i]["g"], sets[i]["beta"],
+                sets[i]["initial_state"], None, out, fin, checkpoint_interval=interval,
+                checkpoints=ck_buf, workspace=ws, stream=stream)
+        ck_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for i in range(reps):
+            s_ = sets[i % len(sets)]
+            ck_ev[i][0].record(stream)
+            kda.kda_chunk_prefill_checkpoints(
+                s_["q"], s_["k"], s_["v"], s_["g"], s_["beta"], s_["initial_state"], None, out,
+                fin, checkpoint_interval=interval, checkpoints=ck_buf, workspace=ws,
+                stream=stream)
+            ck_ev[i][1].record(stream)
+        torch.cuda.synchronize(dev)
+        ck_us = float(np.median([a.elapsed_time(b) for a, b in ck_ev])) * 1e3
+        ckpt[f"every_{interval}_chunks"] = {
+            "checkpoints": n_ck, "bytes_written": n_ck * H * D * D * 4,
+            "median_call_us": ck_us,
+            "overhead_vs_plain_median": ck_us / (float(np.median(call_ms)) * 1e3) - 1.0}
+        del ck_buf
+
     # ------------------------------------------------------------------ decode
     dw = make_config_decode(3, device=dev, steps=args.decode_steps)
     state = dw["state"]
@@ -257,6 +286,7 @@ def main():
             "mfma_view_frac": prefill_executed_flops(T, H, D) / call_avg_s / 1e12 / BF16_PEAK_TFLOPS,
         },
         "cpu_baseline": cpu,
+        "prefill_checkpoints": ckpt,
         "decode": {
             "workload": CONFIGS[3].name.replace(", 100 steps", ""),
             "steps": args.decode_steps,

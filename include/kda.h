@@ -119,7 +119,7 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Inside a 64-token chunk the
  * decay ratios are factored around 16-token block boundaries; every factor
- * stays within exp(+-40) when g >= -5 in every channel of every token (per-token
+ * stays within exp(+-80) when g >= -5 in every channel of every token (per-token
  * retention alpha >= 0.0067).  Below that the diagonal 16-token blocks may
  * under- or overflow and lose accuracy.
  */
@@ -128,6 +128,46 @@ kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
                              const float* initial_state, const int32_t* cu_seqlens,
                              void* out, float* final_state, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Number of intermediate states kda_chunk_prefill_checkpoints writes: for each
+ * sequence of c = ceil(len / 64) chunks, floor((c - 1) / checkpoint_interval)
+ * (none for an empty sequence).  host_cu_seqlens is HOST memory, int32 [N + 1]
+ * (NULL: N equal lengths, as in kda_chunk_prefill).  Returns -1 when the
+ * descriptor or the interval (must be >= 1) is invalid. */
+int64_t kda_checkpoint_count(const kda_dims* dims, const int32_t* host_cu_seqlens,
+                             int32_t checkpoint_interval);
+
+/* Chunked prefill that also records intermediate states, so that a later call
+ * can resume any sequence from a saved prefix instead of recomputing it.  A
+ * fixed-size state is overwritten as the sequence advances, so reusing an
+ * earlier prefix needs a snapshot taken before it changes ("Kimi K3: The Manos,
+ * The Mythos, The Legendos", Context: the serving engine keeps selected state
+ * checkpoints).
+ *
+ * Same arguments, rules and results as kda_chunk_prefill, plus:
+ *   checkpoint_interval : >= 1; one checkpoint every checkpoint_interval
+ *                         chunks (64 * checkpoint_interval tokens) of each sequence
+ *   checkpoints         : device fp32 [C, H, d_k, d_v] with C =
+ *                         kda_checkpoint_count(dims, cu_seqlens on the host,
+ *                         checkpoint_interval), 4-byte aligned, required when
+ *                         C > 0.  The checkpoints of sequence n follow those of
+ *                         sequences 0..n-1; its j-th (j = 0, 1, ...) is the state
+ *                         after its first 64 * checkpoint_interval * (j + 1) tokens,
+ *                         for every such boundary strictly inside the sequence (the
+ *                         state at its end is final_state).  It is bitwise the
+ *                         final state of a prefill of that prefix alone.  Must not
+ *                         overlap any other buffer.
+ * A boundary that is not a multiple of 64 tokens (a prompt boundary) is served
+ * by ending a sequence there: final_state is exact at any length, and a prefill
+ * started from it continues exactly.
+ */
+kda_status kda_chunk_prefill_checkpoints(const kda_dims* dims, const void* q, const void* k,
+                                         const void* v, const void* g, const void* beta,
+                                         const float* initial_state,
+                                         const int32_t* cu_seqlens, void* out,
+                                         float* final_state, int32_t checkpoint_interval,
+                                         float* checkpoints, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* One decode step: one new token for each of N sequences.
  *

@@ -5,8 +5,10 @@ this package holds its sources (csrc/), the in-tree build script and a thin
 ctypes binding whose functions carry the C ABI's names.
 """
 
-from .kda import (KDAError, kda_chunk_prefill, kda_decode_step, kda_dims,
+from .kda import (KDAError, kda_checkpoint_count, kda_chunk_prefill,
+                  kda_chunk_prefill_checkpoints, kda_decode_step, kda_dims,
                   kda_prefill_workspace_bytes, load_library, make_dims, status_string)
 
-__all__ = ["KDAError", "kda_chunk_prefill", "kda_decode_step", "kda_dims",
+__all__ = ["KDAError", "kda_checkpoint_count", "kda_chunk_prefill",
+           "kda_chunk_prefill_checkpoints", "kda_decode_step", "kda_dims",
            "kda_prefill_workspace_bytes", "load_library", "make_dims", "status_string"]

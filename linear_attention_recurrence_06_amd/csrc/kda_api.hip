@@ -104,16 +104,23 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
         .total();
 }
 
-kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, const void* v,
-                             const void* g, const void* beta, const float* initial_state,
-                             const int32_t* cu_seqlens, void* out, float* final_state,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two prefill entry points (interval 0: no checkpoints).
+kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
+                        const void* g, const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, void* out, float* final_state,
+                        int32_t interval, float* checkpoints, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     kda_status st = check_dims(d, true);
     if (st != KDA_OK) return st;
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads, D = d->d_k;
     if (N == 0) return T == 0 ? KDA_OK : KDA_ERR_INVALID_ARG;
     if (!cu_seqlens && T % N != 0) return KDA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
+    if (interval > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
     // q, k, v, g rows and the workspace are read with 16-byte vector accesses;
     // beta, out and the states element by element
@@ -124,7 +131,7 @@ kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, co
     const void* elt_ptrs[] = {beta, out};
     for (const void* p : elt_ptrs)
         if (p && !aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
-    const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens};
+    const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens, checkpoints};
     for (const void* p : f32_ptrs)
         if (p && !aligned_to(p, 4)) return KDA_ERR_MISALIGNED;
     if (workspace_bytes < kda_prefill_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
@@ -152,6 +159,18 @@ kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, co
         for (const Range& r : others)
             if (overlap(r_fin, r)) return KDA_ERR_INVALID_ARG;
     }
+    if (interval > 0 && !cu_seqlens) {
+        // equal lengths: the checkpoint count is known here, so check its buffer too
+        const int64_t C = kda_checkpoint_count(d, nullptr, interval);
+        const Range r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
+        const Range all[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
+                             range_of(g, qb), range_of(beta, bb), r_out,
+                             initial_state ? range_of(initial_state, sb) : Range{0, 0},
+                             final_state ? range_of(final_state, sb) : Range{0, 0},
+                             range_of(workspace, workspace_bytes)};
+        for (const Range& r : all)
+            if (overlap(r_ck, r)) return KDA_ERR_INVALID_ARG;
+    }
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -167,10 +186,54 @@ kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, co
     a.bf16 = d->io_dtype == KDA_BF16;
     a.scale = d->scale;
     a.l2norm = d->qk_l2norm;
+    a.ckpt_interval = interval;
+    a.checkpoints = checkpoints;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
     a.cu_count = current_cu_count();
     hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, const float* initial_state,
+                             const int32_t* cu_seqlens, void* out, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, 0,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+int64_t kda_checkpoint_count(const kda_dims* d, const int32_t* host_cu_seqlens,
+                             int32_t checkpoint_interval) {
+    if (check_dims(d, true) != KDA_OK || checkpoint_interval < 1) return -1;
+    const int64_t N = d->num_seqs, T = d->total_tokens;
+    if (N == 0) return 0;
+    if (!host_cu_seqlens && T % N != 0) return -1;
+    int64_t count = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t len = host_cu_seqlens
+                                ? (int64_t)host_cu_seqlens[n + 1] - host_cu_seqlens[n]
+                                : T / N;
+        if (len < 0) return -1;
+        const int64_t c = (len + 63) / 64;
+        if (c > 0) count += (c - 1) / checkpoint_interval;
+    }
+    return count;
+}
+
+kda_status kda_chunk_prefill_checkpoints(const kda_dims* d, const void* q, const void* k,
+                                         const void* v, const void* g, const void* beta,
+                                         const float* initial_state,
+                                         const int32_t* cu_seqlens, void* out,
+                                         float* final_state, int32_t checkpoint_interval,
+                                         float* checkpoints, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (checkpoint_interval < 1) return KDA_ERR_INVALID_ARG;
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                        checkpoint_interval, checkpoints, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, const void* v,

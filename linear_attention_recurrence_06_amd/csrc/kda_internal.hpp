@@ -21,6 +21,7 @@ struct DecodeArgs {
 };
 
 // Workspace for one prefill call: a chunk index (first chunk slot of each
+// sequence, int32 [N+1]), a checkpoint index (first checkpoint of each
 // sequence, int32 [N+1]), one descriptor per chunk slot (first token and
 // length, int32 x 2; length 0 marks an unused slot), then one record per
 // (chunk slot, head) with the factors the recurrence kernel consumes, stored head-major
@@ -38,11 +39,13 @@ struct PrefillLayout {
     int elt;               // bytes per I/O element
     int64_t slots;         // chunk slots (upper bound on the chunk count)
     int64_t heads;
-    size_t index_bytes;    // chunk index, padded to 256 B
+    size_t index_bytes;    // chunk index, padded to 256 B (checkpoint index: the same)
     size_t desc_bytes;     // chunk-slot descriptors, padded to 256 B
     size_t rec_bytes;      // bytes per (slot, head) record
     size_t off_w, off_q, off_m, off_kt, off_u, off_gc;
-    __host__ __device__ size_t records_offset() const { return index_bytes + desc_bytes; }
+    __host__ __device__ size_t ckidx_offset() const { return index_bytes; }
+    __host__ __device__ size_t desc_offset() const { return 2 * index_bytes; }
+    __host__ __device__ size_t records_offset() const { return 2 * index_bytes + desc_bytes; }
     size_t total() const { return records_offset() + rec_bytes * (size_t)slots * (size_t)heads; }
 };
 
@@ -84,6 +87,8 @@ struct PrefillArgs {
     float scale;
     int l2norm;
     int cu_count;                // compute units of the device (persistent grids)
+    int32_t ckpt_interval;       // 0: no checkpoints
+    float* checkpoints;          // [C, H, d, d] when ckpt_interval > 0
     PrefillLayout layout;
 };
 

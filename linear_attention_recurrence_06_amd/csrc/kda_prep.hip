@@ -163,7 +163,7 @@ struct PrepParams {
 
 // (first token, length) of a chunk slot; length 0 marks an unused slot.
 __device__ __forceinline__ int2 slot_desc(const PrepParams& p, int64_t slot) {
-    if (p.cu) return reinterpret_cast<const int2*>(p.ws + p.L.index_bytes)[slot];
+    if (p.cu) return reinterpret_cast<const int2*>(p.ws + p.L.desc_offset())[slot];
     // equal lengths: T < 2^31, so every quantity here fits 32 bits
     const uint32_t N = (uint32_t)p.n_seqs;
     const uint32_t each = (uint32_t)(p.total_tokens / N);
@@ -231,7 +231,6 @@ template <typename T, int D>
 __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
                                           int h, const RawRows<T, D>& raw) {
     constexpr int CPT = D / 16;  // channels per thread in the row layout
-    typedef T V __attribute__((ext_vector_type(CPT)));
     typedef T V2 __attribute__((ext_vector_type(2)));
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int rg = t >> 4, cg = t & 15, lrow = lane >> 4;
@@ -533,35 +532,50 @@ __global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
     prep_item<T, D>(p, sm, slot, h, raw);
 }
 
-// Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks.
-// One workgroup; sequences are processed 256 at a time with a running carry.
+// Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks;
+// with checkpoints every `interval` chunks also ck[n] = first checkpoint of
+// sequence n (floor((chunks - 1) / interval) per non-empty sequence).  One
+// workgroup; sequences are processed 256 at a time with running carries.
 __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t* __restrict__ cu,
                                                           int32_t n_seqs, int64_t total_tokens,
-                                                          int32_t* __restrict__ cf) {
-    __shared__ int32_t s_scan[256];
+                                                          int32_t* __restrict__ cf,
+                                                          int32_t* __restrict__ ck,
+                                                          int32_t interval) {
+    __shared__ int32_t s_scan[2][256];
     const int t = threadIdx.x;
     const int64_t each = n_seqs ? total_tokens / n_seqs : 0;
-    int32_t carry = 0;
+    int32_t carry = 0, ccarry = 0;
     for (int base = 0; base < n_seqs; base += 256) {
         const int n = base + t;
-        int32_t c = 0;
+        int32_t c = 0, kc = 0;
         if (n < n_seqs) {
             const int64_t len = cu ? (int64_t)cu[n + 1] - cu[n] : each;
             c = (int32_t)((len + 63) / 64);
+            kc = (interval > 0 && c > 0) ? (c - 1) / interval : 0;
         }
-        s_scan[t] = c;
+        s_scan[0][t] = c;
+        s_scan[1][t] = kc;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
-            const int32_t x = (t >= off) ? s_scan[t - off] : 0;
+            const int32_t x = (t >= off) ? s_scan[0][t - off] : 0;
+            const int32_t y = (t >= off) ? s_scan[1][t - off] : 0;
             __syncthreads();
-            s_scan[t] += x;
+            s_scan[0][t] += x;
+            s_scan[1][t] += y;
             __syncthreads();
         }
-        if (n < n_seqs) cf[n] = carry + s_scan[t] - c;
-        carry += s_scan[255];
+        if (n < n_seqs) {
+            cf[n] = carry + s_scan[0][t] - c;
+            ck[n] = ccarry + s_scan[1][t] - kc;
+        }
+        carry += s_scan[0][255];
+        ccarry += s_scan[1][255];
         __syncthreads();
     }
-    if (t == 0) cf[n_seqs] = carry;
+    if (t == 0) {
+        cf[n_seqs] = carry;
+        ck[n_seqs] = ccarry;
+    }
 }
 
 // Chunk-slot descriptors for packed sequences: desc[s] = (first token, length)
@@ -598,8 +612,9 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     p.l2norm = a.l2norm;
     p.L = a.layout;
     int32_t* cf = reinterpret_cast<int32_t*>(a.workspace);
+    int32_t* ck = reinterpret_cast<int32_t*>(a.workspace + a.layout.ckidx_offset());
     hipLaunchKernelGGL((chunk_index_kernel), dim3(1), dim3(256), 0, stream, a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, cf);
+                       a.n_seqs, a.total_tokens, cf, ck, a.ckpt_interval);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.total_tokens == 0) return hipSuccess;
@@ -607,7 +622,7 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
         const unsigned nb = (unsigned)((a.layout.slots + 255) / 256);
         hipLaunchKernelGGL((chunk_desc_kernel), dim3(nb), dim3(256), 0, stream, a.cu_seqlens,
                            a.n_seqs, cf, a.layout.slots,
-                           reinterpret_cast<int2*>(a.workspace + a.layout.index_bytes));
+                           reinterpret_cast<int2*>(a.workspace + a.layout.desc_offset()));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t items = a.layout.slots * a.n_heads;

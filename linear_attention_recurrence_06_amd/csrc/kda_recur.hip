@@ -52,8 +52,10 @@ struct RecurParams {
     const float* init;
     float* fin;
     void* out;
+    float* ckpt;            // checkpoints [C, H, d, d] (checkpointing variant only)
     int64_t total_tokens;
     int32_t n_seqs, n_heads, ntiles;
+    int32_t ckpt_interval;  // chunks between checkpoints (checkpointing variant only)
     PrefillLayout L;
 };
 
@@ -109,6 +111,7 @@ struct WaveCtx {
     int64_t s_len;
     int64_t H;
     int h, col0, tile, w, lane, b, rb;
+    int64_t ck0;                // first checkpoint of the sequence
     uint32_t pf_off;            // byte offset of this lane's prefetch line in a record
     bool uwave, has_rows;
     __device__ __forceinline__ const unsigned char* rec(int64_t kc) const {
@@ -117,7 +120,8 @@ struct WaveCtx {
 };
 
 // One chunk: consume `ops` (chunk kc), then refill it with chunk kc + NBUF.
-template <typename T, int D, int NT, int NBUF, int PF>
+// CK: also store the state after every ckpt_interval-th chunk (a checkpoint).
+template <typename T, int D, int NT, int NBUF, int PF, bool CK>
 __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[NT / 16],
                                            WaveOps<T, D, NT>& ops, const RecurParams& p,
                                            const WaveCtx& c, int64_t kc) {
@@ -170,6 +174,21 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
             for (int e = 0; e < 4; ++e) x[e] = from_f32<T>(S[nb][e]);
             *reinterpret_cast<V4*>(&sm.ST[16 * nb + (lane & 15)][16 * c.rb + 4 * (lane >> 4)]) = x;
         }
+        if constexpr (CK) {
+            // state after chunk kc, when kc + 1 is a multiple of the interval and
+            // the sequence goes on
+            if ((kc + 1) % p.ckpt_interval == 0 && kc < c.last) {
+                const int64_t idx = c.ck0 + (kc + 1) / p.ckpt_interval - 1;
+                float* dst = p.ckpt + ((idx * c.H + c.h) * D) * D;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int col = c.col0 + 16 * nb + (lane & 15);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(int64_t)(16 * c.rb + 4 * (lane >> 4) + e) * D + col] = S[nb][e];
+                }
+            }
+        }
     }
     if (!c.uwave) {
 #pragma unroll
@@ -202,7 +221,7 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
     __syncthreads();
 }
 
-template <typename T, int D, int NT, int NBUF, int PF>
+template <typename T, int D, int NT, int NBUF, int PF, bool CK>
 __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     constexpr int NB = NT / 16;
     __shared__ RecurSmem<T, D, NT> sm;
@@ -233,6 +252,7 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     c.last = nch > 0 ? nch - 1 : 0;
     c.rec_bytes = p.L.rec_bytes;
     c.rec0 = p.ws + p.L.records_offset() + ((size_t)c.h * p.L.slots + cf[n]) * p.L.rec_bytes;
+    c.ck0 = CK ? reinterpret_cast<const int32_t*>(p.ws + p.L.ckidx_offset())[n] : 0;
     const int lane = c.lane;
     {
         // prefetch share: lines [tile * per, (tile + 1) * per) of each record,
@@ -288,19 +308,19 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
         if constexpr (NBUF > 4) prime(b4, 4);
         int64_t kc = 0;
         for (; kc + NBUF <= nch; kc += NBUF) {
-            recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
-            recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
-            if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
-            if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF>(sm, S, b3, p, c, kc + 3);
-            if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF>(sm, S, b4, p, c, kc + 4);
+            recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b0, p, c, kc);
+            recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b1, p, c, kc + 1);
+            if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b2, p, c, kc + 2);
+            if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b3, p, c, kc + 3);
+            if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b4, p, c, kc + 4);
         }
-        if (kc < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b0, p, c, kc);
+        if (kc < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b0, p, c, kc);
         if constexpr (NBUF > 2)
-            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b1, p, c, kc + 1);
+            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b1, p, c, kc + 1);
         if constexpr (NBUF > 3)
-            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b2, p, c, kc + 2);
+            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b2, p, c, kc + 2);
         if constexpr (NBUF > 4)
-            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF>(sm, S, b3, p, c, kc + 3);
+            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b3, p, c, kc + 3);
     }
 
     if (p.fin && c.has_rows) {
@@ -336,6 +356,8 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     p.init = a.initial_state;
     p.fin = a.final_state;
     p.out = a.out;
+    p.ckpt = a.checkpoints;
+    p.ckpt_interval = a.ckpt_interval;
     p.total_tokens = a.total_tokens;
     p.n_seqs = a.n_seqs;
     p.n_heads = a.n_heads;
@@ -344,7 +366,12 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t groups = (chains + 7) / 8;
     const int64_t grid = 8 * p.ntiles * groups;
-    hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    if (a.ckpt_interval > 0)
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch, true>),
+                           dim3((unsigned)grid), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch, false>),
+                           dim3((unsigned)grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED, \
 KDA_BF16, KDA_FP32 = 0, 1
 
 #: every symbol include/kda.h declares
-EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_decode_step",
-            "kda_status_string", "kda_version")
+EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
+            "kda_chunk_prefill_checkpoints", "kda_decode_step", "kda_status_string",
+            "kda_version")
 
 
 class kda_dims(ctypes.Structure):
@@ -71,6 +72,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_prefill.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_checkpoint_count.argtypes = [D, P, ctypes.c_int32]
+    lib.kda_checkpoint_count.restype = ctypes.c_int64
+    lib.kda_chunk_prefill_checkpoints.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_int32,
+                                                  P, P, ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_checkpoints.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -174,6 +180,81 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_prefill")
     return out, final_state
+
+
+def kda_checkpoint_count(dims: kda_dims, host_cu_seqlens=None, checkpoint_interval: int = 1) -> int:
+    """Number of intermediate states a checkpointed prefill writes (host
+    cu_seqlens: any int sequence, or None for equal lengths)."""
+    lib = load_library()
+    if host_cu_seqlens is None:
+        return int(lib.kda_checkpoint_count(ctypes.byref(dims), None, int(checkpoint_interval)))
+    arr = (ctypes.c_int32 * len(host_cu_seqlens))(*[int(x) for x in host_cu_seqlens])
+    return int(lib.kda_checkpoint_count(ctypes.byref(dims), arr, int(checkpoint_interval)))
+
+
+def kda_chunk_prefill_checkpoints(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  g: torch.Tensor, beta: torch.Tensor,
+                                  initial_state: Optional[torch.Tensor] = None,
+                                  cu_seqlens: Optional[torch.Tensor] = None,
+                                  out: Optional[torch.Tensor] = None,
+                                  final_state: Optional[torch.Tensor] = None, *,
+                                  checkpoint_interval: int,
+                                  checkpoints: Optional[torch.Tensor] = None,
+                                  host_cu_seqlens=None, num_seqs: Optional[int] = None,
+                                  scale: float = 1.0, qk_l2norm: bool = True,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  output_final_state: bool = True, stream=None):
+    """Chunked prefill that also returns intermediate states (include/kda.h,
+    kda_chunk_prefill_checkpoints).  Returns ``(out, final_state, checkpoints)``
+    with checkpoints ``[C, H, d_k, d_v]`` float32: sequence n's states after
+    each ``64 * checkpoint_interval`` of its tokens, strictly inside it.  Sizing
+    needs the lengths on the host: pass ``host_cu_seqlens`` or they are copied
+    from ``cu_seqlens``."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+        if host_cu_seqlens is None:
+            host_cu_seqlens = cu_seqlens.cpu().tolist()
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+        host_cu_seqlens = None
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("g", g, (T, H, dk)),
+                         ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
+        _check_tensor(name, t, shp, dt, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (T, H, dv), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    C = kda_checkpoint_count(dims, host_cu_seqlens, checkpoint_interval)
+    if C < 0:
+        raise KDAError(KDA_ERR_INVALID_ARG, "kda_checkpoint_count")
+    if checkpoints is None:
+        checkpoints = torch.empty((max(C, 1), H, dk, dv), dtype=torch.float32, device=dev)
+    elif checkpoints.shape[0] < C or tuple(checkpoints.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"checkpoints must be [>= {C}, {H}, {dk}, {dv}] float32")
+    need = kda_prefill_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_prefill_checkpoints(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+        int(checkpoint_interval), _ptr(checkpoints), _ptr(workspace), workspace.numel(),
+        _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_prefill_checkpoints")
+    return out, final_state, checkpoints[:C]
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

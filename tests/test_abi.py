@@ -50,13 +50,13 @@ def test_status_strings(kda):
 def test_workspace_bytes(kda):
     d = kda.make_dims(8192, 1, 32, 128, 128, kda.KDA_BF16)
     ws = kda.kda_prefill_workspace_bytes(d)
-    # chunk index (N+1 int32) and one (token, length) descriptor per chunk slot,
-    # each padded to 256 B, then per (chunk slot, head): W, Qhat, U (64x128),
-    # Kprime^T (128x64), M (64x64) bf16 and 128 fp32
+    # chunk index and checkpoint index (N+1 int32 each) and one (token, length)
+    # descriptor per chunk slot, each padded to 256 B, then per (chunk slot,
+    # head): W, Qhat, U (64x128), Kprime^T (128x64), M (64x64) bf16 and 128 fp32
     rec = (4 * 64 * 128 + 64 * 64) * 2 + 128 * 4
     slots = 8192 // 64 + 1
     desc = -(-slots * 8 // 256) * 256
-    assert ws == 256 + desc + rec * slots * 32
+    assert ws == 2 * 256 + desc + rec * slots * 32
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 128, 128, kda.KDA_FP32)) == 0
@@ -121,3 +121,47 @@ def test_decode_validation(kda):
     bad = kda.make_dims(9, 8, 2, 128, 128, kda.KDA_BF16)   # decode needs T == N
     assert call(args, bad) == kda.KDA_ERR_INVALID_ARG
     assert call(args, kda.make_dims(0, 0, 2, 128, 128, kda.KDA_BF16)) == kda.KDA_OK
+
+
+def test_checkpoint_count(kda):
+    """floor((ceil(len / 64) - 1) / interval) states per non-empty sequence."""
+    d = kda.make_dims(8192, 1, 32, 128, 128, kda.KDA_BF16)
+    assert kda.kda_checkpoint_count(d, None, 1) == 127
+    assert kda.kda_checkpoint_count(d, None, 16) == 7
+    assert kda.kda_checkpoint_count(d, None, 128) == 0
+    lens = [1, 63, 64, 65, 0, 127, 128, 129, 300]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    dv = kda.make_dims(cu[-1], len(lens), 3, 128, 128, kda.KDA_BF16)
+    chunks = [-(-L // 64) for L in lens]
+    for interval in (1, 2, 3):
+        expect = sum((c - 1) // interval for c in chunks if c > 0)
+        assert kda.kda_checkpoint_count(dv, cu, interval) == expect
+    assert kda.kda_checkpoint_count(dv, cu, 0) == -1
+    assert kda.kda_checkpoint_count(kda.make_dims(100, 3, 1, 128, 128, kda.KDA_BF16), None, 1) == -1
+
+
+def test_checkpoint_validation(kda):
+    lib = kda.load_library()
+    d = kda.make_dims(1024, 2, 4, 128, 128, kda.KDA_BF16)
+    T, H, D = 1024, 4, 128
+    big = T * H * D * 2 + 4096
+    base = dict(q=FAKE, k=FAKE + big, v=FAKE + 2 * big, g=FAKE + 3 * big, beta=FAKE + 4 * big,
+                out=FAKE + 5 * big, ws=FAKE + 6 * big, ck=FAKE + 20 * big)
+    wsb = kda.kda_prefill_workspace_bytes(d)
+
+    def call(interval, **over):
+        p = dict(base)
+        p.update(over)
+        return lib.kda_chunk_prefill_checkpoints(
+            ctypes.byref(d), p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, p["out"],
+            None, interval, p["ck"], p["ws"], wsb, None)
+
+    assert call(0) == kda.KDA_ERR_INVALID_ARG
+    assert call(-3) == kda.KDA_ERR_INVALID_ARG
+    assert call(1, ck=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(1, ck=FAKE + 20 * big + 2) == kda.KDA_ERR_MISALIGNED
+    # equal lengths: the checkpoint buffer (2 seqs x 7 states x 4 heads x 64 KiB) must
+    # not overlap the output
+    assert call(1, ck=FAKE + 5 * big + 64) == kda.KDA_ERR_INVALID_ARG

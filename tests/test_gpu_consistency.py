@@ -9,7 +9,10 @@
 * the prefill of T tokens and T decode steps agree (two independent kernels);
 * a non-finite value in one sequence leaves every other sequence untouched;
 * scale != 1 and qk_l2norm = 0, odd head counts, many short sequences, against
-  the fp64 oracle.
+  the fp64 oracle;
+* checkpointed prefill: every intermediate state against the oracle's final
+  state of that prefix, bitwise equal to a prefill of the prefix alone, and the
+  outputs unchanged.
 """
 
 import sys
@@ -253,3 +256,83 @@ def test_many_short_sequences(lib, oracle):
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
     # the empty sequence returns its initial state unchanged
     assert torch.equal(f[5], inp["initial_state"][5])
+
+
+# ----------------------------------------------------------------------------- checkpoints
+def _prefix_oracle_states(oracle, inp, lens, interval, heads=None):
+    """Oracle final states of every checkpointed prefix: sequence n, prefix
+    64 * interval * (j + 1) tokens, for each such length strictly inside n."""
+    cu = np.cumsum([0] + list(lens))
+    hs = list(range(inp["q"].shape[1])) if heads is None else list(heads)
+    sel = lambda x: host(x[:, hs].contiguous())
+    q, k, v, g = sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["g"])
+    b = host(inp["beta"][:, hs].contiguous())
+    s0 = None if inp["initial_state"] is None else host(inp["initial_state"][:, hs].contiguous())
+    pieces, plens, init = [], [], []
+    for n, L in enumerate(lens):
+        step = 64 * interval
+        P = step
+        while P < L:
+            pieces.append(slice(cu[n], cu[n] + P))
+            plens.append(P)
+            init.append(n)
+            P += step
+    if not pieces:
+        return np.zeros((0, len(hs), q.shape[2], v.shape[2]))
+    cat = lambda x: np.concatenate([x[sl] for sl in pieces], axis=0)
+    pcu = np.cumsum([0] + plens).astype(np.int32)
+    ps0 = None if s0 is None else s0[init]
+    _, fin = oracle.prefill(cat(q), cat(k), cat(v), cat(g), cat(b), cu_seqlens=pcu,
+                            initial_state=ps0, n_seqs=len(plens))
+    return fin
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("interval", [1, 2, 3])
+def test_checkpoints_match_oracle_prefixes(lib, oracle, io, d, interval):
+    from kda_inputs import make_prefill
+    lens = [1, 63, 64, 65, 0, 127, 128, 129, 300, 700]
+    inp = make_prefill(lens, 3, d, io, g_scale=0.5, s0_std=0.02, seed=44, device="cuda")
+    out, fin, ck = lib.kda_chunk_prefill_checkpoints(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], checkpoint_interval=interval)
+    torch.cuda.synchronize()
+    ref = _prefix_oracle_states(oracle, inp, lens, interval)
+    assert ck.shape[0] == ref.shape[0] > 0
+    e = maxerr(host(ck), ref)
+    say(f"checkpoints {io} d={d} interval={interval}: {ck.shape[0]} states, err {e:.3e}")
+    assert e <= TOL[io]
+    # the plain call's results are unchanged, bit for bit
+    o2, f2 = prefill(lib, inp)
+    assert torch.equal(out, o2) and torch.equal(fin, f2)
+
+
+def test_checkpoint_is_the_prefix_final_state(lib):
+    """A checkpoint is bitwise the final state of a prefill of that prefix."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([1000], 4, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=45, device="cuda")
+    _, _, ck = lib.kda_chunk_prefill_checkpoints(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"], None,
+        checkpoint_interval=4)
+    torch.cuda.synchronize()
+    assert ck.shape[0] == 3  # after 256, 512, 768 tokens
+    for j in range(3):
+        P = 256 * (j + 1)
+        _, f = prefill(lib, slice_tokens(inp, 0, P, inp["initial_state"]))
+        assert torch.equal(ck[j], f[0]), f"checkpoint {j}"
+
+
+def test_checkpoints_config1(lib, oracle):
+    """T=8192, H=32: a checkpoint every 16 chunks (7 states per head); 2 seeded
+    heads against the oracle's prefix states."""
+    from kda_inputs import make_config_prefill, seeded_heads
+    inp = make_config_prefill(1, device="cuda")
+    out, fin, ck = lib.kda_chunk_prefill_checkpoints(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"], None,
+        checkpoint_interval=16)
+    torch.cuda.synchronize()
+    hs = seeded_heads(32, 2, 101)
+    ref = _prefix_oracle_states(oracle, inp, [8192], 16, heads=hs)
+    e = maxerr(host(ck[:, hs].contiguous()), ref)
+    say(f"config1 checkpoints: {ck.shape[0]} states, err {e:.3e}")
+    assert ck.shape[0] == 7 and e <= TOL["bf16"]
