@@ -178,6 +178,23 @@ def main():
             "overhead_vs_plain_median": ck_us / (float(np.median(call_ms)) * 1e3) - 1.0}
         del ck_buf
 
+    # per-head (scalar) gate: g [T, H], same workload otherwise
+    from kda_inputs import make_prefill as _mk
+    sg_in = _mk([T], H, D, "bf16", g_scale=0.5, s0_std=0.02, seed=1, device=dev, scalar_gate=True)
+    for i in range(2):
+        kda.kda_chunk_prefill(sg_in["q"], sg_in["k"], sg_in["v"], sg_in["g"], sg_in["beta"],
+                              sg_in["initial_state"], None, out, fin, workspace=ws, stream=stream)
+    sg_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(max(3, args.steps // 4))]
+    for a_, b_ in sg_ev:
+        a_.record(stream)
+        kda.kda_chunk_prefill(sg_in["q"], sg_in["k"], sg_in["v"], sg_in["g"], sg_in["beta"],
+                              sg_in["initial_state"], None, out, fin, workspace=ws, stream=stream)
+        b_.record(stream)
+    torch.cuda.synchronize(dev)
+    sg_us = float(np.median([a_.elapsed_time(b_) for a_, b_ in sg_ev])) * 1e3
+    del sg_in
+
     # ------------------------------------------------------------------ decode
     dw = make_config_decode(3, device=dev, steps=args.decode_steps)
     state = dw["state"]
@@ -287,6 +304,9 @@ def main():
         },
         "cpu_baseline": cpu,
         "prefill_checkpoints": ckpt,
+        "prefill_scalar_gate": {"g": "[T, H] (one decay per token and head)",
+                                "median_call_us": sg_us, "tokens_per_s": T / (sg_us * 1e-6),
+                                "algorithmic_bytes_per_call": p_bytes - 2 * (D - 1) * T * H},
         "decode": {
             "workload": CONFIGS[3].name.replace(", 100 steps", ""),
             "steps": args.decode_steps,

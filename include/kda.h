@@ -24,7 +24,7 @@
  *
  * Layouts (all row-major, contiguous, token-major):
  *   q, k, g : [T_total, H, d_k]      v, out : [T_total, H, d_v]
- *   beta    : [T_total, H]
+ *   beta    : [T_total, H]           (g: [T_total, H] with KDA_GATE_HEAD)
  *   states  : [N, H, d_k, d_v] fp32; S[i][j], i = key channel, j = value
  *             channel (fastest)
  *   cu_seqlens : int32 [N + 1], cu[0] = 0, non-decreasing, cu[N] = T_total
@@ -41,9 +41,9 @@
  * Errors: every call returns a kda_status and never throws.  Validation uses
  * only the descriptor and pointer values (no device reads, no sync):
  * NULL required pointers, unsupported sizes or dtypes, misaligned pointers,
- * undersized workspace, forbidden overlaps.  Alignment: prefill q, k, v, g and
- * the workspace 16 bytes; the decode state 16 bytes; every other pointer its
- * element size.  The contents of
+ * undersized workspace, forbidden overlaps.  Alignment: prefill q, k, v, g
+ * (per-channel gate) and the workspace 16 bytes; the decode state 16 bytes;
+ * every other pointer its element size.  The contents of
  * cu_seqlens and the value ranges (g <= 0, 0 <= beta <= 1) are preconditions
  * the library does not check.  For full prefill accuracy, per-token decay
  * should also satisfy g >= -5 in every channel; see kda_chunk_prefill.
@@ -76,6 +76,16 @@ typedef enum {
     KDA_FP32 = 1  /* fp32 inputs and outputs, fp32 state, fp32 MFMA                            */
 } kda_dtype;
 
+/* Shape of the forget gate g.  KDA's retention is a diagonal matrix, one decay
+ * per key channel; the scalar forget gate it refines keeps one decay per token
+ * and head ("Kimi K3: The Manos, The Mythos, The Legendos", bullet on KDA as
+ * online learning: gating adds a forget gate, KDA makes it diagonal). */
+typedef enum {
+    KDA_GATE_CHANNEL = 0, /* g [T_total, H, d_k] (decode: [N, H, d_k]): KDA          */
+    KDA_GATE_HEAD = 1     /* g [T_total, H] (decode: [N, H]): one decay shared by all
+                             key channels, alpha_t = exp(g_t) times the identity     */
+} kda_gate;
+
 /* Problem descriptor (host memory, read during the call only). */
 typedef struct {
     int64_t total_tokens; /* T_total: length of the packed token axis (decode: = num_seqs) */
@@ -86,6 +96,7 @@ typedef struct {
     int32_t io_dtype;     /* kda_dtype                                                    */
     float scale;          /* multiplies q after its L2 normalisation (1.0 for plain KDA)  */
     int32_t qk_l2norm;    /* 1: the library L2-normalises q and k; 0: used as given        */
+    int32_t gate;         /* kda_gate: layout of g (KDA_GATE_CHANNEL unless stated)       */
 } kda_dims;
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes (0 on a

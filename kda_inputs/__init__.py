@@ -105,14 +105,15 @@ def _randn(shape, gen, device) -> torch.Tensor:
 def make_prefill(T_lens, heads: int, d: int, io_dtype: str = "bf16", *,
                  g_mu: float = 0.0, g_scale: float = 1.0, s0_std: Optional[float] = None,
                  seed: int = 0, device="cpu", packed_cu: bool = True,
-                 d_v: Optional[int] = None) -> dict:
+                 d_v: Optional[int] = None, scalar_gate: bool = False) -> dict:
     """Draw one prefill batch.
 
     ``T_lens`` is a list of sequence lengths (packed back to back).  Returns a
     dict with q, k, g ``[T,H,d]``, v ``[T,H,d_v]``, beta ``[T,H]`` in the I/O
     dtype, ``initial_state`` ``[N,H,d,d_v]`` fp32 (or None), ``cu_seqlens`` int32
     ``[N+1]`` (or None when ``packed_cu`` is False and all lengths are equal),
-    and the lengths.
+    and the lengths.  ``scalar_gate``: g is ``[T,H]`` (one decay per token and
+    head) instead of ``[T,H,d]``.
     """
     d_v = d if d_v is None else d_v
     lens = [int(x) for x in T_lens]
@@ -125,8 +126,8 @@ def make_prefill(T_lens, heads: int, d: int, io_dtype: str = "bf16", *,
     k = _unit_rows(_randn((T, heads, d), gen, device)).to(dt)
     v = _randn((T, heads, d_v), gen, device).to(dt)
     beta = torch.sigmoid(_randn((T, heads), gen, device)).to(dt)
-    g = (-torch.nn.functional.softplus(_randn((T, heads, d), gen, device) + g_mu)
-         * g_scale).to(dt)
+    g = (-torch.nn.functional.softplus(_randn((T, heads) if scalar_gate else (T, heads, d),
+                                              gen, device) + g_mu) * g_scale).to(dt)
     s0 = None
     if s0_std is not None:
         s0 = _randn((N, heads, d, d_v), gen, device) * s0_std
@@ -154,7 +155,7 @@ def make_config_prefill(cfg_id: int, device="cpu") -> dict:
 
 def make_decode(n_seqs: int, heads: int, d: int, io_dtype: str = "bf16", steps: int = 1,
                 *, g_mu: float = 0.0, g_scale: float = 0.5, s0_std: float = 0.02,
-                seed: int = 3, device="cpu") -> dict:
+                seed: int = 3, device="cpu", scalar_gate: bool = False) -> dict:
     """Draw a decode workload: one fp32 state per (sequence, head) and ``steps``
     batches of one token per sequence.  Per-step tensors are stacked on a
     leading step axis: q, k, g ``[steps,N,H,d]``, v ``[steps,N,H,d]``,
@@ -169,7 +170,8 @@ def make_decode(n_seqs: int, heads: int, d: int, io_dtype: str = "bf16", steps: 
         ks.append(_unit_rows(_randn((n_seqs, heads, d), gen, device)).to(dt))
         vs.append(_randn((n_seqs, heads, d), gen, device).to(dt))
         bs.append(torch.sigmoid(_randn((n_seqs, heads), gen, device)).to(dt))
-        gs.append((-torch.nn.functional.softplus(_randn((n_seqs, heads, d), gen, device)
+        gshape = (n_seqs, heads) if scalar_gate else (n_seqs, heads, d)
+        gs.append((-torch.nn.functional.softplus(_randn(gshape, gen, device)
                                                  + g_mu) * g_scale).to(dt))
     return dict(state=state, q=torch.stack(qs), k=torch.stack(ks), v=torch.stack(vs),
                 beta=torch.stack(bs), g=torch.stack(gs), n_seqs=n_seqs, heads=heads,

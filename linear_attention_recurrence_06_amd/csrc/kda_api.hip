@@ -48,6 +48,7 @@ kda_status check_dims(const kda_dims* d, bool prefill) {
     if (d->io_dtype != KDA_BF16 && d->io_dtype != KDA_FP32) return KDA_ERR_UNSUPPORTED;
     if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->qk_l2norm != 0 && d->qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (d->gate != KDA_GATE_CHANNEL && d->gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARG;
     if (prefill) {
         if (d->chunk != 0 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
         // fp32 I/O keeps fp32 operand tiles in LDS; at d = 128 they exceed it
@@ -82,7 +83,7 @@ int current_cu_count() {
 
 extern "C" {
 
-int kda_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int kda_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 const char* kda_status_string(kda_status s) {
     switch (s) {
@@ -125,10 +126,11 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     // q, k, v, g rows and the workspace are read with 16-byte vector accesses;
     // beta, out and the states element by element
     const uintptr_t E_al = d->io_dtype == KDA_BF16 ? 2 : 4;
-    const void* vec_ptrs[] = {q, k, v, g, workspace};
+    const bool sg = d->gate == KDA_GATE_HEAD;
+    const void* vec_ptrs[] = {q, k, v, sg ? nullptr : g, workspace};
     for (const void* p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return KDA_ERR_MISALIGNED;
-    const void* elt_ptrs[] = {beta, out};
+    const void* elt_ptrs[] = {beta, out, sg ? g : nullptr};
     for (const void* p : elt_ptrs)
         if (p && !aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
     const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens, checkpoints};
@@ -139,8 +141,9 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     // overlaps: out must not touch any input; final_state may equal initial_state exactly
     const size_t E = elt_bytes(d);
     const size_t qb = (size_t)T * H * D * E, bb = (size_t)T * H * E, sb = (size_t)N * H * D * D * 4;
+    const size_t gb = sg ? bb : qb;
     const Range r_out = range_of(out, qb);
-    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, qb),
+    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, gb),
                          range_of(beta, bb),
                          initial_state ? range_of(initial_state, sb) : Range{0, 0},
                          cu_seqlens ? range_of(cu_seqlens, (size_t)(N + 1) * 4) : Range{0, 0},
@@ -154,7 +157,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
             overlap(r_fin, range_of(initial_state, sb)))
             return KDA_ERR_INVALID_ARG;
         const Range others[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                                range_of(g, qb), range_of(beta, bb), r_out,
+                                range_of(g, gb), range_of(beta, bb), r_out,
                                 range_of(workspace, workspace_bytes)};
         for (const Range& r : others)
             if (overlap(r_fin, r)) return KDA_ERR_INVALID_ARG;
@@ -164,7 +167,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
         const int64_t C = kda_checkpoint_count(d, nullptr, interval);
         const Range r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
         const Range all[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                             range_of(g, qb), range_of(beta, bb), r_out,
+                             range_of(g, gb), range_of(beta, bb), r_out,
                              initial_state ? range_of(initial_state, sb) : Range{0, 0},
                              final_state ? range_of(final_state, sb) : Range{0, 0},
                              range_of(workspace, workspace_bytes)};
@@ -184,6 +187,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.n_heads = (int32_t)H;
     a.d = (int32_t)D;
     a.bf16 = d->io_dtype == KDA_BF16;
+    a.scalar_g = sg;
     a.scale = d->scale;
     a.l2norm = d->qk_l2norm;
     a.ckpt_interval = interval;
@@ -252,8 +256,9 @@ kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, cons
         if (!aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
     const size_t E = elt_bytes(d);
     const size_t qb = (size_t)N * H * D * E, bb = (size_t)N * H * E, sb = (size_t)N * H * D * D * 4;
+    const size_t gb = d->gate == KDA_GATE_HEAD ? bb : qb;
     const Range r_out = range_of(out, qb);
-    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, qb),
+    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, gb),
                          range_of(beta, bb), range_of(state_inout, sb)};
     for (const Range& r : ins)
         if (overlap(r_out, r)) return KDA_ERR_INVALID_ARG;
@@ -269,6 +274,7 @@ kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, cons
     a.n_heads = (int32_t)H;
     a.d = (int32_t)D;
     a.bf16 = d->io_dtype == KDA_BF16;
+    a.scalar_g = d->gate == KDA_GATE_HEAD;
     a.scale = d->scale;
     a.l2norm = d->qk_l2norm;
     hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));

@@ -1,7 +1,8 @@
 // KDA decode step on gfx950: one token per sequence, state advanced in place.
 //
 // Per (sequence, head) the step is, with qb, kb the L2-normalised q, k and
-// alpha = exp(g) (retention per key channel):
+// alpha = exp(g) (retention per key channel, or one value for all channels
+// with the per-head gate):
 //     S' = Diag(alpha) S;  vh = S'^T kb;  y = S'^T qb       (one pass over S)
 //     delta = beta (v - vh);  S = S' + kb delta^T;  o = y + (qb . kb) delta
 // The second form of o follows from o = (S' + kb delta^T)^T qb, so the state
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ beta,
                                                      float* __restrict__ S,
                                                      T* __restrict__ out, float scale,
-                                                     int l2norm) {
+                                                     int l2norm, int scalar_g) {
     constexpr int TPR = D / 4;       // threads per state row
     constexpr int RG = 256 / TPR;    // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
             const int i = lane + kWave * e;
             s_q[i] = qv[e] * rq * scale;
             s_k[i] = kv[e] * rk;
-            s_a[i] = __expf(to_f32(g[unit * D + i]));
+            s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
         }
     }
     const float b = to_f32(beta[unit]);
@@ -146,7 +147,8 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)units), dim3(256), 0, stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                       (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm);
+                       (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                       a.scalar_g ? 1 : 0);
     return hipGetLastError();
 }
 

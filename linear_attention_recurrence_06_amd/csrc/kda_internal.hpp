@@ -16,6 +16,7 @@ struct DecodeArgs {
     void* out;
     int32_t n_seqs, n_heads, d;
     bool bf16;
+    bool scalar_g;               // g is [N, H] (one decay per head) instead of [N, H, d]
     float scale;
     int l2norm;
 };
@@ -84,6 +85,7 @@ struct PrefillArgs {
     int64_t total_tokens;
     int32_t n_seqs, n_heads, d;
     bool bf16;
+    bool scalar_g;               // g is [T, H] (one decay per head) instead of [T, H, d]
     float scale;
     int l2norm;
     int cu_count;                // compute units of the device (persistent grids)

@@ -190,12 +190,14 @@ __device__ __forceinline__ void wave_rows_scan(float x, int row, float& excl, fl
 // One thread's share of a chunk's raw rows: tokens 2rg, 2rg+1, channels
 // (d_k/16) cg.. of q, k, g, v, and beta, in the I/O type.  Rows past the chunk's
 // length read as zeros (buffer range check), so the loads are never predicated.
-template <typename T, int D>
+// SG: the gate is one value per token and head (g [T, H]) instead of one per
+// key channel; it is then used as a per-channel gate with equal channels.
+template <typename T, int D, bool SG>
 struct RawRows {
     static constexpr int CPT = D / 16;
     typedef T V __attribute__((ext_vector_type(CPT)));
     V q[2], k[2], g[2], v[2];
-    T b[2];
+    T b[2], gs[2];
     __device__ __forceinline__ void load(const PrepParams& p, int2 d, int h, int rg, int cg) {
         const int64_t H = p.n_heads;
         const uint32_t E = sizeof(T);
@@ -204,7 +206,9 @@ struct RawRows {
         const int64_t first = ((int64_t)d.x * H + h) * D;
         const auto rq = make_rsrc((const T*)p.q + first, span);
         const auto rk = make_rsrc((const T*)p.k + first, span);
-        const auto rgg = make_rsrc((const T*)p.g + first, span);
+        const auto rgg = SG ? make_rsrc((const T*)p.g + (int64_t)d.x * H + h,
+                                        (uint32_t)((d.y - 1) * H + 1) * E)
+                            : make_rsrc((const T*)p.g + first, span);
         const auto rv = make_rsrc((const T*)p.v + first, span);
         const auto rb = make_rsrc((const T*)p.beta + (int64_t)d.x * H + h,
                                   (uint32_t)((d.y - 1) * H + 1) * E);
@@ -216,7 +220,10 @@ struct RawRows {
             const uint32_t off = r * rstride + CPT * cg * E;
             q[i] = buffer_load<V>(rq, off);
             k[i] = buffer_load<V>(rk, off);
-            g[i] = buffer_load<V>(rgg, off);
+            if constexpr (SG)
+                gs[i] = buffer_load<T>(rgg, r * (uint32_t)H * E);
+            else
+                g[i] = buffer_load<V>(rgg, off);
             b[i] = buffer_load<T>(rb, r * (uint32_t)H * E);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the v loads behind the others
@@ -227,9 +234,9 @@ struct RawRows {
 };
 
 // Everything for one (chunk slot, head) item whose raw rows are in `raw`.
-template <typename T, int D>
+template <typename T, int D, bool SG>
 __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
-                                          int h, const RawRows<T, D>& raw) {
+                                          int h, const RawRows<T, D, SG>& raw) {
     constexpr int CPT = D / 16;  // channels per thread in the row layout
     typedef T V2 __attribute__((ext_vector_type(2)));
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -245,7 +252,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         for (int c = 0; c < CPT; ++c) {
             qf[i][c] = to_f32(raw.q[i][c]);
             kf[i][c] = to_f32(raw.k[i][c]);
-            gf[i][c] = to_f32(raw.g[i][c]) * 1.4426950408889634f;
+            gf[i][c] = to_f32(SG ? raw.gs[i] : raw.g[i][c]) * 1.4426950408889634f;
         }
         bt[i] = to_f32(raw.b[i]);
     }
@@ -517,7 +524,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
 
 // One (chunk slot, head) item per workgroup; two workgroups share a CU (80 KB
 // of LDS and at most 128 VGPRs each).
-template <typename T, int D>
+template <typename T, int D, bool SG>
 __global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
     __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x;
@@ -527,9 +534,9 @@ __global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
     const int h = (int)(item - slot * H);
     const int2 d = slot_desc(p, slot);
     if (d.y <= 0) return;
-    RawRows<T, D> raw;
+    RawRows<T, D, SG> raw;
     raw.load(p, d, h, t >> 4, t & 15);
-    prep_item<T, D>(p, sm, slot, h, raw);
+    prep_item<T, D, SG>(p, sm, slot, h, raw);
 }
 
 // Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks;
@@ -626,7 +633,10 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t items = a.layout.slots * a.n_heads;
-    hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)items), dim3(512), 0, stream, p);
+    if (a.scalar_g)
+        hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3((unsigned)items), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prep_kernel<T, D, false>), dim3((unsigned)items), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

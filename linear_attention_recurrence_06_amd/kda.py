@@ -9,6 +9,7 @@ is no CPU path.  If libkda.so is missing or fails to load, every call raises.
 
 Layouts (contiguous, token-major): q, k, g ``[T, H, d_k]``; v, out ``[T, H, d_v]``;
 beta ``[T, H]``; states ``[N, H, d_k, d_v]`` float32; cu_seqlens int32 ``[N+1]``.
+A g of shape ``[T, H]`` (decode ``[N, H]``) selects the per-head (scalar) gate.
 q, k, v, g, beta share one dtype (bfloat16 or float32), which is also out's.
 """
 
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED, \
     KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(6)
 KDA_BF16, KDA_FP32 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 
 #: every symbol include/kda.h declares
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
@@ -44,6 +46,7 @@ class kda_dims(ctypes.Structure):
         ("io_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("qk_l2norm", ctypes.c_int32),
+        ("gate", ctypes.c_int32),
     ]
 
 
@@ -111,9 +114,14 @@ def _stream_handle(stream, device) -> int:
 
 def make_dims(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
               io_dtype: int, scale: float = 1.0, qk_l2norm: bool = True,
-              chunk: int = 64) -> kda_dims:
+              chunk: int = 64, gate: int = KDA_GATE_CHANNEL) -> kda_dims:
     return kda_dims(int(total_tokens), int(num_seqs), int(num_heads), int(d_k), int(d_v),
-                    int(chunk), int(io_dtype), float(scale), 1 if qk_l2norm else 0)
+                    int(chunk), int(io_dtype), float(scale), 1 if qk_l2norm else 0, int(gate))
+
+
+def _gate(g: torch.Tensor, lead) -> int:
+    """KDA_GATE_HEAD when g has no key-channel axis ([T, H] / [N, H])."""
+    return KDA_GATE_HEAD if g.dim() == len(lead) else KDA_GATE_CHANNEL
 
 
 def kda_prefill_workspace_bytes(dims: kda_dims) -> int:
@@ -156,7 +164,9 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
     else:
         N = 1 if num_seqs is None else int(num_seqs)
-    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("g", g, (T, H, dk)),
+    gate = _gate(g, (T, H))
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)),
+                         ("g", g, (T, H) if gate else (T, H, dk)),
                          ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
         _check_tensor(name, t, shp, dt, dev)
     if initial_state is not None:
@@ -169,7 +179,7 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
-    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
     need = kda_prefill_workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -223,7 +233,9 @@ def kda_chunk_prefill_checkpoints(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     else:
         N = 1 if num_seqs is None else int(num_seqs)
         host_cu_seqlens = None
-    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("g", g, (T, H, dk)),
+    gate = _gate(g, (T, H))
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)),
+                         ("g", g, (T, H) if gate else (T, H, dk)),
                          ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
         _check_tensor(name, t, shp, dt, dev)
     if initial_state is not None:
@@ -236,7 +248,7 @@ def kda_chunk_prefill_checkpoints(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
-    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
     C = kda_checkpoint_count(dims, host_cu_seqlens, checkpoint_interval)
     if C < 0:
         raise KDAError(KDA_ERR_INVALID_ARG, "kda_checkpoint_count")
@@ -268,7 +280,9 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     dv = v.shape[2]
     dev = q.device
     dt = q.dtype
-    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("g", g, (N, H, dk)),
+    gate = _gate(g, (N, H))
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)),
+                         ("g", g, (N, H) if gate else (N, H, dk)),
                          ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
         _check_tensor(name, t, shp, dt, dev)
     _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
@@ -276,7 +290,7 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check_tensor("out", out, (N, H, dv), dt, dev)
-    dims = make_dims(N, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm)
+    dims = make_dims(N, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
     rc = lib.kda_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                              _ptr(beta), _ptr(state), _ptr(out), _stream_handle(stream, dev))
     if rc != KDA_OK:

@@ -165,3 +165,20 @@ def test_checkpoint_validation(kda):
     # equal lengths: the checkpoint buffer (2 seqs x 7 states x 4 heads x 64 KiB) must
     # not overlap the output
     assert call(1, ck=FAKE + 5 * big + 64) == kda.KDA_ERR_INVALID_ARG
+
+
+def test_gate_field_and_validation(kda):
+    # the descriptor as laid out in include/kda.h: int64 + nine 4-byte fields, 8-aligned
+    assert ctypes.sizeof(kda.kda_dims) == 48
+    assert kda.kda_dims.gate.offset == 40
+    d = kda.make_dims(1024, 1, 2, 128, 128, kda.KDA_BF16, gate=2)
+    assert kda.kda_prefill_workspace_bytes(d) == 0
+    assert prefill_call(kda, d) == kda.KDA_ERR_INVALID_ARG
+    # the per-head gate reads g element by element: 2-byte alignment is enough
+    d1 = kda.make_dims(1024, 1, 2, 128, 128, kda.KDA_BF16, gate=kda.KDA_GATE_HEAD)
+    assert kda.kda_prefill_workspace_bytes(d1) == kda.kda_prefill_workspace_bytes(
+        kda.make_dims(1024, 1, 2, 128, 128, kda.KDA_BF16))
+    assert prefill_call(kda, d1, g=FAKE + 3 * (1024 * 2 * 128 * 2 + 4096) + 2,
+                        ws_bytes=0) == kda.KDA_ERR_WORKSPACE
+    assert prefill_call(kda, d1, g=FAKE + 3 * (1024 * 2 * 128 * 2 + 4096) + 1) == \
+        kda.KDA_ERR_MISALIGNED
