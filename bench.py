@@ -195,6 +195,28 @@ def main():
     sg_us = float(np.median([a_.elapsed_time(b_) for a_, b_ in sg_ev])) * 1e3
     del sg_in
 
+    def median_call_us(fn, reps):
+        for _ in range(2):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize(dev)
+        return float(np.median([a_.elapsed_time(b_) for a_, b_ in evs])) * 1e3
+
+    # output gate fused into the output write: out = o * sigmoid(z), z [T, H, d_v]
+    from kda_inputs import make_out_gate
+    z_pf = make_out_gate((T, H, D), "bf16", seed=2, device=dev)
+    og_us = median_call_us(
+        lambda: kda.kda_chunk_prefill_ex(base["q"], base["k"], base["v"], base["g"],
+                                         base["beta"], base["initial_state"], None, out, fin,
+                                         out_gate_z=z_pf, workspace=ws, stream=stream),
+        max(3, args.steps // 4))
+    del z_pf
+
     # ------------------------------------------------------------------ decode
     dw = make_config_decode(3, device=dev, steps=args.decode_steps)
     state = dw["state"]
@@ -221,6 +243,15 @@ def main():
     sb = decode_state_bytes(DECODE_N, DECODE_H, D)
     tb = decode_token_bytes(DECODE_N, DECODE_H, D)
     d_traffic = counter_traffic("decode")
+
+    # decode with the output gate per value channel (z [N, H, d_v])
+    z_dec = make_out_gate((DECODE_N, DECODE_H, D), "bf16", seed=3, device=dev)
+    og_dec_us = median_call_us(
+        lambda: kda.kda_decode_step_ex(dw["q"][0], dw["k"][0], dw["v"][0], dw["g"][0],
+                                       dw["beta"][0], state, dout, out_gate_z=z_dec,
+                                       stream=stream),
+        max(10, args.decode_steps // 4))
+    del z_dec
 
     # plain 1 GiB device-to-device copy: the practical HBM ceiling on this machine
     # (and, in --profile runs, the known-size transfer that scales the counters)
@@ -307,6 +338,11 @@ def main():
         "prefill_scalar_gate": {"g": "[T, H] (one decay per token and head)",
                                 "median_call_us": sg_us, "tokens_per_s": T / (sg_us * 1e-6),
                                 "algorithmic_bytes_per_call": p_bytes - 2 * (D - 1) * T * H},
+        "prefill_output_gate": {"z": "[T, H, d_v] (one gate per value channel)",
+                                "median_call_us": og_us, "tokens_per_s": T / (og_us * 1e-6),
+                                "overhead_vs_plain_median":
+                                    og_us / (float(np.median(call_ms)) * 1e3) - 1.0,
+                                "algorithmic_bytes_per_call": p_bytes + T * H * D * 2},
         "decode": {
             "workload": CONFIGS[3].name.replace(", 100 steps", ""),
             "steps": args.decode_steps,
@@ -328,6 +364,10 @@ def main():
                 "practical_hbm_GBps": copy_GBps,
                 "frac_of_practical": (sb + tb) / d_avg_s / 1e9 / copy_GBps,
             },
+            "output_gate": {"z": "[N, H, d_v]", "median_call_us": og_dec_us,
+                            "algorithmic_bytes_per_call": sb + tb + DECODE_N * DECODE_H * D * 2,
+                            "achieved_GBps": (sb + tb + DECODE_N * DECODE_H * D * 2)
+                            / (og_dec_us * 1e-6) / 1e9},
         },
     }
     print(json.dumps(res), flush=True)

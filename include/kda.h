@@ -180,6 +180,49 @@ kda_status kda_chunk_prefill_checkpoints(const kda_dims* dims, const void* q, co
                                          float* checkpoints, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* Output gate, fused into the output write: out = o * sigmoid(z) with z a
+ * caller-supplied pre-activation ("Kimi K3: The Manos, The Mythos, The
+ * Legendos", bullet on stability details: a per-head output forget gate).  z
+ * has out's element type and either out's layout (one gate per value channel
+ * of each head) or [T_total, H] (decode: [N, H]; one gate per token and head). */
+typedef enum {
+    KDA_OUT_GATE_NONE = 0,
+    KDA_OUT_GATE_CHANNEL = 1, /* z [T_total, H, d_v] */
+    KDA_OUT_GATE_HEAD = 2     /* z [T_total, H]      */
+} kda_out_gate;
+
+/* Options of kda_chunk_prefill_ex; all-zero means none (kda_chunk_prefill). */
+typedef struct {
+    int32_t checkpoint_interval; /* 0, or as in kda_chunk_prefill_checkpoints            */
+    int32_t out_gate;            /* kda_out_gate                                          */
+    float* checkpoints;          /* as in kda_chunk_prefill_checkpoints (interval > 0)    */
+    const void* out_gate_z;      /* device, io_dtype, required unless KDA_OUT_GATE_NONE;
+                                    element-size aligned; read only; must not overlap
+                                    out, final_state or checkpoints                      */
+} kda_prefill_options;
+
+/* Chunked prefill with options: checkpoints (see kda_chunk_prefill_checkpoints)
+ * and/or the output gate.  opts NULL means none.  Same arguments, rules and
+ * results as kda_chunk_prefill otherwise; with an output gate, out holds the
+ * gated outputs (states and checkpoints are unchanged by it).
+ * Errors: KDA_ERR_INVALID_ARG for an out_gate outside kda_out_gate, a NULL
+ * out_gate_z with a gate (T_total > 0), or z overlapping an output;
+ * KDA_ERR_MISALIGNED for a z not aligned to its element size. */
+kda_status kda_chunk_prefill_ex(const kda_dims* dims, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta,
+                                const float* initial_state, const int32_t* cu_seqlens,
+                                void* out, float* final_state, const kda_prefill_options* opts,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step with the output gate (out_gate: kda_out_gate; out_gate_z as
+ * above with N in place of T_total, and it must not overlap out or
+ * state_inout).  KDA_OUT_GATE_NONE is kda_decode_step.  Errors as for
+ * kda_decode_step, plus those listed for the gate at kda_chunk_prefill_ex. */
+kda_status kda_decode_step_ex(const kda_dims* dims, const void* q, const void* k,
+                              const void* v, const void* g, const void* beta,
+                              float* state_inout, void* out, int32_t out_gate,
+                              const void* out_gate_z, void* stream);
+
 /* One decode step: one new token for each of N sequences.
  *
  * dims->total_tokens must equal dims->num_seqs.  q, k, g [N,H,d_k], v [N,H,d_v],

@@ -12,6 +12,7 @@ Recipe (the workloads the library is measured on; there is no dataset):
 * beta = sigmoid(N(0, 1)), one value per (token, head);
 * g = -softplus(N(mu, 1)) * s per (token, head, key channel), so g <= 0;
 * initial state ~ N(0, std^2) in fp32 (or zeros), one per (sequence, head);
+* output-gate pre-activations z ~ N(0, 2^2) (own generator and seed);
 * varlen batches draw integer lengths uniformly in [lo, hi] (both ends
   inclusive) on the CPU generator before any tensor, so the packing does not
   depend on the device.
@@ -185,6 +186,15 @@ def make_config_decode(cfg_id: int = 3, device="cpu", steps: Optional[int] = Non
                        cfg.steps if steps is None else steps, g_mu=cfg.g_mu,
                        g_scale=cfg.g_scale, s0_std=cfg.s0_std, seed=cfg.seed,
                        device=device)
+
+
+def make_out_gate(shape, io_dtype: str = "bf16", *, std: float = 2.0, seed: int = 7,
+                  device="cpu") -> torch.Tensor:
+    """Output-gate pre-activations z ~ N(0, std^2) of the given shape ([T, H, d_v]
+    per value channel or [T, H] per head), drawn from their own generator."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return (_randn(tuple(shape), gen, device) * std).to(torch_dtype(io_dtype))
 
 
 def seeded_heads(n_heads: int, count: int, seed: int) -> List[int]:

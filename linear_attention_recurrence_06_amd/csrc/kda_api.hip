@@ -109,19 +109,24 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
 
 namespace {
 
-// Shared body of the two prefill entry points (interval 0: no checkpoints).
+// Shared body of the prefill entry points (interval 0: no checkpoints;
+// out_gate 0: no output gate).
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
                         const int32_t* cu_seqlens, void* out, float* final_state,
-                        int32_t interval, float* checkpoints, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        int32_t interval, float* checkpoints, int32_t out_gate,
+                        const void* out_gate_z, void* workspace, size_t workspace_bytes,
+                        void* stream) {
     kda_status st = check_dims(d, true);
     if (st != KDA_OK) return st;
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads, D = d->d_k;
+    if (interval < 0) return KDA_ERR_INVALID_ARG;
+    if (out_gate < KDA_OUT_GATE_NONE || out_gate > KDA_OUT_GATE_HEAD) return KDA_ERR_INVALID_ARG;
     if (N == 0) return T == 0 ? KDA_OK : KDA_ERR_INVALID_ARG;
     if (!cu_seqlens && T % N != 0) return KDA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
     if (interval > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
+    if (out_gate != KDA_OUT_GATE_NONE && T > 0 && !out_gate_z) return KDA_ERR_INVALID_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
     // q, k, v, g rows and the workspace are read with 16-byte vector accesses;
     // beta, out and the states element by element
@@ -130,7 +135,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     const void* vec_ptrs[] = {q, k, v, sg ? nullptr : g, workspace};
     for (const void* p : vec_ptrs)
         if (p && !aligned_to(p, 16)) return KDA_ERR_MISALIGNED;
-    const void* elt_ptrs[] = {beta, out, sg ? g : nullptr};
+    const void* elt_ptrs[] = {beta, out, sg ? g : nullptr, out_gate ? out_gate_z : nullptr};
     for (const void* p : elt_ptrs)
         if (p && !aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
     const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens, checkpoints};
@@ -151,13 +156,17 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     if (T > 0)
         for (const Range& r : ins)
             if (overlap(r_out, r)) return KDA_ERR_INVALID_ARG;
+    const Range r_z = out_gate != KDA_OUT_GATE_NONE
+                          ? range_of(out_gate_z, out_gate == KDA_OUT_GATE_HEAD ? bb : qb)
+                          : Range{0, 0};
+    if (T > 0 && overlap(r_out, r_z)) return KDA_ERR_INVALID_ARG;
     if (final_state) {
         const Range r_fin = range_of(final_state, sb);
         if (initial_state && initial_state != final_state &&
             overlap(r_fin, range_of(initial_state, sb)))
             return KDA_ERR_INVALID_ARG;
         const Range others[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                                range_of(g, gb), range_of(beta, bb), r_out,
+                                range_of(g, gb), range_of(beta, bb), r_out, r_z,
                                 range_of(workspace, workspace_bytes)};
         for (const Range& r : others)
             if (overlap(r_fin, r)) return KDA_ERR_INVALID_ARG;
@@ -167,7 +176,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
         const int64_t C = kda_checkpoint_count(d, nullptr, interval);
         const Range r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
         const Range all[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                             range_of(g, gb), range_of(beta, bb), r_out,
+                             range_of(g, gb), range_of(beta, bb), r_out, r_z,
                              initial_state ? range_of(initial_state, sb) : Range{0, 0},
                              final_state ? range_of(final_state, sb) : Range{0, 0},
                              range_of(workspace, workspace_bytes)};
@@ -192,6 +201,8 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.l2norm = d->qk_l2norm;
     a.ckpt_interval = interval;
     a.checkpoints = checkpoints;
+    a.out_gate = out_gate;
+    a.out_gate_z = out_gate_z;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
     a.cu_count = current_cu_count();
     hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
@@ -207,7 +218,19 @@ kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, co
                              const int32_t* cu_seqlens, void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, 0,
-                        nullptr, workspace, workspace_bytes, stream);
+                        nullptr, KDA_OUT_GATE_NONE, nullptr, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_ex(const kda_dims* d, const void* q, const void* k, const void* v,
+                                const void* g, const void* beta, const float* initial_state,
+                                const int32_t* cu_seqlens, void* out, float* final_state,
+                                const kda_prefill_options* o, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const kda_prefill_options none = {0, KDA_OUT_GATE_NONE, nullptr, nullptr};
+    if (!o) o = &none;
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                        o->checkpoint_interval, o->checkpoints, o->out_gate, o->out_gate_z,
+                        workspace, workspace_bytes, stream);
 }
 
 int64_t kda_checkpoint_count(const kda_dims* d, const int32_t* host_cu_seqlens,
@@ -237,17 +260,24 @@ kda_status kda_chunk_prefill_checkpoints(const kda_dims* d, const void* q, const
                                          size_t workspace_bytes, void* stream) {
     if (checkpoint_interval < 1) return KDA_ERR_INVALID_ARG;
     return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                        checkpoint_interval, checkpoints, workspace, workspace_bytes, stream);
+                        checkpoint_interval, checkpoints, KDA_OUT_GATE_NONE, nullptr, workspace,
+                        workspace_bytes, stream);
 }
 
-kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, const void* v,
-                           const void* g, const void* beta, float* state_inout, void* out,
-                           void* stream) {
+}  // extern "C"
+
+static kda_status decode_impl(const kda_dims* d, const void* q, const void* k, const void* v,
+                              const void* g, const void* beta, float* state_inout, void* out,
+                              int32_t out_gate, const void* out_gate_z, void* stream) {
     kda_status st = check_dims(d, false);
     if (st != KDA_OK) return st;
+    if (out_gate < KDA_OUT_GATE_NONE || out_gate > KDA_OUT_GATE_HEAD) return KDA_ERR_INVALID_ARG;
     const int64_t N = d->num_seqs, H = d->num_heads, D = d->d_k;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    if (out_gate != KDA_OUT_GATE_NONE && !out_gate_z) return KDA_ERR_INVALID_ARG;
+    if (out_gate != KDA_OUT_GATE_NONE && !aligned_to(out_gate_z, d->io_dtype == KDA_BF16 ? 2 : 4))
+        return KDA_ERR_MISALIGNED;
     // the state is streamed with 16-byte accesses; token vectors element by element
     const uintptr_t E_al = d->io_dtype == KDA_BF16 ? 2 : 4;
     if (!aligned_to(state_inout, 16)) return KDA_ERR_MISALIGNED;
@@ -262,9 +292,14 @@ kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, cons
                          range_of(beta, bb), range_of(state_inout, sb)};
     for (const Range& r : ins)
         if (overlap(r_out, r)) return KDA_ERR_INVALID_ARG;
+    const Range r_z = out_gate != KDA_OUT_GATE_NONE
+                          ? range_of(out_gate_z, out_gate == KDA_OUT_GATE_HEAD ? bb : qb)
+                          : Range{0, 0};
+    if (overlap(r_out, r_z)) return KDA_ERR_INVALID_ARG;
     const Range r_state = range_of(state_inout, sb);
     for (int i = 0; i < 5; ++i)
         if (overlap(r_state, ins[i])) return KDA_ERR_INVALID_ARG;
+    if (overlap(r_state, r_z)) return KDA_ERR_INVALID_ARG;
 
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -275,10 +310,28 @@ kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, cons
     a.d = (int32_t)D;
     a.bf16 = d->io_dtype == KDA_BF16;
     a.scalar_g = d->gate == KDA_GATE_HEAD;
+    a.out_gate = out_gate;
+    a.out_gate_z = out_gate_z;
     a.scale = d->scale;
     a.l2norm = d->qk_l2norm;
     hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+
+extern "C" {
+
+kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, float* state_inout, void* out,
+                           void* stream) {
+    return decode_impl(d, q, k, v, g, beta, state_inout, out, KDA_OUT_GATE_NONE, nullptr,
+                       stream);
+}
+
+kda_status kda_decode_step_ex(const kda_dims* d, const void* q, const void* k, const void* v,
+                              const void* g, const void* beta, float* state_inout, void* out,
+                              int32_t out_gate, const void* out_gate_z, void* stream) {
+    return decode_impl(d, q, k, v, g, beta, state_inout, out, out_gate, out_gate_z, stream);
 }
 
 }  // extern "C"

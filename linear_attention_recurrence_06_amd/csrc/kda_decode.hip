@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ beta,
                                                      float* __restrict__ S,
                                                      T* __restrict__ out, float scale,
-                                                     int l2norm, int scalar_g) {
+                                                     int l2norm, int scalar_g, int out_gate,
+                                                     const T* __restrict__ og_z) {
     constexpr int TPR = D / 4;       // threads per state row
     constexpr int RG = 256 / TPR;    // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -137,7 +138,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     }
     if (rg == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[unit * D + 4 * cq + j] = from_f32<T>(o[j]);
+        for (int j = 0; j < 4; ++j) {
+            float oj = o[j];
+            if (out_gate) {  // out = o * sigmoid(z), z per value channel or per head
+                const float zz = to_f32(out_gate == 2 ? og_z[unit] : og_z[unit * D + 4 * cq + j]);
+                oj *= __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+            }
+            out[unit * D + 4 * cq + j] = from_f32<T>(oj);
+        }
     }
 }
 
@@ -148,7 +156,7 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)units), dim3(256), 0, stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                        (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                       a.scalar_g ? 1 : 0);
+                       a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z);
     return hipGetLastError();
 }
 

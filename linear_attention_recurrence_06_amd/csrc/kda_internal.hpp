@@ -19,6 +19,8 @@ struct DecodeArgs {
     bool scalar_g;               // g is [N, H] (one decay per head) instead of [N, H, d]
     float scale;
     int l2norm;
+    int out_gate;                // 0 none, 1 z [N, H, d], 2 z [N, H]: out = o * sigmoid(z)
+    const void* out_gate_z;
 };
 
 // Workspace for one prefill call: a chunk index (first chunk slot of each
@@ -91,6 +93,8 @@ struct PrefillArgs {
     int cu_count;                // compute units of the device (persistent grids)
     int32_t ckpt_interval;       // 0: no checkpoints
     float* checkpoints;          // [C, H, d, d] when ckpt_interval > 0
+    int out_gate;                // 0 none, 1 z [T, H, d], 2 z [T, H]: out = o * sigmoid(z)
+    const void* out_gate_z;
     PrefillLayout layout;
 };
 

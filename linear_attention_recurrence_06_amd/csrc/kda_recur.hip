@@ -53,9 +53,11 @@ struct RecurParams {
     float* fin;
     void* out;
     float* ckpt;            // checkpoints [C, H, d, d] (checkpointing variant only)
+    const void* og_z;       // output-gate pre-activation (gated variant only)
     int64_t total_tokens;
     int32_t n_seqs, n_heads, ntiles;
     int32_t ckpt_interval;  // chunks between checkpoints (checkpointing variant only)
+    int32_t og_per_head;    // gated variant: 1 z [T, H], 0 z [T, H, d]
     PrefillLayout L;
 };
 
@@ -71,6 +73,7 @@ struct WaveOps {
     Frag<T> Kt[2];    // Kprime^T rows of this wave's state row block
     f32x4 gc;         // Gamma_C of this wave's state rows (4 per lane)
     uint32_t pf;      // one word of a later chunk's record (L2 prefetch; never used)
+    uint32_t zpf;     // one element of a later chunk's output-gate rows (the same)
 
     // Loads for the phase-one operands (A, and U or M) of record `rec`.
     __device__ __forceinline__ void load_front(const unsigned char* rec, const PrefillLayout& L,
@@ -113,6 +116,8 @@ struct WaveCtx {
     int h, col0, tile, w, lane, b, rb;
     int64_t ck0;                // first checkpoint of the sequence
     uint32_t pf_off;            // byte offset of this lane's prefetch line in a record
+    uint32_t zpf_off;           // byte offset (in a chunk's z rows) of this lane's z line
+    bool zpf_wave;              // the wave that touches z lines ahead (gated variant)
     bool uwave, has_rows;
     __device__ __forceinline__ const unsigned char* rec(int64_t kc) const {
         return rec0 + (size_t)min(kc, last) * rec_bytes;
@@ -121,7 +126,8 @@ struct WaveCtx {
 
 // One chunk: consume `ops` (chunk kc), then refill it with chunk kc + NBUF.
 // CK: also store the state after every ckpt_interval-th chunk (a checkpoint).
-template <typename T, int D, int NT, int NBUF, int PF, bool CK>
+// OG: write out = o * sigmoid(z) (the output gate).
+template <typename T, int D, int NT, int NBUF, int PF, bool CK, bool OG>
 __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[NT / 16],
                                            WaveOps<T, D, NT>& ops, const RecurParams& p,
                                            const WaveCtx& c, int64_t kc) {
@@ -129,6 +135,34 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
     constexpr int NB = NT / 16;
     typedef T V4 __attribute__((ext_vector_type(4)));
     const int lane = c.lane;
+    const int Lc = (int)min((int64_t)64, c.s_len - 64 * kc);
+    const int64_t tok0 = c.s_begin + 64 * kc;
+
+    // Output-gate pre-activations of this chunk's rows, requested before any
+    // other load of the step: a load completes only after every load issued
+    // before it, so z asked for here is not held up by the operand refills
+    // below.  Rows past the sequence's end read as zero (range-checked).
+    T zv[NB][4];
+    if constexpr (OG) {
+        if (!c.uwave) {
+            const int64_t zs = p.og_per_head ? c.H : c.H * D;  // elements between tokens
+            const int64_t zw = p.og_per_head ? 1 : D;
+            const __amdgpu_buffer_rsrc_t zr = make_rsrc(
+                reinterpret_cast<const T*>(p.og_z) + (tok0 * c.H + c.h) * zw,
+                (uint32_t)(((int64_t)(Lc - 1) * zs + zw) * (int64_t)sizeof(T)));
+            const uint32_t zrow = (uint32_t)(zs * (int64_t)sizeof(T));
+            const uint32_t zcol = p.og_per_head ? 0u : (uint32_t)sizeof(T);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int col = c.col0 + 16 * nb + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * c.b + 4 * (lane >> 4) + e;
+                    zv[nb][e] = buffer_load<T>(zr, (uint32_t)row * zrow + (uint32_t)col * zcol);
+                }
+            }
+        }
+    }
 
     // ---- phase one: A S for token block b (A = W or Qhat)
     Frag<T> Sb[NKS][NB];
@@ -204,24 +238,40 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
         asm volatile("" ::"v"(ops.pf));
         ops.pf = *reinterpret_cast<const uint32_t*>(c.rec(kc + NBUF + PF) + c.pf_off);
     }
+    if constexpr (OG && sizeof(T) == 2) {
+        // touch this workgroup's share of the z lines of chunk kc + 2, so that
+        // the z loads at the start of that step hit L2 (bf16 only: the fp32
+        // variant has no registers to spare for it)
+        if (c.zpf_wave && kc + 2 <= c.last) {
+            asm volatile("" ::"v"(ops.zpf));
+            const int L2c = (int)min((int64_t)64, c.s_len - 64 * (kc + 2));
+            const int64_t zs = p.og_per_head ? c.H : c.H * D;
+            const int64_t zw = p.og_per_head ? 1 : D;
+            const __amdgpu_buffer_rsrc_t zr = make_rsrc(
+                reinterpret_cast<const T*>(p.og_z) + ((tok0 + 128) * c.H + c.h) * zw,
+                (uint32_t)(((int64_t)(L2c - 1) * zs + zw) * (int64_t)sizeof(T)));
+            ops.zpf = (uint32_t)__builtin_bit_cast(
+                uint16_t, buffer_load<uint16_t>(zr, c.zpf_off));
+        }
+    }
     if (!c.uwave) {
-        const int Lc = (int)min((int64_t)64, c.s_len - 64 * kc);
         T* outp = reinterpret_cast<T*>(p.out);
-        const int64_t tok0 = c.s_begin + 64 * kc;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int col = c.col0 + 16 * nb + (lane & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * c.b + 4 * (lane >> 4) + e;
-                if (row < Lc) outp[((tok0 + row) * c.H + c.h) * D + col] = from_f32<T>(acc[nb][e]);
+                float o = acc[nb][e];
+                if constexpr (OG) o *= __builtin_amdgcn_rcpf(1.f + __expf(-to_f32(zv[nb][e])));
+                if (row < Lc) outp[((tok0 + row) * c.H + c.h) * D + col] = from_f32<T>(o);
             }
         }
     }
     __syncthreads();
 }
 
-template <typename T, int D, int NT, int NBUF, int PF, bool CK>
+template <typename T, int D, int NT, int NBUF, int PF, bool CK, bool OG>
 __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     constexpr int NB = NT / 16;
     __shared__ RecurSmem<T, D, NT> sm;
@@ -262,6 +312,19 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
         const uint32_t i = (uint32_t)t < per ? (uint32_t)t : 0u;
         const uint32_t line = min((uint32_t)tile * per + i, lines - 1);
         c.pf_off = line * 128;
+    }
+    {
+        // z prefetch share (gated variant): (row, 128-byte part) pairs i = tile +
+        // ntiles * lane of a chunk's 64 z rows, one per lane of wave 4 (lanes past
+        // the share repeat the first pair)
+        const int zrow_bytes = (int)((p.og_per_head ? 1 : D) * sizeof(T));
+        const int J = (zrow_bytes + 127) / 128;
+        const int per = (64 * J + p.ntiles - 1) / p.ntiles;
+        const int l = lane < per ? lane : 0;
+        const int i = min(tile + p.ntiles * l, 64 * J - 1);
+        const int64_t zs = p.og_per_head ? c.H : c.H * D;
+        c.zpf_off = (uint32_t)((i / J) * zs * (int64_t)sizeof(T) + (i % J) * 128);
+        c.zpf_wave = OG && c.w == 4;
     }
     // waves without state rows (d_k = 64) read the rows of block 0 in load_back
     // and never use them
@@ -308,19 +371,19 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
         if constexpr (NBUF > 4) prime(b4, 4);
         int64_t kc = 0;
         for (; kc + NBUF <= nch; kc += NBUF) {
-            recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b0, p, c, kc);
-            recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b1, p, c, kc + 1);
-            if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b2, p, c, kc + 2);
-            if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b3, p, c, kc + 3);
-            if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b4, p, c, kc + 4);
+            recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b0, p, c, kc);
+            recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b1, p, c, kc + 1);
+            if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b2, p, c, kc + 2);
+            if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b3, p, c, kc + 3);
+            if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b4, p, c, kc + 4);
         }
-        if (kc < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b0, p, c, kc);
+        if (kc < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b0, p, c, kc);
         if constexpr (NBUF > 2)
-            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b1, p, c, kc + 1);
+            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b1, p, c, kc + 1);
         if constexpr (NBUF > 3)
-            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b2, p, c, kc + 2);
+            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b2, p, c, kc + 2);
         if constexpr (NBUF > 4)
-            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF, CK>(sm, S, b3, p, c, kc + 3);
+            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b3, p, c, kc + 3);
     }
 
     if (p.fin && c.has_rows) {
@@ -358,6 +421,8 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     p.out = a.out;
     p.ckpt = a.checkpoints;
     p.ckpt_interval = a.ckpt_interval;
+    p.og_z = a.out_gate_z;
+    p.og_per_head = a.out_gate == 2 ? 1 : 0;
     p.total_tokens = a.total_tokens;
     p.n_seqs = a.n_seqs;
     p.n_heads = a.n_heads;
@@ -366,12 +431,17 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t groups = (chains + 7) / 8;
     const int64_t grid = 8 * p.ntiles * groups;
-    if (a.ckpt_interval > 0)
-        hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch, true>),
-                           dim3((unsigned)grid), dim3(512), 0, stream, p);
+    const dim3 gd((unsigned)grid), bd(512);
+    constexpr int B = kRecurDepth, F = kRecurPrefetch;
+    const bool ck = a.ckpt_interval > 0, og = a.out_gate != 0;
+    if (!ck && !og)
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, false>), gd, bd, 0, stream, p);
+    else if (ck && !og)
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, true, false>), gd, bd, 0, stream, p);
+    else if (!ck && og)
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, true>), gd, bd, 0, stream, p);
     else
-        hipLaunchKernelGGL((recur_kernel<T, D, NT, kRecurDepth, kRecurPrefetch, false>),
-                           dim3((unsigned)grid), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, true, true>), gd, bd, 0, stream, p);
     return hipGetLastError();
 }
 

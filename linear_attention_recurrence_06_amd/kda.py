@@ -31,8 +31,8 @@ KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 
 #: every symbol include/kda.h declares
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
-            "kda_chunk_prefill_checkpoints", "kda_decode_step", "kda_status_string",
-            "kda_version")
+            "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_decode_step",
+            "kda_decode_step_ex", "kda_status_string", "kda_version")
 
 
 class kda_dims(ctypes.Structure):
@@ -47,6 +47,18 @@ class kda_dims(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("qk_l2norm", ctypes.c_int32),
         ("gate", ctypes.c_int32),
+    ]
+
+
+KDA_OUT_GATE_NONE, KDA_OUT_GATE_CHANNEL, KDA_OUT_GATE_HEAD = 0, 1, 2
+
+
+class kda_prefill_options(ctypes.Structure):
+    _fields_ = [
+        ("checkpoint_interval", ctypes.c_int32),
+        ("out_gate", ctypes.c_int32),
+        ("checkpoints", ctypes.c_void_p),
+        ("out_gate_z", ctypes.c_void_p),
     ]
 
 
@@ -80,6 +92,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_prefill_checkpoints.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_int32,
                                                   P, P, ctypes.c_size_t, P]
     lib.kda_chunk_prefill_checkpoints.restype = ctypes.c_int
+    lib.kda_chunk_prefill_ex.argtypes = [D, P, P, P, P, P, P, P, P, P,
+                                         ctypes.POINTER(kda_prefill_options), P,
+                                         ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_ex.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.kda_decode_step_ex.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -296,3 +314,111 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     if rc != KDA_OK:
         raise KDAError(rc, "kda_decode_step")
     return out
+
+
+def _out_gate(z: Optional[torch.Tensor], lead, dv: int, dt, dev) -> int:
+    if z is None:
+        return KDA_OUT_GATE_NONE
+    if z.dim() == len(lead):
+        _check_tensor("out_gate_z", z, tuple(lead), dt, dev)
+        return KDA_OUT_GATE_HEAD
+    _check_tensor("out_gate_z", z, tuple(lead) + (dv,), dt, dev)
+    return KDA_OUT_GATE_CHANNEL
+
+
+def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                         beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         final_state: Optional[torch.Tensor] = None, *,
+                         out_gate_z: Optional[torch.Tensor] = None,
+                         checkpoint_interval: int = 0,
+                         checkpoints: Optional[torch.Tensor] = None,
+                         host_cu_seqlens=None, num_seqs: Optional[int] = None,
+                         scale: float = 1.0, qk_l2norm: bool = True,
+                         workspace: Optional[torch.Tensor] = None,
+                         output_final_state: bool = True, stream=None):
+    """Chunked prefill with options (include/kda.h, kda_chunk_prefill_ex): the
+    output gate out = o * sigmoid(z) (z ``[T,H,d_v]`` per channel or ``[T,H]``
+    per head) and/or checkpoints.  Returns ``(out, final_state, checkpoints)``
+    (checkpoints None without an interval)."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    gate = _gate(g, (T, H))
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)),
+                         ("g", g, (T, H) if gate else (T, H, dk)),
+                         ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
+        _check_tensor(name, t, shp, dt, dev)
+    og = _out_gate(out_gate_z, (T, H), dv, dt, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (T, H, dv), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
+    C = 0
+    if checkpoint_interval:
+        if cu_seqlens is not None and host_cu_seqlens is None:
+            host_cu_seqlens = cu_seqlens.cpu().tolist()
+        C = kda_checkpoint_count(dims, host_cu_seqlens if cu_seqlens is not None else None,
+                                 checkpoint_interval)
+        if C < 0:
+            raise KDAError(KDA_ERR_INVALID_ARG, "kda_checkpoint_count")
+        if checkpoints is None:
+            checkpoints = torch.empty((max(C, 1), H, dk, dv), dtype=torch.float32, device=dev)
+    opts = kda_prefill_options(int(checkpoint_interval), og, _ptr(checkpoints), _ptr(out_gate_z))
+    need = kda_prefill_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.kda_chunk_prefill_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
+                                  _ptr(final_state), ctypes.byref(opts), _ptr(workspace),
+                                  workspace.numel(), _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_prefill_ex")
+    return out, final_state, (checkpoints[:C] if checkpoint_interval else None)
+
+
+def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                       beta: torch.Tensor, state: torch.Tensor,
+                       out: Optional[torch.Tensor] = None, *,
+                       out_gate_z: Optional[torch.Tensor] = None, scale: float = 1.0,
+                       qk_l2norm: bool = True, stream=None) -> torch.Tensor:
+    """One decode step with the output gate (z ``[N,H,d_v]`` or ``[N,H]``)."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    gate = _gate(g, (N, H))
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)),
+                         ("g", g, (N, H) if gate else (N, H, dk)),
+                         ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
+        _check_tensor(name, t, shp, dt, dev)
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    og = _out_gate(out_gate_z, (N, H), dv, dt, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (N, H, dv), dt, dev)
+    dims = make_dims(N, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
+    rc = lib.kda_decode_step_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(state), _ptr(out), og, _ptr(out_gate_z),
+                                _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_decode_step_ex")
+    return out
+

@@ -22,6 +22,9 @@ Technical Details, Kimi Delta Attention bullet, and "Kimi K3: The Manos, The
 Mythos, The Legendos", bullets on KDA as online learning and on the stability
 details (L2-normalised queries and keys).
 
+``apply_output_gate`` (numpy) is the output forget gate that may follow the
+read-out: out * sigmoid(z), z per value channel or per head.
+
 Inputs are float32 numpy arrays holding the exact upcast of what the GPU path
 reads (bf16 -> fp32 is exact), token-major: q, k, g ``[T, H, d_k]``,
 v ``[T, H, d_v]``, beta ``[T, H]``; states ``[N, H, d_k, d_v]``.
@@ -201,6 +204,23 @@ def decode_step(q, k, v, g, beta, state: np.ndarray, scale: float = 1.0,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode_step failed with code {rc}")
     return out
+
+
+def apply_output_gate(out, z) -> np.ndarray:
+    """Output forget gate on the attention read-out, in fp64.
+
+    "Kimi K3: The Manos, The Mythos, The Legendos", stability-details bullet,
+    lists a per-head output forget gate.  Read here as the usual sigmoid gate:
+    out' = out * sigmoid(z) with z a caller-supplied pre-activation, either one
+    value per value channel (z shaped like ``out``, ``[..., d_v]``) or one value
+    per head (z ``[...]``, broadcast over the d_v channels).
+    """
+    o = np.asarray(out, dtype=np.float64)
+    zz = np.asarray(z, dtype=np.float64)
+    if zz.shape == o.shape[:-1]:
+        zz = zz[..., None]
+    assert zz.shape[:-1] == o.shape[:-1] and zz.shape[-1] in (1, o.shape[-1])
+    return o * (1.0 / (1.0 + np.exp(-zz)))
 
 
 def naive_expansion(q, k, v, g, beta, initial_state=None, scale: float = 1.0,

@@ -182,3 +182,70 @@ def test_gate_field_and_validation(kda):
                         ws_bytes=0) == kda.KDA_ERR_WORKSPACE
     assert prefill_call(kda, d1, g=FAKE + 3 * (1024 * 2 * 128 * 2 + 4096) + 1) == \
         kda.KDA_ERR_MISALIGNED
+
+
+def test_prefill_options_layout(kda):
+    # struct kda_prefill_options in include/kda.h: two int32, then two pointers
+    assert ctypes.sizeof(kda.kda_prefill_options) == 24
+    assert kda.kda_prefill_options.checkpoints.offset == 8
+    assert kda.kda_prefill_options.out_gate_z.offset == 16
+
+
+def test_output_gate_validation(kda):
+    lib = kda.load_library()
+    d = kda.make_dims(1024, 2, 4, 128, 128, kda.KDA_BF16)
+    T, H, D = 1024, 4, 128
+    big = T * H * D * 2 + 4096
+    base = dict(q=FAKE, k=FAKE + big, v=FAKE + 2 * big, g=FAKE + 3 * big, beta=FAKE + 4 * big,
+                out=FAKE + 5 * big, ws=FAKE + 6 * big, z=FAKE + 30 * big, fin=None)
+    wsb = kda.kda_prefill_workspace_bytes(d)
+
+    def call(og, interval=0, null_opts=False, **over):
+        p = dict(base)
+        p.update(over)
+        o = kda.kda_prefill_options(interval, og, None, p["z"])
+        return lib.kda_chunk_prefill_ex(
+            ctypes.byref(d), p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, p["out"],
+            p["fin"], None if null_opts else ctypes.byref(o), p["ws"], wsb, None)
+
+    assert call(3) == kda.KDA_ERR_INVALID_ARG
+    assert call(-1) == kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_HEAD, z=FAKE + 30 * big + 1) == kda.KDA_ERR_MISALIGNED
+    # z is read element by element: 2-byte alignment is enough for bf16
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 30 * big + 2, ws=None) == kda.KDA_ERR_WORKSPACE
+    # z (an input) must not overlap out: T*H*d_v elements per channel, T*H per head
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 5 * big - 64) == kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_HEAD, z=FAKE + 5 * big - T * H * 2 + 2) == \
+        kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 5 * big - T * H * 2) == \
+        kda.KDA_ERR_INVALID_ARG
+    # nor the final state
+    assert call(kda.KDA_OUT_GATE_CHANNEL, fin=FAKE + 30 * big + 256) == kda.KDA_ERR_INVALID_ARG
+    # with no gate, z is ignored (NULL options mean "no options")
+    assert call(kda.KDA_OUT_GATE_NONE, z=None, ws=None) == kda.KDA_ERR_WORKSPACE
+    assert call(0, null_opts=True, ws=None) == kda.KDA_ERR_WORKSPACE
+    # an empty batch is a no-op even with a gate and no z
+    e = kda.make_dims(0, 0, 4, 128, 128, kda.KDA_BF16)
+    o = kda.kda_prefill_options(0, kda.KDA_OUT_GATE_CHANNEL, None, None)
+    assert lib.kda_chunk_prefill_ex(ctypes.byref(e), None, None, None, None, None, None, None,
+                                    None, None, ctypes.byref(o), FAKE, 0, None) == kda.KDA_OK
+
+
+def test_decode_output_gate_validation(kda):
+    lib = kda.load_library()
+    d = kda.make_dims(8, 8, 2, 128, 128, kda.KDA_BF16)
+    n = 8 * 2 * 128 * 2 + 4096
+    args = [FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, FAKE + 4 * n, FAKE + 8 * n, FAKE + 5 * n]
+    z = FAKE + 12 * n
+
+    def call(og, zz=z, a=args):
+        return lib.kda_decode_step_ex(ctypes.byref(d), *a, og, zz, None)
+
+    assert call(5) == kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_HEAD, None) == kda.KDA_ERR_INVALID_ARG
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z + 1) == kda.KDA_ERR_MISALIGNED
+    assert call(kda.KDA_OUT_GATE_CHANNEL, args[6] + 64) == kda.KDA_ERR_INVALID_ARG  # overlaps out
+    a = list(args); a[5] = FAKE + 8 * n + 4
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z, a) == kda.KDA_ERR_MISALIGNED
+    assert call(kda.KDA_OUT_GATE_HEAD, args[5] + 4096) == kda.KDA_ERR_INVALID_ARG  # in the state

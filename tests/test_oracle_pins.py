@@ -322,3 +322,44 @@ def test_thread_count_does_not_change_results(oracle):
     o2, f2 = oracle.prefill(q, k, v, g, beta, cu_seqlens=cu, threads=5)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(f1, f2)
+
+
+# ---------------------------------------------------------------- output gate
+# The output forget gate ("Kimi K3: The Manos, The Mythos, The Legendos",
+# stability-details bullet), read as out * sigmoid(z).  Pinned by values of the
+# logistic function that follow from its definition alone.
+
+def test_output_gate_closed_form_values(oracle):
+    rng = np.random.default_rng(31)
+    o = rng.standard_normal((5, 3, 4))
+    # sigmoid(0) = 1/2 and sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4, per head
+    np.testing.assert_allclose(oracle.apply_output_gate(o, np.zeros((5, 3))), 0.5 * o,
+                               rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.apply_output_gate(o, np.full((5, 3), np.log(3.0))),
+                               0.75 * o, rtol=1e-14, atol=1e-15)
+    # a strongly open gate passes the read-out, a strongly closed one blocks it
+    np.testing.assert_allclose(oracle.apply_output_gate(o, np.full((5, 3), 40.0)), o,
+                               rtol=1e-15, atol=0)
+    assert np.abs(oracle.apply_output_gate(o, np.full((5, 3), -40.0))).max() < 1e-17
+
+
+def test_output_gate_complement_and_broadcast(oracle):
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((6, 2, 5))
+    z = rng.standard_normal((6, 2, 5)) * 3
+    # sigmoid(z) + sigmoid(-z) = 1
+    np.testing.assert_allclose(oracle.apply_output_gate(o, z) + oracle.apply_output_gate(o, -z),
+                               o, rtol=1e-14, atol=1e-14)
+    # per channel: channel c is scaled by its own gate only
+    for c in range(5):
+        np.testing.assert_allclose(oracle.apply_output_gate(o, z)[..., c],
+                                   oracle.apply_output_gate(o[..., c:c + 1], z[..., c:c + 1])[..., 0],
+                                   rtol=0, atol=0)
+    # a per-head z equals the same value repeated over the channels
+    zh = rng.standard_normal((6, 2))
+    np.testing.assert_array_equal(oracle.apply_output_gate(o, zh),
+                                  oracle.apply_output_gate(o, np.repeat(zh[..., None], 5, -1)))
+    # monotone in z
+    a = oracle.apply_output_gate(np.ones((1, 1, 1)), np.full((1, 1, 1), 0.3))
+    b = oracle.apply_output_gate(np.ones((1, 1, 1)), np.full((1, 1, 1), 0.4))
+    assert 0.5 < a[0, 0, 0] < b[0, 0, 0] < 1.0
