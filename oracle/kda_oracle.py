@@ -22,6 +22,10 @@ Technical Details, Kimi Delta Attention bullet, and "Kimi K3: The Manos, The
 Mythos, The Legendos", bullets on KDA as online learning and on the stability
 details (L2-normalised queries and keys).
 
+``short_conv`` and ``low_rank_gate`` (numpy) are the front end that may
+produce q, k, v and g from raw projections: a short causal convolution per
+channel and g = -softplus(a b^T + bias).
+
 ``apply_output_gate`` (numpy) is the output forget gate that may follow the
 read-out: out * sigmoid(z), z per value channel or per head.
 
@@ -221,6 +225,70 @@ def apply_output_gate(out, z) -> np.ndarray:
         zz = zz[..., None]
     assert zz.shape[:-1] == o.shape[:-1] and zz.shape[-1] in (1, o.shape[-1])
     return o * (1.0 / (1.0 + np.exp(-zz)))
+
+
+def _seq_bounds(cu_seqlens, T: int, n_seqs: Optional[int]) -> np.ndarray:
+    return _cu(cu_seqlens, T, n_seqs)
+
+
+def short_conv(x, weight, cu_seqlens=None, n_seqs=None, state=None, silu: bool = False):
+    """Short causal depthwise convolution over each sequence's tokens, in fp64.
+
+    "Kimi K3: The Manos, The Mythos, The Legendos", stability-details bullet,
+    names short convolutions on q, k and v for local dependencies; the reading
+    taken here is the plain one: per channel, an FIR filter of width W over the
+    current token and the W-1 before it, within the sequence,
+        y_t[c] = sum_{j=0}^{W-1} weight[c][j] * x_{t-(W-1)+j}[c],
+    optionally followed by SiLU (y * sigmoid(y)).  Tokens before a sequence's
+    start are the rows of its conv state (state[n][j] is token start-(W-1)+j),
+    or zero without one.
+
+    x ``[T, H, d]``; weight ``[H, d, W]``; state ``[N, W-1, H, d]`` or None.
+    Returns ``(y [T, H, d], final_state [N, W-1, H, d])``, the final state
+    holding each sequence's last W-1 input rows (continuing from its state
+    when the sequence is shorter than W-1).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    T, H, d = x.shape
+    W = w.shape[2]
+    assert w.shape == (H, d, W) and W >= 1
+    cu = _seq_bounds(cu_seqlens, T, n_seqs)
+    N = cu.shape[0] - 1
+    st = np.zeros((N, W - 1, H, d)) if state is None else np.asarray(state, dtype=np.float64)
+    assert st.shape == (N, W - 1, H, d)
+    y = np.zeros((T, H, d))
+    fin = np.zeros((N, W - 1, H, d))
+    for n in range(N):
+        b, e = int(cu[n]), int(cu[n + 1])
+        ext = np.concatenate([st[n], x[b:e]], axis=0)  # ext[i] is token b-(W-1)+i
+        for t in range(e - b):
+            acc = np.zeros((H, d))
+            for j in range(W):
+                acc += w[:, :, j] * ext[t + j]
+            y[b + t] = acc
+        fin[n] = ext[ext.shape[0] - (W - 1):]
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    return y, fin
+
+
+def low_rank_gate(a, b, bias=None):
+    """Decay gate from a low-rank projection, in fp64.
+
+    "Kimi K3: The Manos, The Mythos, The Legendos", stability-details bullet,
+    names low-rank decay gates.  Read as: the layer's hidden state is projected
+    to rank r (``a [T, r]``, a projection outside this path), then up to every
+    head's key channels by ``b [H, d_k, r]`` (plus an optional per-channel
+    ``bias [H, d_k]``), and the log-retention is g = -softplus(a b^T + bias),
+    which is <= 0 as the recurrence needs.  Returns g ``[T, H, d_k]``.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    z = np.einsum("tj,hcj->thc", a, b)
+    if bias is not None:
+        z = z + np.asarray(bias, dtype=np.float64)[None]
+    return -np.logaddexp(0.0, z)
 
 
 def naive_expansion(q, k, v, g, beta, initial_state=None, scale: float = 1.0,
