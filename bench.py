@@ -217,6 +217,23 @@ def main():
         max(3, args.steps // 4))
     del z_pf
 
+    # front end: raw q, k, v through a width-4 convolution with SiLU, g from a
+    # rank-64 projection (g not read)
+    from kda_inputs import make_front_end
+    fe_in = make_front_end(T, 1, H, D, "bf16", width=4, rank=64, bias_std=0.3, seed=4,
+                           device=dev)
+    fe_state_out = torch.empty_like(fe_in["conv_state"])
+    fe_us = median_call_us(
+        lambda: kda.kda_chunk_prefill_ex(base["q"], base["k"], base["v"], None, base["beta"],
+                                         base["initial_state"], None, out, fin,
+                                         conv_weight=fe_in["conv_weight"], conv_silu=True,
+                                         conv_state_in=fe_in["conv_state"],
+                                         conv_state_out=fe_state_out, gate_a=fe_in["gate_a"],
+                                         gate_b=fe_in["gate_b"], gate_bias=fe_in["gate_bias"],
+                                         workspace=ws, stream=stream),
+        max(3, args.steps // 4))
+    fe_bytes = p_bytes - 2 * D * T * H + 2 * 64 * T + 2 * H * D * 64
+
     # ------------------------------------------------------------------ decode
     dw = make_config_decode(3, device=dev, steps=args.decode_steps)
     state = dw["state"]
@@ -252,6 +269,19 @@ def main():
                                        stream=stream),
         max(10, args.decode_steps // 4))
     del z_dec
+
+    # decode with the front end (width-4 convolution state advanced in place,
+    # rank-64 gate)
+    fe_dec = make_front_end(DECODE_N, DECODE_N, DECODE_H, D, "bf16", width=4, rank=64,
+                            bias_std=0.3, seed=5, device=dev)
+    fe_dec_us = median_call_us(
+        lambda: kda.kda_decode_step_ex(dw["q"][0], dw["k"][0], dw["v"][0], None, dw["beta"][0],
+                                       state, dout, conv_weight=fe_dec["conv_weight"],
+                                       conv_silu=True, conv_state=fe_dec["conv_state"],
+                                       gate_a=fe_dec["gate_a"], gate_b=fe_dec["gate_b"],
+                                       gate_bias=fe_dec["gate_bias"], stream=stream),
+        max(10, args.decode_steps // 4))
+    del fe_dec
 
     # plain 1 GiB device-to-device copy: the practical HBM ceiling on this machine
     # (and, in --profile runs, the known-size transfer that scales the counters)
@@ -343,6 +373,13 @@ def main():
                                 "overhead_vs_plain_median":
                                     og_us / (float(np.median(call_ms)) * 1e3) - 1.0,
                                 "algorithmic_bytes_per_call": p_bytes + T * H * D * 2},
+        "prefill_front_end": {"front_end": "raw q, k, v through a width-4 causal "
+                                            "convolution + SiLU; g = -softplus(a b^T + bias), "
+                                            "rank 64 (no g read)",
+                              "median_call_us": fe_us, "tokens_per_s": T / (fe_us * 1e-6),
+                              "overhead_vs_plain_median":
+                                  fe_us / (float(np.median(call_ms)) * 1e3) - 1.0,
+                              "algorithmic_bytes_per_call": fe_bytes},
         "decode": {
             "workload": CONFIGS[3].name.replace(", 100 steps", ""),
             "steps": args.decode_steps,
@@ -364,6 +401,8 @@ def main():
                 "practical_hbm_GBps": copy_GBps,
                 "frac_of_practical": (sb + tb) / d_avg_s / 1e9 / copy_GBps,
             },
+            "front_end": {"median_call_us": fe_dec_us,
+                          "note": "width-4 convolution state advanced in place, rank-64 gate"},
             "output_gate": {"z": "[N, H, d_v]", "median_call_us": og_dec_us,
                             "algorithmic_bytes_per_call": sb + tb + DECODE_N * DECODE_H * D * 2,
                             "achieved_GBps": (sb + tb + DECODE_N * DECODE_H * D * 2)

@@ -191,6 +191,45 @@ typedef enum {
     KDA_OUT_GATE_HEAD = 2     /* z [T_total, H]      */
 } kda_out_gate;
 
+/* Front end fused ahead of the recurrence ("Kimi K3: The Manos, The Mythos,
+ * The Legendos", bullet on stability details: short convolutions on q, k and
+ * v for local dependencies, and low-rank decay gates).  With a front end the
+ * q, k and v handed to the call are the raw projections, and the library
+ * forms, per sequence, for x in (q, k, v) and every head h and channel c,
+ *
+ *     x'_t[h][c] = sum_{j < W} conv_weight[x][h][j][c] * x_{t-(W-1)+j}[h][c]
+ *
+ * (tap W-1 is the current token; tokens before a sequence's start are the
+ * rows of conv_state_in, or zero without it), then SiLU(x') = x' sigmoid(x')
+ * if conv_silu; and, with gate_rank r > 0,
+ *
+ *     g_t[h][c] = -softplus(sum_{j < r} gate_a[t][j] gate_b[h][c][j] + gate_bias[h][c])
+ *
+ * in place of a g argument (which must then be NULL).  The recurrence runs on
+ * x' and g exactly as it runs on given q, k, v, g; x' and g stay in fp32 on
+ * chip and never reach memory.  conv_width 0 means no convolution (and no
+ * SiLU).  For full accuracy the computed g should satisfy g >= -5, as a given
+ * g should (softplus(z) <= 5 for z <= 4.99).
+ *
+ * conv_state_* hold, per sequence, the W-1 raw rows before the sequence
+ * (in) and the last W-1 raw rows of the sequence (out; for a sequence shorter
+ * than W-1 they continue from its input rows), so a later call continues the
+ * convolution exactly.  In prefill conv_state_out must not overlap any other
+ * buffer; in decode it may be the same pointer as conv_state_in (advanced in
+ * place). */
+typedef struct {
+    int32_t conv_width;        /* 0 (none) or W = 1..4                                   */
+    int32_t conv_silu;         /* 0 or 1                                                 */
+    const void* conv_weight;   /* [3, H, W, d] io_dtype (q, k, v filters), 16-byte aligned */
+    const void* conv_state_in; /* [N, 3, W-1, H, d] io_dtype, 16-byte aligned, nullable   */
+    void* conv_state_out;      /* [N, 3, W-1, H, d] io_dtype, 16-byte aligned, nullable   */
+    int32_t gate_rank;         /* 0 (g is given) or r in {32, 64, 96, 128}               */
+    int32_t reserved;          /* must be 0                                              */
+    const void* gate_a;        /* [T_total, r] io_dtype (decode: [N, r]), 16-byte aligned */
+    const void* gate_b;        /* [H, d_k, r] io_dtype, 16-byte aligned                  */
+    const float* gate_bias;    /* [H, d_k] fp32, nullable (zero)                         */
+} kda_front_end;
+
 /* Options of kda_chunk_prefill_ex; all-zero means none (kda_chunk_prefill). */
 typedef struct {
     int32_t checkpoint_interval; /* 0, or as in kda_chunk_prefill_checkpoints            */
@@ -199,29 +238,44 @@ typedef struct {
     const void* out_gate_z;      /* device, io_dtype, required unless KDA_OUT_GATE_NONE;
                                     element-size aligned; read only; must not overlap
                                     out, final_state or checkpoints                      */
+    const kda_front_end* front_end; /* nullable: q, k, v (and g) as given                */
 } kda_prefill_options;
 
-/* Chunked prefill with options: checkpoints (see kda_chunk_prefill_checkpoints)
- * and/or the output gate.  opts NULL means none.  Same arguments, rules and
- * results as kda_chunk_prefill otherwise; with an output gate, out holds the
- * gated outputs (states and checkpoints are unchanged by it).
+/* Chunked prefill with options: checkpoints (see kda_chunk_prefill_checkpoints),
+ * the output gate and/or the front end.  opts NULL means none.  Same
+ * arguments, rules and results as kda_chunk_prefill otherwise; with an output
+ * gate, out holds the gated outputs (states and checkpoints are unchanged by
+ * it); with a front end, q, k, v are the raw projections (see kda_front_end).
  * Errors: KDA_ERR_INVALID_ARG for an out_gate outside kda_out_gate, a NULL
- * out_gate_z with a gate (T_total > 0), or z overlapping an output;
- * KDA_ERR_MISALIGNED for a z not aligned to its element size. */
+ * out_gate_z with a gate (T_total > 0), z overlapping an output, a front end
+ * with conv_width outside 0..4, conv_silu outside 0..1, a NULL conv_weight
+ * with W > 0, a gate_rank other than 0, 32, 64, 96, 128, nonzero reserved
+ * fields, gate_rank > 0 with a non-NULL g, NULL gate factors or
+ * KDA_GATE_HEAD, or a conv_state_out overlapping another buffer;
+ * KDA_ERR_MISALIGNED for a z not aligned to its element size or a front-end
+ * tensor not 16-byte aligned (gate_bias: 4). */
 kda_status kda_chunk_prefill_ex(const kda_dims* dims, const void* q, const void* k,
                                 const void* v, const void* g, const void* beta,
                                 const float* initial_state, const int32_t* cu_seqlens,
                                 void* out, float* final_state, const kda_prefill_options* opts,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* One decode step with the output gate (out_gate: kda_out_gate; out_gate_z as
- * above with N in place of T_total, and it must not overlap out or
- * state_inout).  KDA_OUT_GATE_NONE is kda_decode_step.  Errors as for
- * kda_decode_step, plus those listed for the gate at kda_chunk_prefill_ex. */
+/* Options of kda_decode_step_ex; all-zero means none (kda_decode_step). */
+typedef struct {
+    int32_t out_gate;            /* kda_out_gate                                          */
+    int32_t reserved;            /* must be 0                                             */
+    const void* out_gate_z;      /* as in kda_prefill_options with N in place of T_total;
+                                    must not overlap out or state_inout                   */
+    const kda_front_end* front_end; /* nullable; gate_a is [N, r]                         */
+} kda_decode_options;
+
+/* One decode step with options: the output gate and/or the front end.  opts
+ * NULL means none.  Errors as for kda_decode_step, plus those listed for the
+ * options at kda_chunk_prefill_ex. */
 kda_status kda_decode_step_ex(const kda_dims* dims, const void* q, const void* k,
                               const void* v, const void* g, const void* beta,
-                              float* state_inout, void* out, int32_t out_gate,
-                              const void* out_gate_z, void* stream);
+                              float* state_inout, void* out, const kda_decode_options* opts,
+                              void* stream);
 
 /* One decode step: one new token for each of N sequences.
  *

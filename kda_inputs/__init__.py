@@ -13,6 +13,9 @@ Recipe (the workloads the library is measured on; there is no dataset):
 * g = -softplus(N(mu, 1)) * s per (token, head, key channel), so g <= 0;
 * initial state ~ N(0, std^2) in fp32 (or zeros), one per (sequence, head);
 * output-gate pre-activations z ~ N(0, 2^2) (own generator and seed);
+* front end (own generator and seed): raw q, k, v as above but not
+  normalised; conv weights N(0, 1/W); conv states N(0, 1); low-rank gate
+  factors a ~ N(0, 1), b ~ N(0, 1/r) (so a b^T ~ N(0, 1)), bias N(0, s^2);
 * varlen batches draw integer lengths uniformly in [lo, hi] (both ends
   inclusive) on the CPU generator before any tensor, so the packing does not
   depend on the device.
@@ -195,6 +198,28 @@ def make_out_gate(shape, io_dtype: str = "bf16", *, std: float = 2.0, seed: int 
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return (_randn(tuple(shape), gen, device) * std).to(torch_dtype(io_dtype))
+
+
+def make_front_end(n_tokens: int, n_seqs: int, heads: int, d: int, io_dtype: str = "bf16", *,
+                   width: int = 4, rank: int = 64, bias_std: float = 0.0, seed: int = 11,
+                   device="cpu") -> dict:
+    """Front-end tensors, drawn from their own generator in this order: conv
+    weights ``[3, H, W, d]`` ~ N(0, 1/W); conv state ``[N, 3, W-1, H, d]`` ~
+    N(0, 1); gate factors a ``[T, r]`` ~ N(0, 1) and b ``[H, d, r]`` ~ N(0, 1/r),
+    so a b^T ~ N(0, 1) like the g logits of the plain recipe; bias ``[H, d]``
+    fp32 ~ N(0, bias_std^2) (None when bias_std is 0)."""
+    dt = torch_dtype(io_dtype)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    if width > 0:
+        out["conv_weight"] = (_randn((3, heads, width, d), gen, device) / width ** 0.5).to(dt)
+        out["conv_state"] = _randn((n_seqs, 3, max(width - 1, 0), heads, d), gen, device).to(dt)
+    if rank > 0:
+        out["gate_a"] = _randn((n_tokens, rank), gen, device).to(dt)
+        out["gate_b"] = (_randn((heads, d, rank), gen, device) / rank ** 0.5).to(dt)
+        out["gate_bias"] = (_randn((heads, d), gen, device) * bias_std) if bias_std else None
+    return out
 
 
 def seeded_heads(n_heads: int, count: int, seed: int) -> List[int]:

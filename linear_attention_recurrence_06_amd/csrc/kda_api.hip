@@ -83,7 +83,7 @@ int current_cu_count() {
 
 extern "C" {
 
-int kda_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int kda_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 const char* kda_status_string(kda_status s) {
     switch (s) {
@@ -109,22 +109,82 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
 
 namespace {
 
-// Shared body of the prefill entry points (interval 0: no checkpoints;
-// out_gate 0: no output gate).
+// Front-end checks shared by prefill and decode (need_g: there are tokens,
+// so a decay gate must come from g or the low-rank factors).  Fills `fe`
+// (inactive when f is NULL).
+kda_status check_front_end(const kda_dims* d, const kda_front_end* f, const void* g,
+                           bool need_g, kda::FrontEnd& fe) {
+    fe = kda::FrontEnd();
+    if (!f) return (g || !need_g) ? KDA_OK : KDA_ERR_INVALID_ARG;
+    if (f->conv_width < 0 || f->conv_width > 4 || f->conv_silu < 0 || f->conv_silu > 1 ||
+        f->reserved != 0)
+        return KDA_ERR_INVALID_ARG;
+    const int r = f->gate_rank;
+    if (r != 0 && r != 32 && r != 64 && r != 96 && r != 128) return KDA_ERR_INVALID_ARG;
+    if (f->conv_width > 0 && !f->conv_weight) return KDA_ERR_INVALID_ARG;
+    if (r > 0 && (g || (need_g && (!f->gate_a || !f->gate_b)) || d->gate == KDA_GATE_HEAD))
+        return KDA_ERR_INVALID_ARG;
+    if (r == 0 && !g && need_g) return KDA_ERR_INVALID_ARG;
+    const bool states = f->conv_width > 1;
+    const void* v16[] = {f->conv_width > 0 ? f->conv_weight : nullptr,
+                         states ? f->conv_state_in : nullptr,
+                         states ? f->conv_state_out : nullptr, r > 0 ? f->gate_a : nullptr,
+                         r > 0 ? f->gate_b : nullptr};
+    for (const void* p : v16)
+        if (p && !aligned_to(p, 16)) return KDA_ERR_MISALIGNED;
+    if (r > 0 && f->gate_bias && !aligned_to(f->gate_bias, 4)) return KDA_ERR_MISALIGNED;
+    fe.conv_w = f->conv_width;
+    fe.silu = f->conv_width > 0 ? f->conv_silu : 0;
+    fe.conv_weight = f->conv_width > 0 ? f->conv_weight : nullptr;
+    fe.state_in = states ? f->conv_state_in : nullptr;
+    fe.state_out = states ? f->conv_state_out : nullptr;
+    fe.rank = r;
+    fe.gate_a = r > 0 ? f->gate_a : nullptr;
+    fe.gate_b = r > 0 ? f->gate_b : nullptr;
+    fe.gate_bias = r > 0 ? f->gate_bias : nullptr;
+    return KDA_OK;
+}
+
+// Byte ranges of the front end's inputs and of its state output.
+struct FrontEndRanges {
+    Range in[5];  // weight, state in, a, b, bias
+    Range state_out;
+};
+FrontEndRanges front_end_ranges(const kda_dims* d, const kda::FrontEnd& fe, int64_t T) {
+    const size_t E = elt_bytes(d);
+    const int64_t N = d->num_seqs, H = d->num_heads, D = d->d_k;
+    const size_t wb = (size_t)3 * H * fe.conv_w * D * E;
+    const size_t cb = fe.conv_w > 1 ? (size_t)N * 3 * (fe.conv_w - 1) * H * D * E : 0;
+    FrontEndRanges r;
+    r.in[0] = fe.conv_weight ? range_of(fe.conv_weight, wb) : Range{0, 0};
+    r.in[1] = fe.state_in ? range_of(fe.state_in, cb) : Range{0, 0};
+    r.in[2] = fe.gate_a ? range_of(fe.gate_a, (size_t)T * fe.rank * E) : Range{0, 0};
+    r.in[3] = fe.gate_b ? range_of(fe.gate_b, (size_t)H * D * fe.rank * E) : Range{0, 0};
+    r.in[4] = fe.gate_bias ? range_of(fe.gate_bias, (size_t)H * D * 4) : Range{0, 0};
+    r.state_out = fe.state_out ? range_of(fe.state_out, cb) : Range{0, 0};
+    return r;
+}
+
+// Shared body of the prefill entry points.
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
                         const int32_t* cu_seqlens, void* out, float* final_state,
-                        int32_t interval, float* checkpoints, int32_t out_gate,
-                        const void* out_gate_z, void* workspace, size_t workspace_bytes,
+                        const kda_prefill_options& o, void* workspace, size_t workspace_bytes,
                         void* stream) {
     kda_status st = check_dims(d, true);
     if (st != KDA_OK) return st;
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads, D = d->d_k;
+    const int32_t interval = o.checkpoint_interval, out_gate = o.out_gate;
+    float* checkpoints = o.checkpoints;
+    const void* out_gate_z = o.out_gate_z;
     if (interval < 0) return KDA_ERR_INVALID_ARG;
     if (out_gate < KDA_OUT_GATE_NONE || out_gate > KDA_OUT_GATE_HEAD) return KDA_ERR_INVALID_ARG;
     if (N == 0) return T == 0 ? KDA_OK : KDA_ERR_INVALID_ARG;
     if (!cu_seqlens && T % N != 0) return KDA_ERR_INVALID_ARG;
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_INVALID_ARG;
+    kda::FrontEnd fe;
+    st = check_front_end(d, o.front_end, g, T > 0, fe);
+    if (st != KDA_OK) return st;
+    if (T > 0 && (!q || !k || !v || !beta || !out)) return KDA_ERR_INVALID_ARG;
     if (interval > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
     if (out_gate != KDA_OUT_GATE_NONE && T > 0 && !out_gate_z) return KDA_ERR_INVALID_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
@@ -143,45 +203,53 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
         if (p && !aligned_to(p, 4)) return KDA_ERR_MISALIGNED;
     if (workspace_bytes < kda_prefill_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
 
-    // overlaps: out must not touch any input; final_state may equal initial_state exactly
+    // overlaps: no output may touch an input or another output; final_state
+    // may equal initial_state exactly
     const size_t E = elt_bytes(d);
     const size_t qb = (size_t)T * H * D * E, bb = (size_t)T * H * E, sb = (size_t)N * H * D * D * 4;
     const size_t gb = sg ? bb : qb;
+    const FrontEndRanges fr = front_end_ranges(d, fe, T);
     const Range r_out = range_of(out, qb);
-    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, gb),
-                         range_of(beta, bb),
-                         initial_state ? range_of(initial_state, sb) : Range{0, 0},
-                         cu_seqlens ? range_of(cu_seqlens, (size_t)(N + 1) * 4) : Range{0, 0},
-                         range_of(workspace, workspace_bytes)};
-    if (T > 0)
-        for (const Range& r : ins)
-            if (overlap(r_out, r)) return KDA_ERR_INVALID_ARG;
     const Range r_z = out_gate != KDA_OUT_GATE_NONE
                           ? range_of(out_gate_z, out_gate == KDA_OUT_GATE_HEAD ? bb : qb)
                           : Range{0, 0};
-    if (T > 0 && overlap(r_out, r_z)) return KDA_ERR_INVALID_ARG;
-    if (final_state) {
-        const Range r_fin = range_of(final_state, sb);
-        if (initial_state && initial_state != final_state &&
-            overlap(r_fin, range_of(initial_state, sb)))
-            return KDA_ERR_INVALID_ARG;
-        const Range others[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                                range_of(g, gb), range_of(beta, bb), r_out, r_z,
-                                range_of(workspace, workspace_bytes)};
-        for (const Range& r : others)
-            if (overlap(r_fin, r)) return KDA_ERR_INVALID_ARG;
-    }
+    const Range r_ws = range_of(workspace, workspace_bytes);
+    const Range r_s0 = initial_state ? range_of(initial_state, sb) : Range{0, 0};
+    const Range r_cu = cu_seqlens ? range_of(cu_seqlens, (size_t)(N + 1) * 4) : Range{0, 0};
+    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
+                         g ? range_of(g, gb) : Range{0, 0}, range_of(beta, bb), r_s0, r_cu, r_z,
+                         fr.in[0], fr.in[1], fr.in[2], fr.in[3], fr.in[4]};
+    const Range r_fin = final_state ? range_of(final_state, sb) : Range{0, 0};
+    Range r_ck{0, 0};
     if (interval > 0 && !cu_seqlens) {
         // equal lengths: the checkpoint count is known here, so check its buffer too
         const int64_t C = kda_checkpoint_count(d, nullptr, interval);
-        const Range r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
-        const Range all[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
-                             range_of(g, gb), range_of(beta, bb), r_out, r_z,
-                             initial_state ? range_of(initial_state, sb) : Range{0, 0},
-                             final_state ? range_of(final_state, sb) : Range{0, 0},
-                             range_of(workspace, workspace_bytes)};
-        for (const Range& r : all)
-            if (overlap(r_ck, r)) return KDA_ERR_INVALID_ARG;
+        r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
+    }
+    if (T > 0) {
+        // outputs against inputs (final_state == initial_state is allowed)
+        const Range outs[] = {r_out, r_fin, r_ck, fr.state_out};
+        for (int oi = 0; oi < 4; ++oi)
+            for (const Range& r : ins) {
+                if (oi == 1 && initial_state == final_state && r.lo == r_s0.lo && r.hi == r_s0.hi)
+                    continue;
+                if (overlap(outs[oi], r)) return KDA_ERR_INVALID_ARG;
+            }
+        // outputs against each other and the workspace
+        for (int a = 0; a < 4; ++a) {
+            if (overlap(outs[a], r_ws)) return KDA_ERR_INVALID_ARG;
+            for (int b = a + 1; b < 4; ++b)
+                if (overlap(outs[a], outs[b])) return KDA_ERR_INVALID_ARG;
+        }
+    } else {
+        // no tokens: only the final states and the conv states are written
+        if (final_state && initial_state && initial_state != final_state && overlap(r_fin, r_s0))
+            return KDA_ERR_INVALID_ARG;
+        const Range touched[] = {r_fin, fr.state_out};
+        for (const Range& r : touched)
+            if (overlap(r, r_ws) || overlap(r, fr.in[1]) || overlap(r, r_cu))
+                return KDA_ERR_INVALID_ARG;
+        if (overlap(r_fin, fr.state_out) || overlap(fr.state_out, r_s0)) return KDA_ERR_INVALID_ARG;
     }
 
     kda::PrefillArgs a;
@@ -203,11 +271,15 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.checkpoints = checkpoints;
     a.out_gate = out_gate;
     a.out_gate_z = out_gate_z;
+    a.fe = fe;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
     a.cu_count = current_cu_count();
     hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+const kda_prefill_options kNoPrefillOptions = {0, KDA_OUT_GATE_NONE, nullptr, nullptr, nullptr};
+const kda_decode_options kNoDecodeOptions = {KDA_OUT_GATE_NONE, 0, nullptr, nullptr};
 
 }  // namespace
 
@@ -217,8 +289,8 @@ kda_status kda_chunk_prefill(const kda_dims* d, const void* q, const void* k, co
                              const void* g, const void* beta, const float* initial_state,
                              const int32_t* cu_seqlens, void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, 0,
-                        nullptr, KDA_OUT_GATE_NONE, nullptr, workspace, workspace_bytes, stream);
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                        kNoPrefillOptions, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_prefill_ex(const kda_dims* d, const void* q, const void* k, const void* v,
@@ -226,11 +298,8 @@ kda_status kda_chunk_prefill_ex(const kda_dims* d, const void* q, const void* k,
                                 const int32_t* cu_seqlens, void* out, float* final_state,
                                 const kda_prefill_options* o, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-    const kda_prefill_options none = {0, KDA_OUT_GATE_NONE, nullptr, nullptr};
-    if (!o) o = &none;
     return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                        o->checkpoint_interval, o->checkpoints, o->out_gate, o->out_gate_z,
-                        workspace, workspace_bytes, stream);
+                        o ? *o : kNoPrefillOptions, workspace, workspace_bytes, stream);
 }
 
 int64_t kda_checkpoint_count(const kda_dims* d, const int32_t* host_cu_seqlens,
@@ -259,22 +328,30 @@ kda_status kda_chunk_prefill_checkpoints(const kda_dims* d, const void* q, const
                                          float* checkpoints, void* workspace,
                                          size_t workspace_bytes, void* stream) {
     if (checkpoint_interval < 1) return KDA_ERR_INVALID_ARG;
-    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                        checkpoint_interval, checkpoints, KDA_OUT_GATE_NONE, nullptr, workspace,
-                        workspace_bytes, stream);
+    kda_prefill_options o = kNoPrefillOptions;
+    o.checkpoint_interval = checkpoint_interval;
+    o.checkpoints = checkpoints;
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, o,
+                        workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
 
 static kda_status decode_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                               const void* g, const void* beta, float* state_inout, void* out,
-                              int32_t out_gate, const void* out_gate_z, void* stream) {
+                              const kda_decode_options& o, void* stream) {
     kda_status st = check_dims(d, false);
     if (st != KDA_OK) return st;
-    if (out_gate < KDA_OUT_GATE_NONE || out_gate > KDA_OUT_GATE_HEAD) return KDA_ERR_INVALID_ARG;
+    const int32_t out_gate = o.out_gate;
+    const void* out_gate_z = o.out_gate_z;
+    if (out_gate < KDA_OUT_GATE_NONE || out_gate > KDA_OUT_GATE_HEAD || o.reserved != 0)
+        return KDA_ERR_INVALID_ARG;
     const int64_t N = d->num_seqs, H = d->num_heads, D = d->d_k;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    kda::FrontEnd fe;
+    st = check_front_end(d, o.front_end, g, true, fe);
+    if (st != KDA_OK) return st;
+    if (!q || !k || !v || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
     if (out_gate != KDA_OUT_GATE_NONE && !out_gate_z) return KDA_ERR_INVALID_ARG;
     if (out_gate != KDA_OUT_GATE_NONE && !aligned_to(out_gate_z, d->io_dtype == KDA_BF16 ? 2 : 4))
         return KDA_ERR_MISALIGNED;
@@ -283,23 +360,33 @@ static kda_status decode_impl(const kda_dims* d, const void* q, const void* k, c
     if (!aligned_to(state_inout, 16)) return KDA_ERR_MISALIGNED;
     const void* ptrs[] = {q, k, v, g, beta, out};
     for (const void* p : ptrs)
-        if (!aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
+        if (p && !aligned_to(p, E_al)) return KDA_ERR_MISALIGNED;
     const size_t E = elt_bytes(d);
     const size_t qb = (size_t)N * H * D * E, bb = (size_t)N * H * E, sb = (size_t)N * H * D * D * 4;
     const size_t gb = d->gate == KDA_GATE_HEAD ? bb : qb;
+    const FrontEndRanges fr = front_end_ranges(d, fe, N);
     const Range r_out = range_of(out, qb);
-    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb), range_of(g, gb),
-                         range_of(beta, bb), range_of(state_inout, sb)};
-    for (const Range& r : ins)
-        if (overlap(r_out, r)) return KDA_ERR_INVALID_ARG;
+    const Range r_state = range_of(state_inout, sb);
     const Range r_z = out_gate != KDA_OUT_GATE_NONE
                           ? range_of(out_gate_z, out_gate == KDA_OUT_GATE_HEAD ? bb : qb)
                           : Range{0, 0};
-    if (overlap(r_out, r_z)) return KDA_ERR_INVALID_ARG;
-    const Range r_state = range_of(state_inout, sb);
-    for (int i = 0; i < 5; ++i)
-        if (overlap(r_state, ins[i])) return KDA_ERR_INVALID_ARG;
-    if (overlap(r_state, r_z)) return KDA_ERR_INVALID_ARG;
+    const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
+                         g ? range_of(g, gb) : Range{0, 0}, range_of(beta, bb), r_z,
+                         fr.in[0], fr.in[2], fr.in[3], fr.in[4], fr.in[1]};
+    constexpr int kInsNoState = 10;  // every input but the conv state
+    // out: no overlap with anything; the state: only itself; the conv state:
+    // only the input conv state, and only exactly
+    for (const Range& r : ins)
+        if (overlap(r_out, r) || overlap(r_state, r)) return KDA_ERR_INVALID_ARG;
+    if (overlap(r_out, r_state)) return KDA_ERR_INVALID_ARG;
+    if (fe.state_out) {
+        for (int i = 0; i < kInsNoState; ++i)
+            if (overlap(fr.state_out, ins[i])) return KDA_ERR_INVALID_ARG;
+        if (overlap(fr.state_out, r_out) || overlap(fr.state_out, r_state))
+            return KDA_ERR_INVALID_ARG;
+        if (fe.state_in && fe.state_in != fe.state_out && overlap(fr.state_out, fr.in[1]))
+            return KDA_ERR_INVALID_ARG;
+    }
 
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -312,6 +399,7 @@ static kda_status decode_impl(const kda_dims* d, const void* q, const void* k, c
     a.scalar_g = d->gate == KDA_GATE_HEAD;
     a.out_gate = out_gate;
     a.out_gate_z = out_gate_z;
+    a.fe = fe;
     a.scale = d->scale;
     a.l2norm = d->qk_l2norm;
     hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));
@@ -324,14 +412,14 @@ extern "C" {
 kda_status kda_decode_step(const kda_dims* d, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, float* state_inout, void* out,
                            void* stream) {
-    return decode_impl(d, q, k, v, g, beta, state_inout, out, KDA_OUT_GATE_NONE, nullptr,
-                       stream);
+    return decode_impl(d, q, k, v, g, beta, state_inout, out, kNoDecodeOptions, stream);
 }
 
 kda_status kda_decode_step_ex(const kda_dims* d, const void* q, const void* k, const void* v,
                               const void* g, const void* beta, float* state_inout, void* out,
-                              int32_t out_gate, const void* out_gate_z, void* stream) {
-    return decode_impl(d, q, k, v, g, beta, state_inout, out, out_gate, out_gate_z, stream);
+                              const kda_decode_options* o, void* stream) {
+    return decode_impl(d, q, k, v, g, beta, state_inout, out, o ? *o : kNoDecodeOptions,
+                       stream);
 }
 
 }  // extern "C"

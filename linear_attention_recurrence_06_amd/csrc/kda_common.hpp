@@ -149,6 +149,24 @@ __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off)
     }
 }
 
+// A buffer offset past every range used here (and far from wrapping), for
+// loads that must read zero.
+constexpr uint32_t kFarOffset = 0x80000000u;
+
+// Fragment (8 consecutive elements) at byte offset `off` of a buffer; past the
+// range it reads zeros.
+template <typename T>
+__device__ __forceinline__ Frag<T> buffer_load_frag(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+        f.v = buffer_load<bf16x8>(r, off);
+    } else {
+        const f32x4 lo = buffer_load<f32x4>(r, off), hi = buffer_load<f32x4>(r, off + 16);
+        f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    return f;
+}
+
 // 2^x on the hardware exponential unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -23,7 +23,55 @@
 
 namespace kda {
 
+// Front end of one decode step (kernel argument): the short convolution of the
+// raw q, k, v against each sequence's conv state, advanced in place, and the
+// low-rank decay gate.
+struct DecodeFE {
+    int conv_w, silu, rank;
+    const void* weight;     // [3, H, W, d]
+    const void* state_in;   // [N, 3, W-1, H, d] or null (zeros)
+    void* state_out;        // [N, 3, W-1, H, d] or null; may equal state_in
+    const void* a;          // [N, r]
+    const void* b;          // [H, d, r]
+    const float* bias;      // [H, d] or null
+};
+
+// Convolved (and SiLU-activated) element i of tensor x (0 q, 1 k, 2 v) of
+// unit (n, h), whose raw value is `raw`; hist receives the W-1 state rows.
 template <typename T, int D>
+__device__ __forceinline__ float fe_conv(const DecodeFE& fe, int x, int64_t n, int h, int H,
+                                         int i, float raw, float (&hist)[3]) {
+    const int W = fe.conv_w;
+    if (W == 0) return raw;
+    const T* w = reinterpret_cast<const T*>(fe.weight) + ((int64_t)(x * H + h) * W) * D + i;
+    const T* st = reinterpret_cast<const T*>(fe.state_in);
+    float y = to_f32(w[(int64_t)(W - 1) * D]) * raw;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        hist[j] = 0.f;
+        if (j < W - 1) {
+            if (st) hist[j] = to_f32(st[(((n * 3 + x) * (W - 1) + j) * H + h) * D + i]);
+            y += to_f32(w[(int64_t)j * D]) * hist[j];
+        }
+    }
+    return fe.silu ? y * __builtin_amdgcn_rcpf(1.f + __expf(-y)) : y;
+}
+
+// Writes the advanced conv state of element i: rows hist[1..W-2], then raw.
+template <typename T, int D>
+__device__ __forceinline__ void fe_conv_store(const DecodeFE& fe, int x, int64_t n, int h, int H,
+                                              int i, float raw, const float (&hist)[3]) {
+    const int W = fe.conv_w;
+    if (W <= 1 || !fe.state_out) return;
+    T* st = reinterpret_cast<T*>(fe.state_out);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (j < W - 1)
+            st[(((n * 3 + x) * (W - 1) + j) * H + h) * D + i] =
+                from_f32<T>(j + 1 < W - 1 ? hist[j + 1] : raw);
+}
+
+template <typename T, int D, bool FE>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
@@ -32,7 +80,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      float* __restrict__ S,
                                                      T* __restrict__ out, float scale,
                                                      int l2norm, int scalar_g, int out_gate,
-                                                     const T* __restrict__ og_z) {
+                                                     const T* __restrict__ og_z, int H,
+                                                     DecodeFE fe) {
     constexpr int TPR = D / 4;       // threads per state row
     constexpr int RG = 256 / TPR;    // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -58,12 +107,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     // 2. token vectors: every wave computes the norms itself (no barrier needed for them)
     const T* qu = q + unit * D;
     const T* ku = k + unit * D;
+    const int64_t n = unit / H;
+    const int h = (int)(unit - n * H);
     float qv[EPL], kv[EPL];
+    float qraw[EPL], kraw[EPL], qhist[EPL][3], khist[EPL][3];
     float ssq = 0.f, ssk = 0.f, sqk = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        qv[e] = to_f32(qu[lane + kWave * e]);
-        kv[e] = to_f32(ku[lane + kWave * e]);
+        qraw[e] = to_f32(qu[lane + kWave * e]);
+        kraw[e] = to_f32(ku[lane + kWave * e]);
+        if constexpr (FE) {
+            qv[e] = fe_conv<T, D>(fe, 0, n, h, H, lane + kWave * e, qraw[e], qhist[e]);
+            kv[e] = fe_conv<T, D>(fe, 1, n, h, H, lane + kWave * e, kraw[e], khist[e]);
+        } else {
+            qv[e] = qraw[e];
+            kv[e] = kraw[e];
+        }
         ssq += qv[e] * qv[e];
         ssk += kv[e] * kv[e];
         sqk += qv[e] * kv[e];
@@ -83,14 +142,67 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
             const int i = lane + kWave * e;
             s_q[i] = qv[e] * rq * scale;
             s_k[i] = kv[e] * rk;
-            s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
+            if (!(FE && fe.rank > 0)) s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
+        }
+    }
+    if (FE && fe.rank > 0) {
+        // low-rank decay gate g = -softplus(a[n] . b[h][c] + bias[h][c]): the
+        // TPC = 256/D threads of channel c = t / TPC each take rank/TPC of the
+        // products (loads past the rank read zero), then sum with lane swaps
+        constexpr int TPC = 256 / D;
+        constexpr int MAXJ = 128 / TPC;  // the largest slice
+        const int c = t / TPC, part = t % TPC;
+        const int R = fe.rank, slice = R / TPC;
+        const uint32_t E = sizeof(T);
+        // (the resources are uniform over the workgroup: a lane-dependent base
+        // would make the compiler loop over the lanes' descriptors)
+        const auto ra = make_rsrc(reinterpret_cast<const T*>(fe.a) + n * R, (uint32_t)R * E);
+        const auto rb = make_rsrc(reinterpret_cast<const T*>(fe.b) + (int64_t)h * D * R,
+                                  (uint32_t)(D * R) * E);
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < MAXJ; j += 8) {
+            const bool in = j < slice;
+            const uint32_t k = (uint32_t)(part * slice + j);
+            const Frag<T> af = buffer_load_frag<T>(ra, in ? k * E : kFarOffset);
+            const Frag<T> bf = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + k) * E : kFarOffset);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) z += to_f32(af.v[m]) * to_f32(bf.v[m]);
+        }
+#pragma unroll
+        for (int off = 1; off < TPC; off <<= 1) z += xor_shfl(z, off);
+        if (part == 0) {
+            z += fe.bias ? fe.bias[h * D + c] : 0.f;
+            s_a[c] = __expf(-(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)))));
         }
     }
     const float b = to_f32(beta[unit]);
-    float vj[4];
+    float vj[4], vraw[4], vhist[4][3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vj[j] = to_f32(v[unit * D + 4 * cq + j]);
+    for (int j = 0; j < 4; ++j) {
+        vraw[j] = to_f32(v[unit * D + 4 * cq + j]);
+        if constexpr (FE)
+            vj[j] = fe_conv<T, D>(fe, 2, n, h, H, 4 * cq + j, vraw[j], vhist[j]);
+        else
+            vj[j] = vraw[j];
+    }
     __syncthreads();
+    if constexpr (FE) {
+        // every read of this unit's conv state is behind the barrier, so the
+        // state may be advanced in place
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                fe_conv_store<T, D>(fe, 0, n, h, H, lane + kWave * e, qraw[e], qhist[e]);
+                fe_conv_store<T, D>(fe, 1, n, h, H, lane + kWave * e, kraw[e], khist[e]);
+            }
+        }
+        if (rg == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fe_conv_store<T, D>(fe, 2, n, h, H, 4 * cq + j, vraw[j], vhist[j]);
+        }
+    }
 
     // 3. decay the rows and accumulate both read-outs
     f32x4 vh = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -153,10 +265,20 @@ template <typename T, int D>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)a.n_seqs * a.n_heads;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)units), dim3(256), 0, stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                       (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                       a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z);
+    DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
+                a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
+    if (a.fe.active())
+        hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3((unsigned)units), dim3(256), 0,
+                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
+                           fe);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3((unsigned)units), dim3(256), 0,
+                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
+                           fe);
     return hipGetLastError();
 }
 

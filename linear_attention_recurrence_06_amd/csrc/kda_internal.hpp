@@ -10,6 +10,24 @@ namespace kda {
 // epsilon inside the L2-norm square root: x / sqrt(sum x^2 + eps)
 constexpr float kL2Eps = 1e-6f;
 
+// Front end ahead of the recurrence: short causal convolution of the raw q,
+// k, v (width conv_w, 0 = none; tap conv_w-1 is the current token; optional
+// SiLU) and the low-rank decay gate g = -softplus(a b^T + bias) (rank 0 = g
+// given).  Layouts: weight [3, H, W, d], states [N, 3, W-1, H, d], a [T, r],
+// b [H, d, r], bias [H, d] fp32.
+struct FrontEnd {
+    int conv_w = 0;
+    int silu = 0;
+    const void* conv_weight = nullptr;
+    const void* state_in = nullptr;
+    void* state_out = nullptr;
+    int rank = 0;
+    const void* gate_a = nullptr;
+    const void* gate_b = nullptr;
+    const float* gate_bias = nullptr;
+    bool active() const { return conv_w > 0 || rank > 0; }
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
     float* state;
@@ -21,6 +39,7 @@ struct DecodeArgs {
     int l2norm;
     int out_gate;                // 0 none, 1 z [N, H, d], 2 z [N, H]: out = o * sigmoid(z)
     const void* out_gate_z;
+    FrontEnd fe;
 };
 
 // Workspace for one prefill call: a chunk index (first chunk slot of each
@@ -95,6 +114,7 @@ struct PrefillArgs {
     float* checkpoints;          // [C, H, d, d] when ckpt_interval > 0
     int out_gate;                // 0 none, 1 z [T, H, d], 2 z [T, H]: out = o * sigmoid(z)
     const void* out_gate_z;
+    FrontEnd fe;
     PrefillLayout layout;
 };
 

@@ -104,6 +104,10 @@ struct PrepSmem {
             T Tb[64][64 + P];  // T Diag(beta)
             float X[4][16][17];
         } b;
+        struct {
+            float wsum[8][D];     // the same words as wsum above
+            float G[64][D + 4];   // front end: the low-rank gate's pre-activations
+        } fe;
     } u;
 };
 
@@ -150,6 +154,17 @@ __device__ __forceinline__ void decay_block(PrepSmem<T, D>& sm, T* Mg, int R, in
     store_n<T, 4>(Mg + aorder_index(16 * R + col, 16 * J + 4 * (lane >> 4), 64), m);
 }
 
+// Front end of the preparation (kernel argument): the short convolution of the
+// raw q, k, v and the low-rank decay gate.
+struct PrepFE {
+    int conv_w, silu, rank, scalar_g;
+    const void* weight;    // [3, H, W, D]
+    const void* state_in;  // [N, 3, W-1, H, D] or null (zeros)
+    const void* a;         // [T, r]
+    const void* b;         // [H, D, r]
+    const float* bias;     // [H, D] or null
+};
+
 struct PrepParams {
     const void *q, *k, *v, *g, *beta;
     const int32_t* cu;
@@ -159,6 +174,7 @@ struct PrepParams {
     float scale;
     int l2norm;
     PrefillLayout L;
+    PrepFE fe;
 };
 
 // (first token, length) of a chunk slot; length 0 marks an unused slot.
@@ -233,10 +249,36 @@ struct RawRows {
     }
 };
 
-// Everything for one (chunk slot, head) item whose raw rows are in `raw`.
+// One thread's share of a chunk's rows as the preparation consumes them:
+// tokens 2rg, 2rg+1, channels (d_k/16) cg.. of q, k, g (fp32, g in natural
+// units), v (in the I/O type) and beta.
+template <typename T, int D>
+struct ItemRows {
+    static constexpr int CPT = D / 16;
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    float q[2][CPT], k[2][CPT], g[2][CPT], b[2];
+    V v[2];
+};
+
 template <typename T, int D, bool SG>
+__device__ __forceinline__ void rows_from_raw(const RawRows<T, D, SG>& raw, ItemRows<T, D>& r) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            r.q[i][c] = to_f32(raw.q[i][c]);
+            r.k[i][c] = to_f32(raw.k[i][c]);
+            r.g[i][c] = to_f32(SG ? raw.gs[i] : raw.g[i][c]);
+        }
+        r.b[i] = to_f32(raw.b[i]);
+        r.v[i] = raw.v[i];
+    }
+}
+
+// Everything for one (chunk slot, head) item whose rows are in `rows`.
+template <typename T, int D>
 __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
-                                          int h, const RawRows<T, D, SG>& raw) {
+                                          int h, const ItemRows<T, D>& rows) {
     constexpr int CPT = D / 16;  // channels per thread in the row layout
     typedef T V2 __attribute__((ext_vector_type(2)));
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
@@ -250,11 +292,11 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            qf[i][c] = to_f32(raw.q[i][c]);
-            kf[i][c] = to_f32(raw.k[i][c]);
-            gf[i][c] = to_f32(SG ? raw.gs[i] : raw.g[i][c]) * 1.4426950408889634f;
+            qf[i][c] = rows.q[i][c];
+            kf[i][c] = rows.k[i][c];
+            gf[i][c] = rows.g[i][c] * 1.4426950408889634f;
         }
-        bt[i] = to_f32(raw.b[i]);
+        bt[i] = rows.b[i];
     }
 
     // ---------------------------------------------------------------- P0
@@ -408,7 +450,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     // here, so its loads have had P0-P2 to arrive.
     {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) rv[c] = __builtin_bit_cast(W2, V2{raw.v[0][c], raw.v[1][c]});
+        for (int c = 0; c < CPT; ++c) rv[c] = __builtin_bit_cast(W2, V2{rows.v[0][c], rows.v[1][c]});
 #pragma unroll
         for (int sh = 1; sh < CPT; sh <<= 1) {
             const bool on = (cg & sh) != 0;
@@ -522,6 +564,277 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     }
 }
 
+// ------------------------------------------------------------------ front end
+// One thread's raw rows for the front end: tokens 2rg-3 .. 2rg+1 of the chunk
+// (the three before its own two feed the convolution) of q, k, v, and its two
+// rows of g (when given) and beta.  Rows outside [sequence start, chunk end)
+// read as zeros; for a sequence's first chunk the rows before it come from the
+// conv state.
+template <typename T, int D>
+struct FeRaw {
+    static constexpr int CPT = D / 16;
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    V x[3][5];
+    V g[2];
+    T gs[2], b[2];
+    __device__ __forceinline__ void load(const PrepParams& p, int2 d, int64_t n, int64_t s_begin,
+                                         int h, int rg, int cg) {
+        const int64_t H = p.n_heads;
+        const uint32_t E = sizeof(T);
+        const uint32_t rstride = (uint32_t)(H * D) * E;
+        const uint32_t col = CPT * cg * E;
+        const int64_t tb = max((int64_t)d.x - 3, s_begin);  // first token in range
+        const uint32_t span = (uint32_t)((d.x + d.y - 1 - tb) * rstride) + D * E;
+        const int64_t first = (tb * H + h) * D;
+        const T* src[3] = {(const T*)p.q, (const T*)p.k, (const T*)p.v};
+#pragma unroll
+        for (int xi = 0; xi < 3; ++xi) {
+            const auto r = make_rsrc(src[xi] + first, span);
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                // rows before tb take an offset far past the range (read as zero)
+                const int64_t rel = (int64_t)d.x + 2 * rg - 3 + m - tb;
+                const uint32_t off = rel < 0 ? kFarOffset : (uint32_t)rel * rstride + col;
+                x[xi][m] = buffer_load<V>(r, off);
+            }
+        }
+        const uint32_t cspan = (uint32_t)(d.y - 1) * rstride + D * E;
+        const int64_t cfirst = ((int64_t)d.x * H + h) * D;
+        const auto rb = make_rsrc((const T*)p.beta + (int64_t)d.x * H + h,
+                                  (uint32_t)((d.y - 1) * H + 1) * E);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) b[i] = buffer_load<T>(rb, (2 * rg + i) * (uint32_t)H * E);
+        if (p.fe.rank == 0) {
+            if (p.fe.scalar_g) {
+                const auto rg1 = make_rsrc((const T*)p.g + (int64_t)d.x * H + h,
+                                           (uint32_t)((d.y - 1) * H + 1) * E);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) gs[i] = buffer_load<T>(rg1, (2 * rg + i) * (uint32_t)H * E);
+            } else {
+                const auto rgc = make_rsrc((const T*)p.g + cfirst, cspan);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) g[i] = buffer_load<V>(rgc, (2 * rg + i) * rstride + col);
+            }
+        }
+        const int W = p.fe.conv_w;
+        if (W > 1 && p.fe.state_in && d.x == s_begin) {
+            // first chunk: token 2rg-3+m < 0 is row (W-1) + (2rg-3+m) of the state
+            const uint32_t sspan = (uint32_t)((W - 2) * H * D + D) * E;
+#pragma unroll
+            for (int xi = 0; xi < 3; ++xi) {
+                const auto r = make_rsrc((const T*)p.fe.state_in +
+                                             ((n * 3 + xi) * (W - 1) * H + h) * D,
+                                         sspan);
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const int o = 2 * rg - 3 + m;
+                    const int j = (W - 1) + o;
+                    const uint32_t off = (o < 0 && j >= 0) ? (uint32_t)j * rstride + col : kFarOffset;
+                    const V sv = buffer_load<V>(r, off);
+                    if (o < 0) x[xi][m] = sv;
+                }
+            }
+        }
+    }
+};
+
+// The front end's rows: the convolution (and SiLU) of q, k, v, and g given or
+// from the low-rank projection.  Rows past the chunk's length are zero, as
+// without a front end.
+template <typename T, int D>
+__device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm, int2 d, int h,
+                                        const FeRaw<T, D>& raw, ItemRows<T, D>& r) {
+    constexpr int CPT = D / 16;
+    typedef T V __attribute__((ext_vector_type(CPT)));
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int rg = t >> 4, cg = t & 15;
+    const int64_t H = p.n_heads;
+    const int W = p.fe.conv_w;
+    const bool live[2] = {2 * rg < d.y, 2 * rg + 1 < d.y};
+
+    // ---- short convolution: tap j' of 4 (tap j' - (4 - W) of the filter)
+    // multiplies row i + j' for output row i
+    float y[3][2][CPT];
+#pragma unroll
+    for (int xi = 0; xi < 3; ++xi) {
+        if (W == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) y[xi][i][c] = to_f32(raw.x[xi][3 + i][c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) y[xi][i][c] = 0.f;
+            // the W taps of this head's filter; taps 0 .. 3-W of the four read zero
+            const auto rw = make_rsrc((const T*)p.fe.weight + ((int64_t)(xi * H + h) * W) * D,
+                                      (uint32_t)(W * D * sizeof(T)));
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const int tap = jp - (4 - W);
+                const uint32_t off =
+                    tap < 0 ? kFarOffset : (uint32_t)((tap * D + CPT * cg) * sizeof(T));
+                const V wv = buffer_load<V>(rw, off);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c)
+                        y[xi][i][c] += to_f32(wv[c]) * to_f32(raw.x[xi][i + jp][c]);
+            }
+            if (p.fe.silu) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c)
+                        y[xi][i][c] *= __builtin_amdgcn_rcpf(1.f + __expf(-y[xi][i][c]));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            r.q[i][c] = live[i] ? y[0][i][c] : 0.f;
+            r.k[i][c] = live[i] ? y[1][i][c] : 0.f;
+            r.v[i][c] = from_f32<T>(live[i] ? y[2][i][c] : 0.f);
+        }
+        r.b[i] = to_f32(raw.b[i]);
+    }
+
+    // ---- decay gate
+    if (p.fe.rank == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c)
+                r.g[i][c] = to_f32(p.fe.scalar_g ? raw.gs[i] : raw.g[i][c]);
+        return;
+    }
+    // G = a b_h^T on MFMA: wave w forms token tile w % 4 against channel tiles
+    // (D/32) (w / 4) .. +D/32-1, into LDS; then each thread takes its rows
+    {
+        constexpr int NTW = D / 32;
+        const int R = p.fe.rank;
+        const int tb = w & 3;
+        const uint32_t E = sizeof(T);
+        const auto ra = make_rsrc((const T*)p.fe.a + (int64_t)d.x * R, (uint32_t)(d.y * R) * E);
+        // every 32-deep step up to rank 128 is issued; steps past the rank read
+        // zeros (their products add nothing), so all loads can be in flight at once
+        const auto rbm = make_rsrc((const T*)p.fe.b + (int64_t)h * D * R, (uint32_t)(D * R) * E);
+        f32x4 acc[NTW];
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bool in = 32 * ks < R;
+            const uint32_t k0 = 32 * ks + 8 * (lane >> 4);
+            const Frag<T> af = buffer_load_frag<T>(
+                ra, in ? ((16 * tb + (lane & 15)) * R + k0) * E : kFarOffset);
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int ct = NTW * (w >> 2) + i;
+                const Frag<T> bf = buffer_load_frag<T>(
+                    rbm, in ? ((16 * ct + (lane & 15)) * R + k0) * E : kFarOffset);
+                mma(acc[i], af, bf);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int ct = NTW * (w >> 2) + i;
+            const int ch = 16 * ct + (lane & 15);
+            const float bias = p.fe.bias ? p.fe.bias[h * D + ch] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.u.fe.G[16 * tb + 4 * (lane >> 4) + e][ch] = acc[i][e] + bias;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const float z = sm.u.fe.G[2 * rg + i][CPT * cg + c];
+            // g = -softplus(z) = -(max(z, 0) + log(1 + e^-|z|))
+            const float gv = -(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))));
+            r.g[i][c] = live[i] ? gv : 0.f;
+        }
+    }
+}
+
+// Sequence index and first token of the sequence that holds token `tok`.
+__device__ __forceinline__ void seq_of_token(const PrepParams& p, int64_t tok, int64_t& n,
+                                             int64_t& s_begin) {
+    if (!p.cu) {
+        const int64_t each = p.total_tokens / p.n_seqs;
+        n = tok / each;
+        s_begin = n * each;
+        return;
+    }
+    int lo = 0, hi = p.n_seqs - 1;  // largest n with cu[n] <= tok
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    s_begin = p.cu[lo];
+}
+
+// The preparation with the front end: raw q, k, v, and g given or low-rank.
+template <typename T, int D>
+__global__ __launch_bounds__(512, 4) void prep_fe_kernel(PrepParams p) {
+    __shared__ PrepSmem<T, D> sm;
+    const int t = threadIdx.x;
+    const uint32_t H = (uint32_t)p.n_heads;
+    const uint32_t item = blockIdx.x;
+    const uint32_t slot = item / H;
+    const int h = (int)(item - slot * H);
+    const int2 d = slot_desc(p, slot);
+    if (d.y <= 0) return;
+    int64_t n, s_begin;
+    seq_of_token(p, d.x, n, s_begin);
+    ItemRows<T, D> rows;
+    {
+        FeRaw<T, D> raw;
+        raw.load(p, d, n, s_begin, h, t >> 4, t & 15);
+        fe_rows<T, D>(p, sm, d, h, raw, rows);
+    }
+    prep_item<T, D>(p, sm, slot, h, rows);
+}
+
+// Each sequence's final conv state: its last W-1 raw rows of q, k, v (rows
+// before the sequence's start continue from the input state, or are zero).
+// One workgroup per (sequence, tensor, state row); threads over H*D elements.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void conv_state_kernel(PrepParams p, void* state_out) {
+    const int W = p.fe.conv_w;
+    const int64_t blk = blockIdx.x;  // ((n * 3 + x) * (W - 1)) + j
+    const int j = (int)(blk % (W - 1));
+    const int64_t nx = blk / (W - 1);
+    const int x = (int)(nx % 3);
+    const int64_t n = nx / 3;
+    const int64_t HD = (int64_t)p.n_heads * D;
+    int64_t s_begin, len;
+    if (p.cu) {
+        s_begin = p.cu[n];
+        len = (int64_t)p.cu[n + 1] - s_begin;
+    } else {
+        len = p.total_tokens / p.n_seqs;
+        s_begin = n * len;
+    }
+    const int64_t rel = len - (W - 1) + j;  // token of state row j, from the sequence start
+    const T* src = x == 0 ? (const T*)p.q : (x == 1 ? (const T*)p.k : (const T*)p.v);
+    const T* st = (const T*)p.fe.state_in;
+    T* dst = (T*)state_out + blk * HD;
+    for (int64_t e = threadIdx.x; e < HD; e += 256) {
+        T val = from_f32<T>(0.f);
+        if (rel >= 0)
+            val = src[(s_begin + rel) * HD + e];
+        else if (st)
+            val = st[(nx * (W - 1) + (j + len)) * HD + e];
+        dst[e] = val;
+    }
+}
+
 // One (chunk slot, head) item per workgroup; two workgroups share a CU (80 KB
 // of LDS and at most 128 VGPRs each).
 template <typename T, int D, bool SG>
@@ -536,7 +849,9 @@ __global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
     if (d.y <= 0) return;
     RawRows<T, D, SG> raw;
     raw.load(p, d, h, t >> 4, t & 15);
-    prep_item<T, D, SG>(p, sm, slot, h, raw);
+    ItemRows<T, D> rows;
+    rows_from_raw<T, D, SG>(raw, rows);
+    prep_item<T, D>(p, sm, slot, h, rows);
 }
 
 // Chunk index: cf[n] = first chunk slot of sequence n, cf[N] = number of chunks;
@@ -624,6 +939,15 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
                        a.n_seqs, a.total_tokens, cf, ck, a.ckpt_interval);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.fe.active() && a.fe.conv_w > 1 && a.fe.state_out) {
+        // final conv states (also for sequences without tokens)
+        p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
+                      a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
+        const int64_t blocks = (int64_t)a.n_seqs * 3 * (a.fe.conv_w - 1);
+        hipLaunchKernelGGL((conv_state_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, p, a.fe.state_out);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.total_tokens == 0) return hipSuccess;
     if (a.cu_seqlens) {
         const unsigned nb = (unsigned)((a.layout.slots + 255) / 256);
@@ -633,6 +957,12 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t items = a.layout.slots * a.n_heads;
+    if (a.fe.active()) {
+        p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
+                      a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
+        hipLaunchKernelGGL((prep_fe_kernel<T, D>), dim3((unsigned)items), dim3(512), 0, stream, p);
+        return hipGetLastError();
+    }
     if (a.scalar_g)
         hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3((unsigned)items), dim3(512), 0, stream, p);
     else

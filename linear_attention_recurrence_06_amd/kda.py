@@ -53,12 +53,37 @@ class kda_dims(ctypes.Structure):
 KDA_OUT_GATE_NONE, KDA_OUT_GATE_CHANNEL, KDA_OUT_GATE_HEAD = 0, 1, 2
 
 
+class kda_front_end(ctypes.Structure):
+    _fields_ = [
+        ("conv_width", ctypes.c_int32),
+        ("conv_silu", ctypes.c_int32),
+        ("conv_weight", ctypes.c_void_p),
+        ("conv_state_in", ctypes.c_void_p),
+        ("conv_state_out", ctypes.c_void_p),
+        ("gate_rank", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("gate_a", ctypes.c_void_p),
+        ("gate_b", ctypes.c_void_p),
+        ("gate_bias", ctypes.c_void_p),
+    ]
+
+
 class kda_prefill_options(ctypes.Structure):
     _fields_ = [
         ("checkpoint_interval", ctypes.c_int32),
         ("out_gate", ctypes.c_int32),
         ("checkpoints", ctypes.c_void_p),
         ("out_gate_z", ctypes.c_void_p),
+        ("front_end", ctypes.POINTER(kda_front_end)),
+    ]
+
+
+class kda_decode_options(ctypes.Structure):
+    _fields_ = [
+        ("out_gate", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("out_gate_z", ctypes.c_void_p),
+        ("front_end", ctypes.POINTER(kda_front_end)),
     ]
 
 
@@ -96,7 +121,8 @@ def load_library(path: str = LIB_PATH):
                                          ctypes.POINTER(kda_prefill_options), P,
                                          ctypes.c_size_t, P]
     lib.kda_chunk_prefill_ex.restype = ctypes.c_int
-    lib.kda_decode_step_ex.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.kda_decode_step_ex.argtypes = [D, P, P, P, P, P, P, P,
+                                       ctypes.POINTER(kda_decode_options), P]
     lib.kda_decode_step_ex.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [D, P, P, P, P, P, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -326,22 +352,65 @@ def _out_gate(z: Optional[torch.Tensor], lead, dv: int, dt, dev) -> int:
     return KDA_OUT_GATE_CHANNEL
 
 
-def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                         beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+def _front_end(lead, N: int, H: int, d: int, dt, dev, conv_weight, conv_silu, conv_state_in,
+               conv_state_out, gate_a, gate_b, gate_bias):
+    """Checks the front-end tensors and builds the kda_front_end descriptor
+    (None without a front end)."""
+    if conv_weight is None and gate_a is None:
+        return None
+    fe = kda_front_end()
+    if conv_weight is not None:
+        W = conv_weight.shape[2]
+        _check_tensor("conv_weight", conv_weight, (3, H, W, d), dt, dev)
+        fe.conv_width = W
+        fe.conv_silu = 1 if conv_silu else 0
+        fe.conv_weight = _ptr(conv_weight)
+        for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+            if t is not None:
+                _check_tensor(name, t, (N, 3, W - 1, H, d), dt, dev)
+        fe.conv_state_in = _ptr(conv_state_in)
+        fe.conv_state_out = _ptr(conv_state_out)
+    if gate_a is not None:
+        r = gate_a.shape[-1]
+        _check_tensor("gate_a", gate_a, tuple(lead) + (r,), dt, dev)
+        _check_tensor("gate_b", gate_b, (H, d, r), dt, dev)
+        if gate_bias is not None:
+            _check_tensor("gate_bias", gate_bias, (H, d), torch.float32, dev)
+        fe.gate_rank = r
+        fe.gate_a = _ptr(gate_a)
+        fe.gate_b = _ptr(gate_b)
+        fe.gate_bias = _ptr(gate_bias)
+    return fe
+
+
+def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         g: Optional[torch.Tensor], beta: torch.Tensor,
+                         initial_state: Optional[torch.Tensor] = None,
                          cu_seqlens: Optional[torch.Tensor] = None,
                          out: Optional[torch.Tensor] = None,
                          final_state: Optional[torch.Tensor] = None, *,
                          out_gate_z: Optional[torch.Tensor] = None,
                          checkpoint_interval: int = 0,
                          checkpoints: Optional[torch.Tensor] = None,
+                         conv_weight: Optional[torch.Tensor] = None, conv_silu: bool = False,
+                         conv_state_in: Optional[torch.Tensor] = None,
+                         conv_state_out: Optional[torch.Tensor] = None,
+                         output_conv_state: bool = False,
+                         gate_a: Optional[torch.Tensor] = None,
+                         gate_b: Optional[torch.Tensor] = None,
+                         gate_bias: Optional[torch.Tensor] = None,
                          host_cu_seqlens=None, num_seqs: Optional[int] = None,
                          scale: float = 1.0, qk_l2norm: bool = True,
                          workspace: Optional[torch.Tensor] = None,
                          output_final_state: bool = True, stream=None):
-    """Chunked prefill with options (include/kda.h, kda_chunk_prefill_ex): the
-    output gate out = o * sigmoid(z) (z ``[T,H,d_v]`` per channel or ``[T,H]``
-    per head) and/or checkpoints.  Returns ``(out, final_state, checkpoints)``
-    (checkpoints None without an interval)."""
+    """Chunked prefill with options (include/kda.h, kda_chunk_prefill_ex):
+    checkpoints; the output gate out = o * sigmoid(z) (z ``[T,H,d_v]`` per
+    channel or ``[T,H]`` per head); the front end (q, k, v raw projections
+    convolved with ``conv_weight [3,H,W,d]``, optional SiLU, conv states
+    ``[N,3,W-1,H,d]``; g = -softplus(gate_a gate_b^T + gate_bias) with
+    ``gate_a [T,r]``, ``gate_b [H,d,r]``, ``gate_bias [H,d]`` fp32, g None).
+    Returns ``(out, final_state, checkpoints, conv_state_out)`` (None where not
+    asked for)."""
     lib = load_library()
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -352,12 +421,18 @@ def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
         _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
     else:
         N = 1 if num_seqs is None else int(num_seqs)
-    gate = _gate(g, (T, H))
+    gate = _gate(g, (T, H)) if g is not None else KDA_GATE_CHANNEL
     for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)),
-                         ("g", g, (T, H) if gate else (T, H, dk)),
                          ("v", v, (T, H, dv)), ("beta", beta, (T, H))):
         _check_tensor(name, t, shp, dt, dev)
+    if g is not None:
+        _check_tensor("g", g, (T, H) if gate else (T, H, dk), dt, dev)
     og = _out_gate(out_gate_z, (T, H), dv, dt, dev)
+    if conv_weight is not None and conv_state_out is None and output_conv_state:
+        W = conv_weight.shape[2]
+        conv_state_out = torch.empty((N, 3, W - 1, H, dk), dtype=dt, device=dev)
+    fe = _front_end((T,), N, H, dk, dt, dev, conv_weight, conv_silu, conv_state_in,
+                    conv_state_out, gate_a, gate_b, gate_bias)
     if initial_state is not None:
         _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
     if out is None:
@@ -379,7 +454,8 @@ def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
             raise KDAError(KDA_ERR_INVALID_ARG, "kda_checkpoint_count")
         if checkpoints is None:
             checkpoints = torch.empty((max(C, 1), H, dk, dv), dtype=torch.float32, device=dev)
-    opts = kda_prefill_options(int(checkpoint_interval), og, _ptr(checkpoints), _ptr(out_gate_z))
+    opts = kda_prefill_options(int(checkpoint_interval), og, _ptr(checkpoints), _ptr(out_gate_z),
+                               ctypes.pointer(fe) if fe is not None else None)
     need = kda_prefill_workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -389,36 +465,47 @@ def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
                                   workspace.numel(), _stream_handle(stream, dev))
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_prefill_ex")
-    return out, final_state, (checkpoints[:C] if checkpoint_interval else None)
+    return out, final_state, (checkpoints[:C] if checkpoint_interval else None), conv_state_out
 
 
-def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                       beta: torch.Tensor, state: torch.Tensor,
+def kda_decode_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       g: Optional[torch.Tensor], beta: torch.Tensor, state: torch.Tensor,
                        out: Optional[torch.Tensor] = None, *,
-                       out_gate_z: Optional[torch.Tensor] = None, scale: float = 1.0,
-                       qk_l2norm: bool = True, stream=None) -> torch.Tensor:
-    """One decode step with the output gate (z ``[N,H,d_v]`` or ``[N,H]``)."""
+                       out_gate_z: Optional[torch.Tensor] = None,
+                       conv_weight: Optional[torch.Tensor] = None, conv_silu: bool = False,
+                       conv_state: Optional[torch.Tensor] = None,
+                       gate_a: Optional[torch.Tensor] = None,
+                       gate_b: Optional[torch.Tensor] = None,
+                       gate_bias: Optional[torch.Tensor] = None,
+                       scale: float = 1.0, qk_l2norm: bool = True, stream=None) -> torch.Tensor:
+    """One decode step with options: the output gate (z ``[N,H,d_v]`` or
+    ``[N,H]``) and/or the front end (``conv_state [N,3,W-1,H,d]`` advanced in
+    place; ``gate_a [N,r]``)."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
     dt = q.dtype
-    gate = _gate(g, (N, H))
+    gate = _gate(g, (N, H)) if g is not None else KDA_GATE_CHANNEL
     for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)),
-                         ("g", g, (N, H) if gate else (N, H, dk)),
                          ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
         _check_tensor(name, t, shp, dt, dev)
+    if g is not None:
+        _check_tensor("g", g, (N, H) if gate else (N, H, dk), dt, dev)
     _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
     og = _out_gate(out_gate_z, (N, H), dv, dt, dev)
+    fe = _front_end((N,), N, H, dk, dt, dev, conv_weight, conv_silu, conv_state, conv_state,
+                    gate_a, gate_b, gate_bias)
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check_tensor("out", out, (N, H, dv), dt, dev)
     dims = make_dims(N, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
+    opts = kda_decode_options(og, 0, _ptr(out_gate_z),
+                              ctypes.pointer(fe) if fe is not None else None)
     rc = lib.kda_decode_step_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                _ptr(beta), _ptr(state), _ptr(out), og, _ptr(out_gate_z),
+                                _ptr(beta), _ptr(state), _ptr(out), ctypes.byref(opts),
                                 _stream_handle(stream, dev))
     if rc != KDA_OK:
         raise KDAError(rc, "kda_decode_step_ex")
     return out
-

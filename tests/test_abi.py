@@ -184,11 +184,20 @@ def test_gate_field_and_validation(kda):
         kda.KDA_ERR_MISALIGNED
 
 
-def test_prefill_options_layout(kda):
-    # struct kda_prefill_options in include/kda.h: two int32, then two pointers
-    assert ctypes.sizeof(kda.kda_prefill_options) == 24
+def test_options_layout(kda):
+    # the option structs as laid out in include/kda.h
+    assert ctypes.sizeof(kda.kda_prefill_options) == 32
     assert kda.kda_prefill_options.checkpoints.offset == 8
     assert kda.kda_prefill_options.out_gate_z.offset == 16
+    assert kda.kda_prefill_options.front_end.offset == 24
+    assert ctypes.sizeof(kda.kda_decode_options) == 24
+    assert kda.kda_decode_options.out_gate_z.offset == 8
+    assert kda.kda_decode_options.front_end.offset == 16
+    assert ctypes.sizeof(kda.kda_front_end) == 64
+    assert kda.kda_front_end.conv_weight.offset == 8
+    assert kda.kda_front_end.gate_rank.offset == 32
+    assert kda.kda_front_end.gate_a.offset == 40
+    assert kda.kda_front_end.gate_bias.offset == 56
 
 
 def test_output_gate_validation(kda):
@@ -240,7 +249,8 @@ def test_decode_output_gate_validation(kda):
     z = FAKE + 12 * n
 
     def call(og, zz=z, a=args):
-        return lib.kda_decode_step_ex(ctypes.byref(d), *a, og, zz, None)
+        o = kda.kda_decode_options(og, 0, zz, None)
+        return lib.kda_decode_step_ex(ctypes.byref(d), *a, ctypes.byref(o), None)
 
     assert call(5) == kda.KDA_ERR_INVALID_ARG
     assert call(kda.KDA_OUT_GATE_HEAD, None) == kda.KDA_ERR_INVALID_ARG
@@ -249,3 +259,86 @@ def test_decode_output_gate_validation(kda):
     a = list(args); a[5] = FAKE + 8 * n + 4
     assert call(kda.KDA_OUT_GATE_CHANNEL, z, a) == kda.KDA_ERR_MISALIGNED
     assert call(kda.KDA_OUT_GATE_HEAD, args[5] + 4096) == kda.KDA_ERR_INVALID_ARG  # in the state
+
+
+def test_front_end_validation(kda):
+    lib = kda.load_library()
+    d = kda.make_dims(1024, 2, 4, 128, 128, kda.KDA_BF16)
+    T, H, D = 1024, 4, 128
+    big = T * H * D * 2 + 4096
+    base = dict(q=FAKE, k=FAKE + big, v=FAKE + 2 * big, g=FAKE + 3 * big, beta=FAKE + 4 * big,
+                out=FAKE + 5 * big, ws=FAKE + 6 * big)
+    wsb = kda.kda_prefill_workspace_bytes(d)
+    W0, A0, B0, S0, S1 = (FAKE + 40 * big, FAKE + 41 * big, FAKE + 42 * big, FAKE + 43 * big,
+                          FAKE + 44 * big)
+
+    def fe(**over):
+        f = dict(conv_width=4, conv_silu=1, conv_weight=W0, conv_state_in=S0, conv_state_out=S1,
+                 gate_rank=64, reserved=0, gate_a=A0, gate_b=B0, gate_bias=None)
+        f.update(over)
+        return kda.kda_front_end(**f)
+
+    def call(f, **over):
+        p = dict(base)
+        p.update(over)
+        o = kda.kda_prefill_options(0, 0, None, None, ctypes.pointer(f) if f else None)
+        return lib.kda_chunk_prefill_ex(ctypes.byref(over.get("dims", d)), p["q"], p["k"], p["v"],
+                                        p["g"], p["beta"], None, None, p["out"], None,
+                                        ctypes.byref(o), p["ws"], wsb, None)
+
+    INV, MIS, WS = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_MISALIGNED, kda.KDA_ERR_WORKSPACE
+    # a valid front end (low-rank gate, so g NULL) reaches the workspace check
+    assert call(fe(), g=None, ws=None) == WS
+    # with a low-rank gate g must be NULL; without one it is required
+    assert call(fe()) == INV
+    assert call(fe(gate_rank=0, gate_a=None, gate_b=None), g=None) == INV
+    assert call(fe(gate_rank=0, gate_a=None, gate_b=None), ws=None) == WS
+    assert call(None, g=None) == INV
+    for bad in (dict(conv_width=5), dict(conv_width=-1), dict(conv_silu=2), dict(reserved=1),
+                dict(gate_rank=48), dict(gate_rank=256), dict(conv_weight=None),
+                dict(gate_a=None), dict(gate_b=None)):
+        assert call(fe(**bad), g=None) == INV, bad
+    # the low-rank gate is per channel: not with the per-head gate descriptor
+    dh = kda.make_dims(1024, 2, 4, 128, 128, kda.KDA_BF16, gate=kda.KDA_GATE_HEAD)
+    assert call(fe(), g=None, dims=dh) == INV
+    # alignment: 16 bytes for the tensors, 4 for the bias
+    for name, val in (("conv_weight", W0 + 8), ("conv_state_in", S0 + 8),
+                      ("conv_state_out", S1 + 8), ("gate_a", A0 + 8), ("gate_b", B0 + 8),
+                      ("gate_bias", FAKE + 45 * big + 2)):
+        assert call(fe(**{name: val}), g=None) == MIS, name
+    # conv states are not read or written at width 1, so they are not checked
+    assert call(fe(conv_width=1, conv_state_in=S0 + 8, conv_state_out=S1 + 8), g=None,
+                ws=None) == WS
+    # the conv state output must not overlap an input or another output
+    assert call(fe(conv_state_out=base["q"] + 64), g=None) == INV
+    assert call(fe(conv_state_out=base["out"] + 64), g=None) == INV
+    assert call(fe(conv_state_out=S0 + 64), g=None) == INV
+    assert call(fe(conv_state_out=A0), g=None) == INV
+    # out must not overlap the front end's inputs
+    assert call(fe(), g=None, out=W0) == INV
+    assert call(fe(), g=None, out=B0 - 64) == INV
+
+
+def test_decode_front_end_validation(kda):
+    lib = kda.load_library()
+    d = kda.make_dims(8, 8, 2, 128, 128, kda.KDA_BF16)
+    n = 8 * 2 * 128 * 2 + 4096
+    args = [FAKE, FAKE + n, FAKE + 2 * n, None, FAKE + 4 * n, FAKE + 8 * n, FAKE + 5 * n]
+    W0, A0, B0, S0 = FAKE + 20 * n, FAKE + 21 * n, FAKE + 22 * n, FAKE + 23 * n
+
+    def call(a=args, **over):
+        f = dict(conv_width=3, conv_silu=0, conv_weight=W0, conv_state_in=S0, conv_state_out=S0,
+                 gate_rank=32, reserved=0, gate_a=A0, gate_b=B0, gate_bias=None)
+        f.update(over)
+        fe = kda.kda_front_end(**f)
+        o = kda.kda_decode_options(0, 0, None, ctypes.pointer(fe))
+        return lib.kda_decode_step_ex(ctypes.byref(d), *a, ctypes.byref(o), None)
+
+    INV, MIS = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_MISALIGNED
+    # (the in-place conv state is allowed; a misaligned recurrent state stops the call)
+    a = list(args); a[5] = FAKE + 8 * n + 4
+    assert call(a) == MIS
+    assert call(conv_state_out=S0 + 64) == INV      # partial overlap with the input state
+    assert call(conv_state_out=args[6]) == INV      # the conv state over out
+    assert call(gate_rank=0, gate_a=None, gate_b=None) == INV  # no gate at all
+    assert call(gate_a=A0 + 4) == MIS

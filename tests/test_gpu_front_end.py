@@ -1,0 +1,252 @@
+"""The front end fused ahead of the recurrence: the short causal convolution of
+the raw q, k, v (optionally with SiLU) and the low-rank decay gate ("Kimi K3:
+The Manos, The Mythos, The Legendos", stability-details bullet).  The reference
+is the oracle's front end (``short_conv``, ``low_rank_gate``; pinned in
+test_oracle_front_end.py) feeding the fp64 recurrence.  The convolved rows and
+the gate reach the oracle as float32 (a relative change of at most 6e-8,
+far inside both tolerances)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+LENS = [1, 63, 64, 65, 0, 127, 129, 300, 2]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+def maxerr(a, b):
+    a = np.asarray(a, np.float64)
+    return float(np.max(np.abs(a - np.asarray(b, np.float64)))) if a.size else 0.0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_recurrence_06_amd as kda
+    kda.load_library()
+    return kda
+
+
+def oracle_front(oracle, inp, fe, cu, n_seqs, silu, state_in=True):
+    """q', k', v', g and the final conv states from the oracle's front end."""
+    st = host(fe["conv_state"]) if ("conv_weight" in fe and state_in) else None
+    xs, fins = [], []
+    for xi, name in enumerate(("q", "k", "v")):
+        if "conv_weight" in fe:
+            w = np.transpose(host(fe["conv_weight"])[xi], (0, 2, 1))  # [H, d, W]
+            y, f = oracle.short_conv(host(inp[name]), w, cu_seqlens=cu, n_seqs=n_seqs,
+                                     state=None if st is None else st[:, xi], silu=silu)
+        else:
+            y, f = host(inp[name]).astype(np.float64), None
+        xs.append(y)
+        fins.append(f)
+    if "gate_a" in fe:
+        g = oracle.low_rank_gate(host(fe["gate_a"]), host(fe["gate_b"]), host(fe["gate_bias"]))
+    else:
+        g = host(inp["g"])
+    conv_fin = np.stack(fins, axis=1) if fins[0] is not None else None
+    return xs[0], xs[1], xs[2], g, conv_fin
+
+
+def run_case(lib, oracle, io, d, width, silu, rank, bias_std, H=3, lens=LENS, seed=71,
+             state_in=True):
+    from kda_inputs import make_front_end, make_prefill
+    inp = make_prefill(lens, H, d, io, g_scale=0.5, s0_std=0.02, seed=seed, device="cuda")
+    T, N = sum(lens), len(lens)
+    fe = make_front_end(T, N, H, d, io, width=width, rank=rank, bias_std=bias_std,
+                        seed=seed + 1, device="cuda")
+    out, fin, _, cst = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], None if rank else inp["g"], inp["beta"],
+        inp["initial_state"], inp["cu_seqlens"], conv_weight=fe.get("conv_weight"),
+        conv_silu=silu, conv_state_in=fe.get("conv_state") if state_in else None,
+        output_conv_state=width > 1, gate_a=fe.get("gate_a"), gate_b=fe.get("gate_b"),
+        gate_bias=fe.get("gate_bias"))
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].cpu().numpy()
+    q2, k2, v2, g2, cfin = oracle_front(oracle, inp, fe, cu, N, silu, state_in)
+    o_ref, f_ref = oracle.prefill(q2, k2, v2, g2, host(inp["beta"]), cu_seqlens=cu,
+                                  initial_state=host(inp["initial_state"]), n_seqs=N)
+    eo, ef = maxerr(host(out), o_ref), maxerr(host(fin), f_ref)
+    say(f"front end {io} d={d} W={width} silu={silu} r={rank}: err_out={eo:.3e} "
+        f"err_state={ef:.3e} max|o|={np.abs(o_ref).max():.2f}")
+    assert eo <= TOL[io] and ef <= TOL[io]
+    if width > 1:
+        # the final conv states are raw rows: exact
+        assert np.array_equal(host(cst), cfin)
+    return inp, fe
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_conv_silu_and_low_rank_gate(lib, oracle, io, d):
+    run_case(lib, oracle, io, d, width=4, silu=True, rank=64, bias_std=0.3)
+
+
+@pytest.mark.parametrize("width", [1, 2, 3])
+def test_conv_widths_with_given_gate(lib, oracle, width):
+    run_case(lib, oracle, "bf16", 128, width=width, silu=False, rank=0, bias_std=0.0,
+             seed=80 + width)
+
+
+@pytest.mark.parametrize("rank", [32, 96, 128])
+def test_low_rank_gate_only(lib, oracle, rank):
+    run_case(lib, oracle, "bf16", 128, width=0, silu=False, rank=rank, bias_std=0.5,
+             seed=90 + rank)
+
+
+def test_conv_without_input_state(lib, oracle):
+    run_case(lib, oracle, "bf16", 128, width=4, silu=True, rank=0, bias_std=0.0, seed=77,
+             state_in=False)
+
+
+def test_conv_with_per_head_gate(lib, oracle):
+    """The front end's convolution with a given per-head g [T, H]."""
+    from kda_inputs import make_front_end, make_prefill
+    H, d = 3, 128
+    inp = make_prefill(LENS, H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=78, device="cuda",
+                       scalar_gate=True)
+    T, N = sum(LENS), len(LENS)
+    fe = make_front_end(T, N, H, d, "bf16", width=4, rank=0, seed=79, device="cuda")
+    out, fin, _, _ = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], conv_weight=fe["conv_weight"], conv_silu=True,
+        conv_state_in=fe["conv_state"])
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].cpu().numpy()
+    gb = inp["g"].unsqueeze(-1).expand(T, H, d).contiguous()
+    q2, k2, v2, _, _ = oracle_front(oracle, dict(inp, g=gb), fe, cu, N, True)
+    o_ref, f_ref = oracle.prefill(q2, k2, v2, host(gb), host(inp["beta"]), cu_seqlens=cu,
+                                  initial_state=host(inp["initial_state"]), n_seqs=N)
+    eo, ef = maxerr(host(out), o_ref), maxerr(host(fin), f_ref)
+    say(f"front end with per-head gate: err_out={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_empty_batch_passes_conv_state_through(lib):
+    from kda_inputs import make_front_end, make_prefill
+    H, d = 2, 128
+    inp = make_prefill([0, 0, 0], H, d, "bf16", s0_std=0.02, seed=5, device="cuda")
+    fe = make_front_end(0, 3, H, d, "bf16", width=4, rank=0, seed=6, device="cuda")
+    _, fin, _, cst = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], conv_weight=fe["conv_weight"], conv_state_in=fe["conv_state"],
+        output_conv_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(cst, fe["conv_state"])
+    assert torch.equal(fin, inp["initial_state"])
+
+
+def test_front_end_full_size(lib, oracle):
+    """T=8192, H=32, d=128 bf16 with W=4 + SiLU and a rank-64 gate: every head
+    against the oracle."""
+    from kda_inputs import make_front_end, make_prefill
+    say("front end T=8192 H=32 d=128")
+    H, d, T = 32, 128, 8192
+    inp = make_prefill([T], H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=101, device="cuda")
+    fe = make_front_end(T, 1, H, d, "bf16", width=4, rank=64, bias_std=0.3, seed=102,
+                        device="cuda")
+    out, fin, _, cst = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], None, inp["beta"], inp["initial_state"], None,
+        conv_weight=fe["conv_weight"], conv_silu=True, conv_state_in=fe["conv_state"],
+        output_conv_state=True, gate_a=fe["gate_a"], gate_b=fe["gate_b"],
+        gate_bias=fe["gate_bias"])
+    torch.cuda.synchronize()
+    q2, k2, v2, g2, cfin = oracle_front(oracle, inp, fe, None, 1, True)
+    o_ref, f_ref = oracle.prefill(q2, k2, v2, g2, host(inp["beta"]),
+                                  initial_state=host(inp["initial_state"]))
+    eo, ef = maxerr(host(out), o_ref), maxerr(host(fin), f_ref)
+    say(f"  err_out={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    assert np.array_equal(host(cst), cfin)
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_prefill_then_decode_continues(lib, oracle, io, d):
+    """Prefill with the front end, then decode steps that carry the conv state
+    and recurrent state forward, against the oracle over the whole sequences."""
+    from kda_inputs import make_front_end, make_prefill
+    H, lens, steps, W, r = 2, [70, 1, 130], 3, 4, 32
+    N = len(lens)
+    total = [L + steps for L in lens]
+    inp = make_prefill(total, H, d, io, g_scale=0.5, s0_std=0.02, seed=111, device="cuda")
+    T = sum(total)
+    fe = make_front_end(T, N, H, d, io, width=W, rank=r, bias_std=0.2, seed=112, device="cuda")
+    cu_all = np.concatenate([[0], np.cumsum(total)])
+    # prefill the first lens[n] tokens of each sequence, decode the rest
+    pre_idx = np.concatenate([np.arange(cu_all[n], cu_all[n] + lens[n]) for n in range(N)])
+    pre = {x: inp[x][torch.as_tensor(pre_idx, device="cuda")].contiguous()
+           for x in ("q", "k", "v", "beta")}
+    a_pre = fe["gate_a"][torch.as_tensor(pre_idx, device="cuda")].contiguous()
+    cu_pre = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32,
+                          device="cuda")
+    _, state, _, cst = lib.kda_chunk_prefill_ex(
+        pre["q"], pre["k"], pre["v"], None, pre["beta"], inp["initial_state"], cu_pre,
+        conv_weight=fe["conv_weight"], conv_silu=True, conv_state_in=fe["conv_state"],
+        output_conv_state=True, gate_a=a_pre, gate_b=fe["gate_b"], gate_bias=fe["gate_bias"])
+    outs = []
+    for s in range(steps):
+        idx = torch.as_tensor([cu_all[n] + lens[n] + s for n in range(N)], device="cuda")
+        outs.append(lib.kda_decode_step_ex(
+            inp["q"][idx].contiguous(), inp["k"][idx].contiguous(), inp["v"][idx].contiguous(),
+            None, inp["beta"][idx].contiguous(), state, conv_weight=fe["conv_weight"],
+            conv_silu=True, conv_state=cst, gate_a=fe["gate_a"][idx].contiguous(),
+            gate_b=fe["gate_b"], gate_bias=fe["gate_bias"]))
+    torch.cuda.synchronize()
+    q2, k2, v2, g2, cfin = oracle_front(oracle, inp, fe, cu_all, N, True)
+    o_ref, f_ref = oracle.prefill(q2, k2, v2, g2, host(inp["beta"]), cu_seqlens=cu_all,
+                                  initial_state=host(inp["initial_state"]), n_seqs=N)
+    for s in range(steps):
+        idx = [cu_all[n] + lens[n] + s for n in range(N)]
+        e = maxerr(host(outs[s]), o_ref[idx])
+        say(f"prefill+decode {io} d={d} step {s}: err={e:.3e}")
+        assert e <= TOL[io]
+    assert maxerr(host(state), f_ref) <= TOL[io]
+    assert np.array_equal(host(cst), cfin)
+
+
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
+def test_decode_front_end_matches_oracle(lib, oracle, io, d):
+    from kda_inputs import make_decode, make_front_end
+    N, H, steps, W, r = 5, 3, 3, 3, 64
+    w = make_decode(N, H, d, io, steps=steps, seed=121, device="cuda")
+    fe = make_front_end(N * steps, N, H, d, io, width=W, rank=r, bias_std=0.3, seed=122,
+                        device="cuda")
+    st = w["state"].clone()
+    cst = fe["conv_state"].clone()
+    st_ref = host(w["state"]).astype(np.float64)
+    cst_ref = host(fe["conv_state"]).astype(np.float64)
+    wq = host(fe["conv_weight"])
+    for s in range(steps):
+        a_s = fe["gate_a"][s * N:(s + 1) * N].contiguous()
+        o = lib.kda_decode_step_ex(w["q"][s], w["k"][s], w["v"][s], None, w["beta"][s], st,
+                                   conv_weight=fe["conv_weight"], conv_state=cst,
+                                   gate_a=a_s, gate_b=fe["gate_b"], gate_bias=fe["gate_bias"])
+        torch.cuda.synchronize()
+        xs = []
+        for xi, name in enumerate(("q", "k", "v")):
+            # one token per sequence: cu = 0, 1, ..., N
+            y, f = oracle.short_conv(host(w[name][s]), np.transpose(wq[xi], (0, 2, 1)),
+                                     cu_seqlens=np.arange(N + 1), state=cst_ref[:, xi])
+            cst_ref[:, xi] = f
+            xs.append(y)
+        g = oracle.low_rank_gate(host(a_s), host(fe["gate_b"]), host(fe["gate_bias"]))
+        o_ref = oracle.decode_step(xs[0], xs[1], xs[2], g, host(w["beta"][s]), st_ref)
+        e = maxerr(host(o), o_ref)
+        say(f"front-end decode {io} d={d} step {s}: err={e:.3e}")
+        assert e <= TOL[io]
+        assert np.array_equal(host(cst), cst_ref)
+    assert maxerr(host(st), st_ref) <= TOL[io]

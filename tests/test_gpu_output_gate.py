@@ -52,7 +52,7 @@ def test_gated_prefill_matches_oracle(lib, oracle, io, d, per_head):
     inp = make_prefill(LENS, H, d, io, g_scale=0.5, s0_std=0.02, seed=61, device="cuda")
     T = sum(LENS)
     z = make_out_gate((T, H) if per_head else (T, H, d), io, seed=62, device="cuda")
-    out, fin, ck = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+    out, fin, ck, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                             inp["initial_state"], inp["cu_seqlens"],
                                             out_gate_z=z)
     torch.cuda.synchronize()
@@ -78,7 +78,7 @@ def test_gate_at_zero_halves_the_output(lib):
     inp = make_prefill(LENS, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=63, device="cuda")
     T = sum(LENS)
     z = torch.zeros((T, 2, 128), dtype=torch.bfloat16, device="cuda")
-    out, _, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+    out, _, _, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                          inp["initial_state"], inp["cu_seqlens"], out_gate_z=z)
     o0, _ = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                   inp["initial_state"], inp["cu_seqlens"])
@@ -94,7 +94,7 @@ def test_gate_with_checkpoints(lib, oracle):
     inp = make_prefill(LENS, H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=64, device="cuda")
     T = sum(LENS)
     z = make_out_gate((T, H, d), "bf16", seed=65, device="cuda")
-    out, fin, ck = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+    out, fin, ck, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                             inp["initial_state"], inp["cu_seqlens"],
                                             out_gate_z=z, checkpoint_interval=1)
     o0, f0, ck0 = lib.kda_chunk_prefill_checkpoints(inp["q"], inp["k"], inp["v"], inp["g"],
@@ -119,7 +119,7 @@ def test_gated_prefill_full_size(lib, oracle):
     inp = make_prefill([8192], 32, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=66,
                        device="cuda")
     z = make_out_gate((8192, 32, 128), "bf16", seed=67, device="cuda")
-    out, fin, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+    out, fin, _, _ = lib.kda_chunk_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                            inp["initial_state"], None, out_gate_z=z)
     torch.cuda.synchronize()
     o_ref, f_ref = oracle.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]),
