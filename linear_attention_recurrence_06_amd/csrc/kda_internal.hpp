@@ -42,7 +42,7 @@ struct DecodeArgs {
     FrontEnd fe;
 };
 
-// Workspace for one prefill call: a chunk index (first chunk slot of each
+// Workspace for one prefill call: a chunk index (packed sequences only; first chunk slot of each
 // sequence, int32 [N+1]), a checkpoint index (first checkpoint of each
 // sequence, int32 [N+1]), one descriptor per chunk slot (first token and
 // length, int32 x 2; length 0 marks an unused slot), then one record per

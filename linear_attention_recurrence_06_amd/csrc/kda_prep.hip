@@ -442,35 +442,19 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     __syncthreads();
 
     // ---------------------------------------------------------------- P3
-    // transposed Khat and V tiles (the operands of W^T and U).  Lane
-    // (rg, cg) holds 2 tokens x CPT channels; at write step j it stores channel
-    // (j + cg) % CPT, so the 16 lanes of a token group spread over the banks
-    // (a plain channel order puts them on one bank).  The rotation is a barrel
-    // shift of packed token pairs across the channel index.  V is first used
-    // here, so its loads have had P0-P2 to arrive.
+    // transposed Khat and V tiles (the operands of W^T and U).  Lane (rg, cg)
+    // holds 2 tokens x CPT channels and stores each channel's token pair at
+    // token octet (rg / 4) ^ (cg % 8): an XOR swizzle by channel group, undone
+    // by the readers, that spreads the 16 lanes of a token group over the banks
+    // (without it they all land on one bank).  V is first used here, so its
+    // loads have had P0-P2 to arrive.
     {
+        const int col = 8 * ((rg >> 2) ^ (cg & 7)) + 2 * (rg & 3);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) rv[c] = __builtin_bit_cast(W2, V2{rows.v[0][c], rows.v[1][c]});
-#pragma unroll
-        for (int sh = 1; sh < CPT; sh <<= 1) {
-            const bool on = (cg & sh) != 0;
-            W2 tk[CPT], tv[CPT];
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                tk[j] = on ? rk[(j + sh) % CPT] : rk[j];
-                tv[j] = on ? rv[(j + sh) % CPT] : rv[j];
-            }
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                rk[j] = tk[j];
-                rv[j] = tv[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = CPT * cg + ((j + cg) % CPT);
-            *reinterpret_cast<W2*>(&sm.u.b.BK[c][2 * rg]) = rk[j];
-            *reinterpret_cast<W2*>(&sm.u.b.BV[c][2 * rg]) = rv[j];
+        for (int c = 0; c < CPT; ++c) {
+            rv[c] = __builtin_bit_cast(W2, V2{rows.v[0][c], rows.v[1][c]});
+            *reinterpret_cast<W2*>(&sm.u.b.BK[CPT * cg + c][col]) = rk[c];
+            *reinterpret_cast<W2*>(&sm.u.b.BV[CPT * cg + c][col]) = rv[c];
         }
     }
     if (w == 0) {
@@ -549,9 +533,11 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks < nks) {
-                    const int c0 = 32 * ks + 8 * (lane >> 4);
-                    const Frag<T> bk = load_frag<T>(&sm.u.b.BK[16 * nb + (lane & 15)][c0]);
-                    const Frag<T> bv = load_frag<T>(&sm.u.b.BV[16 * nb + (lane & 15)][c0]);
+                    // token octet 4 ks + lane / 16 of channel row n, swizzled as stored
+                    const int n = 16 * nb + (lane & 15);
+                    const int c0 = 8 * ((4 * ks + (lane >> 4)) ^ ((n / CPT) & 7));
+                    const Frag<T> bk = load_frag<T>(&sm.u.b.BK[n][c0]);
+                    const Frag<T> bv = load_frag<T>(&sm.u.b.BV[n][c0]);
                     mma(aw, bk, ta[ks]);  // W^T[n][r]
                     mma(au, ta[ks], bv);  // U[r][n]
                 }
@@ -935,10 +921,13 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     p.L = a.layout;
     int32_t* cf = reinterpret_cast<int32_t*>(a.workspace);
     int32_t* ck = reinterpret_cast<int32_t*>(a.workspace + a.layout.ckidx_offset());
-    hipLaunchKernelGGL((chunk_index_kernel), dim3(1), dim3(256), 0, stream, a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, cf, ck, a.ckpt_interval);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (a.cu_seqlens) {
+        // equal lengths need no index: the recurrence derives it
+        hipLaunchKernelGGL((chunk_index_kernel), dim3(1), dim3(256), 0, stream, a.cu_seqlens,
+                           a.n_seqs, a.total_tokens, cf, ck, a.ckpt_interval);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.fe.active() && a.fe.conv_w > 1 && a.fe.state_out) {
         // final conv states (also for sequences without tokens)
         p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,

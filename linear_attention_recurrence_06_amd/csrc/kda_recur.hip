@@ -297,12 +297,21 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     const int64_t each = p.n_seqs ? p.total_tokens / p.n_seqs : 0;
     c.s_begin = p.cu ? (int64_t)p.cu[n] : (int64_t)n * each;
     c.s_len = p.cu ? (int64_t)p.cu[n + 1] - c.s_begin : each;
-    const int32_t* cf = reinterpret_cast<const int32_t*>(p.ws);
     const int64_t nch = (c.s_len + 63) / 64;
     c.last = nch > 0 ? nch - 1 : 0;
     c.rec_bytes = p.L.rec_bytes;
-    c.rec0 = p.ws + p.L.records_offset() + ((size_t)c.h * p.L.slots + cf[n]) * p.L.rec_bytes;
-    c.ck0 = CK ? reinterpret_cast<const int32_t*>(p.ws + p.L.ckidx_offset())[n] : 0;
+    // first chunk slot and first checkpoint of the sequence: from the chunk
+    // index for packed sequences, by arithmetic for equal lengths
+    int64_t slot0, ck0 = 0;
+    if (p.cu) {
+        slot0 = reinterpret_cast<const int32_t*>(p.ws)[n];
+        if (CK) ck0 = reinterpret_cast<const int32_t*>(p.ws + p.L.ckidx_offset())[n];
+    } else {
+        slot0 = (int64_t)n * nch;
+        if (CK) ck0 = (int64_t)n * (nch > 0 ? (nch - 1) / p.ckpt_interval : 0);
+    }
+    c.rec0 = p.ws + p.L.records_offset() + ((size_t)c.h * p.L.slots + slot0) * p.L.rec_bytes;
+    c.ck0 = ck0;
     const int lane = c.lane;
     {
         // prefetch share: lines [tile * per, (tile + 1) * per) of each record,
