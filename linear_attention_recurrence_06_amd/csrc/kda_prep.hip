@@ -203,6 +203,77 @@ __device__ __forceinline__ void wave_rows_scan(float x, int row, float& excl, fl
     excl = incl - x;
 }
 
+// Exchange of one 32-bit word with the lane 16 (row) or 32 (half) away: the
+// swap instructions hand the even row's (lower half's) value to the odd row
+// (upper half) in the first result and the other way round in the second.
+__device__ __forceinline__ uint32_t xchg_row(uint32_t x, bool odd_row) {
+    const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return odd_row ? s[0] : s[1];
+}
+__device__ __forceinline__ uint32_t xchg_half(uint32_t x, bool upper) {
+    const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return upper ? s[0] : s[1];
+}
+
+// Kprime^T store.  The four lane rows of a wave hold token pairs 0..3 of the
+// wave's token octet for the same CPT channels; a 4 x 4 transpose of
+// (channel-group) units across the rows, in two swap stages, leaves lane row
+// r with all 8 tokens of its channels, so each lane writes whole 16-byte
+// fragment runs (instead of CPT scattered 4-byte pieces).
+template <typename T, int CPT>
+__device__ __forceinline__ void store_kt(T* Ktg, const float (&kp)[CPT][2], int cg, int w,
+                                         int lrow) {
+    constexpr int WPC = sizeof(T) / 2;   // 32-bit words per channel's token pair
+    constexpr int NW = CPT * WPC, US = NW / 4, CHU = US / WPC;
+    typedef T V2 __attribute__((ext_vector_type(2)));
+    uint32_t wd[NW];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        if constexpr (WPC == 1) {
+            wd[c] = __builtin_bit_cast(uint32_t, V2{from_f32<T>(kp[c][0]), from_f32<T>(kp[c][1])});
+        } else {
+            wd[2 * c] = __float_as_uint(kp[c][0]);
+            wd[2 * c + 1] = __float_as_uint(kp[c][1]);
+        }
+    }
+    const bool odd = lrow & 1, up = lrow >= 2;
+    // stage 1: keep the units k with k % 2 == row % 2, trade the others with row ^ 1
+    uint32_t lo[2][US], hi[2][US];  // rows (row & ~1) and (row | 1)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const uint32_t keep = odd ? wd[(2 * j + 1) * US + u] : wd[2 * j * US + u];
+            const uint32_t got = xchg_row(odd ? wd[2 * j * US + u] : wd[(2 * j + 1) * US + u], odd);
+            lo[j][u] = odd ? got : keep;
+            hi[j][u] = odd ? keep : got;
+        }
+    // stage 2: keep the units k == row, trade k == row ^ 2 with row ^ 2
+    uint32_t fin[4][US];  // by source row 0..3
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+        const uint32_t klo = up ? lo[1][u] : lo[0][u], khi = up ? hi[1][u] : hi[0][u];
+        const uint32_t glo = xchg_half(up ? lo[0][u] : lo[1][u], up);
+        const uint32_t ghi = xchg_half(up ? hi[0][u] : hi[1][u], up);
+        fin[0][u] = up ? glo : klo;
+        fin[1][u] = up ? ghi : khi;
+        fin[2][u] = up ? klo : glo;
+        fin[3][u] = up ? khi : ghi;
+    }
+    // lane row r now holds unit r: channels CPT cg + CHU r .. of tokens 8w .. 8w+7
+#pragma unroll
+    for (int ch = 0; ch < CHU; ++ch) {
+        uint32_t x[4 * WPC];
+#pragma unroll
+        for (int row = 0; row < 4; ++row)
+#pragma unroll
+            for (int v = 0; v < WPC; ++v) x[row * WPC + v] = fin[row][ch * WPC + v];
+        u32x4* dst = reinterpret_cast<u32x4*>(Ktg + aorder_index(CPT * cg + CHU * lrow + ch, 8 * w, 64));
+#pragma unroll
+        for (int q = 0; q < WPC; ++q) dst[q] = u32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+    }
+}
+
 // One thread's share of a chunk's raw rows: tokens 2rg, 2rg+1, channels
 // (d_k/16) cg.. of q, k, g, v, and beta, in the I/O type.  Rows past the chunk's
 // length read as zeros (buffer range check), so the loads are never predicated.
@@ -410,8 +481,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) rk[c] = __builtin_bit_cast(W2, kh[c]);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) store_n<T, 2>(Ktg + aorder_index(CPT * cg + c, 2 * rg, 64), kpT[c]);
+    store_kt<T, CPT>(Ktg, kpT, cg, w, lrow);
     if (rg == 0) {
         float* gC = reinterpret_cast<float*>(rec + p.L.off_gc);
 #pragma unroll
