@@ -52,7 +52,9 @@ struct DecodeArgs {
 // of the I/O type, all matrices in MFMA fragment order:
 //   W    64 x D   (A order)   W = T Diag(beta) Khat
 //   Qh   64 x D   (A order)   Qhat = q * exp(gamma)
-//   M    64 x 64  (A order)   inclusive-lower Q K decay products
+//   M    64 x 64  (A order)   inclusive-lower Q K decay products (the two
+//                             fragment tiles of rows 0..31, columns 32..63 are
+//                             all zero; they are neither written nor read)
 //   Kt   D  x 64  (A order)   Kprime^T, Kprime = k * exp(gamma_C - gamma)
 //   U    64 x D   (C order)   U = T Diag(beta) V
 //   gC   D fp32               exp(gamma_C)

@@ -494,14 +494,15 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         T* Mg = reinterpret_cast<T*>(rec + p.L.off_m);
         // waves 0-6: blocks (0,0) (1,1) (2,2) (3,3) (2,0) (3,0) (3,1), which all
         // scale their K-side operand; wave 7: (1,0) (2,1) (3,2), which do not.
-        // Waves 0-5 also write the six zero blocks of M above the diagonal.
+        // Waves 0 and 5 also write the zero blocks (0,1) and (2,3) of M, which
+        // share 16 x 32 fragment tiles with nonzero blocks; the tiles of blocks
+        // (0..1, 2..3) are all zero and are never read, so never written.
         if (w < 7) {
             const int R = (0x3323210 >> (4 * w)) & 15;
             const int J = (0x1003210 >> (4 * w)) & 15;
             decay_block<T, D>(sm, Mg, R, J, lane);
-            if (w < 6) {
-                const int zR = (0x211000 >> (4 * w)) & 15;
-                const int zJ = (0x332321 >> (4 * w)) & 15;
+            if (w == 0 || w == 5) {
+                const int zR = w == 0 ? 0 : 2, zJ = w == 0 ? 1 : 3;
                 const float z[4] = {0.f, 0.f, 0.f, 0.f};
                 store_n<T, 4>(Mg + aorder_index(16 * zR + (lane & 15), 16 * zJ + 4 * (lane >> 4), 64), z);
             }

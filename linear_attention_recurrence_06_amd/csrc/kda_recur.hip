@@ -100,7 +100,9 @@ struct WaveOps {
         if (!uwave) {
             const T* m = reinterpret_cast<const T*>(rec + L.off_m);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) Mf[ks] = load_frag<T>(m + ((b * 2 + ks) * kWave + lane) * 8);
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks == 0 || b >= 2)  // tokens 32.. of blocks 0 and 1 are above the diagonal
+                    Mf[ks] = load_frag<T>(m + ((b * 2 + ks) * kWave + lane) * 8);
         }
     }
 };
@@ -228,7 +230,7 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             mma(acc[nb], ops.Mf[0], Ub[0][nb]);
-            mma(acc[nb], ops.Mf[1], Ub[1][nb]);
+            if (c.b >= 2) mma(acc[nb], ops.Mf[1], Ub[1][nb]);
         }
     }
     ops.load_back(c.rec(kc + NBUF), p.L, c.uwave, c.b, c.rb, lane);
