@@ -36,39 +36,34 @@ struct DecodeFE {
     const float* bias;      // [H, d] or null
 };
 
-// Convolved (and SiLU-activated) element i of tensor x (0 q, 1 k, 2 v) of
-// unit (n, h), whose raw value is `raw`; hist receives the W-1 state rows.
+// One front-end step of element i of tensor x (0 q, 1 k, 2 v) of unit (n, h):
+// the convolution of the raw value with the W-1 conv-state rows (then SiLU if
+// asked), and the conv state advanced by one token (row j takes old row j+1,
+// the last row the raw value).  The caller is the only reader and writer of
+// this element's state, and every row is read before any is written, so the
+// state may be advanced in place.
 template <typename T, int D>
-__device__ __forceinline__ float fe_conv(const DecodeFE& fe, int x, int64_t n, int h, int H,
-                                         int i, float raw, float (&hist)[3]) {
+__device__ __forceinline__ float fe_step(const DecodeFE& fe, int x, int64_t n, int h, int H,
+                                         int i, float raw) {
     const int W = fe.conv_w;
     if (W == 0) return raw;
     const T* w = reinterpret_cast<const T*>(fe.weight) + ((int64_t)(x * H + h) * W) * D + i;
-    const T* st = reinterpret_cast<const T*>(fe.state_in);
+    const T* si = reinterpret_cast<const T*>(fe.state_in);
+    T* so = reinterpret_cast<T*>(fe.state_out);
+    const int64_t base = ((n * 3 + x) * (W - 1) * H + h) * D + i, row = (int64_t)H * D;
+    float hist[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hist[j] = (j < W - 1 && si) ? to_f32(si[base + j * row]) : 0.f;
     float y = to_f32(w[(int64_t)(W - 1) * D]) * raw;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        hist[j] = 0.f;
-        if (j < W - 1) {
-            if (st) hist[j] = to_f32(st[(((n * 3 + x) * (W - 1) + j) * H + h) * D + i]);
-            y += to_f32(w[(int64_t)j * D]) * hist[j];
-        }
+    for (int j = 0; j < 3; ++j)
+        if (j < W - 1) y += to_f32(w[(int64_t)j * D]) * hist[j];
+    if (so) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < W - 1) so[base + j * row] = from_f32<T>(j + 1 < W - 1 ? hist[j + 1] : raw);
     }
     return fe.silu ? y * __builtin_amdgcn_rcpf(1.f + __expf(-y)) : y;
-}
-
-// Writes the advanced conv state of element i: rows hist[1..W-2], then raw.
-template <typename T, int D>
-__device__ __forceinline__ void fe_conv_store(const DecodeFE& fe, int x, int64_t n, int h, int H,
-                                              int i, float raw, const float (&hist)[3]) {
-    const int W = fe.conv_w;
-    if (W <= 1 || !fe.state_out) return;
-    T* st = reinterpret_cast<T*>(fe.state_out);
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < W - 1)
-            st[(((n * 3 + x) * (W - 1) + j) * H + h) * D + i] =
-                from_f32<T>(j + 1 < W - 1 ? hist[j + 1] : raw);
 }
 
 template <typename T, int D, bool FE>
@@ -93,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     const int wave = t >> 6, lane = t & 63;
     const int cq = t % TPR, rg = t / TPR;
 
-    __shared__ float s_q[D], s_k[D], s_a[D];
+    __shared__ float s_q[D], s_k[D], s_a[D], s_v[FE ? D : 1], s_qk;
     __shared__ float s_red[4][TPR][8];
 
     // 1. stream the state in (all loads in flight before any arithmetic)
@@ -104,104 +99,120 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
         s[m] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(Su + (int64_t)(rg + RG * m) * D + 4 * cq));
 
-    // 2. token vectors: every wave computes the norms itself (no barrier needed for them)
+    // 2. token vectors
     const T* qu = q + unit * D;
     const T* ku = k + unit * D;
     const int64_t n = unit / H;
     const int h = (int)(unit - n * H);
-    float qv[EPL], kv[EPL];
-    float qraw[EPL], kraw[EPL], qhist[EPL][3], khist[EPL][3];
-    float ssq = 0.f, ssk = 0.f, sqk = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        qraw[e] = to_f32(qu[lane + kWave * e]);
-        kraw[e] = to_f32(ku[lane + kWave * e]);
-        if constexpr (FE) {
-            qv[e] = fe_conv<T, D>(fe, 0, n, h, H, lane + kWave * e, qraw[e], qhist[e]);
-            kv[e] = fe_conv<T, D>(fe, 1, n, h, H, lane + kWave * e, kraw[e], khist[e]);
-        } else {
-            qv[e] = qraw[e];
-            kv[e] = kraw[e];
-        }
-        ssq += qv[e] * qv[e];
-        ssk += kv[e] * kv[e];
-        sqk += qv[e] * kv[e];
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        ssq += xor_shfl(ssq, m);
-        ssk += xor_shfl(ssk, m);
-        sqk += xor_shfl(sqk, m);
-    }
-    const float rq = l2norm ? 1.0f / sqrtf(ssq + kL2Eps) : 1.0f;
-    const float rk = l2norm ? 1.0f / sqrtf(ssk + kL2Eps) : 1.0f;
-    const float qk = sqk * rq * rk * scale;   // (scale * qb) . kb
-    if (wave == 0) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int i = lane + kWave * e;
-            s_q[i] = qv[e] * rq * scale;
-            s_k[i] = kv[e] * rk;
-            if (!(FE && fe.rank > 0)) s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
-        }
-    }
-    if (FE && fe.rank > 0) {
-        // low-rank decay gate g = -softplus(a[n] . b[h][c] + bias[h][c]): the
-        // TPC = 256/D threads of channel c = t / TPC each take rank/TPC of the
-        // products (loads past the rank read zero), then sum with lane swaps
-        constexpr int TPC = 256 / D;
-        constexpr int MAXJ = 128 / TPC;  // the largest slice
-        const int c = t / TPC, part = t % TPC;
-        const int R = fe.rank, slice = R / TPC;
-        const uint32_t E = sizeof(T);
-        // (the resources are uniform over the workgroup: a lane-dependent base
-        // would make the compiler loop over the lanes' descriptors)
-        const auto ra = make_rsrc(reinterpret_cast<const T*>(fe.a) + n * R, (uint32_t)R * E);
-        const auto rb = make_rsrc(reinterpret_cast<const T*>(fe.b) + (int64_t)h * D * R,
-                                  (uint32_t)(D * R) * E);
-        float z = 0.f;
-#pragma unroll
-        for (int j = 0; j < MAXJ; j += 8) {
-            const bool in = j < slice;
-            const uint32_t k = (uint32_t)(part * slice + j);
-            const Frag<T> af = buffer_load_frag<T>(ra, in ? k * E : kFarOffset);
-            const Frag<T> bf = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + k) * E : kFarOffset);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) z += to_f32(af.v[m]) * to_f32(bf.v[m]);
-        }
-#pragma unroll
-        for (int off = 1; off < TPC; off <<= 1) z += xor_shfl(z, off);
-        if (part == 0) {
-            z += fe.bias ? fe.bias[h * D + c] : 0.f;
-            s_a[c] = __expf(-(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)))));
-        }
-    }
     const float b = to_f32(beta[unit]);
-    float vj[4], vraw[4], vhist[4][3];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        vraw[j] = to_f32(v[unit * D + 4 * cq + j]);
-        if constexpr (FE)
-            vj[j] = fe_conv<T, D>(fe, 2, n, h, H, 4 * cq + j, vraw[j], vhist[j]);
-        else
-            vj[j] = vraw[j];
-    }
-    __syncthreads();
+    float qk, vj[4];
     if constexpr (FE) {
-        // every read of this unit's conv state is behind the barrier, so the
-        // state may be advanced in place
+        // front end: wave 0 alone takes q and k through the front end, and its
+        // first TPR lanes (row group 0) v, each advancing its elements' conv
+        // state; the results reach the other waves through LDS
         if (wave == 0) {
+            float qv[EPL], kv[EPL];
+            float ssq = 0.f, ssk = 0.f, sqk = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                fe_conv_store<T, D>(fe, 0, n, h, H, lane + kWave * e, qraw[e], qhist[e]);
-                fe_conv_store<T, D>(fe, 1, n, h, H, lane + kWave * e, kraw[e], khist[e]);
+                const int i = lane + kWave * e;
+                qv[e] = fe_step<T, D>(fe, 0, n, h, H, i, to_f32(qu[i]));
+                kv[e] = fe_step<T, D>(fe, 1, n, h, H, i, to_f32(ku[i]));
+                ssq += qv[e] * qv[e];
+                ssk += kv[e] * kv[e];
+                sqk += qv[e] * kv[e];
             }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                ssq += xor_shfl(ssq, m);
+                ssk += xor_shfl(ssk, m);
+                sqk += xor_shfl(sqk, m);
+            }
+            const float rq = l2norm ? 1.0f / sqrtf(ssq + kL2Eps) : 1.0f;
+            const float rk = l2norm ? 1.0f / sqrtf(ssk + kL2Eps) : 1.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int i = lane + kWave * e;
+                s_q[i] = qv[e] * rq * scale;
+                s_k[i] = kv[e] * rk;
+                if (fe.rank == 0) s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
+            }
+            if (lane == 0) s_qk = sqk * rq * rk * scale;
         }
         if (rg == 0) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                fe_conv_store<T, D>(fe, 2, n, h, H, 4 * cq + j, vraw[j], vhist[j]);
+                s_v[4 * cq + j] = fe_step<T, D>(fe, 2, n, h, H, 4 * cq + j,
+                                                to_f32(v[unit * D + 4 * cq + j]));
         }
+        if (fe.rank > 0) {
+            // low-rank decay gate g = -softplus(a[n] . b[h][c] + bias[h][c]): the
+            // TPC = 256/D threads of channel c = t / TPC each take rank/TPC of the
+            // products (loads past the rank read zero), then sum with lane swaps
+            constexpr int TPC = 256 / D;
+            constexpr int MAXJ = 128 / TPC;  // the largest slice
+            const int c = t / TPC, part = t % TPC;
+            const int R = fe.rank, slice = R / TPC;
+            const uint32_t E = sizeof(T);
+            // (the resources are uniform over the workgroup: a lane-dependent base
+            // would make the compiler loop over the lanes' descriptors)
+            const auto ra = make_rsrc(reinterpret_cast<const T*>(fe.a) + n * R, (uint32_t)R * E);
+            const auto rb = make_rsrc(reinterpret_cast<const T*>(fe.b) + (int64_t)h * D * R,
+                                      (uint32_t)(D * R) * E);
+            float z = 0.f;
+#pragma unroll
+            for (int j = 0; j < MAXJ; j += 8) {
+                const bool in = j < slice;
+                const uint32_t kk = (uint32_t)(part * slice + j);
+                const Frag<T> af = buffer_load_frag<T>(ra, in ? kk * E : kFarOffset);
+                const Frag<T> bf = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + kk) * E : kFarOffset);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) z += to_f32(af.v[m]) * to_f32(bf.v[m]);
+            }
+#pragma unroll
+            for (int off = 1; off < TPC; off <<= 1) z += xor_shfl(z, off);
+            if (part == 0) {
+                z += fe.bias ? fe.bias[h * D + c] : 0.f;
+                s_a[c] = __expf(-(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)))));
+            }
+        }
+        __syncthreads();
+        qk = s_qk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vj[j] = s_v[4 * cq + j];
+    } else {
+        // every wave computes the norms itself (no barrier needed for them)
+        float qv[EPL], kv[EPL];
+        float ssq = 0.f, ssk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            qv[e] = to_f32(qu[lane + kWave * e]);
+            kv[e] = to_f32(ku[lane + kWave * e]);
+            ssq += qv[e] * qv[e];
+            ssk += kv[e] * kv[e];
+            sqk += qv[e] * kv[e];
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            ssq += xor_shfl(ssq, m);
+            ssk += xor_shfl(ssk, m);
+            sqk += xor_shfl(sqk, m);
+        }
+        const float rq = l2norm ? 1.0f / sqrtf(ssq + kL2Eps) : 1.0f;
+        const float rk = l2norm ? 1.0f / sqrtf(ssk + kL2Eps) : 1.0f;
+        qk = sqk * rq * rk * scale;   // (scale * qb) . kb
+        if (wave == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int i = lane + kWave * e;
+                s_q[i] = qv[e] * rq * scale;
+                s_k[i] = kv[e] * rk;
+                s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vj[j] = to_f32(v[unit * D + 4 * cq + j]);
+        __syncthreads();
     }
 
     // 3. decay the rows and accumulate both read-outs
