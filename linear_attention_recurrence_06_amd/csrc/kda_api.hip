@@ -1,8 +1,6 @@
 // C ABI of libkda.so: argument validation, workspace sizing and dispatch.
 // See include/kda.h for the contract.  Nothing here reads device memory or
 // synchronises; every launch goes on the caller's stream.
-#include <atomic>
-
 #include "../../include/kda.h"
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
@@ -61,23 +59,6 @@ kda_status check_dims(const kda_dims* d, bool prefill) {
 }
 
 size_t elt_bytes(const kda_dims* d) { return d->io_dtype == KDA_BF16 ? 2 : 4; }
-
-// Compute units of the current device, queried once per device.
-int current_cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
 
 }  // namespace
 
@@ -273,7 +254,6 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.out_gate_z = out_gate_z;
     a.fe = fe;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
-    a.cu_count = current_cu_count();
     hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -111,7 +111,6 @@ struct PrefillArgs {
     bool scalar_g;               // g is [T, H] (one decay per head) instead of [T, H, d]
     float scale;
     int l2norm;
-    int cu_count;                // compute units of the device (persistent grids)
     int32_t ckpt_interval;       // 0: no checkpoints
     float* checkpoints;          // [C, H, d, d] when ckpt_interval > 0
     int out_gate;                // 0 none, 1 z [T, H, d], 2 z [T, H]: out = o * sigmoid(z)

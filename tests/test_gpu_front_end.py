@@ -250,3 +250,44 @@ def test_decode_front_end_matches_oracle(lib, oracle, io, d):
         assert e <= TOL[io]
         assert np.array_equal(host(cst), cst_ref)
     assert maxerr(host(st), st_ref) <= TOL[io]
+
+
+def test_front_end_with_output_gate_and_checkpoints(lib, oracle):
+    """Every prefill option in one call on two packed sequences: front end (W = 4
+    + SiLU, rank 64), output gate per head and a checkpoint every chunk, against
+    the oracle's gated read-out, final states and prefix states."""
+    from kda_inputs import make_front_end, make_out_gate, make_prefill
+    H, d, lens = 2, 128, [300, 130]
+    inp = make_prefill(lens, H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=131, device="cuda")
+    T, N = sum(lens), len(lens)
+    fe = make_front_end(T, N, H, d, "bf16", width=4, rank=64, bias_std=0.3, seed=132,
+                        device="cuda")
+    z = make_out_gate((T, H), "bf16", seed=133, device="cuda")
+    out, fin, ck, cst = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], None, inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], out_gate_z=z, checkpoint_interval=1,
+        conv_weight=fe["conv_weight"], conv_silu=True, conv_state_in=fe["conv_state"],
+        output_conv_state=True, gate_a=fe["gate_a"], gate_b=fe["gate_b"],
+        gate_bias=fe["gate_bias"])
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].cpu().numpy()
+    q2, k2, v2, g2, cfin = oracle_front(oracle, inp, fe, cu, N, True)
+    o_ref, f_ref = oracle.prefill(q2, k2, v2, g2, host(inp["beta"]), cu_seqlens=cu,
+                                  initial_state=host(inp["initial_state"]), n_seqs=N)
+    eo = maxerr(host(out), oracle.apply_output_gate(o_ref, host(z)))
+    ef = maxerr(host(fin), f_ref)
+    say(f"all options: err_out={eo:.3e} err_state={ef:.3e} checkpoints={ck.shape[0]}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    assert np.array_equal(host(cst), cfin)
+    # checkpoints: sequence 0 has chunks 0..4 (states after chunks 0..3), then
+    # sequence 1 has chunks 0..2 (states after chunks 0, 1)
+    assert ck.shape[0] == 4 + 2
+    s0 = host(inp["initial_state"])
+    idx = 0
+    for n, L in enumerate(lens):
+        for c in range((L + 63) // 64 - 1):
+            b, e = cu[n], cu[n] + 64 * (c + 1)
+            _, fp = oracle.prefill(q2[b:e], k2[b:e], v2[b:e], g2[b:e], host(inp["beta"])[b:e],
+                                   initial_state=s0[n:n + 1])
+            assert maxerr(host(ck[idx]), fp[0]) <= TOL["bf16"]
+            idx += 1
