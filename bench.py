@@ -92,9 +92,9 @@ def main():
                          "device copy as a traffic calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the KDA path shards by head and sequence with no exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads and sequences shard across GPUs with no exchange, so one GPU's "
+              "throughput is the per-GPU figure)", file=sys.stderr)
         sys.exit(2)
     if args.profile:
         args.steps, args.warmup, args.decode_steps = 5, 2, 10
