@@ -698,7 +698,7 @@ struct FeRaw {
 // The front end's rows: the convolution (and SiLU) of q, k, v, and g given or
 // from the low-rank projection.  Rows past the chunk's length are zero, as
 // without a front end.
-template <typename T, int D>
+template <typename T, int D, int KS>
 __device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm, int2 d, int h,
                                         const FeRaw<T, D>& raw, ItemRows<T, D>& r) {
     constexpr int CPT = D / 16;
@@ -776,14 +776,15 @@ __device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm,
         const int tb = w & 3;
         const uint32_t E = sizeof(T);
         const auto ra = make_rsrc((const T*)p.fe.a + (int64_t)d.x * R, (uint32_t)(d.y * R) * E);
-        // every 32-deep step up to rank 128 is issued; steps past the rank read
-        // zeros (their products add nothing), so all loads can be in flight at once
+        // KS 32-deep steps (the rank rounded up to 64 or 128) are issued; steps
+        // past the rank read zeros (their products add nothing), so all loads can
+        // be in flight at once
         const auto rbm = make_rsrc((const T*)p.fe.b + (int64_t)h * D * R, (uint32_t)(D * R) * E);
         f32x4 acc[NTW];
 #pragma unroll
         for (int i = 0; i < NTW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const bool in = 32 * ks < R;
             const uint32_t k0 = 32 * ks + 8 * (lane >> 4);
             const Frag<T> af = buffer_load_frag<T>(
@@ -837,7 +838,7 @@ __device__ __forceinline__ void seq_of_token(const PrepParams& p, int64_t tok, i
 }
 
 // The preparation with the front end: raw q, k, v, and g given or low-rank.
-template <typename T, int D>
+template <typename T, int D, int KS>
 __global__ __launch_bounds__(512, 4) void prep_fe_kernel(PrepParams p) {
     __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x;
@@ -853,7 +854,7 @@ __global__ __launch_bounds__(512, 4) void prep_fe_kernel(PrepParams p) {
     {
         FeRaw<T, D> raw;
         raw.load(p, d, n, s_begin, h, t >> 4, t & 15);
-        fe_rows<T, D>(p, sm, d, h, raw, rows);
+        fe_rows<T, D, KS>(p, sm, d, h, raw, rows);
     }
     prep_item<T, D>(p, sm, slot, h, rows);
 }
@@ -1020,7 +1021,11 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     if (a.fe.active()) {
         p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
                       a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
-        hipLaunchKernelGGL((prep_fe_kernel<T, D>), dim3((unsigned)items), dim3(512), 0, stream, p);
+        // ranks up to 64 take two 32-deep steps of the gate's product, larger ones four
+        if (a.fe.rank <= 64)
+            hipLaunchKernelGGL((prep_fe_kernel<T, D, 2>), dim3((unsigned)items), dim3(512), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prep_fe_kernel<T, D, 4>), dim3((unsigned)items), dim3(512), 0, stream, p);
         return hipGetLastError();
     }
     if (a.scalar_g)
