@@ -2,16 +2,18 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
 
-One step = one chunked prefill (chunk index + chunk prep + chunked recurrence)
-of the single-sequence workload T=8192, H=32, d_k=d_v=128, bf16 I/O, fp32
-state, with seeded synthetic inputs resident in HBM.  Four copies of the inputs
-are rotated so a step never finds its inputs in the 256 MB MALL.  K steps are
-timed between device synchronisations; each call is also bracketed by HIP
-events on the stream the library launches on, which gives the per-call
-duration behind the roofline figure.  In the same run the decode step is timed
-on 256 sequences x 32 heads (512 MiB fp32 state, advanced in place), and the
-fp64 oracle is timed on the host cores on the full prefill workload
-(repeated to ~10 s of CPU work).
+One step = one chunked prefill (chunk prep + chunked recurrence) of the
+single-sequence workload T=8192, H=32, d_k=d_v=128, bf16 I/O, fp32 state, with
+seeded synthetic inputs resident in HBM.  Four copies of the inputs are rotated
+so a step never finds its inputs in the 256 MB MALL.  Before the W warm-up
+steps, untimed calls run until --ramp-ms of GPU time has passed, because the
+shader clock rises over the first ~25 ms of load.  K back-to-back steps are
+timed between device synchronisations, with two HIP events on the launch stream
+around them giving the average call duration behind the roofline figure; a
+separate loop with events around each call gives the per-call spread.  In
+the same run the decode step is timed on 256 sequences x 32 heads (512 MiB
+fp32 state, advanced in place), and the fp64 oracle is timed on the host cores
+on the full prefill workload (repeated to ~10 s of CPU work).
 
 Prints one JSON line (rank 0, N = 1).
 """
@@ -83,9 +85,12 @@ def counter_traffic(kind: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--ramp-ms", type=float, default=80.0,
+                    help="untimed prefill calls before the warm-up steps until this much GPU "
+                         "time has passed (the shader clock rises over the first ~25 ms of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for profilers: few steps, no CPU baseline, one 1 GiB "
@@ -99,6 +104,7 @@ def main():
     if args.profile:
         args.steps, args.warmup, args.decode_steps = 5, 2, 10
         args.no_cpu_baseline = True
+        args.ramp_ms = 0.0
 
     import numpy as np
     import torch
@@ -128,23 +134,42 @@ def main():
         kda.kda_chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["initial_state"],
                               None, out, fin, workspace=ws, stream=stream)
 
+    # clock ramp: untimed calls until ramp_ms of GPU time has passed
+    ramp_s, r_i = 0.0, 0
+    while ramp_s * 1e3 < args.ramp_ms:
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(10):
+            prefill(r_i)
+            r_i += 1
+        r1.record(stream)
+        torch.cuda.synchronize(dev)
+        ramp_s += r0.elapsed_time(r1) * 1e-3
     for i in range(args.warmup):
         prefill(i)
-    torch.cuda.synchronize(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region: K back-to-back calls bracketed by two events on the
+    # launch stream (per-call events inside it would serialise the calls)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
+    e_start.record(stream)
+    for i in range(args.steps):
+        prefill(i)
+    e_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    call_avg_s = e_start.elapsed_time(e_end) * 1e-3 / args.steps
+    tokens_per_s = T / (wall / args.steps)
+    # per-call spread, in a separate loop with events around each call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
         prefill(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
     call_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
-    call_avg_s = float(np.mean(call_ms)) * 1e-3
-    tokens_per_s = T / (wall / args.steps)
     p_bytes = prefill_algorithmic_bytes(T, H, D)
     p_achieved = p_bytes / call_avg_s / 1e9
     p_traffic = counter_traffic("prefill")
@@ -246,17 +271,25 @@ def main():
     for s in range(min(3, args.decode_steps)):
         decode(s)
     torch.cuda.synchronize(dev)
-    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.decode_steps)]
+    d_start, d_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t1 = time.perf_counter()
+    d_start.record(stream)
     for s in range(args.decode_steps):
+        decode(s)
+    d_end.record(stream)
+    torch.cuda.synchronize(dev)
+    d_wall = time.perf_counter() - t1
+    d_avg_s = d_start.elapsed_time(d_end) * 1e-3 / args.decode_steps
+    # per-step spread, in a separate loop with events around each step
+    n_spread = min(20, args.decode_steps)
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_spread)]
+    for s in range(n_spread):
         dev_ev[s][0].record(stream)
         decode(s)
         dev_ev[s][1].record(stream)
     torch.cuda.synchronize(dev)
-    d_wall = time.perf_counter() - t1
     d_ms = [a.elapsed_time(b) for a, b in dev_ev]
-    d_avg_s = float(np.mean(d_ms)) * 1e-3
     sb = decode_state_bytes(DECODE_N, DECODE_H, D)
     tb = decode_token_bytes(DECODE_N, DECODE_H, D)
     d_traffic = counter_traffic("decode")
@@ -397,7 +430,7 @@ def main():
                 "algorithmic_bytes_per_call": sb + tb,
                 "avg_call_us": d_avg_s * 1e6,
                 "median_call_us": float(np.median(d_ms)) * 1e3,
-                "total_ms": float(np.sum(d_ms)),
+                "total_ms": d_avg_s * 1e3 * args.decode_steps,
                 "practical_hbm_GBps": copy_GBps,
                 "frac_of_practical": (sb + tb) / d_avg_s / 1e9 / copy_GBps,
             },
