@@ -93,7 +93,7 @@ def main():
                          "time has passed (the shader clock rises over the first ~25 ms of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="short run for profilers: few steps, no CPU baseline, one 1 GiB "
+                    help="short run for profilers: the clock ramp, few steps, no CPU baseline, one 1 GiB "
                          "device copy as a traffic calibration")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -104,7 +104,6 @@ def main():
     if args.profile:
         args.steps, args.warmup, args.decode_steps = 5, 2, 10
         args.no_cpu_baseline = True
-        args.ramp_ms = 0.0
 
     import numpy as np
     import torch
