@@ -213,8 +213,10 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
         if constexpr (CK) {
             // state after chunk kc, when kc + 1 is a multiple of the interval and
             // the sequence goes on
-            if ((kc + 1) % p.ckpt_interval == 0 && kc < c.last) {
-                const int64_t idx = c.ck0 + (kc + 1) / p.ckpt_interval - 1;
+            // (chunk counts fit 32 bits: 32-bit division is far cheaper than 64-bit)
+            const uint32_t k1 = (uint32_t)kc + 1, iv = (uint32_t)p.ckpt_interval;
+            if (k1 % iv == 0 && kc < c.last) {
+                const int64_t idx = c.ck0 + (int64_t)(k1 / iv) - 1;
                 float* dst = p.ckpt + ((idx * c.H + c.h) * D) * D;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
