@@ -106,7 +106,13 @@ struct PrepSmem {
         } b;
         struct {
             float wsum[8][D];     // the same words as wsum above
-            float G[64][D + 4];   // front end: the low-rank gate's pre-activations
+            union {
+                float G[64][D + 4];  // front end: the low-rank gate's pre-activations
+                struct {
+                    T A[64][64 + P];  // 64 ranks of the chunk's gate rows a
+                    T B[D][64 + P];   // the same ranks of the head's b
+                } st;
+            };
         } fe;
     } u;
 };
@@ -768,34 +774,49 @@ __device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm,
                 r.g[i][c] = to_f32(p.fe.scalar_g ? raw.gs[i] : raw.g[i][c]);
         return;
     }
-    // G = a b_h^T on MFMA: wave w forms token tile w % 4 against channel tiles
-    // (D/32) (w / 4) .. +D/32-1, into LDS; then each thread takes its rows
+    // G = a b_h^T on MFMA.  The chunk's gate rows a [64 x R] and the head's b
+    // [D x R] go through LDS 64 ranks at a time, so each element is loaded once
+    // per workgroup (from registers, each token tile would be fetched by two
+    // waves and each channel tile by four).  Wave w forms token tile w % 4
+    // against channel tiles (D/32) (w / 4) .. +D/32-1; the pre-activations then
+    // go to LDS over the staging area, and each thread takes its rows.
     {
         constexpr int NTW = D / 32;
         const int R = p.fe.rank;
         const int tb = w & 3;
         const uint32_t E = sizeof(T);
+        // rows of a past the chunk and ranks past R read zero (range-checked);
+        // R is a multiple of 32, so an 8-rank octet is wholly in or out
         const auto ra = make_rsrc((const T*)p.fe.a + (int64_t)d.x * R, (uint32_t)(d.y * R) * E);
-        // KS 32-deep steps (the rank rounded up to 64 or 128) are issued; steps
-        // past the rank read zeros (their products add nothing), so all loads can
-        // be in flight at once
         const auto rbm = make_rsrc((const T*)p.fe.b + (int64_t)h * D * R, (uint32_t)(D * R) * E);
         f32x4 acc[NTW];
 #pragma unroll
         for (int i = 0; i < NTW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bool in = 32 * ks < R;
-            const uint32_t k0 = 32 * ks + 8 * (lane >> 4);
-            const Frag<T> af = buffer_load_frag<T>(
-                ra, in ? ((16 * tb + (lane & 15)) * R + k0) * E : kFarOffset);
-#pragma unroll
-            for (int i = 0; i < NTW; ++i) {
-                const int ct = NTW * (w >> 2) + i;
-                const Frag<T> bf = buffer_load_frag<T>(
-                    rbm, in ? ((16 * ct + (lane & 15)) * R + k0) * E : kFarOffset);
-                mma(acc[i], af, bf);
+        for (int pc = 0; pc < KS / 2; ++pc) {
+            {
+                const int row = t >> 3, k = 64 * pc + 8 * (t & 7);
+                store_frag<T>(&sm.u.fe.st.A[row][8 * (t & 7)],
+                              buffer_load_frag<T>(ra, k < R ? (uint32_t)(row * R + k) * E : kFarOffset));
             }
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) {
+                const int i = t + 512 * j, row = i >> 3, k = 64 * pc + 8 * (i & 7);
+                store_frag<T>(&sm.u.fe.st.B[row][8 * (i & 7)],
+                              buffer_load_frag<T>(rbm, k < R ? (uint32_t)(row * R + k) * E : kFarOffset));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int k0 = 32 * ks + 8 * (lane >> 4);
+                const Frag<T> af = load_frag<T>(&sm.u.fe.st.A[16 * tb + (lane & 15)][k0]);
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) {
+                    const int ct = NTW * (w >> 2) + i;
+                    mma(acc[i], af, load_frag<T>(&sm.u.fe.st.B[16 * ct + (lane & 15)][k0]));
+                }
+            }
+            __syncthreads();
         }
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
