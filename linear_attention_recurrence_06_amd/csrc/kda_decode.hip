@@ -36,37 +36,84 @@ struct DecodeFE {
     const float* bias;      // [H, d] or null
 };
 
-// One front-end step of element i of tensor x (0 q, 1 k, 2 v) of unit (n, h):
-// the convolution of the raw value with the W-1 conv-state rows (then SiLU if
-// asked), and the conv state advanced by one token (row j takes old row j+1,
-// the last row the raw value).  The caller is the only reader and writer of
-// this element's state, and every row is read before any is written, so the
-// state may be advanced in place.
-template <typename T, int D>
-__device__ __forceinline__ float fe_step(const DecodeFE& fe, int x, int64_t n, int h, int H,
-                                         int i, float raw) {
+// Front-end operands of N consecutive elements of one tensor of one unit:
+// the raw token values, the filter taps aligned to the last four tokens (tap
+// jp - (4 - W) of the W; the first 4 - W read zero), and the conv-state rows
+// aligned the same way (row jp - (4 - W) of the W - 1; rows that do not exist,
+// or all of them without an input state, read zero).  All loads are issued
+// together with no branch on their values, so one wait covers them.
+template <typename T, int N>
+struct FeOps {
+    typedef T V __attribute__((ext_vector_type(N)));
+    V raw, w[4], hist[3];
+};
+
+template <typename T, int D, int N>
+__device__ __forceinline__ void fe_load(const DecodeFE& fe, const T* raw, int x, int64_t n, int h,
+                                        int H, int i0, FeOps<T, N>& f) {
+    typedef typename FeOps<T, N>::V V;
+    const uint32_t E = sizeof(T);
     const int W = fe.conv_w;
-    if (W == 0) return raw;
-    const T* w = reinterpret_cast<const T*>(fe.weight) + ((int64_t)(x * H + h) * W) * D + i;
-    const T* si = reinterpret_cast<const T*>(fe.state_in);
-    T* so = reinterpret_cast<T*>(fe.state_out);
-    const int64_t base = ((n * 3 + x) * (W - 1) * H + h) * D + i, row = (int64_t)H * D;
-    float hist[3];
+    // (token rows need only element alignment: one load per element)
 #pragma unroll
-    for (int j = 0; j < 3; ++j) hist[j] = (j < W - 1 && si) ? to_f32(si[base + j * row]) : 0.f;
-    float y = to_f32(w[(int64_t)(W - 1) * D]) * raw;
+    for (int c = 0; c < N; ++c) f.raw[c] = raw[i0 + c];
+    if (W == 0) return;  // no convolution: the raw values pass through
+    const auto rw = make_rsrc(reinterpret_cast<const T*>(fe.weight) + (int64_t)(x * H + h) * W * D,
+                              (uint32_t)(W * D) * E);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < W - 1) y += to_f32(w[(int64_t)j * D]) * hist[j];
-    if (so) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-            if (j < W - 1) so[base + j * row] = from_f32<T>(j + 1 < W - 1 ? hist[j + 1] : raw);
+    for (int jp = 0; jp < 4; ++jp) {
+        const int tap = jp - (4 - W);
+        f.w[jp] = buffer_load<V>(rw, tap < 0 ? kFarOffset : (uint32_t)(tap * D + i0) * E);
     }
-    return fe.silu ? y * __builtin_amdgcn_rcpf(1.f + __expf(-y)) : y;
+    const bool has = fe.state_in != nullptr && W > 1;
+    const auto rs = make_rsrc(
+        has ? reinterpret_cast<const T*>(fe.state_in) + ((n * 3 + x) * (W - 1) * H + h) * D
+            : reinterpret_cast<const T*>(fe.weight),
+        has ? (uint32_t)(((W - 2) * H * D + D) * E) : 0u);
+#pragma unroll
+    for (int jp = 0; jp < 3; ++jp) {
+        const int j = jp - (4 - W);
+        f.hist[jp] = buffer_load<V>(rs, j < 0 ? kFarOffset : (uint32_t)(j * H * D + i0) * E);
+    }
 }
 
-template <typename T, int D, bool FE>
+// The convolution of the loaded operands (then SiLU if asked), and the conv
+// state advanced by one token: row j takes old row j + 1, the last row the raw
+// value.  The caller is the only reader and writer of these elements' state,
+// and every row was read before any is written, so the state may be advanced
+// in place.
+template <typename T, int D, int N>
+__device__ __forceinline__ void fe_apply(const DecodeFE& fe, const FeOps<T, N>& f, int x, int64_t n,
+                                         int h, int H, int i0, float (&y)[N]) {
+    typedef typename FeOps<T, N>::V V;
+    const int W = fe.conv_w;
+    if (W == 0) {
+#pragma unroll
+        for (int c = 0; c < N; ++c) y[c] = to_f32(f.raw[c]);
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        float acc = to_f32(f.w[3][c]) * to_f32(f.raw[c]);
+#pragma unroll
+        for (int jp = 0; jp < 3; ++jp) acc += to_f32(f.w[jp][c]) * to_f32(f.hist[jp][c]);
+        y[c] = fe.silu ? acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc)) : acc;
+    }
+    if (fe.state_out) {
+        T* so = reinterpret_cast<T*>(fe.state_out) + ((n * 3 + x) * (W - 1) * H + h) * D + i0;
+#pragma unroll
+        for (int jp = 0; jp < 3; ++jp) {
+            const int j = jp - (4 - W);
+            if (j >= 0)
+                *reinterpret_cast<V*>(so + (int64_t)j * H * D) = jp < 2 ? f.hist[jp + 1] : f.raw;
+        }
+    }
+}
+
+// FE: raw q, k, v go through the front end (and g, unless given, comes from
+// the low-rank gate); GR: the largest gate rank the instantiation serves (64
+// or 128), which sizes the gate's loads.
+template <typename T, int D, bool FE, int GR>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
@@ -81,17 +128,59 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     constexpr int RG = 256 / TPR;    // row groups
     constexpr int RPT = D / RG;      // rows per thread
     constexpr int EPL = D / kWave;   // vector elements per lane in the norm pass
+    constexpr int TPC = 256 / D;     // gate: threads per channel
+    constexpr int NJ = GR / TPC / 8; // gate: fragments per thread
     static_assert(RPT * RG == D && EPL * kWave == D, "bad decode tiling");
 
     const int64_t unit = blockIdx.x;  // = n * H + h
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int cq = t % TPR, rg = t / TPR;
+    const T* qu = q + unit * D;
+    const T* ku = k + unit * D;
+    const int64_t n = unit / H;
+    const int h = (int)(unit - n * H);
 
     __shared__ float s_q[D], s_k[D], s_a[D], s_v[FE ? D : 1], s_qk;
     __shared__ float s_red[4][TPR][8];
 
-    // 1. stream the state in (all loads in flight before any arithmetic).
+    // 0. front end: its operands are requested before the state, so their
+    // arithmetic can start while the state streams in.  Wave 0 takes q and k
+    // (elements EPL*lane ..), its first TPR lanes (row group 0) v (elements
+    // 4*cq ..); every thread loads its share of the gate's products.
+    FeOps<T, EPL> fq, fk;
+    FeOps<T, 4> fv;
+    Frag<T> ga[NJ], gb[NJ];
+    float gbias = 0.f;
+    if constexpr (FE) {
+        if (wave == 0) {
+            fe_load<T, D, EPL>(fe, qu, 0, n, h, H, EPL * lane, fq);
+            fe_load<T, D, EPL>(fe, ku, 1, n, h, H, EPL * lane, fk);
+        }
+        if (rg == 0) fe_load<T, D, 4>(fe, v + unit * D, 2, n, h, H, 4 * cq, fv);
+        if (fe.rank > 0) {
+            // channel c = t / TPC, ranks [part * slice, (part + 1) * slice);
+            // fragments past the slice read zero (the resources are uniform over
+            // the workgroup: a lane-dependent base would make the compiler loop
+            // over the lanes' descriptors)
+            const int c = t / TPC, part = t % TPC;
+            const int R = fe.rank, slice = R / TPC;
+            const uint32_t E = sizeof(T);
+            const auto ra = make_rsrc(reinterpret_cast<const T*>(fe.a) + n * R, (uint32_t)R * E);
+            const auto rb = make_rsrc(reinterpret_cast<const T*>(fe.b) + (int64_t)h * D * R,
+                                      (uint32_t)(D * R) * E);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool in = 8 * j < slice;
+                const uint32_t kk = (uint32_t)(part * slice + 8 * j);
+                ga[j] = buffer_load_frag<T>(ra, in ? kk * E : kFarOffset);
+                gb[j] = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + kk) * E : kFarOffset);
+            }
+            if (fe.bias) gbias = fe.bias[h * D + c];
+        }
+    }
+
+    // 1. stream the state in (all loads in flight before any arithmetic on it).
     // Ordinary loads, non-temporal stores: measured 11% faster than with
     // non-temporal loads as well
     float* Su = S + unit * (int64_t)(D * D);
@@ -101,24 +190,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
         s[m] = *reinterpret_cast<const f32x4*>(Su + (int64_t)(rg + RG * m) * D + 4 * cq);
 
     // 2. token vectors
-    const T* qu = q + unit * D;
-    const T* ku = k + unit * D;
-    const int64_t n = unit / H;
-    const int h = (int)(unit - n * H);
     const float b = to_f32(beta[unit]);
     float qk, vj[4];
     if constexpr (FE) {
-        // front end: wave 0 alone takes q and k through the front end, and its
-        // first TPR lanes (row group 0) v, each advancing its elements' conv
-        // state; the results reach the other waves through LDS
         if (wave == 0) {
             float qv[EPL], kv[EPL];
+            fe_apply<T, D, EPL>(fe, fq, 0, n, h, H, EPL * lane, qv);
+            fe_apply<T, D, EPL>(fe, fk, 1, n, h, H, EPL * lane, kv);
             float ssq = 0.f, ssk = 0.f, sqk = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const int i = lane + kWave * e;
-                qv[e] = fe_step<T, D>(fe, 0, n, h, H, i, to_f32(qu[i]));
-                kv[e] = fe_step<T, D>(fe, 1, n, h, H, i, to_f32(ku[i]));
                 ssq += qv[e] * qv[e];
                 ssk += kv[e] * kv[e];
                 sqk += qv[e] * kv[e];
@@ -133,48 +214,39 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
             const float rk = l2norm ? 1.0f / sqrtf(ssk + kL2Eps) : 1.0f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const int i = lane + kWave * e;
+                const int i = EPL * lane + e;
                 s_q[i] = qv[e] * rq * scale;
                 s_k[i] = kv[e] * rk;
-                if (fe.rank == 0) s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
             }
             if (lane == 0) s_qk = sqk * rq * rk * scale;
         }
         if (rg == 0) {
+            float vv[4];
+            fe_apply<T, D, 4>(fe, fv, 2, n, h, H, 4 * cq, vv);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s_v[4 * cq + j] = fe_step<T, D>(fe, 2, n, h, H, 4 * cq + j,
-                                                to_f32(v[unit * D + 4 * cq + j]));
+            for (int j = 0; j < 4; ++j) s_v[4 * cq + j] = vv[j];
         }
         if (fe.rank > 0) {
             // low-rank decay gate g = -softplus(a[n] . b[h][c] + bias[h][c]): the
-            // TPC = 256/D threads of channel c = t / TPC each take rank/TPC of the
-            // products (loads past the rank read zero), then sum with lane swaps
-            constexpr int TPC = 256 / D;
-            constexpr int MAXJ = 128 / TPC;  // the largest slice
+            // TPC threads of channel c sum their slices with lane swaps
             const int c = t / TPC, part = t % TPC;
-            const int R = fe.rank, slice = R / TPC;
-            const uint32_t E = sizeof(T);
-            // (the resources are uniform over the workgroup: a lane-dependent base
-            // would make the compiler loop over the lanes' descriptors)
-            const auto ra = make_rsrc(reinterpret_cast<const T*>(fe.a) + n * R, (uint32_t)R * E);
-            const auto rb = make_rsrc(reinterpret_cast<const T*>(fe.b) + (int64_t)h * D * R,
-                                      (uint32_t)(D * R) * E);
             float z = 0.f;
 #pragma unroll
-            for (int j = 0; j < MAXJ; j += 8) {
-                const bool in = j < slice;
-                const uint32_t kk = (uint32_t)(part * slice + j);
-                const Frag<T> af = buffer_load_frag<T>(ra, in ? kk * E : kFarOffset);
-                const Frag<T> bf = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + kk) * E : kFarOffset);
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int m = 0; m < 8; ++m) z += to_f32(af.v[m]) * to_f32(bf.v[m]);
-            }
+                for (int m = 0; m < 8; ++m) z += to_f32(ga[j].v[m]) * to_f32(gb[j].v[m]);
 #pragma unroll
             for (int off = 1; off < TPC; off <<= 1) z += xor_shfl(z, off);
             if (part == 0) {
-                z += fe.bias ? fe.bias[h * D + c] : 0.f;
+                z += gbias;
                 s_a[c] = __expf(-(fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)))));
+            }
+        } else if (wave == 0) {
+            // g given: read last, since waiting on it also waits for the state
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int i = EPL * lane + e;
+                s_a[i] = __expf(to_f32(scalar_g ? g[unit] : g[unit * D + i]));
             }
         }
         __syncthreads();
@@ -279,14 +351,20 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     if (units == 0) return hipSuccess;
     DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
                 a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
-    if (a.fe.active())
-        hipLaunchKernelGGL((decode_kernel<T, D, true>), dim3((unsigned)units), dim3(256), 0,
+    if (a.fe.active() && a.fe.rank > 64)
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 128>), dim3((unsigned)units), dim3(256), 0,
+                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
+                           fe);
+    else if (a.fe.active())
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 64>), dim3((unsigned)units), dim3(256), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
                            fe);
     else
-        hipLaunchKernelGGL((decode_kernel<T, D, false>), dim3((unsigned)units), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, false, 64>), dim3((unsigned)units), dim3(256), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
