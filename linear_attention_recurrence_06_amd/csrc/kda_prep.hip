@@ -818,13 +818,21 @@ __device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm,
             }
             __syncthreads();
         }
+        // the bias at this thread's channels, all requested at once (range-checked
+        // loads with no branch; a missing bias reads zero)
+        const auto rbias = make_rsrc(p.fe.bias ? (const void*)(p.fe.bias + (int64_t)h * D)
+                                               : (const void*)p.fe.b,
+                                     p.fe.bias ? (uint32_t)(D * 4) : 0u);
+        float bias[NTW];
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+            bias[i] = buffer_load<float>(rbias, (uint32_t)(16 * (NTW * (w >> 2) + i) + (lane & 15)) * 4);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int ct = NTW * (w >> 2) + i;
-            const int ch = 16 * ct + (lane & 15);
-            const float bias = p.fe.bias ? p.fe.bias[h * D + ch] : 0.f;
+            const int ch = 16 * (NTW * (w >> 2) + i) + (lane & 15);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.u.fe.G[16 * tb + 4 * (lane >> 4) + e][ch] = acc[i][e] + bias;
+            for (int e = 0; e < 4; ++e)
+                sm.u.fe.G[16 * tb + 4 * (lane >> 4) + e][ch] = acc[i][e] + bias[i];
         }
     }
     __syncthreads();
