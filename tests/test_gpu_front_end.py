@@ -252,6 +252,68 @@ def test_decode_front_end_matches_oracle(lib, oracle, io, d):
     assert maxerr(host(st), st_ref) <= TOL[io]
 
 
+@pytest.mark.parametrize("io,d,W,silu,r,with_state,per_head_g", [
+    ("bf16", 128, 1, False, 0, True, False),    # width 1 (no conv state), g given
+    ("bf16", 128, 2, True, 96, True, False),    # a rank above 64 (the wider gate kernel)
+    ("bf16", 128, 4, True, 128, False, False),  # no conv state: the history reads zero
+    ("bf16", 128, 0, False, 64, False, False),  # the gate alone
+    ("bf16", 128, 4, True, 0, True, True),      # the convolution with the per-head gate
+    ("bf16", 64, 3, True, 32, True, False),
+    ("fp32", 64, 2, False, 128, True, False),
+])
+def test_decode_front_end_options(lib, oracle, io, d, W, silu, r, with_state, per_head_g):
+    """Decode steps across the front end's options: every filter width, ranks on
+    both sides of 64, with and without an input conv state, a given g (per
+    channel or per head) against the oracle step by step; the conv state, when
+    given, is advanced in place exactly."""
+    from kda_inputs import make_decode, make_front_end
+    N, H, steps = 4, 3, 3
+    w = make_decode(N, H, d, io, steps=steps, seed=140 + W + r, device="cuda",
+                    scalar_gate=per_head_g)
+    fe = make_front_end(N * steps, N, H, d, io, width=W, rank=r, bias_std=0.3,
+                        seed=141 + W + r, device="cuda")
+    say(f"decode front end {io} d={d} W={W} silu={silu} r={r} state={with_state} "
+        f"per_head_g={per_head_g}")
+    st = w["state"].clone()
+    st_ref = host(w["state"]).astype(np.float64)
+    cst = fe["conv_state"].clone() if (W > 0 and with_state) else None
+    cst_ref = host(cst).astype(np.float64) if cst is not None else None
+    wq = host(fe["conv_weight"]) if W > 0 else None
+    for s in range(steps):
+        a_s = fe["gate_a"][s * N:(s + 1) * N].contiguous() if r else None
+        o = lib.kda_decode_step_ex(w["q"][s], w["k"][s], w["v"][s], None if r else w["g"][s],
+                                   w["beta"][s], st, conv_weight=fe.get("conv_weight"),
+                                   conv_silu=silu, conv_state=cst, gate_a=a_s,
+                                   gate_b=fe.get("gate_b"), gate_bias=fe.get("gate_bias"))
+        torch.cuda.synchronize()
+        xs = []
+        for xi, name in enumerate(("q", "k", "v")):
+            if W == 0:
+                xs.append(host(w[name][s]).astype(np.float64))
+                continue
+            # one token per sequence: cu = 0, 1, ..., N
+            y, f = oracle.short_conv(host(w[name][s]), np.transpose(wq[xi], (0, 2, 1)),
+                                     cu_seqlens=np.arange(N + 1),
+                                     state=None if cst_ref is None else cst_ref[:, xi],
+                                     silu=silu)
+            if cst_ref is not None:
+                cst_ref[:, xi] = f
+            xs.append(y)
+        if r:
+            g = oracle.low_rank_gate(host(a_s), host(fe["gate_b"]), host(fe["gate_bias"]))
+        else:
+            g = host(w["g"][s])
+            if per_head_g:
+                g = np.repeat(g[:, :, None], d, axis=2)
+        o_ref = oracle.decode_step(xs[0], xs[1], xs[2], g, host(w["beta"][s]), st_ref)
+        e = maxerr(host(o), o_ref)
+        say(f"  step {s}: err={e:.3e}")
+        assert e <= TOL[io]
+        if cst is not None:
+            assert np.array_equal(host(cst), cst_ref)
+    assert maxerr(host(st), st_ref) <= TOL[io]
+
+
 def test_front_end_with_output_gate_and_checkpoints(lib, oracle):
     """Every prefill option in one call on two packed sequences: front end (W = 4
     + SiLU, rank 64), output gate per head and a checkpoint every chunk, against
