@@ -143,8 +143,11 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
     // Output-gate pre-activations of this chunk's rows, requested before any
     // other load of the step: a load completes only after every load issued
     // before it, so z asked for here is not held up by the operand refills
-    // below.  Rows past the sequence's end read as zero (range-checked).
-    T zv[NB][4];
+    // below.  Rows past the sequence's end read as zero (range-checked).  Each
+    // is held as its own 32-bit word (16-bit values zero-extended by the load):
+    // packing two 16-bit values into one register needs them at once, which
+    // would wait for every load in flight, the refills of later chunks included.
+    uint32_t zv[NB][4];
     if constexpr (OG) {
         if (!c.uwave) {
             const int64_t zs = p.og_per_head ? c.H : c.H * D;  // elements between tokens
@@ -160,7 +163,11 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 16 * c.b + 4 * (lane >> 4) + e;
-                    zv[nb][e] = buffer_load<T>(zr, (uint32_t)row * zrow + (uint32_t)col * zcol);
+                    const uint32_t off = (uint32_t)row * zrow + (uint32_t)col * zcol;
+                    if constexpr (sizeof(T) == 2)
+                        zv[nb][e] = (uint32_t)__builtin_bit_cast(uint16_t, buffer_load<uint16_t>(zr, off));
+                    else
+                        zv[nb][e] = __builtin_bit_cast(uint32_t, buffer_load<float>(zr, off));
                 }
             }
         }
@@ -259,6 +266,16 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
         }
     }
     if (!c.uwave) {
+        if constexpr (OG) {
+            // the gate's arithmetic needs only z: pin it here, after the refills
+            // are issued (an empty asm that redefines z, ordered after every
+            // memory access above), so the scheduler cannot hoist it, and the
+            // wait for z, up to the z loads
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(zv[nb][e])::"memory");
+        }
         T* outp = reinterpret_cast<T*>(p.out);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -267,7 +284,11 @@ __device__ __forceinline__ void recur_step(RecurSmem<T, D, NT>& sm, f32x4 (&S)[N
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * c.b + 4 * (lane >> 4) + e;
                 float o = acc[nb][e];
-                if constexpr (OG) o *= __builtin_amdgcn_rcpf(1.f + __expf(-to_f32(zv[nb][e])));
+                if constexpr (OG) {
+                    // (a bf16 value is the high half of its fp32 word)
+                    const float z = __uint_as_float(sizeof(T) == 2 ? zv[nb][e] << 16 : zv[nb][e]);
+                    o *= __builtin_amdgcn_rcpf(1.f + __expf(-z));
+                }
                 if (row < Lc) outp[((tok0 + row) * c.H + c.h) * D + col] = from_f32<T>(o);
             }
         }
