@@ -101,7 +101,9 @@ typedef struct {
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes (0 on a
  * descriptor the library would reject).  The workspace holds the per-chunk
- * factors the chunk-prep kernel hands to the recurrence kernel. */
+ * factors the chunk-prep kernel hands to the recurrence kernel and, for a
+ * single sequence (num_seqs == 1), one fp32 state per head for a pipelined call
+ * (see kda_chunk_prefill). */
 size_t kda_prefill_workspace_bytes(const kda_dims* dims);
 
 /* Chunked prefill over packed sequences.
@@ -126,6 +128,20 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  *
  * Supported: d_k = d_v = 128 with bf16 I/O; d_k = d_v = 64 with bf16 or fp32
  * I/O (fp32 I/O at d = 128 returns KDA_ERR_UNSUPPORTED); T_total < 2^31.
+ *
+ * Streams.  Every launch is ordered after the caller's earlier work on stream,
+ * and the caller's later work on stream is ordered after every launch of the
+ * call.  One long sequence (num_seqs == 1, at least 4 * 1024 chunks of 64
+ * tokens) whose recurrence leaves compute units idle (num_heads * d_v / 16
+ * below the device's compute units) is pipelined: the chunk preparation of
+ * later segments runs on a second stream that the library creates on the
+ * current device at its first such call (default priority, non-blocking, kept
+ * until the process ends), joined to stream by events, while the recurrence
+ * works through earlier segments on stream.  The results are bitwise those of
+ * the unpipelined path.  The first pipelined call on a device must not be made
+ * under stream capture (it creates that stream); later calls may be captured.
+ * Concurrent calls on one device share the second stream; each call's own
+ * events keep its launches ordered.
  *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Inside a 64-token chunk the

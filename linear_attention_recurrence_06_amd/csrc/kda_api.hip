@@ -1,6 +1,10 @@
 // C ABI of libkda.so: argument validation, workspace sizing and dispatch.
 // See include/kda.h for the contract.  Nothing here reads device memory or
 // synchronises; every launch goes on the caller's stream.
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
@@ -9,22 +13,144 @@ namespace kda {
 template <typename T, int D> hipError_t launch_prep(const PrefillArgs&, hipStream_t);
 template <typename T, int D> hipError_t launch_recur(const PrefillArgs&, hipStream_t);
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    hipError_t e;
-    if (a.bf16 && a.d == 128) {
-        if ((e = launch_prep<bf16, 128>(a, s)) != hipSuccess) return e;
-        return launch_recur<bf16, 128>(a, s);
-    }
-    if (a.bf16 && a.d == 64) {
-        if ((e = launch_prep<bf16, 64>(a, s)) != hipSuccess) return e;
-        return launch_recur<bf16, 64>(a, s);
-    }
-    if ((e = launch_prep<float, 64>(a, s)) != hipSuccess) return e;
+namespace {
+
+hipError_t launch_prep_any(const PrefillArgs& a, hipStream_t s) {
+    if (a.bf16 && a.d == 128) return launch_prep<bf16, 128>(a, s);
+    if (a.bf16 && a.d == 64) return launch_prep<bf16, 64>(a, s);
+    return launch_prep<float, 64>(a, s);
+}
+
+hipError_t launch_recur_any(const PrefillArgs& a, hipStream_t s) {
+    if (a.bf16 && a.d == 128) return launch_recur<bf16, 128>(a, s);
+    if (a.bf16 && a.d == 64) return launch_recur<bf16, 64>(a, s);
     return launch_recur<float, 64>(a, s);
+}
+
+// The library's second stream on the current device (default priority, not
+// synchronising with the null stream), created on first use and kept until the
+// process ends.
+hipError_t aux_stream(hipStream_t* out) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            streams[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
+
+// Chunks per pipeline segment (at least) and segments per call (at least and
+// at most).  Each segment restarts the recurrence's chains and the first
+// segment's preparation runs alone, so short segments or few of them cost more
+// than the overlap saves (measured: 8,192 tokens x 16 heads in 2 segments +13%,
+// 32,768 x 16 in 8 segments +3%; 2^20 x 16 in 16 segments -9%).
+constexpr int64_t kSegChunks = 1024;
+constexpr int kMinSegments = 4;
+constexpr int kMaxSegments = 16;
+
+// Segments for a pipelined call, or 0 for one launch of each kernel.  One
+// sequence whose recurrence workgroups (one per head and 16-column tile) leave
+// compute units idle: the preparation of later chunks then runs on those units
+// while the recurrence works through earlier ones.
+int pipeline_segments(const PrefillArgs& a) {
+    if (a.n_seqs != 1 || a.total_tokens <= 0 || a.compute_units <= 0) return 0;
+    if ((int64_t)a.n_heads * (a.d / 16) >= a.compute_units) return 0;
+    const int64_t nch = (a.total_tokens + 63) / 64;
+    if (nch < kMinSegments * kSegChunks) return 0;
+    return (int)std::min<int64_t>(kMaxSegments, nch / kSegChunks);
+}
+
+// Pipelined prefill of one sequence in S segments of chunks.  The preparation
+// of segment i goes on the library's second stream, the recurrence over
+// segment i on the caller's stream after an event that marks the preparation
+// done; the fp32 state passes between segments through `state` (the caller's
+// final state, or the workspace).  The caller's stream has every launch of the
+// call behind it when this returns, so its later work is ordered after all of
+// them, and the second stream starts only after the caller's earlier work.
+hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S, float* state) {
+    const int64_t nch = (a0.total_tokens + 63) / 64;
+    hipStream_t s2;
+    hipError_t e = aux_stream(&s2);
+    if (e != hipSuccess) return e;
+    hipEvent_t ev[kMaxSegments + 1];
+    int made = 0;
+    for (; made <= S; ++made)
+        if ((e = hipEventCreateWithFlags(&ev[made], hipEventDisableTiming)) != hipSuccess) break;
+    if (e == hipSuccess) e = hipEventRecord(ev[S], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev[S], 0);
+    for (int i = 0; i < S && e == hipSuccess; ++i) {
+        PrefillArgs a = a0;
+        a.slot_begin = nch * i / S;
+        a.slot_end = i == S - 1 ? -1 : nch * (i + 1) / S;
+        a.prep_setup = i == 0;
+        if ((e = launch_prep_any(a, s2)) == hipSuccess) e = hipEventRecord(ev[i], s2);
+    }
+    for (int i = 0; i < S && e == hipSuccess; ++i) {
+        if ((e = hipStreamWaitEvent(s, ev[i], 0)) != hipSuccess) break;
+        PrefillArgs a = a0;
+        a.chunk_begin = nch * i / S;
+        a.chunk_end = nch * (i + 1) / S;
+        a.initial_state = i == 0 ? a0.initial_state : state;
+        a.final_state = i == S - 1 ? a0.final_state : state;
+        e = launch_recur_any(a, s);
+    }
+    // (events still pending are released once they complete)
+    for (int i = 0; i < made; ++i) {
+        const hipError_t d = hipEventDestroy(ev[i]);
+        if (e == hipSuccess) e = d;
+    }
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    const int S = pipeline_segments(a);
+    if (S >= 2) {
+        float* state = a.final_state ? a.final_state
+                                     : reinterpret_cast<float*>(a.workspace + a.layout.state_offset());
+        return launch_prefill_pipelined(a, s, S, state);
+    }
+    hipError_t e = launch_prep_any(a, s);
+    if (e != hipSuccess) return e;
+    return launch_recur_any(a, s);
 }
 }  // namespace kda
 
 namespace {
+
+// Compute units of the current device, queried once per device (a benign race:
+// every thread stores the same value).
+hipError_t compute_units(int32_t* out) {
+    static std::atomic<int32_t> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) n = 1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
+}
 
 bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -254,6 +380,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.out_gate_z = out_gate_z;
     a.fe = fe;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
+    if (compute_units(&a.compute_units) != hipSuccess) return KDA_ERR_HIP;
     hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -70,7 +70,10 @@ struct PrefillLayout {
     __host__ __device__ size_t ckidx_offset() const { return index_bytes; }
     __host__ __device__ size_t desc_offset() const { return 2 * index_bytes; }
     __host__ __device__ size_t records_offset() const { return 2 * index_bytes + desc_bytes; }
-    size_t total() const { return records_offset() + rec_bytes * (size_t)slots * (size_t)heads; }
+    size_t state_bytes;    // fp32 state of every chain between pipeline segments (one sequence)
+    size_t records_bytes() const { return rec_bytes * (size_t)slots * (size_t)heads; }
+    size_t state_offset() const { return records_offset() + records_bytes(); }
+    size_t total() const { return state_offset() + state_bytes; }
 };
 
 inline PrefillLayout make_layout(int d, int elt, int64_t total_tokens, int64_t n_seqs,
@@ -95,6 +98,7 @@ inline PrefillLayout make_layout(int d, int elt, int64_t total_tokens, int64_t n
     L.off_u = o;  o += (size_t)64 * d * elt;
     L.off_gc = o; o += (size_t)d * 4;
     L.rec_bytes = o;
+    L.state_bytes = n_seqs == 1 ? (size_t)heads * d * d * 4 : 0;
     return L;
 }
 
@@ -117,6 +121,15 @@ struct PrefillArgs {
     const void* out_gate_z;
     FrontEnd fe;
     PrefillLayout layout;
+    // Part of the work one launch pair covers (the whole call by default): the
+    // preparation kernel takes chunk slots [slot_begin, slot_end) and runs the
+    // index / descriptor / conv-state kernels only with prep_setup; the
+    // recurrence takes chunks [chunk_begin, chunk_end) of every chain, reading
+    // initial_state and writing final_state at that range's ends.
+    int64_t slot_begin = 0, slot_end = -1;
+    bool prep_setup = true;
+    int64_t chunk_begin = 0, chunk_end = INT64_MAX;
+    int32_t compute_units = 0;   // of the launching device (0: unknown, no pipeline)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

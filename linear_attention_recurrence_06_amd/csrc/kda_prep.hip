@@ -181,6 +181,7 @@ struct PrepParams {
     int l2norm;
     PrefillLayout L;
     PrepFE fe;
+    int64_t slot_begin;  // first chunk slot of this launch (item i: slot slot_begin + i / H)
 };
 
 // (first token, length) of a chunk slot; length 0 marks an unused slot.
@@ -873,8 +874,9 @@ __global__ __launch_bounds__(512, 4) void prep_fe_kernel(PrepParams p) {
     const int t = threadIdx.x;
     const uint32_t H = (uint32_t)p.n_heads;
     const uint32_t item = blockIdx.x;
-    const uint32_t slot = item / H;
-    const int h = (int)(item - slot * H);
+    const uint32_t ls = item / H;
+    const int h = (int)(item - ls * H);
+    const int64_t slot = p.slot_begin + ls;
     const int2 d = slot_desc(p, slot);
     if (d.y <= 0) return;
     int64_t n, s_begin;
@@ -930,8 +932,9 @@ __global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
     const int t = threadIdx.x;
     const uint32_t H = (uint32_t)p.n_heads;
     const uint32_t item = blockIdx.x;  // the grid is one workgroup per item
-    const uint32_t slot = item / H;
-    const int h = (int)(item - slot * H);
+    const uint32_t ls = item / H;
+    const int h = (int)(item - ls * H);
+    const int64_t slot = p.slot_begin + ls;
     const int2 d = slot_desc(p, slot);
     if (d.y <= 0) return;
     RawRows<T, D, SG> raw;
@@ -1020,16 +1023,18 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     p.L = a.layout;
+    const int64_t s_end = a.slot_end < 0 ? a.layout.slots : a.slot_end;
+    p.slot_begin = a.slot_begin;
     int32_t* cf = reinterpret_cast<int32_t*>(a.workspace);
     int32_t* ck = reinterpret_cast<int32_t*>(a.workspace + a.layout.ckidx_offset());
     hipError_t e;
-    if (a.cu_seqlens) {
+    if (a.prep_setup && a.cu_seqlens) {
         // equal lengths need no index: the recurrence derives it
         hipLaunchKernelGGL((chunk_index_kernel), dim3(1), dim3(256), 0, stream, a.cu_seqlens,
                            a.n_seqs, a.total_tokens, cf, ck, a.ckpt_interval);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (a.fe.active() && a.fe.conv_w > 1 && a.fe.state_out) {
+    if (a.prep_setup && a.fe.active() && a.fe.conv_w > 1 && a.fe.state_out) {
         // final conv states (also for sequences without tokens)
         p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
                       a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
@@ -1039,14 +1044,15 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.total_tokens == 0) return hipSuccess;
-    if (a.cu_seqlens) {
+    if (a.prep_setup && a.cu_seqlens) {
         const unsigned nb = (unsigned)((a.layout.slots + 255) / 256);
         hipLaunchKernelGGL((chunk_desc_kernel), dim3(nb), dim3(256), 0, stream, a.cu_seqlens,
                            a.n_seqs, cf, a.layout.slots,
                            reinterpret_cast<int2*>(a.workspace + a.layout.desc_offset()));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t items = a.layout.slots * a.n_heads;
+    const int64_t items = (s_end - a.slot_begin) * a.n_heads;
+    if (items <= 0) return hipSuccess;
     if (a.fe.active()) {
         p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
                       a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};

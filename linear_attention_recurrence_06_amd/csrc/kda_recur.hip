@@ -58,6 +58,8 @@ struct RecurParams {
     int32_t n_seqs, n_heads, ntiles;
     int32_t ckpt_interval;  // chunks between checkpoints (checkpointing variant only)
     int32_t og_per_head;    // gated variant: 1 z [T, H], 0 z [T, H, d]
+    int64_t chunk_begin;    // chunks [chunk_begin, chunk_end) of every chain; init is the
+    int64_t chunk_end;      // state before chunk_begin, fin the state after the range
     PrefillLayout L;
 };
 
@@ -111,7 +113,8 @@ struct WaveOps {
 struct WaveCtx {
     const unsigned char* rec0;  // record of the chain's first chunk
     size_t rec_bytes;
-    int64_t last;               // index of the last chunk
+    int64_t last;               // index of the sequence's last chunk
+    int64_t rlast;              // index of the last chunk of this launch's range
     int64_t s_begin;            // first token of the sequence
     int64_t s_len;
     int64_t H;
@@ -122,7 +125,7 @@ struct WaveCtx {
     bool zpf_wave;              // the wave that touches z lines ahead (gated variant)
     bool uwave, has_rows;
     __device__ __forceinline__ const unsigned char* rec(int64_t kc) const {
-        return rec0 + (size_t)min(kc, last) * rec_bytes;
+        return rec0 + (size_t)min(kc, rlast) * rec_bytes;
     }
 };
 
@@ -324,6 +327,10 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     c.s_len = p.cu ? (int64_t)p.cu[n + 1] - c.s_begin : each;
     const int64_t nch = (c.s_len + 63) / 64;
     c.last = nch > 0 ? nch - 1 : 0;
+    // this launch's chunks; records past the range (possibly not yet written)
+    // are never read: the operand refills clamp to its last chunk
+    const int64_t kb = min(p.chunk_begin, nch), ke = min(p.chunk_end, nch);
+    c.rlast = ke > kb ? ke - 1 : 0;
     c.rec_bytes = p.L.rec_bytes;
     // first chunk slot and first checkpoint of the sequence: from the chunk
     // index for packed sequences, by arithmetic for equal lengths
@@ -388,9 +395,9 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     }
     __syncthreads();
 
-    if (nch > 0) {
+    if (ke > kb) {
         // NBUF named register buffers (an array of them defeats register
-        // promotion); chunk kc is consumed from buffer kc % NBUF
+        // promotion); chunk kb + j is consumed from buffer j % NBUF
         static_assert(NBUF >= 2 && NBUF <= 5, "prefetch depth");
         WaveOps<T, D, NT> b0, b1, b2, b3, b4;
         auto prime = [&](WaveOps<T, D, NT>& b, int64_t k) {
@@ -398,26 +405,26 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
             b.load_back(c.rec(k), p.L, c.uwave, c.b, c.rb, lane);
             if constexpr (PF > 0) b.pf = *reinterpret_cast<const uint32_t*>(c.rec(k + NBUF) + c.pf_off);
         };
-        prime(b0, 0);
-        prime(b1, 1);
-        if constexpr (NBUF > 2) prime(b2, 2);
-        if constexpr (NBUF > 3) prime(b3, 3);
-        if constexpr (NBUF > 4) prime(b4, 4);
-        int64_t kc = 0;
-        for (; kc + NBUF <= nch; kc += NBUF) {
+        prime(b0, kb);
+        prime(b1, kb + 1);
+        if constexpr (NBUF > 2) prime(b2, kb + 2);
+        if constexpr (NBUF > 3) prime(b3, kb + 3);
+        if constexpr (NBUF > 4) prime(b4, kb + 4);
+        int64_t kc = kb;
+        for (; kc + NBUF <= ke; kc += NBUF) {
             recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b0, p, c, kc);
             recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b1, p, c, kc + 1);
             if constexpr (NBUF > 2) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b2, p, c, kc + 2);
             if constexpr (NBUF > 3) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b3, p, c, kc + 3);
             if constexpr (NBUF > 4) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b4, p, c, kc + 4);
         }
-        if (kc < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b0, p, c, kc);
+        if (kc < ke) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b0, p, c, kc);
         if constexpr (NBUF > 2)
-            if (kc + 1 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b1, p, c, kc + 1);
+            if (kc + 1 < ke) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b1, p, c, kc + 1);
         if constexpr (NBUF > 3)
-            if (kc + 2 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b2, p, c, kc + 2);
+            if (kc + 2 < ke) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b2, p, c, kc + 2);
         if constexpr (NBUF > 4)
-            if (kc + 3 < nch) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b3, p, c, kc + 3);
+            if (kc + 3 < ke) recur_step<T, D, NT, NBUF, PF, CK, OG>(sm, S, b3, p, c, kc + 3);
     }
 
     if (p.fin && c.has_rows) {
@@ -461,6 +468,8 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     p.n_seqs = a.n_seqs;
     p.n_heads = a.n_heads;
     p.ntiles = D / NT;
+    p.chunk_begin = a.chunk_begin;
+    p.chunk_end = a.chunk_end;
     p.L = a.layout;
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t groups = (chains + 7) / 8;

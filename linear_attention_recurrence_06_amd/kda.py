@@ -156,6 +156,20 @@ def _stream_handle(stream, device) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _workspace(need: int, device, stream) -> torch.Tensor:
+    """The call's internal workspace.  torch hands freed memory on to later
+    work of the stream it was allocated on, so a workspace used on another
+    stream is recorded on that stream: its memory is not reused before the
+    call's kernels there are done."""
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(int(stream), device=device)
+        if s != torch.cuda.current_stream(device):
+            ws.record_stream(s)
+    return ws
+
+
 def make_dims(total_tokens: int, num_seqs: int, num_heads: int, d_k: int, d_v: int,
               io_dtype: int, scale: float = 1.0, qk_l2norm: bool = True,
               chunk: int = 64, gate: int = KDA_GATE_CHANNEL) -> kda_dims:
@@ -226,7 +240,7 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
     need = kda_prefill_workspace_bytes(dims)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, stream)
     rc = lib.kda_chunk_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
                                _ptr(final_state), _ptr(workspace), workspace.numel(),
@@ -302,7 +316,7 @@ def kda_chunk_prefill_checkpoints(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         raise ValueError(f"checkpoints must be [>= {C}, {H}, {dk}, {dv}] float32")
     need = kda_prefill_workspace_bytes(dims)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, stream)
     rc = lib.kda_chunk_prefill_checkpoints(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
@@ -458,7 +472,7 @@ def kda_chunk_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                ctypes.pointer(fe) if fe is not None else None)
     need = kda_prefill_workspace_bytes(dims)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = _workspace(need, dev, stream)
     rc = lib.kda_chunk_prefill_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
                                   _ptr(final_state), ctypes.byref(opts), _ptr(workspace),

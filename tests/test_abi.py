@@ -56,7 +56,13 @@ def test_workspace_bytes(kda):
     rec = (4 * 64 * 128 + 64 * 64) * 2 + 128 * 4
     slots = 8192 // 64 + 1
     desc = -(-slots * 8 // 256) * 256
-    assert ws == 2 * 256 + desc + rec * slots * 32
+    # plus, for one sequence, the fp32 state of every head (handed between the
+    # segments of a pipelined call)
+    assert ws == 2 * 256 + desc + rec * slots * 32 + 32 * 128 * 128 * 4
+    d2 = kda.make_dims(8192, 2, 32, 128, 128, kda.KDA_BF16)
+    slots2 = 8192 // 64 + 2
+    desc2 = -(-slots2 * 8 // 256) * 256
+    assert kda.kda_prefill_workspace_bytes(d2) == 2 * 256 + desc2 + rec * slots2 * 32
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 128, 128, kda.KDA_FP32)) == 0
