@@ -156,6 +156,12 @@ kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
                              void* out, float* final_state, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Segments a kda_chunk_prefill with these sizes is pipelined into on the
+ * current device (see Streams at kda_chunk_prefill): 0 for one launch of each
+ * kernel, S >= 4 for S segments, -1 for a descriptor the library would reject
+ * or a device that cannot be queried.  Reads no device memory. */
+int32_t kda_prefill_pipeline_segments(const kda_dims* dims);
+
 /* Number of intermediate states kda_chunk_prefill_checkpoints writes: for each
  * sequence of c = ceil(len / 64) chunks, floor((c - 1) / checkpoint_interval)
  * (none for an empty sequence).  host_cu_seqlens is HOST memory, int32 [N + 1]

@@ -212,6 +212,17 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
         .total();
 }
 
+int32_t kda_prefill_pipeline_segments(const kda_dims* d) {
+    if (check_dims(d, true) != KDA_OK) return -1;
+    kda::PrefillArgs a;
+    a.total_tokens = d->total_tokens;
+    a.n_seqs = d->num_seqs;
+    a.n_heads = d->num_heads;
+    a.d = d->d_k;
+    if (compute_units(&a.compute_units) != hipSuccess) return -1;
+    return kda::pipeline_segments(a);
+}
+
 }  // extern "C"
 
 namespace {

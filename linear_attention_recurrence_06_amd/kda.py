@@ -32,7 +32,8 @@ KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 #: every symbol include/kda.h declares
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
             "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_decode_step",
-            "kda_decode_step_ex", "kda_status_string", "kda_version")
+            "kda_decode_step_ex", "kda_status_string", "kda_version",
+            "kda_prefill_pipeline_segments")
 
 
 class kda_dims(ctypes.Structure):
@@ -130,6 +131,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ctypes.c_int
+    lib.kda_prefill_pipeline_segments.argtypes = [D]
+    lib.kda_prefill_pipeline_segments.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -184,6 +187,12 @@ def _gate(g: torch.Tensor, lead) -> int:
 
 def kda_prefill_workspace_bytes(dims: kda_dims) -> int:
     return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def kda_prefill_pipeline_segments(dims: kda_dims) -> int:
+    """Segments a prefill of these sizes is pipelined into on the current
+    device (0: one launch of each kernel; -1: rejected descriptor)."""
+    return int(load_library().kda_prefill_pipeline_segments(ctypes.byref(dims)))
 
 
 def _check_tensor(name, t, shape, dtype, device):

@@ -50,19 +50,30 @@ def two_seq(inp, T):
     return cu, s0_2
 
 
-@pytest.mark.parametrize("io,d,H", [("bf16", 128, 2), ("fp32", 64, 3)])
-def test_pipelined_equals_single_launch(lib, io, d, H):
+@pytest.mark.parametrize("io,d,H,packed,scalar", [("bf16", 128, 2, False, False),
+                                                  ("fp32", 64, 3, False, False),
+                                                  ("bf16", 128, 3, True, False),
+                                                  ("bf16", 64, 2, False, True)])
+def test_pipelined_equals_single_launch(lib, io, d, H, packed, scalar):
+    """packed: the one sequence given through cu_seqlens = [0, T] (the chunk
+    index path); scalar: the per-head gate g [T, H]."""
     from kda_inputs import make_prefill
-    inp = make_prefill([T_PIPE], H, d, io, g_scale=0.5, s0_std=0.02, seed=201, device="cuda")
-    say(f"pipeline {io} d={d} H={H} T={T_PIPE}")
+    inp = make_prefill([T_PIPE], H, d, io, g_scale=0.5, s0_std=0.02, seed=201, device="cuda",
+                       scalar_gate=scalar)
+    say(f"pipeline {io} d={d} H={H} T={T_PIPE} packed={packed} scalar_gate={scalar}")
+    cu1 = torch.tensor([0, T_PIPE], dtype=torch.int32, device="cuda") if packed else None
+    E = lib.kda.KDA_BF16 if io == "bf16" else lib.kda.KDA_FP32
+    # the call is pipelined (4 segments); the two-sequence form is not
+    assert lib.kda_prefill_pipeline_segments(lib.make_dims(T_PIPE, 1, H, d, d, E)) == 4
+    assert lib.kda_prefill_pipeline_segments(lib.make_dims(T_PIPE, 2, H, d, d, E)) == 0
     o_p, f_p = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                                     inp["initial_state"], None)
+                                     inp["initial_state"], cu1)
     cu, s0_2 = two_seq(inp, T_PIPE)
     o_r, f_r = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                      s0_2, cu)
     # no final state: the segments hand the state over through the workspace
     o_n, f_n = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                                     inp["initial_state"], None, output_final_state=False)
+                                     inp["initial_state"], cu1, output_final_state=False)
     torch.cuda.synchronize()
     assert f_n is None
     assert torch.equal(o_p, o_r) and torch.equal(f_p, f_r[:1])
@@ -72,7 +83,8 @@ def test_pipelined_equals_single_launch(lib, io, d, H):
 
 def test_pipelined_all_options(lib):
     """Front end (W = 4 + SiLU, rank-64 gate), output gate per channel and a
-    checkpoint every 512 chunks, pipelined against single-launch."""
+    checkpoint every 512 chunks, pipelined (the sequence given through
+    cu_seqlens = [0, T]) against single-launch."""
     from kda_inputs import make_front_end, make_out_gate, make_prefill
     H, d, T = 2, 128, T_PIPE
     inp = make_prefill([T], H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=202, device="cuda")
@@ -82,8 +94,9 @@ def test_pipelined_all_options(lib):
     common = dict(out_gate_z=z, checkpoint_interval=512, conv_weight=fe["conv_weight"],
                   conv_silu=True, output_conv_state=True, gate_a=fe["gate_a"],
                   gate_b=fe["gate_b"], gate_bias=fe["gate_bias"])
+    cu1 = torch.tensor([0, T], dtype=torch.int32, device="cuda")
     o_p, f_p, ck_p, cs_p = lib.kda_chunk_prefill_ex(
-        inp["q"], inp["k"], inp["v"], None, inp["beta"], inp["initial_state"], None,
+        inp["q"], inp["k"], inp["v"], None, inp["beta"], inp["initial_state"], cu1,
         conv_state_in=fe["conv_state"], **common)
     cu, s0_2 = two_seq(inp, T)
     cs_in2 = torch.cat([fe["conv_state"], torch.randn_like(fe["conv_state"].float())
@@ -97,6 +110,24 @@ def test_pipelined_all_options(lib):
     assert torch.equal(o_p, o_r) and torch.equal(f_p, f_r[:1])
     assert torch.equal(ck_p, ck_r)
     assert torch.equal(cs_p, cs_r[:1])
+
+
+def test_pipeline_segment_rule(lib):
+    """Segments as documented: min(16, chunks / 1024) when that is at least 4,
+    for one sequence whose H * d / 16 recurrence workgroups leave CUs idle."""
+    K = lib.kda
+    seg = lambda T, N, H, d=128: lib.kda_prefill_pipeline_segments(
+        lib.make_dims(T, N, H, d, d, K.KDA_BF16))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert seg(4095 * 64, 1, 2) == 0                  # 4,095 chunks
+    assert seg(4095 * 64 + 1, 1, 2) == 4              # 4,096 chunks (the last one partial)
+    assert seg(8191 * 64, 1, 2) == 7                  # 8,191 chunks: 7 whole 1,024-chunk segments
+    assert seg(1 << 20, 1, 16) == (16 if 16 * 8 < cus else 0)   # the million-token workload
+    assert seg(1 << 22, 1, 2) == 16                   # at most 16 segments
+    assert seg(8192, 1, 32) == 0                      # the 8,192-token workload: too short
+    assert seg(1 << 20, 1, cus // 8) == 0             # the recurrence fills every CU
+    assert seg(1 << 20, 2, 2) == 0                    # more than one sequence
+    assert seg(1 << 20, 1, 2, 96) == -1               # rejected descriptor
 
 
 def test_pipelined_in_place_and_on_a_side_stream(lib):
