@@ -12,8 +12,10 @@ timed between device synchronisations, with two HIP events on the launch stream
 around them giving the average call duration behind the roofline figure; a
 separate loop with events around each call gives the per-call spread.  In
 the same run the decode step is timed on 256 sequences x 32 heads (512 MiB
-fp32 state, advanced in place), and the fp64 oracle is timed on the host cores
-on the full prefill workload (repeated to ~10 s of CPU work).
+fp32 state, advanced in place), one pipelined prefill of a single 2^20-token
+sequence with 16 heads is timed as a secondary figure, and the fp64 oracle is
+timed on the host cores on the full prefill workload (repeated to ~10 s of CPU
+work).
 
 Prints one JSON line (rank 0, N = 1).
 """
@@ -258,6 +260,7 @@ def main():
         max(3, args.steps // 4))
     fe_bytes = p_bytes - 2 * D * T * H + 2 * 64 * T + 2 * H * D * 64
 
+
     # ------------------------------------------------------------------ decode
     dw = make_config_decode(3, device=dev, steps=args.decode_steps)
     state = dw["state"]
@@ -314,6 +317,24 @@ def main():
                                        gate_bias=fe_dec["gate_bias"], stream=stream),
         max(10, args.decode_steps // 4))
     del fe_dec
+
+    # one long sequence: 2^20 tokens x 16 heads, which the library pipelines over
+    # two streams (chunk prep of later segments beside the recurrence of earlier
+    # ones, since 16 heads x 8 column tiles leave half the CUs to the prep)
+    long_in = make_config_prefill(4, device=dev)
+    LT, LH = long_in["q"].shape[0], long_in["q"].shape[1]
+    l_dims = kda.make_dims(LT, 1, LH, D, D, 0)
+    l_ws = torch.empty(kda.kda_prefill_workspace_bytes(l_dims), dtype=torch.uint8, device=dev)
+    l_out = torch.empty((LT, LH, D), dtype=torch.bfloat16, device=dev)
+    l_fin = torch.empty((1, LH, D, D), dtype=torch.float32, device=dev)
+    long_us = median_call_us(
+        lambda: kda.kda_chunk_prefill(long_in["q"], long_in["k"], long_in["v"], long_in["g"],
+                                      long_in["beta"], long_in["initial_state"], None, l_out,
+                                      l_fin, workspace=l_ws, stream=stream),
+        2 if args.profile else 4)
+    long_segs = kda.kda_prefill_pipeline_segments(l_dims)
+    long_bytes = prefill_algorithmic_bytes(LT, LH, D)
+    del long_in, l_ws, l_out, l_fin
 
     # plain 1 GiB device-to-device copy: the practical HBM ceiling on this machine
     # (and, in --profile runs, the known-size transfer that scales the counters)
@@ -405,6 +426,14 @@ def main():
                                 "overhead_vs_plain_median":
                                     og_us / (float(np.median(call_ms)) * 1e3) - 1.0,
                                 "algorithmic_bytes_per_call": p_bytes + T * H * D * 2},
+        "prefill_long": {
+            "workload": f"one sequence T={LT} H={LH} d={D} bf16 (million-token prefill)",
+            "pipeline_segments": long_segs,
+            "median_call_ms": long_us / 1e3,
+            "tokens_per_s": LT / (long_us * 1e-6),
+            "algorithmic_bytes_per_call": long_bytes,
+            "achieved_GBps": long_bytes / (long_us * 1e-6) / 1e9,
+        },
         "prefill_front_end": {"front_end": "raw q, k, v through a width-4 causal "
                                             "convolution + SiLU; g = -softplus(a b^T + bias), "
                                             "rank 64 (no g read)",

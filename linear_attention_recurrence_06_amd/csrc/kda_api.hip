@@ -88,12 +88,14 @@ hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S,
         if ((e = hipEventCreateWithFlags(&ev[made], hipEventDisableTiming)) != hipSuccess) break;
     if (e == hipSuccess) e = hipEventRecord(ev[S], s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev[S], 0);
+    int recorded = 0;  // K1 segments launched and marked on the second stream
     for (int i = 0; i < S && e == hipSuccess; ++i) {
         PrefillArgs a = a0;
         a.slot_begin = nch * i / S;
         a.slot_end = i == S - 1 ? -1 : nch * (i + 1) / S;
         a.prep_setup = i == 0;
-        if ((e = launch_prep_any(a, s2)) == hipSuccess) e = hipEventRecord(ev[i], s2);
+        if ((e = launch_prep_any(a, s2)) == hipSuccess && (e = hipEventRecord(ev[i], s2)) == hipSuccess)
+            recorded = i + 1;
     }
     for (int i = 0; i < S && e == hipSuccess; ++i) {
         if ((e = hipStreamWaitEvent(s, ev[i], 0)) != hipSuccess) break;
@@ -104,6 +106,9 @@ hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S,
         a.final_state = i == S - 1 ? a0.final_state : state;
         e = launch_recur_any(a, s);
     }
+    // after a failure, still keep the caller's stream behind everything the
+    // second stream has queued, so no work of this call outlives it there
+    if (e != hipSuccess && recorded > 0) (void)hipStreamWaitEvent(s, ev[recorded - 1], 0);
     // (events still pending are released once they complete)
     for (int i = 0; i < made; ++i) {
         const hipError_t d = hipEventDestroy(ev[i]);
