@@ -138,10 +138,10 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * current device at its first such call (default priority, non-blocking, kept
  * until the process ends), joined to stream by events, while the recurrence
  * works through earlier segments on stream.  The results are bitwise those of
- * the unpipelined path.  The first pipelined call on a device must not be made
- * under stream capture (it creates that stream); later calls may be captured.
- * Concurrent calls on one device share the second stream; each call's own
- * events keep its launches ordered.
+ * the unpipelined path.  A call on a stream that is being captured into a graph
+ * is not pipelined: it launches only on that stream.  Concurrent calls on one
+ * device share the second stream; each call's own events keep its launches
+ * ordered.
  *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Inside a 64-token chunk the
@@ -157,7 +157,7 @@ kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
                              size_t workspace_bytes, void* stream);
 
 /* Segments a kda_chunk_prefill with these sizes is pipelined into on the
- * current device (see Streams at kda_chunk_prefill): 0 for one launch of each
+ * current device, outside stream capture (see Streams at kda_chunk_prefill): 0 for one launch of each
  * kernel, S >= 4 for S segments, -1 for a descriptor the library would reject
  * or a device that cannot be queried.  Reads no device memory. */
 int32_t kda_prefill_pipeline_segments(const kda_dims* dims);

@@ -120,7 +120,12 @@ hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S,
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    const int S = pipeline_segments(a);
+    // under stream capture the call stays on the caller's stream: no library
+    // stream or events enter the caller's graph (the results are the same)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e0 = hipStreamIsCapturing(s, &cap);
+    if (e0 != hipSuccess) return e0;
+    const int S = cap == hipStreamCaptureStatusNone ? pipeline_segments(a) : 0;
     if (S >= 2) {
         float* state = a.final_state ? a.final_state
                                      : reinterpret_cast<float*>(a.workspace + a.layout.state_offset());

@@ -151,3 +151,39 @@ def test_pipelined_in_place_and_on_a_side_stream(lib):
     side.synchronize()
     assert torch.equal(out, o_ref) and torch.equal(st, f_ref)
     assert float(total) == float(o_ref.float().sum())
+
+
+@pytest.mark.parametrize("T,H", [(8192 + 37, 4), (T_PIPE, 2)])
+def test_prefill_replayed_from_a_graph(lib, T, H):
+    """A prefill captured into a graph (on a stream under capture the call is
+    not pipelined: it launches only on that stream) and replayed three times,
+    with eager work in between: every replay equals the eager call bit for bit."""
+    from kda_inputs import make_prefill
+    d = 128
+    inp = make_prefill([T], H, d, "bf16", g_scale=0.5, s0_std=0.02, seed=206, device="cuda")
+    o_ref, f_ref = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                         inp["initial_state"], None)
+    torch.cuda.synchronize()
+    dims = lib.make_dims(T, 1, H, d, d, lib.kda.KDA_BF16)
+    ws = torch.empty(lib.kda_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(o_ref)
+    fin = torch.empty_like(f_ref)
+    call = lambda: lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                         inp["initial_state"], None, out, fin, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        fin.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}: T={T} H={H}")
+        assert torch.equal(out, o_ref) and torch.equal(fin, f_ref)
