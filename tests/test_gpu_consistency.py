@@ -13,6 +13,8 @@
 * checkpointed prefill: every intermediate state against the oracle's final
   state of that prefix, bitwise equal to a prefill of the prefix alone, and the
   outputs unchanged.
+* decode steps captured into a graph and replayed over fresh tokens equal the
+  same steps run eagerly, bit for bit.
 """
 
 import sys
@@ -336,3 +338,51 @@ def test_checkpoints_config1(lib, oracle):
     e = maxerr(host(ck[:, hs].contiguous()), ref)
     say(f"config1 checkpoints: {ck.shape[0]} states, err {e:.3e}")
     assert ck.shape[0] == 7 and e <= TOL["bf16"]
+
+
+def test_decode_steps_replayed_from_a_graph(lib):
+    """Four decode steps captured into a graph once (static token buffers, the
+    state advanced in place) and replayed for three rounds of fresh tokens, with
+    eager copies in between: every round's outputs and state equal the same
+    steps run eagerly, bit for bit."""
+    from kda_inputs import make_decode
+    N, H, d, steps, rounds = 8, 4, 128, 4, 3
+    w = make_decode(N, H, d, "bf16", steps=steps * rounds, seed=41, device="cuda")
+    # eager reference
+    st_ref = w["state"].clone()
+    o_ref = []
+    for s in range(steps * rounds):
+        o_ref.append(lib.kda_decode_step(w["q"][s], w["k"][s], w["v"][s], w["g"][s],
+                                         w["beta"][s], st_ref))
+    torch.cuda.synchronize()
+    # static buffers for one round
+    bufs = {n: w[n][:steps].clone() for n in ("q", "k", "v", "g", "beta")}
+    outs = torch.empty((steps, N, H, d), dtype=torch.bfloat16, device="cuda")
+    st = w["state"].clone()
+
+    def round_():
+        for s in range(steps):
+            lib.kda_decode_step(bufs["q"][s], bufs["k"][s], bufs["v"][s], bufs["g"][s],
+                                bufs["beta"][s], st, outs[s])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        round_()                       # warm-up outside the graph (advances a scratch state)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    st.copy_(w["state"])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        round_()
+    torch.cuda.synchronize()
+    st.copy_(w["state"])               # capture does not run the steps
+    for r in range(rounds):
+        for n in bufs:
+            bufs[n].copy_(w[n][r * steps:(r + 1) * steps])
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s], o_ref[r * steps + s]), f"round {r} step {s}"
+        say(f"decode graph round {r}: outputs equal")
+    assert torch.equal(st, st_ref)
