@@ -445,9 +445,13 @@ constexpr int kRecurDepth = 3;
 // Chunks beyond those in flight whose records are touched early (L2 prefetch).
 constexpr int kRecurPrefetch = 1;
 
-// Column-tile width: the widest tile that still gives at least ~2 workgroups
-// per CU; 16 otherwise (fewest columns per chain, most chains).
-static int pick_tile(int64_t chains, int d, bool wide_ok) {
+// Column-tile width.  Every tile of a chain streams the same W, Qhat, M and
+// Kprime^T, so wider tiles read fewer operand bytes per column but give fewer
+// workgroups: 64 columns once that still leaves ~8 workgroups per CU (measured
+// -4% per call on 64 packed sequences x 32 heads against 32 columns; not with
+// the output gate), 32 while that leaves ~2, 16 otherwise.
+static int pick_tile(int64_t chains, int d, bool wide_ok, bool gated) {
+    if (wide_ok && !gated && chains * (d / 64) >= 2048) return 64;
     if (wide_ok && chains * (d / 32) >= 512) return 32;
     return 16;
 }
@@ -481,10 +485,16 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, false>), gd, bd, 0, stream, p);
     else if (ck && !og)
         hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, true, false>), gd, bd, 0, stream, p);
-    else if (!ck && og)
-        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, true>), gd, bd, 0, stream, p);
-    else
-        hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, true, true>), gd, bd, 0, stream, p);
+    else if constexpr (NT <= 32) {
+        // (the gated kernels hold one z word per output element: at 64 columns
+        // they would spill, so gated calls never take 64-column tiles)
+        if (!ck)
+            hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, true>), gd, bd, 0, stream, p);
+        else
+            hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, true, true>), gd, bd, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -492,8 +502,11 @@ template <typename T, int D>
 hipError_t launch_recur(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     if (chains == 0) return hipSuccess;
-    if constexpr (sizeof(T) == 2)
-        if (pick_tile(chains, D, true) == 32) return launch_nt<T, D, 32>(a, stream);
+    if constexpr (sizeof(T) == 2) {
+        const int nt = pick_tile(chains, D, true, a.out_gate != 0);
+        if (nt == 64) return launch_nt<T, D, 64>(a, stream);
+        if (nt == 32) return launch_nt<T, D, 32>(a, stream);
+    }
     return launch_nt<T, D, 16>(a, stream);
 }
 

@@ -260,6 +260,43 @@ def test_many_short_sequences(lib, oracle):
     assert torch.equal(f[5], inp["initial_state"][5])
 
 
+@pytest.mark.parametrize("d,n_seqs", [(128, 600), (64, 520)])
+def test_wide_column_tiles(lib, oracle, d, n_seqs):
+    """Enough chains (sequences x 4 heads >= 2,048 / (d / 64)) that the
+    recurrence takes 64-column tiles: ragged packed sequences of 0..200 tokens
+    against the oracle."""
+    from kda_inputs import make_prefill
+    rng = np.random.default_rng(44 + d)
+    lens = rng.integers(0, 201, size=n_seqs).tolist()
+    lens[3] = 0
+    inp = make_prefill(lens, 4, d, "bf16", g_scale=0.5, s0_std=0.02, seed=44, device="cuda")
+    o, f = prefill(lib, inp)
+    o_ref, f_ref = oracle_prefill(oracle, inp)
+    eo, ef = maxerr(host(o), o_ref), maxerr(host(f), f_ref)
+    say(f"{n_seqs} sequences x 4 heads d={d} ({sum(lens)} tokens): err_out={eo:.3e} err_state={ef:.3e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+    assert torch.equal(f[3], inp["initial_state"][3])
+    # checkpoints (the checkpointing 64-column kernel): every prefix state against
+    # the oracle, and the plain outputs unchanged bit for bit
+    out_c, fin_c, ck = lib.kda_chunk_prefill_checkpoints(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], checkpoint_interval=1)
+    torch.cuda.synchronize()
+    ref = _prefix_oracle_states(oracle, inp, lens, 1)
+    assert ck.shape[0] == ref.shape[0] > 0
+    assert maxerr(host(ck), ref) <= TOL["bf16"]
+    assert torch.equal(out_c, o) and torch.equal(fin_c, f)
+    # the output gate (which keeps 32-column tiles) against the oracle's gated read-out
+    from kda_inputs import make_out_gate
+    z = make_out_gate((sum(lens), 4), "bf16", seed=45, device="cuda")
+    out_g, fin_g, _, _ = lib.kda_chunk_prefill_ex(
+        inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+        inp["cu_seqlens"], out_gate_z=z)
+    torch.cuda.synchronize()
+    assert maxerr(host(out_g), oracle.apply_output_gate(o_ref, host(z))) <= TOL["bf16"]
+    assert torch.equal(fin_g, f)
+
+
 # ----------------------------------------------------------------------------- checkpoints
 def _prefix_oracle_states(oracle, inp, lens, interval, heads=None):
     """Oracle final states of every checkpointed prefix: sequence n, prefix
