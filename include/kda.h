@@ -48,9 +48,13 @@
  * the library does not check.  For full prefill accuracy, per-token decay
  * should also satisfy g >= -5 in every channel; see kda_chunk_prefill.
  *
- * Thread safety and determinism: the library is stateless and reentrant.  The
- * kernels use no atomics, so identical inputs and sizes give bitwise identical
- * results.
+ * Thread safety and determinism: calls are reentrant.  The library's only
+ * state is, per device, the compute-unit count (queried once, cached
+ * atomically) and the second stream of the pipelined prefill (see
+ * kda_chunk_prefill; created once under a lock), both kept until the process
+ * ends; it holds no device memory.  The kernels use no
+ * atomics, so identical inputs and sizes give bitwise identical results (a
+ * pipelined call included).
  */
 #ifndef KDA_H
 #define KDA_H
