@@ -13,7 +13,8 @@ around them giving the average call duration behind the roofline figure; a
 separate loop with events around each call gives the per-call spread.  In
 the same run the decode step is timed on 256 sequences x 32 heads (512 MiB
 fp32 state, advanced in place), one pipelined prefill of a single 2^20-token
-sequence with 16 heads is timed as a secondary figure, and the fp64 oracle is
+sequence with 16 heads and one packed batch of 64 sequences (about 1M tokens,
+32 heads) are timed as secondary figures, and the fp64 oracle is
 timed on the host cores on the full prefill workload (repeated to ~10 s of CPU
 work).
 
@@ -336,6 +337,24 @@ def main():
     long_bytes = prefill_algorithmic_bytes(LT, LH, D)
     del long_in, l_ws, l_out, l_fin
 
+    # 64 packed sequences of 1,024..32,768 tokens (about 1M tokens), 32 heads,
+    # each from its own initial state, final states for every sequence
+    var_in = make_config_prefill(2, device=dev)
+    VT, VH = var_in["q"].shape[0], var_in["q"].shape[1]
+    VN = var_in["cu_seqlens"].numel() - 1
+    v_dims = kda.make_dims(VT, VN, VH, D, D, 0)
+    v_ws = torch.empty(kda.kda_prefill_workspace_bytes(v_dims), dtype=torch.uint8, device=dev)
+    v_out = torch.empty((VT, VH, D), dtype=torch.bfloat16, device=dev)
+    v_fin = torch.empty((VN, VH, D, D), dtype=torch.float32, device=dev)
+    var_us = median_call_us(
+        lambda: kda.kda_chunk_prefill(var_in["q"], var_in["k"], var_in["v"], var_in["g"],
+                                      var_in["beta"], var_in["initial_state"],
+                                      var_in["cu_seqlens"], v_out, v_fin, workspace=v_ws,
+                                      stream=stream),
+        2 if args.profile else 4)
+    var_bytes = prefill_algorithmic_bytes(VT, VH, D, n_seqs=VN)
+    del var_in, v_ws, v_out, v_fin
+
     # plain 1 GiB device-to-device copy: the practical HBM ceiling on this machine
     # (and, in --profile runs, the known-size transfer that scales the counters)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -426,6 +445,13 @@ def main():
                                 "overhead_vs_plain_median":
                                     og_us / (float(np.median(call_ms)) * 1e3) - 1.0,
                                 "algorithmic_bytes_per_call": p_bytes + T * H * D * 2},
+        "prefill_varlen": {
+            "workload": f"{VN} packed sequences, {VT} tokens, H={VH} d={D} bf16 (varlen prefill)",
+            "median_call_ms": var_us / 1e3,
+            "tokens_per_s": VT / (var_us * 1e-6),
+            "algorithmic_bytes_per_call": var_bytes,
+            "achieved_GBps": var_bytes / (var_us * 1e-6) / 1e9,
+        },
         "prefill_long": {
             "workload": f"one sequence T={LT} H={LH} d={D} bf16 (million-token prefill)",
             "pipeline_segments": long_segs,
