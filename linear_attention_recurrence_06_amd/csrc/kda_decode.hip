@@ -11,10 +11,10 @@
 // the delta rule with a diagonal gate of "From KV Cache to Depth Attention:
 // The Bottlenecks Kimi K3 Had to Break", Technical Details, KDA bullet).
 //
-// Work split: one 256-thread workgroup per (sequence, head).  Thread t owns
-// value columns 4*(t % (D/4)) .. +3 of rows (t / (D/4)) + (256/(D/4)) * m, so
+// Work split: one 512-thread workgroup per (sequence, head).  Thread t owns
+// value columns 4*(t % (D/4)) .. +3 of rows (t / (D/4)) + (512/(D/4)) * m, so
 // each wave reads and writes whole 512-byte (D=128) state rows with 16-byte
-// accesses, every lane keeps its D*D/256 state values in registers between the
+// accesses, every lane keeps its D*D/512 state values in registers between the
 // read and the write, and the read-outs reduce over row groups with one
 // cross-lane step inside the wave and one LDS exchange across the four waves.
 // The kernel is bound by HBM: 2 * 4 * D*D bytes of state per unit.
@@ -113,8 +113,8 @@ __device__ __forceinline__ void fe_apply(const DecodeFE& fe, const FeOps<T, N>& 
 // FE: raw q, k, v go through the front end (and g, unless given, comes from
 // the low-rank gate); GR: the largest gate rank the instantiation serves (64
 // or 128), which sizes the gate's loads.
-template <typename T, int D, bool FE, int GR>
-__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
+template <typename T, int D, bool FE, int GR, int NTH>
+__global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
                                                      const T* __restrict__ g,
@@ -125,12 +125,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ og_z, int H,
                                                      DecodeFE fe) {
     constexpr int TPR = D / 4;       // threads per state row
-    constexpr int RG = 256 / TPR;    // row groups
+    constexpr int RG = NTH / TPR;    // row groups
+    constexpr int NW = NTH / kWave;  // waves
     constexpr int RPT = D / RG;      // rows per thread
     constexpr int EPL = D / kWave;   // vector elements per lane in the norm pass
-    constexpr int TPC = 256 / D;     // gate: threads per channel
+    constexpr int TPC = NTH / D;     // gate: threads per channel
     constexpr int NJ = GR / TPC / 8; // gate: fragments per thread
     static_assert(RPT * RG == D && EPL * kWave == D, "bad decode tiling");
+    // the gate's per-thread rank slice (rank / TPC, rank >= 32) must be whole fragments
+    static_assert(!FE || (32 / TPC) % 8 == 0, "front-end gate slice below one fragment");
 
     const int64_t unit = blockIdx.x;  // = n * H + h
     const int t = threadIdx.x;
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     const int h = (int)(unit - n * H);
 
     __shared__ float s_q[D], s_k[D], s_a[D], s_v[FE ? D : 1], s_qk;
-    __shared__ float s_red[4][TPR][8];
+    __shared__ float s_red[NW][TPR][8];
 
     // 0. front end: its operands are requested before the state, so their
     // arithmetic can start while the state streams in.  Wave 0 takes q and k
@@ -317,9 +320,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     float d[4], o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float vhat = (s_red[0][cq][j] + s_red[1][cq][j]) + (s_red[2][cq][j] + s_red[3][cq][j]);
-        const float yy = (s_red[0][cq][4 + j] + s_red[1][cq][4 + j]) +
-                         (s_red[2][cq][4 + j] + s_red[3][cq][4 + j]);
+        float vhat = 0.f, yy = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            vhat += s_red[w2][cq][j];
+            yy += s_red[w2][cq][4 + j];
+        }
         d[j] = b * (vj[j] - vhat);
         o[j] = yy + qk * d[j];
     }
@@ -345,6 +351,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     }
 }
 
+// Threads per (sequence, head) workgroup.  The plain step: eight waves, each
+// lane holding D*D/512 state values (32 at D = 128); measured 163 us per step
+// against 167.5 us with four waves, on 256 sequences x 32 heads.  The
+// front-end step keeps four waves: its gate gives each of the NTH/D threads of a
+// channel a whole number of 8-rank fragments only when NTH/D <= 32/8 at every
+// rank (32 and up), which 512 threads at D = 64 would break.
+constexpr int kDecodeThreads = 512;
+constexpr int kDecodeThreadsFE = 256;
+
 template <typename T, int D>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)a.n_seqs * a.n_heads;
@@ -352,19 +367,22 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
                 a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
     if (a.fe.active() && a.fe.rank > 64)
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 128>), dim3((unsigned)units), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 128, kDecodeThreadsFE>), dim3((unsigned)units),
+                           dim3(kDecodeThreadsFE), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
                            fe);
     else if (a.fe.active())
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 64>), dim3((unsigned)units), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 64, kDecodeThreadsFE>), dim3((unsigned)units),
+                           dim3(kDecodeThreadsFE), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
                            fe);
     else
-        hipLaunchKernelGGL((decode_kernel<T, D, false, 64>), dim3((unsigned)units), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, false, 64, kDecodeThreads>), dim3((unsigned)units),
+                           dim3(kDecodeThreads), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
