@@ -354,11 +354,13 @@ __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
 // Threads per (sequence, head) workgroup.  The plain step: eight waves, each
 // lane holding D*D/512 state values (32 at D = 128); measured 163 us per step
 // against 167.5 us with four waves, on 256 sequences x 32 heads.  The
-// front-end step keeps four waves: its gate gives each of the NTH/D threads of a
-// channel a whole number of 8-rank fragments only when NTH/D <= 32/8 at every
-// rank (32 and up), which 512 threads at D = 64 would break.
+// front-end step: eight waves at D = 128 (rank 128: 193 against 206 us; rank
+// 64: no change), four at D = 64, because its gate gives each of the NTH/D
+// threads of a channel a whole number of 8-rank fragments only when
+// NTH/D <= 32/8 at every rank (32 and up).
 constexpr int kDecodeThreads = 512;
-constexpr int kDecodeThreadsFE = 256;
+template <int D>
+constexpr int kDecodeThreadsFE = D == 128 ? 512 : 256;
 
 template <typename T, int D>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
@@ -367,15 +369,15 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
                 a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
     if (a.fe.active() && a.fe.rank > 64)
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 128, kDecodeThreadsFE>), dim3((unsigned)units),
-                           dim3(kDecodeThreadsFE), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 128, kDecodeThreadsFE<D>>), dim3((unsigned)units),
+                           dim3(kDecodeThreadsFE<D>), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
                            fe);
     else if (a.fe.active())
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 64, kDecodeThreadsFE>), dim3((unsigned)units),
-                           dim3(kDecodeThreadsFE), 0,
+        hipLaunchKernelGGL((decode_kernel<T, D, true, 64, kDecodeThreadsFE<D>>), dim3((unsigned)units),
+                           dim3(kDecodeThreadsFE<D>), 0,
                            stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
                            (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
                            a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
