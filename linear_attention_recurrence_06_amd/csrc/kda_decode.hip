@@ -113,7 +113,7 @@ __device__ __forceinline__ void fe_apply(const DecodeFE& fe, const FeOps<T, N>& 
 // FE: raw q, k, v go through the front end (and g, unless given, comes from
 // the low-rank gate); GR: the largest gate rank the instantiation serves (64
 // or 128), which sizes the gate's loads.
-template <typename T, int D, bool FE, int GR, int NTH>
+template <typename T, int D, bool FE, int GR, int NTH, bool OG>
 __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
@@ -180,6 +180,18 @@ __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
                 gb[j] = buffer_load_frag<T>(rb, in ? ((uint32_t)c * R + kk) * E : kFarOffset);
             }
             if (fe.bias) gbias = fe.bias[h * D + c];
+        }
+    }
+
+    // OG: the output-gate pre-activations of this thread's outputs (row group 0),
+    // requested before the state so that their latency hides under its stream
+    // (asked for after it, they held each workgroup up by an HBM round trip at
+    // its end: 175.5 against 161.6 us per step)
+    T zraw[4] = {};
+    if constexpr (OG) {
+        if (rg == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zraw[j] = out_gate == 2 ? og_z[unit] : og_z[unit * D + 4 * cq + j];
         }
     }
 
@@ -342,7 +354,13 @@ __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float oj = o[j];
-            if (out_gate) {  // out = o * sigmoid(z), z per value channel or per head
+            if constexpr (OG) {  // out = o * sigmoid(z), z per value channel or per head
+                const float zz = to_f32(zraw[j]);
+                oj *= __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+            } else if (out_gate) {
+                // (never taken: gated steps use the OG instantiation.  Kept so that
+                // the ungated kernel keeps the instruction schedule it was measured
+                // with; without it the step measured about 1% slower)
                 const float zz = to_f32(out_gate == 2 ? og_z[unit] : og_z[unit * D + 4 * cq + j]);
                 oj *= __builtin_amdgcn_rcpf(1.f + __expf(-zz));
             }
@@ -362,6 +380,20 @@ constexpr int kDecodeThreads = 512;
 template <int D>
 constexpr int kDecodeThreadsFE = D == 128 ? 512 : 256;
 
+template <typename T, int D, bool FE, int GR, int NTH>
+static void launch_one(const DecodeArgs& a, const DecodeFE& fe, int64_t units, hipStream_t stream) {
+    if (a.out_gate)
+        hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, true>), dim3((unsigned)units), dim3(NTH),
+                           0, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads, fe);
+    else
+        hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, false>), dim3((unsigned)units), dim3(NTH),
+                           0, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
+                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
+                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads, fe);
+}
+
 template <typename T, int D>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)a.n_seqs * a.n_heads;
@@ -369,26 +401,11 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
                 a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
     if (a.fe.active() && a.fe.rank > 64)
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 128, kDecodeThreadsFE<D>>), dim3((unsigned)units),
-                           dim3(kDecodeThreadsFE<D>), 0,
-                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
-                           fe);
+        launch_one<T, D, true, 128, kDecodeThreadsFE<D>>(a, fe, units, stream);
     else if (a.fe.active())
-        hipLaunchKernelGGL((decode_kernel<T, D, true, 64, kDecodeThreadsFE<D>>), dim3((unsigned)units),
-                           dim3(kDecodeThreadsFE<D>), 0,
-                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
-                           fe);
+        launch_one<T, D, true, 64, kDecodeThreadsFE<D>>(a, fe, units, stream);
     else
-        hipLaunchKernelGGL((decode_kernel<T, D, false, 64, kDecodeThreads>), dim3((unsigned)units),
-                           dim3(kDecodeThreads), 0,
-                           stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads,
-                           fe);
+        launch_one<T, D, false, 64, kDecodeThreads>(a, fe, units, stream);
     return hipGetLastError();
 }
 
