@@ -166,8 +166,12 @@ def _workspace(need: int, device, stream) -> torch.Tensor:
     call's kernels there are done."""
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     if stream is not None:
-        s = stream if isinstance(stream, torch.cuda.Stream) else \
-            torch.cuda.ExternalStream(int(stream), device=device)
+        if isinstance(stream, torch.cuda.Stream):
+            s = stream
+        elif int(stream) == 0:   # the null stream
+            s = torch.cuda.default_stream(device)
+        else:
+            s = torch.cuda.ExternalStream(int(stream), device=device)
         if s != torch.cuda.current_stream(device):
             ws.record_stream(s)
     return ws

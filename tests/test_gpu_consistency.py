@@ -423,3 +423,19 @@ def test_decode_steps_replayed_from_a_graph(lib):
             assert torch.equal(outs[s], o_ref[r * steps + s]), f"round {r} step {s}"
         say(f"decode graph round {r}: outputs equal")
     assert torch.equal(st, st_ref)
+
+
+def test_stream_given_as_a_handle(lib):
+    """The binding takes a stream as a torch stream or as a raw handle (0 for the
+    null stream): the same results either way, with the internal workspace kept
+    alive for the stream the call ran on."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([300, 77], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=46, device="cuda")
+    o_ref, f_ref = prefill(lib, inp)
+    side = torch.cuda.Stream()
+    for handle in (0, side.cuda_stream):
+        torch.cuda.synchronize()
+        o, f = lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     inp["initial_state"], inp["cu_seqlens"], stream=handle)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(f, f_ref), f"stream handle {handle}"
