@@ -11,12 +11,13 @@
 // the delta rule with a diagonal gate of "From KV Cache to Depth Attention:
 // The Bottlenecks Kimi K3 Had to Break", Technical Details, KDA bullet).
 //
-// Work split: one 512-thread workgroup per (sequence, head).  Thread t owns
-// value columns 4*(t % (D/4)) .. +3 of rows (t / (D/4)) + (512/(D/4)) * m, so
-// each wave reads and writes whole 512-byte (D=128) state rows with 16-byte
-// accesses, every lane keeps its D*D/512 state values in registers between the
+// Work split: one workgroup of NTH threads per (sequence, head) (512; 256 for
+// the front-end step at D = 64).  Thread t owns value columns 4*(t % (D/4)) ..
+// +3 of rows (t / (D/4)) + (NTH/(D/4)) * m, so each wave reads and writes whole
+// 512-byte (D=128) state rows with 16-byte accesses, every lane keeps its
+// D*D/NTH state values in registers between the
 // read and the write, and the read-outs reduce over row groups with one
-// cross-lane step inside the wave and one LDS exchange across the four waves.
+// cross-lane step inside the wave and one LDS exchange across the waves.
 // The kernel is bound by HBM: 2 * 4 * D*D bytes of state per unit.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
