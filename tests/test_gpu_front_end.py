@@ -353,3 +353,42 @@ def test_front_end_with_output_gate_and_checkpoints(lib, oracle):
                                    initial_state=s0[n:n + 1])
             assert maxerr(host(ck[idx]), fp[0]) <= TOL["bf16"]
             idx += 1
+
+
+@pytest.mark.parametrize("io,d,r,per_head_z", [("bf16", 128, 64, False), ("bf16", 128, 128, True),
+                                               ("fp32", 64, 64, False), ("fp32", 64, 128, True)])
+def test_decode_front_end_with_output_gate(lib, io, d, r, per_head_z):
+    """Decode steps with the front end (W = 4 + SiLU, low-rank gate) and the
+    output gate together (the gated front-end kernels) against the same steps
+    without the gate: the states and conv states are bitwise equal, and the
+    outputs equal the ungated ones times sigmoid(z)."""
+    from kda_inputs import make_decode, make_front_end, make_out_gate
+    N, H, steps = 8, 3, 3
+    w = make_decode(N, H, d, io, steps=steps, seed=150 + r, device="cuda")
+    fe = make_front_end(N * steps, N, H, d, io, width=4, rank=r, bias_std=0.3, seed=151 + r,
+                        device="cuda")
+    z = make_out_gate((steps, N, H) if per_head_z else (steps, N, H, d), io, seed=152,
+                      device="cuda")
+    runs = []
+    for gated in (False, True):
+        st = w["state"].clone()
+        cst = fe["conv_state"].clone()
+        outs = []
+        for s in range(steps):
+            outs.append(lib.kda_decode_step_ex(
+                w["q"][s], w["k"][s], w["v"][s], None, w["beta"][s], st,
+                out_gate_z=z[s] if gated else None, conv_weight=fe["conv_weight"],
+                conv_silu=True, conv_state=cst, gate_a=fe["gate_a"][s * N:(s + 1) * N].contiguous(),
+                gate_b=fe["gate_b"], gate_bias=fe["gate_bias"]))
+        torch.cuda.synchronize()
+        runs.append((outs, st, cst))
+    (o_u, st_u, cst_u), (o_g, st_g, cst_g) = runs
+    assert torch.equal(st_u, st_g) and torch.equal(cst_u, cst_g)
+    for s in range(steps):
+        zz = z[s].float()
+        if per_head_z:
+            zz = zz[..., None]
+        expect = host(o_u[s]).astype(np.float64) / (1.0 + np.exp(-host(zz).astype(np.float64)))
+        e = maxerr(host(o_g[s]), expect)
+        say(f"decode front end + output gate {io} d={d} r={r} per_head_z={per_head_z} step {s}: err={e:.3e}")
+        assert e <= TOL[io]
