@@ -24,8 +24,18 @@
 //     block (R, R):    e^(gamma_r - gamma_j) = E_r (F_j / D_R),  D_R = e^(rho_R - rho_{R-1})
 // so the products run on MFMA from three decayed copies of q and k (E-, E- and
 // F-scaled), the middle factor and 1/D_R applied per channel to the F-scaled
-// operand.  On diagonal blocks F_j / D_R stays below e^80 when every g >= -5,
-// the documented accuracy range.
+// operand.  Off the diagonal every factor is at most 1.  On a diagonal block
+// F_j / D_R can reach 1/D_R, so the factored form is used only while every
+// channel's block decay keeps 1/D_R <= 2^64; a block past that is computed
+// exactly instead, from its raw rows, with every factor at most 1: a pair
+// (r, j), j < r, of one 16-token block is split at the first bisection level
+// that separates them (halves of 8, 4, 2, 1 tokens), and with b the last token
+// of the left half at that level,
+//     e^(gamma_r - gamma_j) = e^(gamma_r - gamma_b) * e^(gamma_b - gamma_j),
+// both factors <= 1.  Each level is one masked MFMA product of row-scaled and
+// column-scaled copies of the block's rows, so any g <= 0 is handled.  Per-token
+// decay is floored at 2^-128 (g log2 e >= -128): a smaller retention makes no
+// difference to any fp32 result, and the floor bounds the in-block sums.
 //
 // Work split: one workgroup of 512 threads (8 waves) per (chunk slot, head);
 // the shared tiles fit in 80 KB, so two workgroups share a CU and one's
@@ -45,6 +55,7 @@
 //   P4 U = (T Diag(beta)) V and W^T = Khat^T (T Diag(beta))^T on MFMA, each
 //      written straight from the accumulators in the layout the recurrence reads.
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -81,16 +92,27 @@ __device__ __forceinline__ void mm16_lds(f32x4& acc, const float* A, int lda, co
     }
 }
 
+// One 16-token block's rows for the exact diagonal products: normalised q and
+// k (in the I/O type, as the MFMA reads them) and the in-block cumulative
+// log2-decay (fp32).
+template <typename T, int D>
+struct ExactRows {
+    static constexpr int P = 16 / sizeof(T);
+    T q[16][D + P];
+    T k[16][D + P];
+    float g[16][D + 4];
+};
+
+// Largest per-channel log2-decay of a 16-token block that the factored
+// diagonal products take (1/D_R <= 2^64); larger ones take the exact path.
+constexpr float kFactoredMaxLog2Decay = 64.f;
+// Floor of a token's log2-decay (retention >= 2^-128).
+constexpr float kMinLog2Decay = -128.f;
+
 template <typename T, int D>
 struct PrepSmem {
     static constexpr int P = 16 / sizeof(T);  // 16-byte row padding
     float A[64][68];  // beta-scaled strictly-lower A, then T = (I + A)^-1 in place
-    float tau[4][D];  // per-block total log-decay
-    // per-channel decay factors, rows: 0-3 e^(-tau_R); 4 e^(tau_1); 5 e^(tau_1+tau_2);
-    // 6 e^(tau_2); 7-10 e^(rho_{R-1}) (chunk start -> block R start); 11-14
-    // e^(rho_3 - rho_R) (block R end -> chunk end); 15 e^(rho_3) = Gamma_C
-    float fac[16][D];
-    float beta[64];
     union {
         float wsum[8][D];  // P0: per-wave sums of g
         struct {
@@ -115,6 +137,16 @@ struct PrepSmem {
             };
         } fe;
     } u;
+    int exact[4];     // block R's diagonal products take the exact path
+    float tau[4][D];  // per-block total log-decay
+    // per-channel decay factors, rows: 0-3 e^(-tau_R); 4 e^(tau_1); 5 e^(tau_1+tau_2);
+    // 6 e^(tau_2); 7-10 e^(rho_{R-1}) (chunk start -> block R start); 11-14
+    // e^(rho_3 - rho_R) (block R end -> chunk end); 15 e^(rho_3) = Gamma_C
+    float fac[16][D];
+    float beta[64];
+    // Between P0 and P1 on the exact path, A and u (adjacent, both unused then)
+    // hold the chunk's rows as four 16-token blocks.
+    __device__ ExactRows<T, D>* stage() { return reinterpret_cast<ExactRows<T, D>*>(&A[0][0]); }
 };
 
 // Block (R, J), J <= R, of A (beta-scaled, strictly lower; to LDS) and of M
@@ -353,6 +385,86 @@ __device__ __forceinline__ void rows_from_raw(const RawRows<T, D, SG>& raw, Item
     }
 }
 
+// Diagonal block (R, R) of A and M computed exactly (see the decay factoring
+// above) from the block's rows xr, by one wave.  Lane l holds token
+// t = l % 16 in both operand positions (A-operand rows and B-operand columns
+// are both lane % 16) and channel octet l / 16 of each 32-deep step.  At level
+// L (half size h = 16 >> L) a token in the right half of its 2h-group is a row
+// scaled by e^(gamma_t - gamma_b) and a token in the left half a column scaled
+// by e^(gamma_b - gamma_t); the level's product is kept only for its own pairs.
+// Level 0 is the diagonal r = j of M (factor 1).  M goes to the record; the
+// beta-scaled A values are returned (row 4 (l / 16) + e, column l % 16).
+template <typename T, int D>
+__device__ __forceinline__ void exact_diag_block(const ExactRows<T, D>& xr, const float* beta,
+                                                 T* Mg, int R, int lane, float (&a_out)[4]) {
+    constexpr int NKS = D / 32;
+    const int tk = lane & 15, oc = lane >> 4;
+    // every pair belongs to exactly one level, so each level's masked product
+    // is selected into the result rather than added
+    f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tm = {0.f, 0.f, 0.f, 0.f};
+    // (loops kept rolled: this path runs while the caller's rows are live)
+#pragma unroll 1
+    for (int L = 0; L <= 4; ++L) {
+        const int h = L == 0 ? 0 : (16 >> L);
+        const int within = L == 0 ? 0 : (tk & (2 * h - 1));
+        const bool right = L > 0 && within >= h;
+        const int b = L == 0 ? tk : tk - within + h - 1;  // reference token
+        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 8 * oc;
+            // per-channel factor of this token at this level (1 at level 0)
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gt = xr.g[tk][c0 + j], gb = xr.g[b][c0 + j];
+                // gamma decreases along the block, so the exponent is <= 0 (the
+                // clamp absorbs rounding in the cumulative sums)
+                f[j] = exp2_hw(fminf(right ? gt - gb : gb - gt, 0.f));
+            }
+            float x[8];
+            load8_f32<T>(&xr.k[tk][c0], x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= f[j];
+            const Frag<T> fk = make_frag<T>(x);  // k scaled by this token's factor
+            const Frag<T> zero = make_frag<T>({0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
+            load8_f32<T>(&xr.q[tk][c0], x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= f[j];
+            const Frag<T> fq = make_frag<T>(x);
+            // rows r carry the right-half tokens, columns j the left-half ones
+            // (level 0: every token in both places, for M's diagonal)
+            const bool as_row = L == 0 || right, as_col = L == 0 || !right;
+            if (L > 0) mma(aa, as_row ? fk : zero, as_col ? fk : zero);  // A[r][j]
+            mma(am, as_col ? fk : zero, as_row ? fq : zero);              // M^T[j][r]
+        }
+        // keep the level's own pairs: accumulator element e is (4 oc + e, tk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hi = 4 * oc + e;  // row of the accumulator tile
+            // A: (r, j) = (hi, tk); M^T: (j, r) = (hi, tk)
+            bool inA, inM;
+            if (L == 0) {
+                inA = false;
+                inM = hi == tk;
+            } else {
+                const int m2 = 2 * h - 1, sh = 5 - L;
+                inA = (hi >> sh) == (tk >> sh) && (hi & m2) >= h && (tk & m2) < h;
+                inM = (hi >> sh) == (tk >> sh) && (tk & m2) >= h && (hi & m2) < h;
+            }
+            ta[e] = inA ? aa[e] : ta[e];
+            tm[e] = inM ? am[e] : tm[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * oc + e;
+        a_out[e] = ta[e] * beta[16 * R + r];
+    }
+    const float m[4] = {tm[0], tm[1], tm[2], tm[3]};
+    store_n<T, 4>(Mg + aorder_index(16 * R + tk, 16 * R + 4 * oc, 64), m);
+}
+
 // Everything for one (chunk slot, head) item whose rows are in `rows`.
 template <typename T, int D>
 __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& sm, int64_t slot,
@@ -364,7 +476,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
     const int Rb = w >> 1;  // 16-token block of this thread's rows
     unsigned char* rec = p.ws + p.L.records_offset() + ((size_t)h * p.L.slots + slot) * p.L.rec_bytes;
 
-    // g is taken in base-2 units (g log2 e) from here on
+    // g is taken in base-2 units (g log2 e) from here on, floored at kMinLog2Decay
     float qf[2][CPT], kf[2][CPT], gf[2][CPT], bt[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -372,7 +484,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         for (int c = 0; c < CPT; ++c) {
             qf[i][c] = rows.q[i][c];
             kf[i][c] = rows.k[i][c];
-            gf[i][c] = rows.g[i][c] * 1.4426950408889634f;
+            gf[i][c] = fmaxf(rows.g[i][c] * 1.4426950408889634f, kMinLog2Decay);
         }
         bt[i] = rows.b[i];
     }
@@ -381,6 +493,7 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         if (cg == 0) sm.beta[2 * rg + i] = bt[i];
+    if (t < 4) sm.exact[t] = 0;
     // L2 norms over the 16 lanes that share a row
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -430,7 +543,10 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         for (int R = 0; R < 4; ++R) tb[R] = sm.u.wsum[2 * R][c] + sm.u.wsum[2 * R + 1][c];
         if (rbase == 0) {
 #pragma unroll
-            for (int R = 0; R < 4; ++R) sm.tau[R][c] = tb[R];
+            for (int R = 0; R < 4; ++R) {
+                sm.tau[R][c] = tb[R];
+                if (-tb[R] > kFactoredMaxLog2Decay) sm.exact[R] = 1;
+            }
         }
 #pragma unroll
         for (int i = 0; i < 16 / RSTEP; ++i) {
@@ -445,10 +561,57 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
             float arg = 0.f;
 #pragma unroll
             for (int R = 0; R < 4; ++R) arg += (lo <= R && R <= hi ? sg : 0.f) * tb[R];
-            sm.fac[row][c] = exp2_hw(arg);
+            // (rows 0-3 serve only the factored diagonal blocks, whose decay is
+            // at most kFactoredMaxLog2Decay; the clamp keeps the others finite)
+            sm.fac[row][c] = exp2_hw(row < 4 ? fminf(arg, kFactoredMaxLog2Decay) : arg);
         }
     }
     __syncthreads();
+
+    // ---------------------------------------------------------------- P0x
+    // diagonal blocks past the factored range: every thread parks its rows in
+    // the staging area (so they are not live meanwhile), wave R computes block
+    // R exactly, and the rows are read back.  q and k come back rounded to the
+    // I/O type, as every MFMA operand made from them is.
+    // (read as wave-uniform values, so the branches below are scalar)
+    const int xmask = __builtin_amdgcn_readfirstlane(
+        (sm.exact[0] ? 1 : 0) | (sm.exact[1] ? 2 : 0) | (sm.exact[2] ? 4 : 0) | (sm.exact[3] ? 8 : 0));
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    if (xmask) {
+        typedef PrepSmem<T, D> Smem;
+        static_assert(offsetof(Smem, u) == sizeof(float) * 64 * 68 &&
+                          4 * sizeof(ExactRows<T, D>) <= sizeof(float) * 64 * 68 + sizeof(sm.u),
+                      "the staging area must fit A and u");
+        ExactRows<T, D>& xr = sm.stage()[Rb];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 2 * rg + i - 16 * Rb;
+            store_n<T, CPT>(&xr.q[r][CPT * cg], qf[i]);
+            store_n<T, CPT>(&xr.k[r][CPT * cg], kf[i]);
+            *reinterpret_cast<f32x4*>(&xr.g[r][CPT * cg]) = f32x4{gf[i][0], gf[i][1], gf[i][2], gf[i][3]};
+            if constexpr (CPT == 8)
+                *reinterpret_cast<f32x4*>(&xr.g[r][CPT * cg + 4]) =
+                    f32x4{gf[i][4], gf[i][5], gf[i][6], gf[i][7]};
+        }
+        __syncthreads();
+        float xa[4] = {0.f, 0.f, 0.f, 0.f};
+        if (wu < 4 && ((xmask >> wu) & 1))
+            exact_diag_block<T, D>(sm.stage()[wu], sm.beta, reinterpret_cast<T*>(rec + p.L.off_m),
+                                   wu, lane, xa);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 2 * rg + i - 16 * Rb;
+            load_n<T, CPT>(&xr.q[r][CPT * cg], qf[i]);
+            load_n<T, CPT>(&xr.k[r][CPT * cg], kf[i]);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) gf[i][c] = xr.g[r][CPT * cg + c];
+        }
+        __syncthreads();
+        if (wu < 4 && ((xmask >> wu) & 1)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.A[16 * wu + 4 * (lane >> 4) + e][16 * wu + (lane & 15)] = xa[e];
+        }
+    }
 
     // ---------------------------------------------------------------- P1
     T* Qg = reinterpret_cast<T*>(rec + p.L.off_q);
@@ -507,7 +670,8 @@ __device__ __forceinline__ void prep_item(const PrepParams& p, PrepSmem<T, D>& s
         if (w < 7) {
             const int R = (0x3323210 >> (4 * w)) & 15;
             const int J = (0x1003210 >> (4 * w)) & 15;
-            decay_block<T, D>(sm, Mg, R, J, lane);
+            // (diagonal blocks on the exact path were written in P0x)
+            if (wu >= 4 || !((xmask >> wu) & 1)) decay_block<T, D>(sm, Mg, R, J, lane);
             if (w == 0 || w == 5) {
                 const int zR = w == 0 ? 0 : 2, zJ = w == 0 ? 1 : 3;
                 const float z[4] = {0.f, 0.f, 0.f, 0.f};

@@ -139,7 +139,9 @@ def test_prefill_equal_lengths_without_cu(lib, oracle):
 
 
 def test_prefill_strong_decay_limit(lib, oracle):
-    """Every g at -5 (alpha = 0.0067), the edge of the documented range."""
+    """Every g at -5 (alpha = 0.0067): each 16-token block decays by 2^115 in
+    every channel, past the factored range, so every diagonal block takes the
+    exact path (more strong-decay cases: test_gpu_strong_decay.py)."""
     from kda_inputs import make_prefill
     inp = make_prefill([200], 2, 128, "bf16", seed=23, device="cuda", s0_std=0.02)
     inp["g"] = torch.full_like(inp["g"], -5.0)

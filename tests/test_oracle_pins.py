@@ -110,6 +110,28 @@ def test_p3_beta0_pure_channel_decay(oracle):
     np.testing.assert_allclose(fin[0], expect, rtol=1e-13, atol=0)
 
 
+def test_complete_forgetting_keeps_only_the_current_write(oracle):
+    """A retention of zero in every channel (g = -inf; also g = -1000, whose
+    exp underflows to exactly 0 in fp64) wipes the memory before each write, so
+    S_t = beta_t kb_t v_t^T and o_t = beta_t (qb_t . kb_t) v_t exactly: the
+    predict-then-write step sees an empty memory.  Channels forget on their own
+    timescales ("From KV Cache to Depth Attention: The Bottlenecks Kimi K3 Had
+    to Break", Technical Details, KDA bullet); this is the limit of a channel
+    that keeps nothing."""
+    rng = np.random.default_rng(12)
+    T, H, dk, dv = 7, 2, 6, 4
+    q, k, v, g, beta = rand_case(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((1, H, dk, dv)).astype(np.float32)
+    for gval in (-np.inf, -1000.0):
+        g[:] = gval
+        out, fin = oracle.prefill(q, k, v, g, beta, initial_state=s0, eps=0.0)
+        qb, kb = unit(q), unit(k)
+        want_o = (beta * (qb * kb).sum(-1))[..., None] * v.astype(np.float64)
+        np.testing.assert_allclose(out, want_o, atol=1e-13, rtol=0)
+        want_s = beta[-1, :, None, None] * kb[-1][:, :, None] * v[-1].astype(np.float64)[:, None, :]
+        np.testing.assert_allclose(fin[0], want_s, atol=1e-13, rtol=0)
+
+
 # ---------------------------------------------------------------- P4 order sensitivity
 def test_p4_token_order_matters(oracle):
     """Processing A->B->C and C->B->A gives different states."""
