@@ -2,8 +2,9 @@
  * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
  *
  * The operation.  Kimi Delta Attention (KDA) keeps, per sequence and head, one
- * fixed-size state matrix S (d_k x d_v, fp32) instead of a growing key/value
- * list ("one matrix replaced the KV cache", post body).  Each token first
+ * fixed-size state matrix S (d_k x d_v, fp32) in place of a key/value list
+ * that grows with every token (the x.com post mirrored as "one matrix replaced
+ * the KV cache", its opening post).  Each token first
  * predicts from the memory, then writes only the difference between the
  * incoming value and the prediction; a learned retention alpha (per key
  * channel, so channels forget on different timescales) and an update strength
@@ -31,8 +32,10 @@
  * q, k, v, g, beta and out share one element type (kda_dims.io_dtype): bf16
  * (raw 16-bit bfloat16 bit patterns) or fp32.  States are always fp32.
  *
- * Ownership: the caller allocates and owns every buffer (device memory).  The
- * library keeps no device memory between calls.
+ * Ownership: the caller allocates and owns every buffer it passes (device
+ * memory).  The library allocates device memory only for a prefill given no
+ * workspace (stream-ordered on the call's stream, freed there by the end of
+ * the call).
  *
  * Asynchrony: every call only enqueues work on `stream` (a hipStream_t, or
  * NULL for the null stream) and returns without synchronising.  A fault in a
@@ -44,15 +47,14 @@
  * undersized workspace, forbidden overlaps.  Alignment: prefill q, k, v, g
  * (per-channel gate) and the workspace 16 bytes; the decode state 16 bytes;
  * every other pointer its element size.  The contents of
- * cu_seqlens and the value ranges (g <= 0, 0 <= beta <= 1) are preconditions
- * the library does not check.  For full prefill accuracy, per-token decay
- * should also satisfy g >= -5 in every channel; see kda_chunk_prefill.
+ * cu_seqlens and the value ranges (g <= 0, -inf allowed; 0 <= beta <= 1) are
+ * preconditions the library does not check.
  *
  * Thread safety and determinism: calls are reentrant.  The library's only
  * state is, per device, the compute-unit count (queried once, cached
- * atomically) and the second stream of the pipelined prefill (see
- * kda_chunk_prefill; created once under a lock), both kept until the process
- * ends; it holds no device memory.  The kernels use no
+ * atomically), the second stream of the pipelined prefill (see
+ * kda_chunk_prefill; created once under a lock), both kept until the
+ * process ends.  The kernels use no
  * atomics, so identical inputs and sizes give bitwise identical results (a
  * pipelined call included).
  */
@@ -71,7 +73,7 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, bad count, bad overlap   */
     KDA_ERR_UNSUPPORTED = 2, /* head size, chunk size or dtype not implemented  */
     KDA_ERR_MISALIGNED = 3,  /* a pointer is not aligned as its access needs    */
-    KDA_ERR_WORKSPACE = 4,   /* workspace smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_WORKSPACE = 4,   /* workspace too small (or none while capturing)    */
     KDA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed       */
 } kda_status;
 
@@ -125,13 +127,17 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  *                      pointer as initial_state (each sequence-head reads its
  *                      slot before writing it), any other overlap is rejected
  *   workspace        : device, at least kda_prefill_workspace_bytes(dims) bytes,
- *                      16-byte aligned, required (NULL -> KDA_ERR_WORKSPACE);
+ *                      16-byte aligned; must not overlap any other buffer;
  *                      contents on entry are ignored and on return are
- *                      unspecified
+ *                      unspecified.  NULL: the library allocates it with
+ *                      hipMallocAsync on stream and frees it there with
+ *                      hipFreeAsync after the call's last launch
+ *                      (KDA_ERR_WORKSPACE while stream is being captured into
+ *                      a graph: a captured call needs a caller-owned workspace)
  *   stream           : hipStream_t (as void*), NULL for the null stream
  *
- * Supported: d_k = d_v = 128 with bf16 I/O; d_k = d_v = 64 with bf16 or fp32
- * I/O (fp32 I/O at d = 128 returns KDA_ERR_UNSUPPORTED); T_total < 2^31.
+ * Supported: d_k = d_v in {64, 128} with bf16 or fp32 I/O; T_total <= 2^31 - 1
+ * tokens and num_heads <= 65536 (larger: KDA_ERR_UNSUPPORTED).
  *
  * Streams.  Every launch is ordered after the caller's earlier work on stream,
  * and the caller's later work on stream is ordered after every launch of the
@@ -148,11 +154,13 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * ordered.
  *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
- * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Inside a 64-token chunk the
- * decay ratios are factored around 16-token block boundaries; every factor
- * stays within exp(+-80) when g >= -5 in every channel of every token (per-token
- * retention alpha >= 0.0067).  Below that the diagonal 16-token blocks may
- * under- or overflow and lose accuracy.
+ * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Any g <= 0 is handled:
+ * inside a 64-token chunk the decay ratios are factored around 16-token block
+ * boundaries with every factor at most 1, except on the diagonal blocks, whose
+ * factored form is used only while a block's decay in every channel stays
+ * within 2^64; a block past that has its diagonal products formed exactly
+ * from per-pair decay ratios that are all at most 1.  A token's retention is
+ * floored at 2^-128 (g >= -88.7), a difference no fp32 result can show.
  */
 kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
                              const void* v, const void* g, const void* beta,
@@ -234,8 +242,7 @@ typedef enum {
  * in place of a g argument (which must then be NULL).  The recurrence runs on
  * x' and g exactly as it runs on given q, k, v, g; x' and g stay in fp32 on
  * chip and never reach memory.  conv_width 0 means no convolution (and no
- * SiLU).  For full accuracy the computed g should satisfy g >= -5, as a given
- * g should (softplus(z) <= 5 for z <= 4.99).
+ * SiLU).  The computed g may take any value <= 0, as a given g may.
  *
  * conv_state_* hold, per sequence, the W-1 raw rows before the sequence
  * (in) and the last W-1 raw rows of the sequence (out; for a sequence shorter

@@ -16,15 +16,13 @@ template <typename T, int D> hipError_t launch_recur(const PrefillArgs&, hipStre
 namespace {
 
 hipError_t launch_prep_any(const PrefillArgs& a, hipStream_t s) {
-    if (a.bf16 && a.d == 128) return launch_prep<bf16, 128>(a, s);
-    if (a.bf16 && a.d == 64) return launch_prep<bf16, 64>(a, s);
-    return launch_prep<float, 64>(a, s);
+    if (a.bf16) return a.d == 128 ? launch_prep<bf16, 128>(a, s) : launch_prep<bf16, 64>(a, s);
+    return a.d == 128 ? launch_prep<float, 128>(a, s) : launch_prep<float, 64>(a, s);
 }
 
 hipError_t launch_recur_any(const PrefillArgs& a, hipStream_t s) {
-    if (a.bf16 && a.d == 128) return launch_recur<bf16, 128>(a, s);
-    if (a.bf16 && a.d == 64) return launch_recur<bf16, 64>(a, s);
-    return launch_recur<float, 64>(a, s);
+    if (a.bf16) return a.d == 128 ? launch_recur<bf16, 128>(a, s) : launch_recur<bf16, 64>(a, s);
+    return a.d == 128 ? launch_recur<float, 128>(a, s) : launch_recur<float, 64>(a, s);
 }
 
 // The library's second stream on the current device (default priority, not
@@ -179,14 +177,14 @@ bool overlap(Range a, Range b) {
 kda_status check_dims(const kda_dims* d, bool prefill) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->num_seqs < 0 || d->num_heads < 1 || d->total_tokens < 0) return KDA_ERR_INVALID_ARG;
+    // (per-chunk buffer ranges are 32-bit: 64 token rows of H * d elements)
+    if (d->num_heads > 65536) return KDA_ERR_UNSUPPORTED;
     if (d->io_dtype != KDA_BF16 && d->io_dtype != KDA_FP32) return KDA_ERR_UNSUPPORTED;
     if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->qk_l2norm != 0 && d->qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
     if (d->gate != KDA_GATE_CHANNEL && d->gate != KDA_GATE_HEAD) return KDA_ERR_INVALID_ARG;
     if (prefill) {
         if (d->chunk != 0 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
-        // fp32 I/O keeps fp32 operand tiles in LDS; at d = 128 they exceed it
-        if (d->io_dtype == KDA_FP32 && d->d_k == 128) return KDA_ERR_UNSUPPORTED;
         if (d->total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     } else {
         if (d->total_tokens != d->num_seqs) return KDA_ERR_INVALID_ARG;
@@ -293,6 +291,7 @@ FrontEndRanges front_end_ranges(const kda_dims* d, const kda::FrontEnd& fe, int6
     return r;
 }
 
+
 // Shared body of the prefill entry points.
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
@@ -315,7 +314,6 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     if (T > 0 && (!q || !k || !v || !beta || !out)) return KDA_ERR_INVALID_ARG;
     if (interval > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
     if (out_gate != KDA_OUT_GATE_NONE && T > 0 && !out_gate_z) return KDA_ERR_INVALID_ARG;
-    if (!workspace) return KDA_ERR_WORKSPACE;
     // q, k, v, g rows and the workspace are read with 16-byte vector accesses;
     // beta, out and the states element by element
     const uintptr_t E_al = d->io_dtype == KDA_BF16 ? 2 : 4;
@@ -329,7 +327,8 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens, checkpoints};
     for (const void* p : f32_ptrs)
         if (p && !aligned_to(p, 4)) return KDA_ERR_MISALIGNED;
-    if (workspace_bytes < kda_prefill_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
+    const size_t ws_need = kda_prefill_workspace_bytes(d);
+    if (workspace && workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
 
     // overlaps: no output may touch an input or another output; final_state
     // may equal initial_state exactly
@@ -341,7 +340,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     const Range r_z = out_gate != KDA_OUT_GATE_NONE
                           ? range_of(out_gate_z, out_gate == KDA_OUT_GATE_HEAD ? bb : qb)
                           : Range{0, 0};
-    const Range r_ws = range_of(workspace, workspace_bytes);
+    const Range r_ws = workspace ? range_of(workspace, workspace_bytes) : Range{0, 0};
     const Range r_s0 = initial_state ? range_of(initial_state, sb) : Range{0, 0};
     const Range r_cu = cu_seqlens ? range_of(cu_seqlens, (size_t)(N + 1) * 4) : Range{0, 0};
     const Range ins[] = {range_of(q, qb), range_of(k, qb), range_of(v, qb),
@@ -354,6 +353,9 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
         const int64_t C = kda_checkpoint_count(d, nullptr, interval);
         r_ck = range_of(checkpoints, (size_t)C * H * D * D * 4);
     }
+    // the workspace is written by the kernels: it may touch no input
+    for (const Range& r : ins)
+        if (overlap(r_ws, r)) return KDA_ERR_INVALID_ARG;
     if (T > 0) {
         // outputs against inputs (final_state == initial_state is allowed)
         const Range outs[] = {r_out, r_fin, r_ck, fr.state_out};
@@ -402,8 +404,23 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.fe = fe;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
     if (compute_units(&a.compute_units) != hipSuccess) return KDA_ERR_HIP;
-    hipError_t e = kda::launch_prefill(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (workspace) {
+        const hipError_t e = kda::launch_prefill(a, hs);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // no workspace given: a stream-ordered allocation on the caller's stream,
+    // freed on it after the last launch (not while the stream is being
+    // captured: a graph needs a caller-owned workspace)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return KDA_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, ws_need, hs) != hipSuccess) return KDA_ERR_HIP;
+    a.workspace = static_cast<unsigned char*>(ws);
+    const hipError_t e = kda::launch_prefill(a, hs);
+    const hipError_t f = hipFreeAsync(ws, hs);
+    return (e == hipSuccess && f == hipSuccess) ? KDA_OK : KDA_ERR_HIP;
 }
 
 const kda_prefill_options kNoPrefillOptions = {0, KDA_OUT_GATE_NONE, nullptr, nullptr, nullptr};

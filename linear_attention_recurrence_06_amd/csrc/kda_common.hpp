@@ -134,10 +134,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
-// Load a V (8 or 16 bytes, or one 2- or 4-byte element) at byte offset `off`.
+// Load a V (8, 16 or 32 bytes, or one 2- or 4-byte element) at byte offset `off`
+// (32 bytes: two 16-byte loads).
 template <typename V>
 __device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (sizeof(V) == 16) {
+    if constexpr (sizeof(V) == 32) {
+        struct Pair {
+            u32x4 lo, hi;
+        };
+        const Pair x{__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0)),
+                     __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, 0))};
+        return __builtin_bit_cast(V, x);
+    } else if constexpr (sizeof(V) == 16) {
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     } else if constexpr (sizeof(V) == 8) {
         return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));

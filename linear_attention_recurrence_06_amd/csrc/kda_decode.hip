@@ -19,6 +19,8 @@
 // read and the write, and the read-outs reduce over row groups with one
 // cross-lane step inside the wave and one LDS exchange across the waves.
 // The kernel is bound by HBM: 2 * 4 * D*D bytes of state per unit.
+#include <algorithm>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -136,7 +138,9 @@ __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
     // the gate's per-thread rank slice (rank / TPC, rank >= 32) must be whole fragments
     static_assert(!FE || (32 / TPC) % 8 == 0, "front-end gate slice below one fragment");
 
-    const int64_t unit = blockIdx.x;  // = n * H + h
+    // a 2-D grid (head, sequence): N * H workgroups of NTH threads would pass the
+    // 32-bit dispatch size in one dimension
+    const int64_t unit = (int64_t)blockIdx.y * H + blockIdx.x;  // = n * H + h
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int cq = t % TPR, rg = t / TPR;
@@ -358,12 +362,6 @@ __global__ __launch_bounds__(NTH) void decode_kernel(const T* __restrict__ q,
             if constexpr (OG) {  // out = o * sigmoid(z), z per value channel or per head
                 const float zz = to_f32(zraw[j]);
                 oj *= __builtin_amdgcn_rcpf(1.f + __expf(-zz));
-            } else if (out_gate) {
-                // (never taken: gated steps use the OG instantiation.  Kept so that
-                // the ungated kernel keeps the instruction schedule it was measured
-                // with; without it the step measured about 1% slower)
-                const float zz = to_f32(out_gate == 2 ? og_z[unit] : og_z[unit * D + 4 * cq + j]);
-                oj *= __builtin_amdgcn_rcpf(1.f + __expf(-zz));
             }
             out[unit * D + 4 * cq + j] = from_f32<T>(oj);
         }
@@ -382,17 +380,32 @@ template <int D>
 constexpr int kDecodeThreadsFE = D == 128 ? 512 : 256;
 
 template <typename T, int D, bool FE, int GR, int NTH>
-static void launch_one(const DecodeArgs& a, const DecodeFE& fe, int64_t units, hipStream_t stream) {
-    if (a.out_gate)
-        hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, true>), dim3((unsigned)units), dim3(NTH),
-                           0, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads, fe);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, false>), dim3((unsigned)units), dim3(NTH),
-                           0, stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g,
-                           (const T*)a.beta, a.state, (T*)a.out, a.scale, a.l2norm,
-                           a.scalar_g ? 1 : 0, a.out_gate, (const T*)a.out_gate_z, a.n_heads, fe);
+static hipError_t launch_one(const DecodeArgs& a, const DecodeFE& fe, hipStream_t stream) {
+    // grid (head, sequence), at most kMaxGridY sequences per launch
+    const int64_t H = a.n_heads;
+    for (int64_t n0 = 0; n0 < a.n_seqs; n0 += kMaxGridY) {
+        const dim3 grid((unsigned)H, (unsigned)std::min<int64_t>(kMaxGridY, a.n_seqs - n0));
+        const int64_t th = n0 * H, td = th * D;  // token-head and element offsets
+        DecodeFE f = fe;
+        if (f.a) f.a = (const T*)f.a + n0 * f.rank;
+        if (f.state_in) f.state_in = (const T*)f.state_in + n0 * 3 * (f.conv_w - 1) * H * D;
+        if (f.state_out) f.state_out = (T*)f.state_out + n0 * 3 * (f.conv_w - 1) * H * D;
+        const T* g = (const T*)a.g + (a.g ? (a.scalar_g ? th : td) : 0);
+        const T* z = (const T*)a.out_gate_z + (a.out_gate_z ? (a.out_gate == 2 ? th : td) : 0);
+        if (a.out_gate)
+            hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, true>), grid, dim3(NTH), 0, stream,
+                               (const T*)a.q + td, (const T*)a.k + td, (const T*)a.v + td, g,
+                               (const T*)a.beta + th, a.state + td * D, (T*)a.out + td, a.scale,
+                               a.l2norm, a.scalar_g ? 1 : 0, a.out_gate, z, a.n_heads, f);
+        else
+            hipLaunchKernelGGL((decode_kernel<T, D, FE, GR, NTH, false>), grid, dim3(NTH), 0, stream,
+                               (const T*)a.q + td, (const T*)a.k + td, (const T*)a.v + td, g,
+                               (const T*)a.beta + th, a.state + td * D, (T*)a.out + td, a.scale,
+                               a.l2norm, a.scalar_g ? 1 : 0, a.out_gate, z, a.n_heads, f);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename T, int D>
@@ -402,12 +415,10 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     DecodeFE fe{a.fe.conv_w, a.fe.silu,     a.fe.rank,  a.fe.conv_weight, a.fe.state_in,
                 a.fe.state_out, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
     if (a.fe.active() && a.fe.rank > 64)
-        launch_one<T, D, true, 128, kDecodeThreadsFE<D>>(a, fe, units, stream);
-    else if (a.fe.active())
-        launch_one<T, D, true, 64, kDecodeThreadsFE<D>>(a, fe, units, stream);
-    else
-        launch_one<T, D, false, 64, kDecodeThreads>(a, fe, units, stream);
-    return hipGetLastError();
+        return launch_one<T, D, true, 128, kDecodeThreadsFE<D>>(a, fe, stream);
+    if (a.fe.active())
+        return launch_one<T, D, true, 64, kDecodeThreadsFE<D>>(a, fe, stream);
+    return launch_one<T, D, false, 64, kDecodeThreads>(a, fe, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

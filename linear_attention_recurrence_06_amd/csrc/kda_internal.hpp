@@ -10,6 +10,10 @@ namespace kda {
 // epsilon inside the L2-norm square root: x / sqrt(sum x^2 + eps)
 constexpr float kL2Eps = 1e-6f;
 
+// Largest grid y dimension a launch uses (the runtime's documented limit);
+// launches split longer ranges.
+constexpr int64_t kMaxGridY = 65535;
+
 // Front end ahead of the recurrence: short causal convolution of the raw q,
 // k, v (width conv_w, 0 = none; tap conv_w-1 is the current token; optional
 // SiLU) and the low-rank decay gate g = -softplus(a b^T + bias) (rank 0 = g

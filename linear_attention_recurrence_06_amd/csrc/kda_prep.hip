@@ -192,6 +192,13 @@ __device__ __forceinline__ void decay_block(PrepSmem<T, D>& sm, T* Mg, int R, in
     store_n<T, 4>(Mg + aorder_index(16 * R + col, 16 * J + 4 * (lane >> 4), 64), m);
 }
 
+// Waves per SIMD the preparation kernels are built for: two workgroups of 8
+// waves per CU (at most 128 VGPRs, 80 KB of LDS each), except fp32 I/O at
+// d = 128, whose fp32 tiles take 129 KB of LDS: one workgroup per CU, which
+// may then use 256 VGPRs.
+template <typename T, int D>
+constexpr int kPrepWavesPerSimd = (sizeof(T) == 4 && D == 128) ? 2 : 4;
+
 // Front end of the preparation (kernel argument): the short convolution of the
 // raw q, k, v and the low-rank decay gate.
 struct PrepFE {
@@ -213,7 +220,7 @@ struct PrepParams {
     int l2norm;
     PrefillLayout L;
     PrepFE fe;
-    int64_t slot_begin;  // first chunk slot of this launch (item i: slot slot_begin + i / H)
+    int64_t slot_begin;  // first chunk slot of this launch (grid row y: slot slot_begin + y)
 };
 
 // (first token, length) of a chunk slot; length 0 marks an unused slot.
@@ -927,6 +934,11 @@ __device__ __forceinline__ void fe_rows(const PrepParams& p, PrepSmem<T, D>& sm,
             r.k[i][c] = live[i] ? y[1][i][c] : 0.f;
             r.v[i][c] = from_f32<T>(live[i] ? y[2][i][c] : 0.f);
         }
+        // rounded and packed here: left to the compiler, the conversion sinks
+        // to v's use in P3 and keeps twice the registers alive until then
+        // (measured: 0 spills instead of 6 up to rank 64; with the rank > 64
+        // gate's longer product the early packing costs more than it saves)
+        if constexpr (KS <= 2) asm volatile("" : "+v"(r.v[i]));
         r.b[i] = to_f32(raw.b[i]);
     }
 
@@ -1033,14 +1045,13 @@ __device__ __forceinline__ void seq_of_token(const PrepParams& p, int64_t tok, i
 
 // The preparation with the front end: raw q, k, v, and g given or low-rank.
 template <typename T, int D, int KS>
-__global__ __launch_bounds__(512, 4) void prep_fe_kernel(PrepParams p) {
+__global__ __launch_bounds__(512, (kPrepWavesPerSimd<T, D>)) void prep_fe_kernel(PrepParams p) {
     __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x;
-    const uint32_t H = (uint32_t)p.n_heads;
-    const uint32_t item = blockIdx.x;
-    const uint32_t ls = item / H;
-    const int h = (int)(item - ls * H);
-    const int64_t slot = p.slot_begin + ls;
+    // 2-D grid (head, chunk slot); the linear workgroup order is slot-major,
+    // so head h runs on XCD h mod 8 when H is a multiple of 8
+    const int h = blockIdx.x;
+    const int64_t slot = p.slot_begin + blockIdx.y;
     const int2 d = slot_desc(p, slot);
     if (d.y <= 0) return;
     int64_t n, s_begin;
@@ -1089,16 +1100,14 @@ __global__ __launch_bounds__(256) void conv_state_kernel(PrepParams p, void* sta
 }
 
 // One (chunk slot, head) item per workgroup; two workgroups share a CU (80 KB
-// of LDS and at most 128 VGPRs each).
+// of LDS and at most 128 VGPRs each; fp32 at d = 128: one per CU).
 template <typename T, int D, bool SG>
-__global__ __launch_bounds__(512, 4) void prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(512, (kPrepWavesPerSimd<T, D>)) void prep_kernel(PrepParams p) {
     __shared__ PrepSmem<T, D> sm;
     const int t = threadIdx.x;
-    const uint32_t H = (uint32_t)p.n_heads;
-    const uint32_t item = blockIdx.x;  // the grid is one workgroup per item
-    const uint32_t ls = item / H;
-    const int h = (int)(item - ls * H);
-    const int64_t slot = p.slot_begin + ls;
+    // 2-D grid (head, chunk slot), one workgroup per item
+    const int h = blockIdx.x;
+    const int64_t slot = p.slot_begin + blockIdx.y;
     const int2 d = slot_desc(p, slot);
     if (d.y <= 0) return;
     RawRows<T, D, SG> raw;
@@ -1215,27 +1224,34 @@ hipError_t launch_prep(const PrefillArgs& a, hipStream_t stream) {
                            reinterpret_cast<int2*>(a.workspace + a.layout.desc_offset()));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t items = (s_end - a.slot_begin) * a.n_heads;
-    if (items <= 0) return hipSuccess;
-    if (a.fe.active()) {
+    const int64_t nslots = s_end - a.slot_begin;
+    if (nslots <= 0) return hipSuccess;
+    if (a.fe.active())
         p.fe = PrepFE{a.fe.conv_w, a.fe.silu, a.fe.rank, a.scalar_g ? 1 : 0, a.fe.conv_weight,
                       a.fe.state_in, a.fe.gate_a, a.fe.gate_b, a.fe.gate_bias};
-        // ranks up to 64 take two 32-deep steps of the gate's product, larger ones four
-        if (a.fe.rank <= 64)
-            hipLaunchKernelGGL((prep_fe_kernel<T, D, 2>), dim3((unsigned)items), dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((prep_fe_kernel<T, D, 4>), dim3((unsigned)items), dim3(512), 0, stream, p);
-        return hipGetLastError();
+    // grid (head, chunk slot), at most kMaxGridY slots per launch
+    for (int64_t s0 = 0; s0 < nslots; s0 += kMaxGridY) {
+        p.slot_begin = a.slot_begin + s0;
+        const dim3 grid((unsigned)a.n_heads, (unsigned)std::min<int64_t>(kMaxGridY, nslots - s0));
+        if (a.fe.active()) {
+            // ranks up to 64 take two 32-deep steps of the gate's product, larger ones four
+            if (a.fe.rank <= 64)
+                hipLaunchKernelGGL((prep_fe_kernel<T, D, 2>), grid, dim3(512), 0, stream, p);
+            else
+                hipLaunchKernelGGL((prep_fe_kernel<T, D, 4>), grid, dim3(512), 0, stream, p);
+        } else if (a.scalar_g) {
+            hipLaunchKernelGGL((prep_kernel<T, D, true>), grid, dim3(512), 0, stream, p);
+        } else {
+            hipLaunchKernelGGL((prep_kernel<T, D, false>), grid, dim3(512), 0, stream, p);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (a.scalar_g)
-        hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3((unsigned)items), dim3(512), 0, stream, p);
-    else
-        hipLaunchKernelGGL((prep_kernel<T, D, false>), dim3((unsigned)items), dim3(512), 0, stream, p);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template hipError_t launch_prep<bf16, 128>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_prep<bf16, 64>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_prep<float, 64>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_prep<float, 128>(const PrefillArgs&, hipStream_t);
 
 }  // namespace kda

@@ -440,8 +440,10 @@ __global__ __launch_bounds__(512) void recur_kernel(RecurParams p) {
     }
 }
 
-// Chunks whose operands are in flight ahead of the one being consumed.
-constexpr int kRecurDepth = 3;
+// Chunks whose operands are in flight ahead of the one being consumed (fp32
+// operands at d = 128 take twice the registers of bf16 ones: two chunks).
+template <typename T, int D>
+constexpr int kRecurDepth = (sizeof(T) == 4 && D == 128) ? 2 : 3;
 // Chunks beyond those in flight whose records are touched early (L2 prefetch).
 constexpr int kRecurPrefetch = 1;
 
@@ -479,7 +481,7 @@ static hipError_t launch_nt(const PrefillArgs& a, hipStream_t stream) {
     const int64_t groups = (chains + 7) / 8;
     const int64_t grid = 8 * p.ntiles * groups;
     const dim3 gd((unsigned)grid), bd(512);
-    constexpr int B = kRecurDepth, F = kRecurPrefetch;
+    constexpr int B = kRecurDepth<T, D>, F = kRecurPrefetch;
     const bool ck = a.ckpt_interval > 0, og = a.out_gate != 0;
     if (!ck && !og)
         hipLaunchKernelGGL((recur_kernel<T, D, NT, B, F, false, false>), gd, bd, 0, stream, p);
@@ -513,5 +515,6 @@ hipError_t launch_recur(const PrefillArgs& a, hipStream_t stream) {
 template hipError_t launch_recur<bf16, 128>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_recur<bf16, 64>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_recur<float, 64>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_recur<float, 128>(const PrefillArgs&, hipStream_t);
 
 }  // namespace kda

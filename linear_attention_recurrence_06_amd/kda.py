@@ -217,13 +217,16 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
                       final_state: Optional[torch.Tensor] = None, *,
                       num_seqs: Optional[int] = None, scale: float = 1.0,
                       qk_l2norm: bool = True, workspace: Optional[torch.Tensor] = None,
-                      output_final_state: bool = True,
+                      output_final_state: bool = True, library_workspace: bool = False,
                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill over packed sequences (see include/kda.h).
 
     Returns ``(out, final_state)``; ``final_state`` is None when
     ``output_final_state`` is False and none was passed.  Without
     ``cu_seqlens`` the T tokens form ``num_seqs`` (default 1) equal sequences.
+    The workspace is ``workspace``, else one allocated here with torch, else
+    (``library_workspace=True``) none: the library then allocates it
+    stream-ordered on ``stream``.
     """
     lib = load_library()
     T, H, dk = q.shape
@@ -252,11 +255,12 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
         _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
     dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
     need = kda_prefill_workspace_bytes(dims)
-    if workspace is None:
+    if workspace is None and not library_workspace:
         workspace = _workspace(need, dev, stream)
     rc = lib.kda_chunk_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),
-                               _ptr(final_state), _ptr(workspace), workspace.numel(),
+                               _ptr(final_state), _ptr(workspace),
+                               0 if workspace is None else workspace.numel(),
                                _stream_handle(stream, dev))
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_prefill")

@@ -67,7 +67,10 @@ def test_workspace_bytes(kda):
     assert kda.kda_prefill_pipeline_segments(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == -1
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
-    assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 128, 128, kda.KDA_FP32)) == 0
+    # fp32 I/O at d = 128: the same record with 4-byte elements
+    rec4 = (4 * 64 * 128 + 64 * 64) * 4 + 128 * 4
+    d4 = kda.make_dims(8192, 2, 32, 128, 128, kda.KDA_FP32)
+    assert kda.kda_prefill_workspace_bytes(d4) == 2 * 256 + desc2 + rec4 * slots2 * 32
 
 
 FAKE = 1 << 40  # 16-byte aligned addresses the validation only compares, never dereferences
@@ -92,8 +95,17 @@ def test_prefill_validation(kda):
     d = kda.make_dims(256, 2, 4, 128, 128, kda.KDA_BF16)
     assert prefill_call(kda, d, q=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(kda, d, out=None) == kda.KDA_ERR_INVALID_ARG
-    assert prefill_call(kda, d, ws=None) == kda.KDA_ERR_WORKSPACE
+    # (no workspace is valid -- the library allocates one on the stream -- so a
+    # NULL workspace is only ever combined here with another error: a call that
+    # passed validation would launch on these fake addresses)
+    assert prefill_call(kda, d, ws=None, q=None) == kda.KDA_ERR_INVALID_ARG
+    assert prefill_call(kda, d, ws=None, q=FAKE + 8) == kda.KDA_ERR_MISALIGNED
     assert prefill_call(kda, d, ws_bytes=1024) == kda.KDA_ERR_WORKSPACE
+    # the workspace must not overlap an input (the kernels write it)
+    big = 256 * 4 * 128 * 2 + 4096
+    assert prefill_call(kda, d, ws=FAKE + 3 * big + 256) == kda.KDA_ERR_INVALID_ARG   # over g
+    assert prefill_call(kda, d, ws=FAKE - 4096) == kda.KDA_ERR_INVALID_ARG            # over q
+    assert prefill_call(kda, d, s0=FAKE + 6 * big + 1024) == kda.KDA_ERR_INVALID_ARG  # S0 in it
     assert prefill_call(kda, d, q=FAKE + 8) == kda.KDA_ERR_MISALIGNED
     assert prefill_call(kda, d, beta=FAKE * 4 + 1) == kda.KDA_ERR_MISALIGNED
     assert prefill_call(kda, d, out=FAKE + 64) == kda.KDA_ERR_INVALID_ARG   # overlaps q
@@ -107,6 +119,13 @@ def test_prefill_validation(kda):
     assert prefill_call(kda, bad) == kda.KDA_ERR_UNSUPPORTED
     bad = kda.make_dims(255, 2, 4, 128, 128, kda.KDA_BF16)   # uneven split without cu_seqlens
     assert prefill_call(kda, bad) == kda.KDA_ERR_INVALID_ARG
+    # the supported range: T_total <= 2^31 - 1, H <= 65536
+    bad = kda.make_dims(1 << 31, 1, 1, 128, 128, kda.KDA_BF16)
+    assert prefill_call(kda, bad) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.kda_prefill_workspace_bytes(bad) == 0
+    bad = kda.make_dims(64, 1, 65537, 128, 128, kda.KDA_BF16)
+    assert prefill_call(kda, bad) == kda.KDA_ERR_UNSUPPORTED
+    assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 65536, 64, 64, kda.KDA_BF16)) > 0
     # final_state may be the same buffer as initial_state, but not a shifted view of it
     s = FAKE * 8
     assert prefill_call(kda, d, s0=s, fin=s + 64) == kda.KDA_ERR_INVALID_ARG
@@ -187,7 +206,7 @@ def test_gate_field_and_validation(kda):
     assert kda.kda_prefill_workspace_bytes(d1) == kda.kda_prefill_workspace_bytes(
         kda.make_dims(1024, 1, 2, 128, 128, kda.KDA_BF16))
     assert prefill_call(kda, d1, g=FAKE + 3 * (1024 * 2 * 128 * 2 + 4096) + 2,
-                        ws_bytes=0) == kda.KDA_ERR_WORKSPACE
+                        ws_bytes=1024) == kda.KDA_ERR_WORKSPACE
     assert prefill_call(kda, d1, g=FAKE + 3 * (1024 * 2 * 128 * 2 + 4096) + 1) == \
         kda.KDA_ERR_MISALIGNED
 
@@ -218,19 +237,19 @@ def test_output_gate_validation(kda):
     wsb = kda.kda_prefill_workspace_bytes(d)
 
     def call(og, interval=0, null_opts=False, **over):
-        p = dict(base)
+        p = dict(base, wsb=wsb)
         p.update(over)
         o = kda.kda_prefill_options(interval, og, None, p["z"])
         return lib.kda_chunk_prefill_ex(
             ctypes.byref(d), p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, p["out"],
-            p["fin"], None if null_opts else ctypes.byref(o), p["ws"], wsb, None)
+            p["fin"], None if null_opts else ctypes.byref(o), p["ws"], p["wsb"], None)
 
     assert call(3) == kda.KDA_ERR_INVALID_ARG
     assert call(-1) == kda.KDA_ERR_INVALID_ARG
     assert call(kda.KDA_OUT_GATE_CHANNEL, z=None) == kda.KDA_ERR_INVALID_ARG
     assert call(kda.KDA_OUT_GATE_HEAD, z=FAKE + 30 * big + 1) == kda.KDA_ERR_MISALIGNED
     # z is read element by element: 2-byte alignment is enough for bf16
-    assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 30 * big + 2, ws=None) == kda.KDA_ERR_WORKSPACE
+    assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 30 * big + 2, wsb=1024) == kda.KDA_ERR_WORKSPACE
     # z (an input) must not overlap out: T*H*d_v elements per channel, T*H per head
     assert call(kda.KDA_OUT_GATE_CHANNEL, z=FAKE + 5 * big - 64) == kda.KDA_ERR_INVALID_ARG
     assert call(kda.KDA_OUT_GATE_HEAD, z=FAKE + 5 * big - T * H * 2 + 2) == \
@@ -240,8 +259,8 @@ def test_output_gate_validation(kda):
     # nor the final state
     assert call(kda.KDA_OUT_GATE_CHANNEL, fin=FAKE + 30 * big + 256) == kda.KDA_ERR_INVALID_ARG
     # with no gate, z is ignored (NULL options mean "no options")
-    assert call(kda.KDA_OUT_GATE_NONE, z=None, ws=None) == kda.KDA_ERR_WORKSPACE
-    assert call(0, null_opts=True, ws=None) == kda.KDA_ERR_WORKSPACE
+    assert call(kda.KDA_OUT_GATE_NONE, z=None, wsb=1024) == kda.KDA_ERR_WORKSPACE
+    assert call(0, null_opts=True, wsb=1024) == kda.KDA_ERR_WORKSPACE
     # an empty batch is a no-op even with a gate and no z
     e = kda.make_dims(0, 0, 4, 128, 128, kda.KDA_BF16)
     o = kda.kda_prefill_options(0, kda.KDA_OUT_GATE_CHANNEL, None, None)
@@ -287,20 +306,20 @@ def test_front_end_validation(kda):
         return kda.kda_front_end(**f)
 
     def call(f, **over):
-        p = dict(base)
+        p = dict(base, wsb=wsb)
         p.update(over)
         o = kda.kda_prefill_options(0, 0, None, None, ctypes.pointer(f) if f else None)
         return lib.kda_chunk_prefill_ex(ctypes.byref(over.get("dims", d)), p["q"], p["k"], p["v"],
                                         p["g"], p["beta"], None, None, p["out"], None,
-                                        ctypes.byref(o), p["ws"], wsb, None)
+                                        ctypes.byref(o), p["ws"], p["wsb"], None)
 
     INV, MIS, WS = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_MISALIGNED, kda.KDA_ERR_WORKSPACE
     # a valid front end (low-rank gate, so g NULL) reaches the workspace check
-    assert call(fe(), g=None, ws=None) == WS
+    assert call(fe(), g=None, wsb=1024) == WS
     # with a low-rank gate g must be NULL; without one it is required
     assert call(fe()) == INV
     assert call(fe(gate_rank=0, gate_a=None, gate_b=None), g=None) == INV
-    assert call(fe(gate_rank=0, gate_a=None, gate_b=None), ws=None) == WS
+    assert call(fe(gate_rank=0, gate_a=None, gate_b=None), wsb=1024) == WS
     assert call(None, g=None) == INV
     for bad in (dict(conv_width=5), dict(conv_width=-1), dict(conv_silu=2), dict(reserved=1),
                 dict(gate_rank=48), dict(gate_rank=256), dict(conv_weight=None),
@@ -316,7 +335,7 @@ def test_front_end_validation(kda):
         assert call(fe(**{name: val}), g=None) == MIS, name
     # conv states are not read or written at width 1, so they are not checked
     assert call(fe(conv_width=1, conv_state_in=S0 + 8, conv_state_out=S1 + 8), g=None,
-                ws=None) == WS
+                wsb=1024) == WS
     # the conv state output must not overlap an input or another output
     assert call(fe(conv_state_out=base["q"] + 64), g=None) == INV
     assert call(fe(conv_state_out=base["out"] + 64), g=None) == INV
@@ -350,3 +369,4 @@ def test_decode_front_end_validation(kda):
     assert call(conv_state_out=args[6]) == INV      # the conv state over out
     assert call(gate_rank=0, gate_a=None, gate_b=None) == INV  # no gate at all
     assert call(gate_a=A0 + 4) == MIS
+
