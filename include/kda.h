@@ -35,7 +35,7 @@
  * Ownership: the caller allocates and owns every buffer it passes (device
  * memory).  The library allocates device memory only for a prefill given no
  * workspace (stream-ordered on the call's stream, freed there by the end of
- * the call).
+ * the call), and holds one array per device for kda_chunk_prefill_noalloc.
  *
  * Asynchrony: every call only enqueues work on `stream` (a hipStream_t, or
  * NULL for the null stream) and returns without synchronising.  A fault in a
@@ -53,8 +53,10 @@
  * Thread safety and determinism: calls are reentrant.  The library's only
  * state is, per device, the compute-unit count (queried once, cached
  * atomically), the second stream of the pipelined prefill (see
- * kda_chunk_prefill; created once under a lock), both kept until the
- * process ends.  The kernels use no
+ * kda_chunk_prefill; created once under a lock) and the device array of
+ * kda_chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES, allocated when the
+ * library is loaded on a device), all kept until the process ends.  The
+ * kernels use no
  * atomics, so identical inputs and sizes give bitwise identical results (a
  * pipelined call included).
  */
@@ -321,6 +323,32 @@ kda_status kda_decode_step_ex(const kda_dims* dims, const void* q, const void* k
 kda_status kda_decode_step(const kda_dims* dims, const void* q, const void* k,
                            const void* v, const void* g, const void* beta,
                            float* state_inout, void* out, void* stream);
+
+/* Bytes of the per-device array kda_chunk_prefill_noalloc uses as its
+ * workspace (320 MiB: the 8,192-token, 32-head, d = 128 bf16 prefill needs
+ * 294 MiB). */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)320 << 20)
+
+/* Chunked prefill that allocates nothing, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments (without the workspace), rules and
+ * results as kda_chunk_prefill.  Its workspace is a device array of the
+ * library, KDA_NOALLOC_SCRATCH_BYTES on each device, allocated when the library
+ * is loaded on that device and held until the process ends; its address is
+ * looked up once per device on the first call there.  The call never uses the
+ * second stream of the pipelined prefill (no library stream or event) and
+ * calls no allocating routine.
+ * Errors: as kda_chunk_prefill, plus KDA_ERR_WORKSPACE when
+ * kda_prefill_workspace_bytes(dims) exceeds KDA_NOALLOC_SCRATCH_BYTES.
+ * Every call on one device shares that device's array: calls that may run at
+ * the same time on one device (different streams without ordering between
+ * them) race and corrupt each other's results; order them on one stream.  The
+ * array's contents are not preserved between calls (nothing needs to start at
+ * zero). */
+kda_status kda_chunk_prefill_noalloc(const kda_dims* dims, const void* q, const void* k,
+                                     const void* v, const void* g, const void* beta,
+                                     const float* initial_state, const int32_t* cu_seqlens,
+                                     void* out, float* final_state, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status status);

@@ -5,14 +5,14 @@ this package holds its sources (csrc/), the in-tree build script and a thin
 ctypes binding whose functions carry the C ABI's names.
 """
 
-from .kda import (KDAError, kda_checkpoint_count, kda_chunk_prefill,
+from .kda import (KDA_NOALLOC_SCRATCH_BYTES, KDAError, kda_checkpoint_count, kda_chunk_prefill,
                   kda_chunk_prefill_checkpoints, kda_chunk_prefill_ex,
-                  kda_decode_step,
+                  kda_chunk_prefill_noalloc, kda_decode_step,
                   kda_decode_step_ex, kda_dims, kda_prefill_pipeline_segments,
                   kda_prefill_workspace_bytes, load_library, make_dims, status_string)
 
-__all__ = ["KDAError", "kda_checkpoint_count", "kda_chunk_prefill",
-           "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex",
+__all__ = ["KDA_NOALLOC_SCRATCH_BYTES", "KDAError", "kda_checkpoint_count", "kda_chunk_prefill",
+           "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_chunk_prefill_noalloc",
            "kda_decode_step",
            "kda_decode_step_ex", "kda_dims", "kda_prefill_pipeline_segments",
            "kda_prefill_workspace_bytes", "load_library", "make_dims", "status_string"]

@@ -123,7 +123,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     hipError_t e0 = hipStreamIsCapturing(s, &cap);
     if (e0 != hipSuccess) return e0;
-    const int S = cap == hipStreamCaptureStatusNone ? pipeline_segments(a) : 0;
+    const int S = (cap == hipStreamCaptureStatusNone && !a.no_pipeline) ? pipeline_segments(a) : 0;
     if (S >= 2) {
         float* state = a.final_state ? a.final_state
                                      : reinterpret_cast<float*>(a.workspace + a.layout.state_offset());
@@ -233,6 +233,13 @@ int32_t kda_prefill_pipeline_segments(const kda_dims* d) {
 
 }  // extern "C"
 
+// ------------------------------------------------------------------ no allocation
+// The workspace of kda_chunk_prefill_noalloc: one array per device, allocated
+// when the library is loaded there and held until the process ends.  Host
+// code never uses this name as an address: kernels get the per-device address
+// from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 // Front-end checks shared by prefill and decode (need_g: there are tokens,
@@ -292,12 +299,32 @@ FrontEndRanges front_end_ranges(const kda_dims* d, const kda::FrontEnd& fe, int6
 }
 
 
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current.
+hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
 // Shared body of the prefill entry points.
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
                         const int32_t* cu_seqlens, void* out, float* final_state,
                         const kda_prefill_options& o, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, bool noalloc = false) {
     kda_status st = check_dims(d, true);
     if (st != KDA_OK) return st;
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads, D = d->d_k;
@@ -405,6 +432,16 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
     if (compute_units(&a.compute_units) != hipSuccess) return KDA_ERR_HIP;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (noalloc) {
+        // the library's per-device array (its address is found only now, after
+        // every argument has been checked); one stream, no library events
+        void* ws = nullptr;
+        if (scratch_address(&ws) != hipSuccess) return KDA_ERR_HIP;
+        a.workspace = static_cast<unsigned char*>(ws);
+        a.no_pipeline = true;
+        const hipError_t e = kda::launch_prefill(a, hs);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     if (workspace) {
         const hipError_t e = kda::launch_prefill(a, hs);
         return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -481,6 +518,18 @@ kda_status kda_chunk_prefill_checkpoints(const kda_dims* d, const void* q, const
 }
 
 }  // extern "C"
+
+extern "C" kda_status kda_chunk_prefill_noalloc(const kda_dims* d, const void* q, const void* k,
+                                                const void* v, const void* g, const void* beta,
+                                                const float* initial_state,
+                                                const int32_t* cu_seqlens, void* out,
+                                                float* final_state, void* stream) {
+    const kda_status st = check_dims(d, true);
+    if (st != KDA_OK) return st;
+    if (kda_prefill_workspace_bytes(d) > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                        kNoPrefillOptions, nullptr, 0, stream, /*noalloc=*/true);
+}
 
 static kda_status decode_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                               const void* g, const void* beta, float* state_inout, void* out,

@@ -134,6 +134,7 @@ struct PrefillArgs {
     bool prep_setup = true;
     int64_t chunk_begin = 0, chunk_end = INT64_MAX;
     int32_t compute_units = 0;   // of the launching device (0: unknown, no pipeline)
+    bool no_pipeline = false;    // one stream only: no library stream or events
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -33,7 +33,10 @@ KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
             "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_decode_step",
             "kda_decode_step_ex", "kda_status_string", "kda_version",
-            "kda_prefill_pipeline_segments")
+            "kda_prefill_pipeline_segments", "kda_chunk_prefill_noalloc")
+
+#: bytes of the per-device array kda_chunk_prefill_noalloc uses as its workspace
+KDA_NOALLOC_SCRATCH_BYTES = 320 << 20
 
 
 class kda_dims(ctypes.Structure):
@@ -133,6 +136,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_version.restype = ctypes.c_int
     lib.kda_prefill_pipeline_segments.argtypes = [D]
     lib.kda_prefill_pipeline_segments.restype = ctypes.c_int32
+    lib.kda_chunk_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -264,6 +269,48 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
                                _stream_handle(stream, dev))
     if rc != KDA_OK:
         raise KDAError(rc, "kda_chunk_prefill")
+    return out, final_state
+
+
+def kda_chunk_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              g: torch.Tensor, beta: torch.Tensor,
+                              initial_state: Optional[torch.Tensor] = None,
+                              cu_seqlens: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None,
+                              final_state: Optional[torch.Tensor] = None, *,
+                              num_seqs: Optional[int] = None, scale: float = 1.0,
+                              qk_l2norm: bool = True, stream=None):
+    """The prefill through kda_chunk_prefill_noalloc (include/kda.h): the library
+    uses its per-device array as the workspace and allocates nothing.  ``out``
+    and ``final_state`` must be given (this wrapper allocates nothing either).
+    Returns ``(out, final_state)``."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    dt = q.dtype
+    if out is None:
+        raise ValueError("kda_chunk_prefill_noalloc: pass out (nothing is allocated here)")
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    gate = _gate(g, (T, H))
+    for name, t, shp in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)),
+                         ("g", g, (T, H) if gate else (T, H, dk)),
+                         ("v", v, (T, H, dv)), ("beta", beta, (T, H)), ("out", out, (T, H, dv))):
+        _check_tensor(name, t, shp, dt, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _check_tensor(name, t, (N, H, dk, dv), torch.float32, dev)
+    dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
+    rc = lib.kda_chunk_prefill_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                                       _ptr(out), _ptr(final_state),
+                                       _stream_handle(stream, dev))
+    if rc != KDA_OK:
+        raise KDAError(rc, "kda_chunk_prefill_noalloc")
     return out, final_state
 
 

@@ -370,3 +370,27 @@ def test_decode_front_end_validation(kda):
     assert call(gate_rank=0, gate_a=None, gate_b=None) == INV  # no gate at all
     assert call(gate_a=A0 + 4) == MIS
 
+
+def test_noalloc_validation(kda):
+    """The no-allocation prefill rejects sizes past its per-device array and bad
+    arguments before touching the device (every call here is rejected: a call
+    that passed validation would launch on these fake addresses)."""
+    lib = kda.load_library()
+    cap = 320 << 20
+    fits = kda.make_dims(8192, 1, 32, 128, 128, kda.KDA_BF16)
+    assert kda.kda_prefill_workspace_bytes(fits) <= cap
+    too_big = kda.make_dims(16384, 1, 32, 128, 128, kda.KDA_BF16)
+    assert kda.kda_prefill_workspace_bytes(too_big) > cap
+    T, H, D = 16384, 32, 128
+    big = T * H * D * 2 + 4096
+    p = [FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, FAKE + 4 * big, None, None,
+         FAKE + 5 * big, None]
+    call = lambda dd, a: lib.kda_chunk_prefill_noalloc(ctypes.byref(dd), *a, None)
+    assert call(too_big, p) == kda.KDA_ERR_WORKSPACE
+    assert call(kda.make_dims(256, 1, 4, 96, 96, kda.KDA_BF16), p) == kda.KDA_ERR_UNSUPPORTED
+    a = list(p); a[0] = None
+    assert call(fits, a) == kda.KDA_ERR_INVALID_ARG
+    a = list(p); a[7] = FAKE + 64                     # out over q
+    assert call(fits, a) == kda.KDA_ERR_INVALID_ARG
+    a = list(p); a[1] = FAKE + big + 8                # k misaligned
+    assert call(fits, a) == kda.KDA_ERR_MISALIGNED
