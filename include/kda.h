@@ -155,6 +155,20 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * device share the second stream; each call's own events keep its launches
  * ordered.
  *
+ * Kernels.  A call with many (sequence, head) chains -- at least twice the
+ * device's compute units -- with bf16 I/O, a per-channel gate and no options
+ * of kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent
+ * workgroups take whole chains, longest sequences first, and step through each
+ * 64-token chunk as four 16-token sub-chunks with the chunk's operands in LDS,
+ * so only the inputs, the outputs and the states touch HBM; it uses only the
+ * first two index areas of the workspace.  Every other call runs the
+ * preparation and recurrence kernels, which hand per-chunk records through the
+ * workspace.  The two compute the same recurrence with the same operand
+ * precision but round in a different order, so their results agree to the
+ * accuracy below, not bit for bit.  The environment variable KDA_PREFILL_PATH
+ * (read at each call) set to "split" or "fused" overrides the choice where the
+ * fused kernel applies.
+ *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Any g <= 0 is handled:
  * inside a 64-token chunk the decay ratios are factored around 16-token block

@@ -3,6 +3,8 @@
 // synchronises; every launch goes on the caller's stream.
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "../../include/kda.h"
@@ -12,6 +14,7 @@
 namespace kda {
 template <typename T, int D> hipError_t launch_prep(const PrefillArgs&, hipStream_t);
 template <typename T, int D> hipError_t launch_recur(const PrefillArgs&, hipStream_t);
+template <int D> hipError_t launch_fused(const PrefillArgs&, hipStream_t);
 
 namespace {
 
@@ -117,7 +120,23 @@ hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S,
 
 }  // namespace
 
+bool fused_path(const PrefillArgs& a) {
+    // the fused kernel covers the plain recurrence in bf16: per-channel gate,
+    // no front end, output gate or checkpoints, the whole call in one launch
+    if (!a.bf16 || a.scalar_g || a.out_gate != 0 || a.fe.active() || a.ckpt_interval > 0) return false;
+    if (a.total_tokens <= 0 || a.slot_begin != 0 || a.slot_end != -1 || a.chunk_begin != 0 ||
+        a.chunk_end != INT64_MAX)
+        return false;
+    const char* env = std::getenv("KDA_PREFILL_PATH");
+    if (env && std::strcmp(env, "split") == 0) return false;
+    if (env && std::strcmp(env, "fused") == 0) return true;
+    const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
+    return a.compute_units > 0 && chains >= kFusedChainsPerCU * (int64_t)a.compute_units;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    if (fused_path(a))
+        return a.d == 128 ? launch_fused<128>(a, s) : launch_fused<64>(a, s);
     // under stream capture the call stays on the caller's stream: no library
     // stream or events enter the caller's graph (the results are the same)
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -452,8 +471,10 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return KDA_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone) return KDA_ERR_WORKSPACE;
+    // (the fused path keeps its records in LDS and needs only the index areas)
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_need, hs) != hipSuccess) return KDA_ERR_HIP;
+    const size_t ws_alloc = kda::fused_path(a) ? a.layout.records_offset() : ws_need;
+    if (hipMallocAsync(&ws, ws_alloc, hs) != hipSuccess) return KDA_ERR_HIP;
     a.workspace = static_cast<unsigned char*>(ws);
     const hipError_t e = kda::launch_prefill(a, hs);
     const hipError_t f = hipFreeAsync(ws, hs);

@@ -1,0 +1,602 @@
+// Fused KDA prefill on gfx950 for calls with many (sequence, head) chains.
+//
+// The two-kernel path hands a record per (chunk, head) from the preparation
+// kernel to the recurrence kernel through HBM, and the record is larger than
+// the chunk's inputs.  With many chains no chain needs more than one workgroup,
+// so here persistent workgroups take whole chains (longest sequences first) and
+// keep everything but the inputs, the outputs and the states on chip.
+//
+// Sub-chunk form.  The delta rule with a diagonal gate ("From KV Cache to
+// Depth Attention: The Bottlenecks Kimi K3 Had to Break", Technical Details,
+// KDA bullet) is unrolled here over blocks of 16 tokens, so the chunk-wise WY
+// form that gives the linear-cost chunked prefill ("Kimi K3: The Manos, The
+// Mythos, The Legendos", bullet on the two-kernel chunked design) runs with
+// the block as its chunk.  In base-2 units (lambda = g log2 e, floored at -128
+// per token), with Gamma_t the inclusive cumulative lambda of token t inside
+// its block, tau the block total, and qhat, khat the normalised rows:
+//     Ke = khat 2^Gamma,  Qe = qhat 2^Gamma,  K' = khat 2^(tau - Gamma)   (all factors <= 1)
+//     A[i][j] = beta_i sum_c khat_i khat_j 2^(Gamma_i - Gamma_j)   (j < i)
+//     M[i][j] =        sum_c qhat_i khat_j 2^(Gamma_i - Gamma_j)   (j <= i)
+//     u = T Diag(beta) (V - Ke S),  T = (I + A)^-1
+//     O = Qe S + M u,   S <- Diag(2^tau) S + K'^T u
+// A chunk of 64 tokens is four such steps.  Compared with the 64-token form of
+// the two-kernel path this drops the blocks of A and M off the 16 x 16
+// diagonal, the blocked inverse and the W and U products, and the recurrence
+// takes one more small product (T Diag(beta) times V - Ke S) per block.
+//
+// Diagonal products.  A and M factor as Ke_i . (K'_j 2^-tau) while every
+// channel's block decay keeps 2^-tau <= 2^64; past that they are taken exactly
+// by bisection levels (halves of 8, 4, 2, 1 tokens; with b the last token of
+// the left half, 2^(Gamma_i - Gamma_j) = 2^(Gamma_i - Gamma_b) 2^(Gamma_b -
+// Gamma_j), both factors <= 1), one masked product per level.
+//
+// Inverse.  N = Diag(beta) A is strictly lower and 16 x 16, so N^16 = 0 and
+//     T = (I - N)(I + N^2)(I + N^4)(I + N^8),
+// eight fp32 16 x 16 products on MFMA inside one wave, no LDS traffic.
+//
+// Layout.  A workgroup has d/16 waves.  In the preparation wave w takes
+// block w % 4 and the channel half w / 4 (64 channels), lane (t, g) = (lane %
+// 16, lane / 16) holding token t of the block and channels 32 ks + 4 g + {0..3}
+// and 32 ks + 16 + 4 g + {0..3} of each 32-channel slice ks.  That channel
+// order is the K order of every 16 x 16 x 32 product here, chosen so the state
+// rows a lane holds as accumulator (rows 4 g + e of each 16-row tile) are, as
+// they stand, its B operand: no state data moves between lanes.  K'^T is
+// transposed by a product with a 0/1 selector operand.  In the recurrence wave
+// w owns value columns 16 w .. 16 w + 15 of the fp32 state (rows in
+// accumulator layout), needs no other wave's state and no barrier; the
+// block's operands come from the record in LDS.
+#include <algorithm>
+#include <atomic>
+
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+constexpr float kSubFactoredMax = 64.f;  // largest block log2-decay of the factored products
+constexpr float kSubMinLog2 = -128.f;    // floor of a token's log2-decay
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Operands of one 64-token chunk (four 16-token blocks), in MFMA lane order.
+template <int D>
+struct SubRecord {
+    static constexpr int NKS = D / 32, NCT = D / 16;
+    bf16x8 ke[4][NKS][kWave];  // Ke (A operand of Ke S, channel order above)
+    bf16x8 qe[4][NKS][kWave];  // Qe
+    bf16x4 kt[4][NCT][kWave];  // K'^T, 16-channel tiles (A operand, K = tokens)
+    bf16x4 tb[4][kWave];       // T Diag(beta)
+    bf16x4 m[4][kWave];        // M
+    f32x4 gend[4][D / 4];      // 2^tau per channel
+};
+
+template <int D>
+struct FusedSmem {
+    static constexpr int NPART = D == 128 ? 4 : 1;
+    SubRecord<D> rec;
+    f32x4 part[NPART][3][kWave];  // second channel half's A, A^T, M^T partial products
+    float sumsq[2][2][64];        // [q, k][channel half][token]: partial sums of squares
+    int exact[4][2];              // [block][channel half]: past the factored range
+    int next;                     // the chain this workgroup takes next
+};
+
+struct FusedParams {
+    const bf16 *q, *k, *v, *g, *beta;
+    const int32_t* cu;      // [N + 1] or null (equal lengths)
+    const float* init;      // [N, H, D, D] or null (zero state)
+    float* fin;             // [N, H, D, D] or null
+    bf16* out;              // [T, H, D]
+    const int32_t* order;   // sequences longest first, or null (natural order)
+    int32_t* counter;       // chains handed out so far (zeroed before the launch)
+    int64_t total_tokens;
+    int32_t n_seqs, n_heads;
+    float scale;
+    int l2norm;
+};
+
+__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (bf16)x[e];
+    return r;
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
+    return r;
+}
+
+// X^T Y for 16 x 16 fp32 matrices held in accumulator layout (lane (n, g)
+// holds rows 4 g .. 4 g + 3 of column n): the K index of step s is 4 g + s, so
+// each lane feeds its own element s of both.
+__device__ __forceinline__ f32x4 mm_tn(const f32x4& X, const f32x4& Y) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[s], Y[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// T^T for T = (I + N)^-1, N strictly lower 16 x 16, from N and N^T.
+__device__ __forceinline__ f32x4 unit_lower_inverse_t(const f32x4& N, const f32x4& Nt, int n16,
+                                                      int g) {
+    const f32x4 N2 = mm_tn(Nt, N), N2t = mm_tn(N, Nt);
+    const f32x4 N4 = mm_tn(N2t, N2), N4t = mm_tn(N2, N2t);
+    const f32x4 N8 = mm_tn(N4t, N4);
+    f32x4 G;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) G[e] = (4 * g + e == n16) ? 1.f : 0.f;
+    G = G - Nt + N2t - mm_tn(N2, Nt);  // (I + N2^T)(I - N^T)
+    G += mm_tn(N4, G);                 // (I + N4^T) G
+    G += mm_tn(N8, G);                 // (I + N8^T) G
+    return G;
+}
+
+// Exact diagonal products of one block at bisection level L (0: the diagonal
+// of M): P = fk fk^T and Q = fk fq^T over this lane's channels, with fk, fq the
+// rows scaled by this token's factor at the level.
+__device__ __forceinline__ void exact_level(int L, int n16, int g, const float (&kh)[2][8],
+                                            const float (&qh)[2][8], const float (&gam)[2][8],
+                                            f32x4& P, f32x4& Q) {
+    const int h = L == 0 ? 0 : (16 >> L);
+    const int within = L == 0 ? 0 : (n16 & (2 * h - 1));
+    const bool right = L > 0 && within >= h;
+    const int b = L == 0 ? n16 : n16 - within + h - 1;  // reference token
+    P = f32x4{0.f, 0.f, 0.f, 0.f};
+    Q = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        float fk[8], fq[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float gb = __shfl(gam[kk][i], b + 16 * g, kWave);
+            // gamma decreases along the block, so the exponent is <= 0 (the clamp
+            // absorbs rounding in the sums); level 0 has factor 1
+            const float f =
+                L == 0 ? 1.f : exp2_hw(fminf(right ? gam[kk][i] - gb : gb - gam[kk][i], 0.f));
+            fk[i] = kh[kk][i] * f;
+            fq[i] = qh[kk][i] * f;
+        }
+        const bf16x8 a = to_bf16x8(fk), c = to_bf16x8(fq);
+        P = mfma32(a, a, P);
+        Q = mfma32(a, c, Q);
+    }
+}
+
+// Where one chunk's rows of head h lie: a load past row Lc - 1 reads zero.
+template <int D>
+struct ChunkRange {
+    int64_t ebase;      // element offset of (first token, head h, channel 0)
+    uint32_t rowb;      // bytes per token row (all heads)
+    uint32_t nbytes;    // bytes from ebase to the end of row Lc - 1 of head h
+    __device__ ChunkRange(int64_t tok0, int Lc, int64_t H, int h)
+        : ebase((tok0 * H + h) * D),
+          rowb((uint32_t)(H * D * 2)),
+          nbytes((uint32_t)(((int64_t)(Lc - 1) * H * D + D) * 2)) {}
+};
+
+// One chunk's inputs for one lane: for the preparation q, k, g of token
+// 16 R + lane % 16 over the lane's 16 channels of half hf, and beta; for the
+// recurrence V at tokens 16 Rb + 4 (lane / 16) + e, column 16 w + lane % 16.
+// The 16-bit values are kept zero-extended, one per register: packing two
+// per register would need the loads to have landed at the point of packing.
+struct ChunkRows {
+    bf16x4 q[2][2], k[2][2], g[2][2];
+    uint32_t beta;
+    uint32_t v[4][4];
+};
+
+// fp32 value of a zero-extended bf16
+__device__ __forceinline__ float bf16_bits_f32(uint32_t x) { return __uint_as_float(x << 16); }
+
+template <int D>
+__device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
+                                                int w, int lane, ChunkRows& r) {
+    const int n16 = lane & 15, g = lane >> 4, R = w & 3, hf = w >> 2, col = 16 * w + n16;
+    const int64_t H = p.n_heads;
+    const ChunkRange<D> c(tok0, Lc, H, h);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.beta + tok0 * H + h, (uint32_t)(((int64_t)(Lc - 1) * H + 1) * 2));
+    const uint32_t roff = (uint32_t)(16 * R + n16) * c.rowb;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+            const uint32_t off = roff + (uint32_t)(32 * (2 * hf + kk) + 16 * hl + 4 * g) * 2;
+            r.q[kk][hl] = buffer_load<bf16x4>(rq, off);
+            r.k[kk][hl] = buffer_load<bf16x4>(rk, off);
+            r.g[kk][hl] = buffer_load<bf16x4>(rg, off);
+        }
+    r.beta = buffer_load<uint16_t>(rb, (uint32_t)(16 * R + n16) * (uint32_t)H * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + c.ebase, c.nbytes);
+#pragma unroll
+    for (int Rb = 0; Rb < 4; ++Rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r.v[Rb][e] = buffer_load<uint16_t>(rv, (uint32_t)(16 * Rb + 4 * g + e) * c.rowb + (uint32_t)col * 2);
+}
+
+// One 64-token chunk of one chain: the preparation writes the chunk's record
+// to LDS, then every wave runs the recurrence over the four blocks on its 16
+// value columns of S.  `rows` holds the chunk's inputs and is refilled with
+// those of the next chunk (next_len > 0) before the recurrence, so their loads
+// overlap it (and every wait of a chunk is for data asked for a chunk
+// earlier: loads and stores share one in-order counter).  `lane` is the lane
+// index (passed in, so the caller can hand over a copy the compiler cannot
+// see through).
+template <int D>
+__device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& sm,
+                                            f32x4 (&S)[D / 16], int w, int lane, int64_t tok0,
+                                            int Lc, int h, ChunkRows& rows, int next_len) {
+    constexpr int NKS = D / 32, NCT = D / 16, NHALF = D / 64;
+    const int n16 = lane & 15, g = lane >> 4, col = 16 * w + n16;
+    const int R = w & 3, hf = w >> 2;  // preparation: block, channel half
+    const int64_t H = p.n_heads;
+
+    // ---- preparation, block R, channels of half hf; lane token 16 R + n16
+    const bf16x4(&qv)[2][2] = rows.q;
+    const bf16x4(&kv)[2][2] = rows.k;
+    const bf16x4(&gv)[2][2] = rows.g;
+    const float bt = bf16_bits_f32(rows.beta);
+
+    // in-block cumulative log2-decay: a scan over the 16 lanes of each row
+    float gam[2][8], tau[2][8];
+    float sq = 0.f, sk = 0.f;
+    bool big = false;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float x = fmaxf(to_f32(gv[kk][i >> 2][i & 3]) * kLog2e, kSubMinLog2);
+            x += dpp<0x111>(x);  // row_shr:1
+            x += dpp<0x112>(x);  // row_shr:2
+            x += dpp<0x114>(x);  // row_shr:4
+            x += dpp<0x118>(x);  // row_shr:8
+            gam[kk][i] = x;
+            tau[kk][i] = __shfl(x, lane | 15, kWave);
+            big |= -tau[kk][i] > kSubFactoredMax;
+            const float qx = to_f32(qv[kk][i >> 2][i & 3]), kx = to_f32(kv[kk][i >> 2][i & 3]);
+            sq += qx * qx;
+            sk += kx * kx;
+        }
+    sq += xor_shfl(sq, 16);
+    sq += xor_shfl(sq, 32);
+    sk += xor_shfl(sk, 16);
+    sk += xor_shfl(sk, 32);
+    int ex = __builtin_amdgcn_readfirstlane(__ballot(big) != 0ull ? 1 : 0);
+    if constexpr (NHALF == 2) {
+        if (g == 0) {
+            sm.sumsq[0][hf][16 * R + n16] = sq;
+            sm.sumsq[1][hf][16 * R + n16] = sk;
+        }
+        if (lane == 0) sm.exact[R][hf] = ex;
+        __syncthreads();  // B1
+        sq += sm.sumsq[0][hf ^ 1][16 * R + n16];
+        sk += sm.sumsq[1][hf ^ 1][16 * R + n16];
+        ex = __builtin_amdgcn_readfirstlane(sm.exact[R][0] | sm.exact[R][1]);
+    }
+    const float rqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f) * p.scale;
+    const float rks = p.l2norm ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
+
+    f32x4 Aa = {0.f, 0.f, 0.f, 0.f}, Ata = Aa, Mta = Aa;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * hf + kk;
+        float ke[8], qe[8], kf[8], kfs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float kh = to_f32(kv[kk][i >> 2][i & 3]) * rks;
+            const float qh = to_f32(qv[kk][i >> 2][i & 3]) * rqs;
+            const float E = exp2_hw(gam[kk][i]);
+            const float F = exp2_hw(tau[kk][i] - gam[kk][i]);
+            ke[i] = kh * E;
+            qe[i] = qh * E;
+            kf[i] = kh * F;
+            // (clamped: unused, but finite, when the block is past the range)
+            kfs[i] = kf[i] * exp2_hw(fminf(-tau[kk][i], kSubFactoredMax));
+        }
+        const bf16x8 KE = to_bf16x8(ke), QE = to_bf16x8(qe), KF = to_bf16x8(kf);
+        sm.rec.ke[R][ks][lane] = KE;
+        sm.rec.qe[R][ks][lane] = QE;
+        if (!ex) {
+            const bf16x8 KS = to_bf16x8(kfs);
+            Aa = mfma32(KE, KS, Aa);    // A[i][j] / beta_i
+            Ata = mfma32(KS, KE, Ata);  // its transpose
+            Mta = mfma32(KS, QE, Mta);  // M^T
+        }
+        // K'^T tiles 2 ks, 2 ks + 1: products with 0/1 selectors that take
+        // channel 32 ks + n (lo) or 32 ks + 16 + n (hi) into output column n
+        bf16x8 sel_lo, sel_hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool mine = g == (n16 >> 2) && (j & 3) == (n16 & 3);
+            sel_lo[j] = (bf16)((mine && j < 4) ? 1.f : 0.f);
+            sel_hi[j] = (bf16)((mine && j >= 4) ? 1.f : 0.f);
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        sm.rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
+        sm.rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
+        if (n16 == 0) {
+            sm.rec.gend[R][8 * ks + g] = f32x4{exp2_hw(tau[kk][0]), exp2_hw(tau[kk][1]),
+                                               exp2_hw(tau[kk][2]), exp2_hw(tau[kk][3])};
+            sm.rec.gend[R][8 * ks + 4 + g] = f32x4{exp2_hw(tau[kk][4]), exp2_hw(tau[kk][5]),
+                                                   exp2_hw(tau[kk][6]), exp2_hw(tau[kk][7])};
+        }
+    }
+    if (ex) {
+        float kh[2][8], qh[2][8];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kh[kk][i] = to_f32(kv[kk][i >> 2][i & 3]) * rks;
+                qh[kk][i] = to_f32(qv[kk][i >> 2][i & 3]) * rqs;
+            }
+        // every pair (i, j) belongs to exactly one level: select, not add
+#pragma unroll 1
+        for (int L = 0; L <= 4; ++L) {
+            f32x4 P, Q;
+            exact_level(L, n16, g, kh, qh, gam, P, Q);
+            const int sh = 5 - L, m2 = (32 >> L) - 1, hh = 16 >> L;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                if (L == 0) {
+                    Mta[e] = r == n16 ? Q[e] : Mta[e];
+                } else {
+                    const bool same = (r >> sh) == (n16 >> sh);
+                    // (i, j) = (r, n16) and (n16, r): i in the right half, j in the left
+                    const bool a_rn = same && (r & m2) >= hh && (n16 & m2) < hh;
+                    const bool a_nr = same && (n16 & m2) >= hh && (r & m2) < hh;
+                    Aa[e] = a_rn ? P[e] : Aa[e];
+                    Ata[e] = a_nr ? P[e] : Ata[e];
+                    Mta[e] = a_nr ? Q[e] : Mta[e];
+                }
+            }
+        }
+    }
+    if constexpr (NHALF == 2) {
+        if (hf == 1) {
+            sm.part[R][0][lane] = Aa;
+            sm.part[R][1][lane] = Ata;
+            sm.part[R][2][lane] = Mta;
+        }
+        __syncthreads();  // B2
+    }
+    if (hf == 0) {
+        if constexpr (NHALF == 2) {
+            Aa += sm.part[R][0][lane];
+            Ata += sm.part[R][1][lane];
+            Mta += sm.part[R][2][lane];
+        }
+        f32x4 N, Nt, Mt, bi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            bi[e] = __shfl(bt, r, kWave);  // beta of token r
+            N[e] = n16 < r ? Aa[e] * bi[e] : 0.f;
+            Nt[e] = r < n16 ? Ata[e] * bt : 0.f;
+            Mt[e] = r <= n16 ? Mta[e] : 0.f;
+        }
+        const f32x4 Tt = unit_lower_inverse_t(N, Nt, n16, g);
+        sm.rec.tb[R][lane] = to_bf16x4(Tt * bi);
+        sm.rec.m[R][lane] = to_bf16x4(Mt);
+    }
+    __syncthreads();  // B3: the record is complete
+
+    uint32_t vv[4][4];  // this chunk's V (rows is refilled next)
+#pragma unroll
+    for (int Rb = 0; Rb < 4; ++Rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[Rb][e] = rows.v[Rb][e];
+    if (next_len > 0) load_chunk_rows<D>(p, tok0 + 64, next_len, h, w, lane, rows);
+
+    // ---- recurrence over the four blocks, value columns of this wave
+#pragma unroll
+    for (int Rb = 0; Rb < 4; ++Rb) {
+        bf16x8 Sb[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Sb[ks][e] = (bf16)S[2 * ks][e];
+                Sb[ks][4 + e] = (bf16)S[2 * ks + 1][e];
+            }
+        f32x4 X = {0.f, 0.f, 0.f, 0.f}, O = X;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            X = mfma32(sm.rec.ke[Rb][ks][lane], Sb[ks], X);
+            O = mfma32(sm.rec.qe[Rb][ks][lane], Sb[ks], O);
+        }
+        bf16x4 Y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(bf16_bits_f32(vv[Rb][e]) - X[e]);
+        const bf16x4 u = to_bf16x4(mfma16(sm.rec.tb[Rb][lane], Y, f32x4{0.f, 0.f, 0.f, 0.f}));
+        O = mfma16(sm.rec.m[Rb][lane], u, O);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * Rb + 4 * g + e;
+            if (row < Lc) p.out[((tok0 + row) * H + h) * D + col] = (bf16)O[e];
+        }
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt)
+            S[rt] = mfma16(sm.rec.kt[Rb][rt][lane], u, S[rt] * sm.rec.gend[Rb][4 * rt + g]);
+    }
+    // (d = 128: the next chunk writes the record only after its B1)
+    if constexpr (NHALF == 1) __syncthreads();
+}
+
+// A workgroup of d/16 waves works on one chain at a time; persistent, chains
+// handed out through `counter` in `order`.  Every workgroup takes chains until
+// the counter passes the last one, so all of them finish.
+template <int D>
+__global__ __launch_bounds__(D * 4, 2) void fused_kernel(FusedParams p) {
+    constexpr int NCT = D / 16;
+    __shared__ FusedSmem<D> sm;
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n16 = lane & 15, g = lane >> 4, col = 16 * w + n16;
+    const int64_t H = p.n_heads;
+    const int64_t chains = (int64_t)p.n_seqs * H;
+    for (;;) {
+        if (t == 0) sm.next = atomicAdd(p.counter, 1);
+        __syncthreads();
+        const int64_t ci = sm.next;
+        __syncthreads();  // every thread has read `next` before it is written again
+        if (ci >= chains) break;
+        const int64_t si = ci / H;
+        const int h = (int)(ci - si * H);
+        const int64_t n = p.order ? (int64_t)p.order[si] : si;
+        int64_t s_begin, s_len;
+        if (p.cu) {
+            s_begin = p.cu[n];
+            s_len = (int64_t)p.cu[n + 1] - s_begin;
+        } else {
+            s_len = p.total_tokens / p.n_seqs;
+            s_begin = n * s_len;
+        }
+        // this lane's state: rows 16 rt + 4 g + e, column col
+        const int64_t sbase = (n * H + h) * D * D;
+        f32x4 S[NCT];
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[rt][e] = p.init ? p.init[sbase + (int64_t)(16 * rt + 4 * g + e) * D + col] : 0.f;
+        const int64_t nch = (s_len + 63) / 64;
+        ChunkRows rows;
+        if (nch > 0) load_chunk_rows<D>(p, s_begin, (int)min((int64_t)64, s_len), h, w, lane, rows);
+        for (int64_t kc = 0; kc < nch; ++kc) {
+            // a copy of the lane index the compiler cannot see through: the
+            // chunk's index arithmetic is redone per chunk instead of hoisted
+            // out of this loop and held in registers across it
+            int lane_c = lane;
+            asm volatile("" : "+v"(lane_c));
+            const int64_t rest = s_len - 64 * kc;  // tokens from this chunk on
+            fused_chunk<D>(p, sm, S, w, lane_c, s_begin + 64 * kc, (int)min((int64_t)64, rest), h,
+                           rows, (int)max((int64_t)0, min((int64_t)64, rest - 64)));
+        }
+        if (p.fin) {
+#pragma unroll
+            for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p.fin[sbase + (int64_t)(16 * rt + 4 * g + e) * D + col] = S[rt][e];
+        }
+    }
+}
+
+// Largest number of sequences the order kernel sorts (in LDS); past it the
+// chains go in their natural order.
+constexpr int kOrderSortMax = 2048;
+
+// Zeroes the chain counter and writes the sequences in order of decreasing
+// length (ties by index): a bitonic sort of (length, index) keys in LDS by one
+// workgroup of 1024 threads, two keys each.
+__global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __restrict__ cu,
+                                                           int32_t n_seqs,
+                                                           int32_t* __restrict__ order,
+                                                           int32_t* __restrict__ counter) {
+    __shared__ uint64_t key[kOrderSortMax];
+    const int t = threadIdx.x;
+    if (t == 0) *counter = 0;
+    if (!cu || n_seqs > kOrderSortMax) {
+        for (int i = t; i < n_seqs; i += 1024) order[i] = i;
+        return;
+    }
+    // ascending keys: (0xffffffff - length) << 32 | index; padding sorts last
+    for (int i = t; i < kOrderSortMax; i += 1024) {
+        uint64_t k = ~0ull;
+        if (i < n_seqs) {
+            const uint32_t len = (uint32_t)(cu[i + 1] - cu[i]);
+            k = ((uint64_t)(0xffffffffu - len) << 32) | (uint32_t)i;
+        }
+        key[i] = k;
+    }
+    __syncthreads();
+    for (int size = 2; size <= kOrderSortMax; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = t; i < kOrderSortMax; i += 1024) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool up = (i & size) == 0;
+                    const uint64_t a = key[i], c = key[j];
+                    if ((a > c) == up) {
+                        key[i] = c;
+                        key[j] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = t; i < n_seqs; i += 1024) order[i] = (int32_t)(key[i] & 0xffffffffu);
+}
+
+// Resident workgroups per CU of fused_kernel<D> (queried once per process; the
+// answer depends only on the kernel's resources and the gfx950 CU).
+template <int D>
+hipError_t fused_blocks_per_cu(int* out) {
+    static std::atomic<int> cached{0};
+    int c = cached.load(std::memory_order_relaxed);
+    if (c <= 0) {
+        const hipError_t e =
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_kernel<D>, D * 4, 0);
+        if (e != hipSuccess) return e;
+        if (c <= 0) c = 1;
+        cached.store(c, std::memory_order_relaxed);
+    }
+    *out = c;
+    return hipSuccess;
+}
+
+}  // namespace
+
+template <int D>
+hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
+    if (!a.bf16 || a.d != D) return hipErrorInvalidValue;
+    FusedParams fp;
+    fp.q = static_cast<const bf16*>(a.q);
+    fp.k = static_cast<const bf16*>(a.k);
+    fp.v = static_cast<const bf16*>(a.v);
+    fp.g = static_cast<const bf16*>(a.g);
+    fp.beta = static_cast<const bf16*>(a.beta);
+    fp.cu = a.cu_seqlens;
+    fp.init = a.initial_state;
+    fp.fin = a.final_state;
+    fp.out = static_cast<bf16*>(a.out);
+    fp.total_tokens = a.total_tokens;
+    fp.n_seqs = a.n_seqs;
+    fp.n_heads = a.n_heads;
+    fp.scale = a.scale;
+    fp.l2norm = a.l2norm;
+    // the chain counter and the order live in the workspace's two index areas
+    int32_t* order = reinterpret_cast<int32_t*>(a.workspace + a.layout.ckidx_offset());
+    fp.counter = reinterpret_cast<int32_t*>(a.workspace);
+    fp.order = a.cu_seqlens ? order : nullptr;
+    hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens,
+                       a.n_seqs, order, fp.counter);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int per_cu = 1;
+    if ((e = fused_blocks_per_cu<D>(&per_cu)) != hipSuccess) return e;
+    const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
+    const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
+    const int grid = (int)std::min<int64_t>(chains, cus * per_cu);
+    hipLaunchKernelGGL((fused_kernel<D>), dim3(grid), dim3(D * 4), 0, stream, fp);
+    return hipGetLastError();
+}
+
+template hipError_t launch_fused<128>(const PrefillArgs&, hipStream_t);
+template hipError_t launch_fused<64>(const PrefillArgs&, hipStream_t);
+
+}  // namespace kda

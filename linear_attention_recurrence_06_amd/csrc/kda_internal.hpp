@@ -138,6 +138,15 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Chains (sequence, head) per compute unit from which a prefill takes the
+// fused kernel (one persistent workgroup per CU working through whole chains)
+// instead of the preparation and recurrence kernels.
+constexpr int64_t kFusedChainsPerCU = 2;
+
+// Whether launch_prefill takes the fused kernel for these arguments.  The
+// environment variable KDA_PREFILL_PATH=split or =fused overrides the choice
+// where the fused kernel applies.
+bool fused_path(const PrefillArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kda

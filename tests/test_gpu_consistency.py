@@ -261,10 +261,13 @@ def test_many_short_sequences(lib, oracle):
 
 
 @pytest.mark.parametrize("d,n_seqs", [(128, 600), (64, 520)])
-def test_wide_column_tiles(lib, oracle, d, n_seqs):
+def test_wide_column_tiles(lib, oracle, monkeypatch, d, n_seqs):
     """Enough chains (sequences x 4 heads >= 2,048 / (d / 64)) that the
     recurrence takes 64-column tiles: ragged packed sequences of 0..200 tokens
-    against the oracle."""
+    against the oracle.  This many chains would take the fused kernel, so the
+    two-kernel path is forced (its checkpoint and output-gate variants are
+    checked bit for bit against its plain result)."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
     from kda_inputs import make_prefill
     rng = np.random.default_rng(44 + d)
     lens = rng.integers(0, 201, size=n_seqs).tolist()

@@ -1,0 +1,190 @@
+"""GPU tests of the fused prefill kernel: persistent workgroups take whole
+(sequence, head) chains and run each 64-token chunk as four 16-token steps,
+with the chunk's operands in LDS, so nothing but the inputs, the outputs and
+the states reaches HBM.
+
+* Parity with the fp64 oracle at the bf16 bar (max abs error 2e-2, every
+  output finite) on packed ragged batches with empty sequences, equal lengths
+  without cu_seqlens, decay strong enough for the exact diagonal products
+  (g = -8, -30, 1% at -100), no initial and no final state, d = 64 and 128.
+* Agreement with the two-kernel path (64-token chunks: the same arithmetic up
+  to rounding order) within twice that bar where the oracle would be slow:
+  more sequences than the length sort takes, a sort full of empty sequences.
+* The automatic choice, the library-allocated workspace and the
+  allocation-free entry point give the same bytes as the forced fused path.
+
+KDA_PREFILL_PATH=split / =fused forces the path for a call.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+def maxerr(a, b):
+    a = np.asarray(a, np.float64)
+    return float(np.max(np.abs(a - np.asarray(b, np.float64)))) if a.size else 0.0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_recurrence_06_amd as kda
+    kda.load_library()
+    return kda
+
+
+def args_of(inp):
+    return (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+            inp["cu_seqlens"])
+
+
+def run(lib, monkeypatch, inp, path, **kw):
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    out, fin = lib.kda_chunk_prefill(*args_of(inp), num_seqs=len(inp["lens"]), **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def same(a, b):
+    if a is None or b is None:
+        return a is None and b is None
+    return torch.equal(a, b)
+
+
+def fused_near_split(lib, monkeypatch, inp, label, **kw):
+    """The fused path, checked against the two-kernel path within 2 TOL."""
+    o_s, f_s = run(lib, monkeypatch, inp, "split", **kw)
+    o_f, f_f = run(lib, monkeypatch, inp, "fused", **kw)
+    eo = maxerr(host(o_f), host(o_s))
+    ef = maxerr(host(f_f), host(f_s)) if f_f is not None else 0.0
+    say(f"[{label}] fused vs split: out {eo:.3e} state {ef:.3e}")
+    assert torch.isfinite(o_f.float()).all()
+    assert (f_f is None) == (f_s is None)
+    assert f_f is None or torch.isfinite(f_f).all()
+    assert eo <= 2 * TOL and ef <= 2 * TOL
+    return o_f, f_f
+
+
+def oracle_check(oracle, inp, out, fin, label):
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].cpu().numpy()
+    o_ref, f_ref = oracle.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]),
+                                  host(inp["beta"]), cu_seqlens=cu,
+                                  initial_state=host(inp["initial_state"]),
+                                  n_seqs=len(inp["lens"]))
+    eo = maxerr(host(out), o_ref)
+    ef = maxerr(host(fin), f_ref) if fin is not None else 0.0
+    say(f"[{label}] oracle err_out={eo:.3e} err_state={ef:.3e} tol={TOL}")
+    assert eo <= TOL and ef <= TOL
+
+
+RAGGED = [1, 63, 64, 65, 0, 127, 128, 129, 300, 1000, 0, 5]
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_ragged_packed(lib, oracle, monkeypatch, d):
+    from kda_inputs import make_prefill
+    inp = make_prefill(RAGGED, 3, d, "bf16", g_scale=0.5, s0_std=0.02, seed=501 + d,
+                       device="cuda")
+    out, fin = fused_near_split(lib, monkeypatch, inp, f"ragged d={d}")
+    oracle_check(oracle, inp, out, fin, f"ragged d={d}")
+
+
+def test_equal_lengths_without_cu(lib, oracle, monkeypatch):
+    from kda_inputs import make_prefill
+    inp = make_prefill([320] * 6, 4, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=511,
+                       device="cuda", packed_cu=False)
+    assert inp["cu_seqlens"] is None
+    out, fin = fused_near_split(lib, monkeypatch, inp, "equal lengths")
+    oracle_check(oracle, inp, out, fin, "equal lengths")
+
+
+def test_more_sequences_than_the_sort(lib, monkeypatch):
+    """2,500 sequences (past the 2,048 the length sort takes: chains go in
+    their natural order), lengths uniform in [0, 130]."""
+    from kda_inputs import draw_lengths, make_prefill
+    lens = draw_lengths(2500, 0, 130, seed=512)
+    inp = make_prefill(lens, 1, 64, "bf16", g_scale=0.5, s0_std=0.02, seed=512, device="cuda")
+    fused_near_split(lib, monkeypatch, inp, "2,500 sequences")
+
+
+def test_sort_with_many_empty_sequences(lib, monkeypatch):
+    """2,048 sequences, most of them empty: the sort's full width, and chains
+    with no chunks (final state = initial state)."""
+    from kda_inputs import make_prefill
+    lens = [0] * 2048
+    for i in range(0, 2048, 97):
+        lens[i] = 1 + (i * 37) % 300
+    inp = make_prefill(lens, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=513, device="cuda")
+    _, fin = fused_near_split(lib, monkeypatch, inp, "2,048 sequences, most empty")
+    empty = [i for i, n in enumerate(lens) if n == 0]
+    assert torch.equal(fin[empty], inp["initial_state"][empty])  # no chunks: copied
+
+
+@pytest.mark.parametrize("g_value", [-8.0, -30.0])
+def test_strong_decay(lib, oracle, monkeypatch, g_value):
+    """Blocks past the factored range in every channel (the exact diagonal
+    blocks), plus 1% of gates at -100."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([200, 77, 64, 1, 130], 2, 128, "bf16", g_scale=0.5, s0_std=0.02,
+                       seed=514, device="cuda")
+    g = torch.full_like(inp["g"], g_value)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(515)
+    g[torch.rand(g.shape, generator=gen, device="cuda") < 0.01] = -100.0
+    inp["g"] = g
+    out, fin = fused_near_split(lib, monkeypatch, inp, f"g={g_value}")
+    oracle_check(oracle, inp, out, fin, f"g={g_value}")
+
+
+def test_no_initial_no_final_state(lib, oracle, monkeypatch):
+    from kda_inputs import make_prefill
+    inp = make_prefill([65, 0, 190, 3], 2, 128, "bf16", g_scale=0.5, s0_std=None, seed=516,
+                       device="cuda")
+    assert inp["initial_state"] is None
+    out, fin = fused_near_split(lib, monkeypatch, inp, "no states", output_final_state=False)
+    assert fin is None
+    oracle_check(oracle, inp, out, None, "no states")
+
+
+def test_auto_choice_many_chains(lib, monkeypatch):
+    """64 sequences of 64..2,048 tokens x 8 heads: 512 chains, enough per CU
+    for the automatic choice to take the fused kernel on a 256-CU device."""
+    from kda_inputs import draw_lengths, make_prefill
+    lens = draw_lengths(64, 64, 2048, seed=517)
+    inp = make_prefill(lens, 8, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=517, device="cuda")
+    o_f, f_f = run(lib, monkeypatch, inp, "fused")
+    o_a, f_a = run(lib, monkeypatch, inp, "auto")
+    assert torch.equal(o_a, o_f) and torch.equal(f_a, f_f)
+
+
+def test_library_workspace_and_noalloc(lib, monkeypatch):
+    """The fused path given no workspace (the library allocates only the index
+    areas on the stream) and through the allocation-free entry point."""
+    from kda_inputs import make_prefill
+    inp = make_prefill(RAGGED, 4, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=518,
+                       device="cuda")
+    o_s, f_s = run(lib, monkeypatch, inp, "fused")
+    o_l, f_l = run(lib, monkeypatch, inp, "fused", library_workspace=True)
+    assert torch.equal(o_l, o_s) and torch.equal(f_l, f_s)
+    o_n, f_n = torch.empty_like(o_s), torch.empty_like(f_s)
+    lib.kda_chunk_prefill_noalloc(*args_of(inp), o_n, f_n, num_seqs=len(inp["lens"]))
+    torch.cuda.synchronize()
+    assert torch.equal(o_n, o_s) and torch.equal(f_n, f_s)
