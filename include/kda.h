@@ -56,9 +56,10 @@
  * kda_chunk_prefill; created once under a lock) and the device array of
  * kda_chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES, allocated when the
  * library is loaded on a device), all kept until the process ends.  The
- * kernels use no
- * atomics, so identical inputs and sizes give bitwise identical results (a
- * pipelined call included).
+ * fused prefill kernel hands out (sequence, head) chains through a device
+ * counter, but a chain's arithmetic does not depend on which workgroup runs
+ * it, and no other kernel uses atomics: identical inputs and sizes give
+ * bitwise identical results (a pipelined call included).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -156,12 +157,12 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * ordered.
  *
  * Kernels.  A call with many (sequence, head) chains -- at least twice the
- * device's compute units -- with bf16 I/O, a per-channel gate and no options
- * of kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent
- * workgroups take whole chains, longest sequences first, and step through each
- * 64-token chunk as four 16-token sub-chunks with the chunk's operands in LDS,
- * so only the inputs, the outputs and the states touch HBM; it uses only the
- * first two index areas of the workspace.  Every other call runs the
+ * device's compute units -- with bf16 I/O, a per-channel gate, out aligned to
+ * 16 bytes and no options of kda_chunk_prefill_ex or checkpoints runs one
+ * fused kernel: persistent workgroups take whole chains, longest sequences
+ * first, and step through each 64-token chunk as four 16-token sub-chunks with
+ * the chunk's operands in LDS, so only the inputs, the outputs and the states
+ * touch HBM; it uses only the first two index areas of the workspace.  Every other call runs the
  * preparation and recurrence kernels, which hand per-chunk records through the
  * workspace.  The two compute the same recurrence with the same operand
  * precision but round in a different order, so their results agree to the

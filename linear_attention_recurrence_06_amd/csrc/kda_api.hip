@@ -122,8 +122,10 @@ hipError_t launch_prefill_pipelined(const PrefillArgs& a0, hipStream_t s, int S,
 
 bool fused_path(const PrefillArgs& a) {
     // the fused kernel covers the plain recurrence in bf16: per-channel gate,
-    // no front end, output gate or checkpoints, the whole call in one launch
+    // no front end, output gate or checkpoints, the whole call in one launch;
+    // it writes the outputs in 16-byte pieces
     if (!a.bf16 || a.scalar_g || a.out_gate != 0 || a.fe.active() || a.ckpt_interval > 0) return false;
+    if ((reinterpret_cast<uintptr_t>(a.out) & 15) != 0) return false;
     if (a.total_tokens <= 0 || a.slot_begin != 0 || a.slot_end != -1 || a.chunk_begin != 0 ||
         a.chunk_end != INT64_MAX)
         return false;

@@ -36,15 +36,17 @@
 //
 // Layout.  A workgroup has d/16 waves.  In the preparation wave w takes
 // block w % 4 and the channel half w / 4 (64 channels), lane (t, g) = (lane %
-// 16, lane / 16) holding token t of the block and channels 32 ks + 4 g + {0..3}
-// and 32 ks + 16 + 4 g + {0..3} of each 32-channel slice ks.  That channel
-// order is the K order of every 16 x 16 x 32 product here, chosen so the state
-// rows a lane holds as accumulator (rows 4 g + e of each 16-row tile) are, as
-// they stand, its B operand: no state data moves between lanes.  K'^T is
-// transposed by a product with a 0/1 selector operand.  In the recurrence wave
-// w owns value columns 16 w .. 16 w + 15 of the fp32 state (rows in
-// accumulator layout), needs no other wave's state and no barrier; the
-// block's operands come from the record in LDS.
+// 16, lane / 16) holding token t of the block and channels 32 ks + 8 g + {0..7}
+// of each 32-channel slice ks (one 16-byte load per row and slice), which is
+// the K order of every 16 x 16 x 32 product over channels.  The state's key
+// channels are placed in its 16-row tiles to match: row 4 g + e of tile 2 ks
+// holds channel 32 ks + 8 g + e, of tile 2 ks + 1 channel 32 ks + 8 g + 4 + e,
+// so the state rows a lane holds as accumulator are, as they stand, its B
+// operand: no state data moves between lanes.  K'^T is transposed into that
+// row order by a product with a 0/1 selector operand.  In the recurrence wave
+// w owns value columns 16 w .. 16 w + 15 of the fp32 state, needs no other
+// wave's state and no barrier; the block's operands come from the record in
+// LDS.
 #include <algorithm>
 #include <atomic>
 
@@ -58,22 +60,32 @@ constexpr float kSubFactoredMax = 64.f;  // largest block log2-decay of the fact
 constexpr float kSubMinLog2 = -128.f;    // floor of a token's log2-decay
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Key channel held by row 4 g + e of state tile rt (see Layout).
+__device__ __forceinline__ int state_channel(int rt, int g, int e) {
+    return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + e;
+}
+
 // Operands of one 64-token chunk (four 16-token blocks), in MFMA lane order.
 template <int D>
 struct SubRecord {
     static constexpr int NKS = D / 32, NCT = D / 16;
     bf16x8 ke[4][NKS][kWave];  // Ke (A operand of Ke S, channel order above)
     bf16x8 qe[4][NKS][kWave];  // Qe
-    bf16x4 kt[4][NCT][kWave];  // K'^T, 16-channel tiles (A operand, K = tokens)
+    bf16x4 kt[4][NCT][kWave];  // K'^T, in the state's row tiles (A operand, K = tokens)
     bf16x4 tb[4][kWave];       // T Diag(beta)
     bf16x4 m[4][kWave];        // M
-    f32x4 gend[4][D / 4];      // 2^tau per channel
+    f32x4 gend[4][D / 4];      // 2^tau per channel (channel order)
 };
 
 template <int D>
 struct FusedSmem {
     static constexpr int NPART = D == 128 ? 4 : 1;
+    // row padding of the token x channel tiles: rows 8 banks apart, so the
+    // recurrence's column reads (4 rows x 16 columns) hit 32 distinct banks
+    static constexpr int TP = 16;
     SubRecord<D> rec;
+    bf16 vt[64][D + TP];          // the chunk's V rows
+    bf16 ot[64][D + TP];          // the chunk's outputs, written out by the next chunk
     f32x4 part[NPART][3][kWave];  // second channel half's A, A^T, M^T partial products
     float sumsq[2][2][64];        // [q, k][channel half][token]: partial sums of squares
     int exact[4][2];              // [block][channel half]: past the factored range
@@ -169,7 +181,8 @@ __device__ __forceinline__ void exact_level(int L, int n16, int g, const float (
     }
 }
 
-// Where one chunk's rows of head h lie: a load past row Lc - 1 reads zero.
+// Where one chunk's rows of head h lie: a load past row Lc - 1 reads zero
+// (Lc = 0: every load reads zero and none touches memory).
 template <int D>
 struct ChunkRange {
     int64_t ebase;      // element offset of (first token, head h, channel 0)
@@ -178,18 +191,16 @@ struct ChunkRange {
     __device__ ChunkRange(int64_t tok0, int Lc, int64_t H, int h)
         : ebase((tok0 * H + h) * D),
           rowb((uint32_t)(H * D * 2)),
-          nbytes((uint32_t)(((int64_t)(Lc - 1) * H * D + D) * 2)) {}
+          nbytes(Lc > 0 ? (uint32_t)(((int64_t)(Lc - 1) * H * D + D) * 2) : 0u) {}
 };
 
-// One chunk's inputs for one lane: for the preparation q, k, g of token
-// 16 R + lane % 16 over the lane's 16 channels of half hf, and beta; for the
-// recurrence V at tokens 16 Rb + 4 (lane / 16) + e, column 16 w + lane % 16.
-// The 16-bit values are kept zero-extended, one per register: packing two
-// per register would need the loads to have landed at the point of packing.
+// One chunk's inputs for one lane: q, k, g, v of token 16 R + lane % 16 over
+// the lane's 8 channels of each of the two slices of half hf, and beta (kept
+// zero-extended in a register of its own: packing 16-bit values would need the
+// load to have landed at the point of packing).
 struct ChunkRows {
-    bf16x4 q[2][2], k[2][2], g[2][2];
+    bf16x8 q[2], k[2], g[2], v[2];
     uint32_t beta;
-    uint32_t v[4][4];
 };
 
 // fp32 value of a zero-extended bf16
@@ -198,55 +209,78 @@ __device__ __forceinline__ float bf16_bits_f32(uint32_t x) { return __uint_as_fl
 template <int D>
 __device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
                                                 int w, int lane, ChunkRows& r) {
-    const int n16 = lane & 15, g = lane >> 4, R = w & 3, hf = w >> 2, col = 16 * w + n16;
+    const int n16 = lane & 15, g = lane >> 4, R = w & 3, hf = w >> 2;
     const int64_t H = p.n_heads;
     const ChunkRange<D> c(tok0, Lc, H, h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + c.ebase, c.nbytes);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + c.ebase, c.nbytes);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + c.ebase, c.nbytes);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.beta + tok0 * H + h, (uint32_t)(((int64_t)(Lc - 1) * H + 1) * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+        p.beta + tok0 * H + h, Lc > 0 ? (uint32_t)(((int64_t)(Lc - 1) * H + 1) * 2) : 0u);
     const uint32_t roff = (uint32_t)(16 * R + n16) * c.rowb;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-            const uint32_t off = roff + (uint32_t)(32 * (2 * hf + kk) + 16 * hl + 4 * g) * 2;
-            r.q[kk][hl] = buffer_load<bf16x4>(rq, off);
-            r.k[kk][hl] = buffer_load<bf16x4>(rk, off);
-            r.g[kk][hl] = buffer_load<bf16x4>(rg, off);
-        }
+    for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t off = roff + (uint32_t)(32 * (2 * hf + kk) + 8 * g) * 2;
+        r.q[kk] = buffer_load<bf16x8>(rq, off);
+        r.k[kk] = buffer_load<bf16x8>(rk, off);
+        r.g[kk] = buffer_load<bf16x8>(rg, off);
+        r.v[kk] = buffer_load<bf16x8>(rv, off);
+    }
     r.beta = buffer_load<uint16_t>(rb, (uint32_t)(16 * R + n16) * (uint32_t)H * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + c.ebase, c.nbytes);
+}
+
+// Writes the outputs of a chunk (first token tok0, Lc rows) from the LDS tile:
+// one 16-byte store per 8 columns of a row.
+template <int D>
+__device__ __forceinline__ void flush_outputs(const FusedParams& p, const FusedSmem<D>& sm,
+                                              int t, int64_t tok0, int Lc, int h) {
+    constexpr int PIECES = 64 * D / 8, THREADS = D * 4;
+    static_assert(PIECES % THREADS == 0, "whole passes over the tile");
 #pragma unroll
-    for (int Rb = 0; Rb < 4; ++Rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            r.v[Rb][e] = buffer_load<uint16_t>(rv, (uint32_t)(16 * Rb + 4 * g + e) * c.rowb + (uint32_t)col * 2);
+    for (int it = 0; it < PIECES / THREADS; ++it) {
+        const int i = t + it * THREADS;
+        const int row = i / (D / 8), c8 = i % (D / 8);
+        if (row < Lc)
+            *reinterpret_cast<bf16x8*>(p.out + ((tok0 + row) * p.n_heads + h) * D + 8 * c8) =
+                *reinterpret_cast<const bf16x8*>(&sm.ot[row][8 * c8]);
+    }
 }
 
 // One 64-token chunk of one chain: the preparation writes the chunk's record
 // to LDS, then every wave runs the recurrence over the four blocks on its 16
-// value columns of S.  `rows` holds the chunk's inputs and is refilled with
-// those of the next chunk (next_len > 0) before the recurrence, so their loads
-// overlap it (and every wait of a chunk is for data asked for a chunk
-// earlier: loads and stores share one in-order counter).  `lane` is the lane
-// index (passed in, so the caller can hand over a copy the compiler cannot
-// see through).
+// value columns of S, leaving the outputs in the LDS tile.  `rows` holds the
+// chunk's inputs and is refilled with those of the next chunk (none when
+// next_len = 0) once the preparation has read them, so their loads overlap
+// the inverse and the recurrence (every wait of a chunk is then for data
+// asked for a chunk earlier: loads and stores share one in-order counter).  The previous chunk's outputs (prev_len > 0) are written out once
+// every wave is past its recurrence.  `lane` is the lane index (passed in, so
+// the caller can hand over a copy the compiler cannot see through).
 template <int D>
 __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& sm,
                                             f32x4 (&S)[D / 16], int w, int lane, int64_t tok0,
-                                            int Lc, int h, ChunkRows& rows, int next_len) {
+                                            int Lc, int h, ChunkRows& rows, int next_len,
+                                            int64_t prev_tok0, int prev_len) {
     constexpr int NKS = D / 32, NCT = D / 16, NHALF = D / 64;
     const int n16 = lane & 15, g = lane >> 4, col = 16 * w + n16;
     const int R = w & 3, hf = w >> 2;  // preparation: block, channel half
-    const int64_t H = p.n_heads;
 
     // ---- preparation, block R, channels of half hf; lane token 16 R + n16
-    const bf16x4(&qv)[2][2] = rows.q;
-    const bf16x4(&kv)[2][2] = rows.k;
-    const bf16x4(&gv)[2][2] = rows.g;
+    const bf16x8(&qv)[2] = rows.q;
+    const bf16x8(&kv)[2] = rows.k;
+    const bf16x8(&gv)[2] = rows.g;
     const float bt = bf16_bits_f32(rows.beta);
+    const int t = 64 * w + lane;
+    // every wave is past the previous chunk's recurrence (d = 64: the barrier
+    // that ended it; d = 128: B1 below): its outputs leave the tile and the
+    // V tile is free
+    const auto stage = [&]() {
+        if (prev_len > 0) flush_outputs<D>(p, sm, t, prev_tok0, prev_len, h);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            *reinterpret_cast<bf16x8*>(&sm.vt[16 * R + n16][32 * (2 * hf + kk) + 8 * g]) = rows.v[kk];
+    };
+    if constexpr (NHALF == 1) stage();
 
     // in-block cumulative log2-decay: a scan over the 16 lanes of each row
     float gam[2][8], tau[2][8];
@@ -256,7 +290,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float x = fmaxf(to_f32(gv[kk][i >> 2][i & 3]) * kLog2e, kSubMinLog2);
+            float x = fmaxf(to_f32(gv[kk][i]) * kLog2e, kSubMinLog2);
             x += dpp<0x111>(x);  // row_shr:1
             x += dpp<0x112>(x);  // row_shr:2
             x += dpp<0x114>(x);  // row_shr:4
@@ -264,7 +298,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
             gam[kk][i] = x;
             tau[kk][i] = __shfl(x, lane | 15, kWave);
             big |= -tau[kk][i] > kSubFactoredMax;
-            const float qx = to_f32(qv[kk][i >> 2][i & 3]), kx = to_f32(kv[kk][i >> 2][i & 3]);
+            const float qx = to_f32(qv[kk][i]), kx = to_f32(kv[kk][i]);
             sq += qx * qx;
             sk += kx * kx;
         }
@@ -283,26 +317,40 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         sq += sm.sumsq[0][hf ^ 1][16 * R + n16];
         sk += sm.sumsq[1][hf ^ 1][16 * R + n16];
         ex = __builtin_amdgcn_readfirstlane(sm.exact[R][0] | sm.exact[R][1]);
+        stage();
     }
     const float rqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f) * p.scale;
     const float rks = p.l2norm ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
 
+    // 0/1 selectors for the K'^T tiles: output column n (state row n of tile
+    // 2 ks or 2 ks + 1) takes channel state_channel(2 ks (+ 1), n / 4, n % 4),
+    // element n % 4 (lo) or 4 + n % 4 (hi) of lane group n / 4
+    bf16x8 sel_lo, sel_hi;
+    {
+        const uint32_t one = (g == (n16 >> 2)) ? 0x3F80u : 0u;  // bf16 1.0
+        const uint32_t w0 = (n16 & 2) ? 0u : one << (16 * (n16 & 1));
+        const uint32_t w1 = (n16 & 2) ? one << (16 * (n16 & 1)) : 0u;
+        sel_lo = __builtin_bit_cast(bf16x8, u32x4{w0, w1, 0u, 0u});
+        sel_hi = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, w0, w1});
+    }
     f32x4 Aa = {0.f, 0.f, 0.f, 0.f}, Ata = Aa, Mta = Aa;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int ks = 2 * hf + kk;
-        float ke[8], qe[8], kf[8], kfs[8];
+        float ke[8], qe[8], kf[8], kfs[8], T[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float kh = to_f32(kv[kk][i >> 2][i & 3]) * rks;
-            const float qh = to_f32(qv[kk][i >> 2][i & 3]) * rqs;
+            const float kh = to_f32(kv[kk][i]) * rks;
+            const float qh = to_f32(qv[kk][i]) * rqs;
             const float E = exp2_hw(gam[kk][i]);
-            const float F = exp2_hw(tau[kk][i] - gam[kk][i]);
+            // (clamped: then unused, but finite, when the block is past the range)
+            const float G = exp2_hw(fminf(-gam[kk][i], kSubFactoredMax));
+            T[i] = __shfl(E, lane | 15, kWave);  // 2^tau, from the block's last token
             ke[i] = kh * E;
             qe[i] = qh * E;
-            kf[i] = kh * F;
-            // (clamped: unused, but finite, when the block is past the range)
-            kfs[i] = kf[i] * exp2_hw(fminf(-tau[kk][i], kSubFactoredMax));
+            kfs[i] = kh * G;
+            // K' = khat 2^(tau - Gamma); past the factored range it is redone below
+            kf[i] = kfs[i] * T[i];
         }
         const bf16x8 KE = to_bf16x8(ke), QE = to_bf16x8(qe), KF = to_bf16x8(kf);
         sm.rec.ke[R][ks][lane] = KE;
@@ -313,23 +361,13 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
             Ata = mfma32(KS, KE, Ata);  // its transpose
             Mta = mfma32(KS, QE, Mta);  // M^T
         }
-        // K'^T tiles 2 ks, 2 ks + 1: products with 0/1 selectors that take
-        // channel 32 ks + n (lo) or 32 ks + 16 + n (hi) into output column n
-        bf16x8 sel_lo, sel_hi;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool mine = g == (n16 >> 2) && (j & 3) == (n16 & 3);
-            sel_lo[j] = (bf16)((mine && j < 4) ? 1.f : 0.f);
-            sel_hi[j] = (bf16)((mine && j >= 4) ? 1.f : 0.f);
-        }
+        // K'^T tiles 2 ks, 2 ks + 1 (products with the selectors)
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         sm.rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
         sm.rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
         if (n16 == 0) {
-            sm.rec.gend[R][8 * ks + g] = f32x4{exp2_hw(tau[kk][0]), exp2_hw(tau[kk][1]),
-                                               exp2_hw(tau[kk][2]), exp2_hw(tau[kk][3])};
-            sm.rec.gend[R][8 * ks + 4 + g] = f32x4{exp2_hw(tau[kk][4]), exp2_hw(tau[kk][5]),
-                                                   exp2_hw(tau[kk][6]), exp2_hw(tau[kk][7])};
+            sm.rec.gend[R][8 * ks + 2 * g] = f32x4{T[0], T[1], T[2], T[3]};
+            sm.rec.gend[R][8 * ks + 2 * g + 1] = f32x4{T[4], T[5], T[6], T[7]};
         }
     }
     if (ex) {
@@ -338,8 +376,8 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                kh[kk][i] = to_f32(kv[kk][i >> 2][i & 3]) * rks;
-                qh[kk][i] = to_f32(qv[kk][i >> 2][i & 3]) * rqs;
+                kh[kk][i] = to_f32(kv[kk][i]) * rks;
+                qh[kk][i] = to_f32(qv[kk][i]) * rqs;
             }
         // every pair (i, j) belongs to exactly one level: select, not add
 #pragma unroll 1
@@ -363,6 +401,24 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
                 }
             }
         }
+        // K' from its own exponent: 2^tau may be far below 2^-64 here
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ks = 2 * hf + kk;
+            float kf[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kf[i] = kh[kk][i] * exp2_hw(tau[kk][i] - gam[kk][i]);
+            const bf16x8 KF = to_bf16x8(kf);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            sm.rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
+            sm.rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
+            if (n16 == 0) {
+                sm.rec.gend[R][8 * ks + 2 * g] = f32x4{exp2_hw(tau[kk][0]), exp2_hw(tau[kk][1]),
+                                                       exp2_hw(tau[kk][2]), exp2_hw(tau[kk][3])};
+                sm.rec.gend[R][8 * ks + 2 * g + 1] = f32x4{exp2_hw(tau[kk][4]), exp2_hw(tau[kk][5]),
+                                                           exp2_hw(tau[kk][6]), exp2_hw(tau[kk][7])};
+            }
+        }
     }
     if constexpr (NHALF == 2) {
         if (hf == 1) {
@@ -372,6 +428,8 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         }
         __syncthreads();  // B2
     }
+    // the rows are read: refill them with the next chunk's
+    load_chunk_rows<D>(p, tok0 + 64, next_len, h, w, lane, rows);
     if (hf == 0) {
         if constexpr (NHALF == 2) {
             Aa += sm.part[R][0][lane];
@@ -393,12 +451,6 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
     }
     __syncthreads();  // B3: the record is complete
 
-    uint32_t vv[4][4];  // this chunk's V (rows is refilled next)
-#pragma unroll
-    for (int Rb = 0; Rb < 4; ++Rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vv[Rb][e] = rows.v[Rb][e];
-    if (next_len > 0) load_chunk_rows<D>(p, tok0 + 64, next_len, h, w, lane, rows);
 
     // ---- recurrence over the four blocks, value columns of this wave
 #pragma unroll
@@ -419,17 +471,15 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         }
         bf16x4 Y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(bf16_bits_f32(vv[Rb][e]) - X[e]);
+        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(to_f32(sm.vt[16 * Rb + 4 * g + e][col]) - X[e]);
         const bf16x4 u = to_bf16x4(mfma16(sm.rec.tb[Rb][lane], Y, f32x4{0.f, 0.f, 0.f, 0.f}));
         O = mfma16(sm.rec.m[Rb][lane], u, O);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * Rb + 4 * g + e;
-            if (row < Lc) p.out[((tok0 + row) * H + h) * D + col] = (bf16)O[e];
-        }
+        for (int e = 0; e < 4; ++e) sm.ot[16 * Rb + 4 * g + e][col] = (bf16)O[e];
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt)
-            S[rt] = mfma16(sm.rec.kt[Rb][rt][lane], u, S[rt] * sm.rec.gend[Rb][4 * rt + g]);
+            S[rt] = mfma16(sm.rec.kt[Rb][rt][lane], u,
+                           S[rt] * sm.rec.gend[Rb][state_channel(rt, g, 0) / 4]);
     }
     // (d = 128: the next chunk writes the record only after its B1)
     if constexpr (NHALF == 1) __syncthreads();
@@ -464,17 +514,23 @@ __global__ __launch_bounds__(D * 4, 2) void fused_kernel(FusedParams p) {
             s_len = p.total_tokens / p.n_seqs;
             s_begin = n * s_len;
         }
-        // this lane's state: rows 16 rt + 4 g + e, column col
+        // this lane's state: key channels state_channel(rt, g, e), value column col
         const int64_t sbase = (n * H + h) * D * D;
         f32x4 S[NCT];
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S[rt][e] = p.init ? p.init[sbase + (int64_t)(16 * rt + 4 * g + e) * D + col] : 0.f;
+                S[rt][e] = p.init ? p.init[sbase + (int64_t)state_channel(rt, g, e) * D + col] : 0.f;
+        // the state's loads complete here, once per chain: left pending, their
+        // first use inside the chunk loop would wait for every load in flight
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[rt]));
         const int64_t nch = (s_len + 63) / 64;
         ChunkRows rows;
-        if (nch > 0) load_chunk_rows<D>(p, s_begin, (int)min((int64_t)64, s_len), h, w, lane, rows);
+        load_chunk_rows<D>(p, s_begin, (int)min((int64_t)64, s_len), h, w, lane, rows);
+        int64_t prev_tok0 = 0;
+        int prev_len = 0;
         for (int64_t kc = 0; kc < nch; ++kc) {
             // a copy of the lane index the compiler cannot see through: the
             // chunk's index arithmetic is redone per chunk instead of hoisted
@@ -482,15 +538,20 @@ __global__ __launch_bounds__(D * 4, 2) void fused_kernel(FusedParams p) {
             int lane_c = lane;
             asm volatile("" : "+v"(lane_c));
             const int64_t rest = s_len - 64 * kc;  // tokens from this chunk on
-            fused_chunk<D>(p, sm, S, w, lane_c, s_begin + 64 * kc, (int)min((int64_t)64, rest), h,
-                           rows, (int)max((int64_t)0, min((int64_t)64, rest - 64)));
+            const int len = (int)min((int64_t)64, rest);
+            fused_chunk<D>(p, sm, S, w, lane_c, s_begin + 64 * kc, len, h, rows,
+                           (int)max((int64_t)0, min((int64_t)64, rest - 64)), prev_tok0, prev_len);
+            prev_tok0 = s_begin + 64 * kc;
+            prev_len = len;
         }
+        __syncthreads();  // the last chunk's outputs are complete
+        if (prev_len > 0) flush_outputs<D>(p, sm, t, prev_tok0, prev_len, h);
         if (p.fin) {
 #pragma unroll
             for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    p.fin[sbase + (int64_t)(16 * rt + 4 * g + e) * D + col] = S[rt][e];
+                    p.fin[sbase + (int64_t)state_channel(rt, g, e) * D + col] = S[rt][e];
         }
     }
 }
