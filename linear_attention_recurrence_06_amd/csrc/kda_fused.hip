@@ -206,9 +206,13 @@ struct ChunkRows {
 // fp32 value of a zero-extended bf16
 __device__ __forceinline__ float bf16_bits_f32(uint32_t x) { return __uint_as_float(x << 16); }
 
-template <int D>
+// PART selects what is loaded: 0 q and k, 1 g and beta, 2 v, -1 everything
+// (the refill for the next chunk is spread over the recurrence, so its
+// requests do not all queue at one point).
+template <int D, int PART = -1>
 __device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
                                                 int w, int lane, ChunkRows& r) {
+    constexpr bool QK = PART < 0 || PART == 0, GB = PART < 0 || PART == 1, V = PART < 0 || PART == 2;
     const int n16 = lane & 15, g = lane >> 4, R = w & 3, hf = w >> 2;
     const int64_t H = p.n_heads;
     const ChunkRange<D> c(tok0, Lc, H, h);
@@ -222,12 +226,14 @@ __device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t to
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const uint32_t off = roff + (uint32_t)(32 * (2 * hf + kk) + 8 * g) * 2;
-        r.q[kk] = buffer_load<bf16x8>(rq, off);
-        r.k[kk] = buffer_load<bf16x8>(rk, off);
-        r.g[kk] = buffer_load<bf16x8>(rg, off);
-        r.v[kk] = buffer_load<bf16x8>(rv, off);
+        if constexpr (QK) {
+            r.q[kk] = buffer_load<bf16x8>(rq, off);
+            r.k[kk] = buffer_load<bf16x8>(rk, off);
+        }
+        if constexpr (GB) r.g[kk] = buffer_load<bf16x8>(rg, off);
+        if constexpr (V) r.v[kk] = buffer_load<bf16x8>(rv, off);
     }
-    r.beta = buffer_load<uint16_t>(rb, (uint32_t)(16 * R + n16) * (uint32_t)H * 2);
+    if constexpr (GB) r.beta = buffer_load<uint16_t>(rb, (uint32_t)(16 * R + n16) * (uint32_t)H * 2);
 }
 
 // Writes the outputs of a chunk (first token tok0, Lc rows) from the LDS tile:
@@ -251,9 +257,10 @@ __device__ __forceinline__ void flush_outputs(const FusedParams& p, const FusedS
 // to LDS, then every wave runs the recurrence over the four blocks on its 16
 // value columns of S, leaving the outputs in the LDS tile.  `rows` holds the
 // chunk's inputs and is refilled with those of the next chunk (none when
-// next_len = 0) once the preparation has read them, so their loads overlap
-// the inverse and the recurrence (every wait of a chunk is then for data
-// asked for a chunk earlier: loads and stores share one in-order counter).  The previous chunk's outputs (prev_len > 0) are written out once
+// next_len = 0) once the preparation has read them, spread over the inverse
+// and the recurrence so the loads overlap them (every wait of a chunk is then
+// for data asked for a chunk earlier: loads and stores share one in-order
+// counter).  The previous chunk's outputs (prev_len > 0) are written out once
 // every wave is past its recurrence.  `lane` is the lane index (passed in, so
 // the caller can hand over a copy the compiler cannot see through).
 template <int D>
@@ -428,8 +435,9 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         }
         __syncthreads();  // B2
     }
-    // the rows are read: refill them with the next chunk's
-    load_chunk_rows<D>(p, tok0 + 64, next_len, h, w, lane, rows);
+    // the rows are read: refill them with the next chunk's (q and k now, the
+    // rest during the recurrence)
+    load_chunk_rows<D, 0>(p, tok0 + 64, next_len, h, w, lane, rows);
     if (hf == 0) {
         if constexpr (NHALF == 2) {
             Aa += sm.part[R][0][lane];
@@ -480,6 +488,8 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         for (int rt = 0; rt < NCT; ++rt)
             S[rt] = mfma16(sm.rec.kt[Rb][rt][lane], u,
                            S[rt] * sm.rec.gend[Rb][state_channel(rt, g, 0) / 4]);
+        if (Rb == 0) load_chunk_rows<D, 1>(p, tok0 + 64, next_len, h, w, lane, rows);
+        if (Rb == 1) load_chunk_rows<D, 2>(p, tok0 + 64, next_len, h, w, lane, rows);
     }
     // (d = 128: the next chunk writes the record only after its B1)
     if constexpr (NHALF == 1) __syncthreads();

@@ -6,7 +6,8 @@ the states reaches HBM.
 * Parity with the fp64 oracle at the bf16 bar (max abs error 2e-2, every
   output finite) on packed ragged batches with empty sequences, equal lengths
   without cu_seqlens, decay strong enough for the exact diagonal products
-  (g = -8, -30, 1% at -100), no initial and no final state, d = 64 and 128.
+  (g = -8, -30, 1% at -100), channels of all three decay regimes in one chunk,
+  no initial and no final state, d = 64 and 128.
 * Agreement with the two-kernel path (64-token chunks: the same arithmetic up
   to rounding order) within twice that bar where the oracle would be slow:
   more sequences than the length sort takes, a sort full of empty sequences.
@@ -152,6 +153,25 @@ def test_strong_decay(lib, oracle, monkeypatch, g_value):
     inp["g"] = g
     out, fin = fused_near_split(lib, monkeypatch, inp, f"g={g_value}")
     oracle_check(oracle, inp, out, fin, f"g={g_value}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_mixed_decay_forms(lib, oracle, monkeypatch, d):
+    """Key channels in all three regimes inside the same chunks: mild decay
+    (the chunk's total within the factored range: decay applied once per
+    chunk), medium (past it over a chunk but not over a 16-token block: block
+    decay, factored diagonal products) and strong (past it within a block:
+    block decay, exact diagonal products)."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([300, 64, 129, 1, 77], 2, d, "bf16", g_scale=0.5, s0_std=0.02,
+                       seed=519 + d, device="cuda")
+    g = inp["g"].float().clone()
+    q4 = d // 4
+    g[:, :, q4:2 * q4] = -2.0           # log2 decay ~ -46 per block, ~ -185 per chunk
+    g[:, :, 2 * q4:3 * q4] = -8.0       # ~ -185 per block
+    inp["g"] = g.to(inp["g"].dtype)
+    out, fin = fused_near_split(lib, monkeypatch, inp, f"mixed decay d={d}")
+    oracle_check(oracle, inp, out, fin, f"mixed decay d={d}")
 
 
 def test_no_initial_no_final_state(lib, oracle, monkeypatch):
