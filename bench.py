@@ -2,11 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
 
-One step = one kda_chunk_prefill call (chunk prep + chunked recurrence) over
-the packed varlen batch: 64 sequences with lengths drawn uniformly in
-[1024, 32768] (1,007,721 tokens with its seed), H=32, d_k=d_v=128, bf16 I/O,
-fp32 per-sequence initial and final states; seeded synthetic inputs resident
-in HBM (33 GB of q, k, v, g per call, far past the 256 MB MALL).  This is the
+One step = one kda_chunk_prefill call over the packed varlen batch: 64
+sequences with lengths drawn uniformly in [1024, 32768] (1,007,721 tokens with
+its seed), H=32, d_k=d_v=128, bf16 I/O, fp32 per-sequence initial and final
+states; seeded synthetic inputs resident in HBM (33 GB of q, k, v, g per call,
+far past the 256 MB MALL).  Its 2,048 (sequence, head) chains take the fused
+kernel (chain order + one persistent kernel); the single-sequence workloads
+below take the preparation and recurrence kernels.  This is the
 largest single-GPU workload.  Untimed calls run first until --ramp-ms of GPU
 time has passed (the shader clock rises over the first ~25 ms of load), then
 W warm-up steps, then K back-to-back steps timed between device
@@ -58,8 +60,17 @@ def prefill_algorithmic_bytes(T, H, d, n_seqs=1):
 
 
 def prefill_executed_flops(T, H, d, C=64):
-    """MFMA work per token-head as executed (full tiles): 6 d^2 + 10 C d + C^2 / 3."""
+    """MFMA work per token-head as executed by the preparation and recurrence
+    kernels (full tiles): 6 d^2 + 10 C d + C^2 / 3."""
     return (6 * d * d + 10 * C * d + C * C / 3) * T * H
+
+
+def fused_executed_flops(T, H, d, C=16):
+    """bf16 MFMA work per token-head as executed by the fused kernel (16-token
+    sub-chunks): X = Ke S and Qe S 4 d^2, the state update 2 d^2, T Diag(beta) Y
+    and M u 2 C d each, the diagonal A, A^T, M^T 6 C d, the K'^T selector
+    products 4 C d (the inverse's fp32 products, 16 C^2, are not counted)."""
+    return (6 * d * d + 14 * C * d) * T * H
 
 
 def decode_state_bytes(n, h, d):
@@ -481,9 +492,9 @@ def main():
                    "num_seqs": VN, "total_tokens": VT, "min_len": min(v_lens),
                    "max_len": max(v_lens), "heads": VH, "d_k": D, "d_v": D, "chunk": 64,
                    "io": "bf16", "state": "fp32"},
-        "roofline": roofline("kda_chunk_prefill call (chunk_index + chunk_desc + prep + recur "
-                             "kernels)", v_bytes, v_avg, p_traffic, copy_GBps,
-                             flops=prefill_executed_flops(VT, VH, D),
+        "roofline": roofline("kda_chunk_prefill call (chain_order_kernel + fused_kernel<128>)",
+                             v_bytes, v_avg, p_traffic, copy_GBps,
+                             flops=fused_executed_flops(VT, VH, D),
                              median_call_ms=float(np.median(v_ms)),
                              min_call_ms=float(np.min(v_ms))),
         "cpu_baseline": cpu,
