@@ -156,7 +156,7 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * device share the second stream; each call's own events keep its launches
  * ordered.
  *
- * Kernels.  A call with many (sequence, head) chains -- at least twice the
+ * Kernels.  A call with many (sequence, head) chains -- at least half the
  * device's compute units -- with bf16 I/O, a per-channel gate, out aligned to
  * 16 bytes and no options of kda_chunk_prefill_ex or checkpoints runs one
  * fused kernel: persistent workgroups take whole chains, longest sequences

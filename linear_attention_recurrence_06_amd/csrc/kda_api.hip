@@ -133,7 +133,7 @@ bool fused_path(const PrefillArgs& a) {
     if (env && std::strcmp(env, "split") == 0) return false;
     if (env && std::strcmp(env, "fused") == 0) return true;
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
-    return a.compute_units > 0 && chains >= kFusedChainsPerCU * (int64_t)a.compute_units;
+    return a.compute_units > 0 && chains * kFusedCUsPerChain >= (int64_t)a.compute_units;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {

@@ -185,8 +185,8 @@ def test_no_initial_no_final_state(lib, oracle, monkeypatch):
 
 
 def test_auto_choice_many_chains(lib, monkeypatch):
-    """64 sequences of 64..2,048 tokens x 8 heads: 512 chains, enough per CU
-    for the automatic choice to take the fused kernel on a 256-CU device."""
+    """64 sequences of 64..2,048 tokens x 8 heads: 512 chains, enough for the
+    automatic choice to take the fused kernel on a 256-CU device."""
     from kda_inputs import draw_lengths, make_prefill
     lens = draw_lengths(64, 64, 2048, seed=517)
     inp = make_prefill(lens, 8, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=517, device="cuda")
