@@ -34,19 +34,23 @@
 //     T = (I - N)(I + N^2)(I + N^4)(I + N^8),
 // eight fp32 16 x 16 products on MFMA inside one wave, no LDS traffic.
 //
-// Layout.  A workgroup has d/16 waves.  In the preparation wave w takes
-// block w % 4 and the channel half w / 4 (64 channels), lane (t, g) = (lane %
-// 16, lane / 16) holding token t of the block and channels 32 ks + 8 g + {0..7}
-// of each 32-channel slice ks (one 16-byte load per row and slice), which is
-// the K order of every 16 x 16 x 32 product over channels.  The state's key
+// Layout.  A preparation wave takes one 16-token block over all its channels,
+// lane (t, g) = (lane % 16, lane / 16) holding token t of the block and
+// channels 32 ks + 8 g + {0..7} of each 32-channel slice ks (one 16-byte load
+// per row and slice), which is the K order of every 16 x 16 x 32 product over
+// channels.  The state's key
 // channels are placed in its 16-row tiles to match: row 4 g + e of tile 2 ks
 // holds channel 32 ks + 8 g + e, of tile 2 ks + 1 channel 32 ks + 8 g + 4 + e,
 // so the state rows a lane holds as accumulator are, as they stand, its B
 // operand: no state data moves between lanes.  K'^T is transposed into that
-// row order by a product with a 0/1 selector operand.  In the recurrence wave
-// w owns value columns 16 w .. 16 w + 15 of the fp32 state, needs no other
-// wave's state and no barrier; the block's operands come from the record in
-// LDS.
+// row order by a product with a 0/1 selector operand.  A recurrence wave owns
+// 16 (d = 64) or 32 (d = 128) value columns of the fp32 state and needs no
+// other wave's state; the block's operands come from the record in LDS.
+//
+// Two kernels.  At d = 64 (fused_kernel) the four waves of a workgroup prepare
+// a chunk's four blocks, meet at a barrier, then run its recurrence on 16
+// value columns each.  At d = 128 (fused_ws_kernel) four waves only prepare
+// and four only run the recurrence, one chunk behind, on the same SIMDs.
 #include <algorithm>
 #include <atomic>
 
@@ -77,19 +81,16 @@ struct SubRecord {
     f32x4 gend[4][D / 4];      // 2^tau per channel (channel order)
 };
 
+// LDS of the d = 64 kernel (fused_kernel).
 template <int D>
 struct FusedSmem {
-    static constexpr int NPART = D == 128 ? 4 : 1;
     // row padding of the token x channel tiles: rows 8 banks apart, so the
     // recurrence's column reads (4 rows x 16 columns) hit 32 distinct banks
     static constexpr int TP = 16;
     SubRecord<D> rec;
-    bf16 vt[64][D + TP];          // the chunk's V rows
-    bf16 ot[64][D + TP];          // the chunk's outputs, written out by the next chunk
-    f32x4 part[NPART][3][kWave];  // second channel half's A, A^T, M^T partial products
-    float sumsq[2][2][64];        // [q, k][channel half][token]: partial sums of squares
-    int exact[4][2];              // [block][channel half]: past the factored range
-    int next;                     // the chain this workgroup takes next
+    bf16 vt[64][D + TP];  // the chunk's V rows
+    bf16 ot[64][D + TP];  // the chunk's outputs, written out by the next chunk
+    int next;             // the chain this workgroup takes next
 };
 
 struct FusedParams {
@@ -194,8 +195,8 @@ struct ChunkRange {
           nbytes(Lc > 0 ? (uint32_t)(((int64_t)(Lc - 1) * H * D + D) * 2) : 0u) {}
 };
 
-// One chunk's inputs for one lane: q, k, g, v of token 16 R + lane % 16 over
-// the lane's 8 channels of each of the two slices of half hf, and beta (kept
+// One chunk's inputs for one lane of the d = 64 kernel: q, k, g, v of token
+// 16 w + lane % 16 over the lane's 8 channels of each of the two slices, and beta (kept
 // zero-extended in a register of its own: packing 16-bit values would need the
 // load to have landed at the point of packing).
 struct ChunkRows {
@@ -213,7 +214,8 @@ template <int D, int PART = -1>
 __device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
                                                 int w, int lane, ChunkRows& r) {
     constexpr bool QK = PART < 0 || PART == 0, GB = PART < 0 || PART == 1, V = PART < 0 || PART == 2;
-    const int n16 = lane & 15, g = lane >> 4, R = w & 3, hf = w >> 2;
+    static_assert(D == 64, "two 32-channel slices");
+    const int n16 = lane & 15, g = lane >> 4, R = w;
     const int64_t H = p.n_heads;
     const ChunkRange<D> c(tok0, Lc, H, h);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + c.ebase, c.nbytes);
@@ -225,7 +227,7 @@ __device__ __forceinline__ void load_chunk_rows(const FusedParams& p, int64_t to
     const uint32_t roff = (uint32_t)(16 * R + n16) * c.rowb;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t off = roff + (uint32_t)(32 * (2 * hf + kk) + 8 * g) * 2;
+        const uint32_t off = roff + (uint32_t)(32 * kk + 8 * g) * 2;
         if constexpr (QK) {
             r.q[kk] = buffer_load<bf16x8>(rq, off);
             r.k[kk] = buffer_load<bf16x8>(rk, off);
@@ -268,26 +270,23 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
                                             f32x4 (&S)[D / 16], int w, int lane, int64_t tok0,
                                             int Lc, int h, ChunkRows& rows, int next_len,
                                             int64_t prev_tok0, int prev_len) {
-    constexpr int NKS = D / 32, NCT = D / 16, NHALF = D / 64;
+    static_assert(D == 64, "one wave per block over all its channels");
+    constexpr int NKS = D / 32, NCT = D / 16;
     const int n16 = lane & 15, g = lane >> 4, col = 16 * w + n16;
-    const int R = w & 3, hf = w >> 2;  // preparation: block, channel half
+    const int R = w;  // preparation: block
 
-    // ---- preparation, block R, channels of half hf; lane token 16 R + n16
+    // ---- preparation, block R; lane token 16 R + n16
     const bf16x8(&qv)[2] = rows.q;
     const bf16x8(&kv)[2] = rows.k;
     const bf16x8(&gv)[2] = rows.g;
     const float bt = bf16_bits_f32(rows.beta);
     const int t = 64 * w + lane;
-    // every wave is past the previous chunk's recurrence (d = 64: the barrier
-    // that ended it; d = 128: B1 below): its outputs leave the tile and the
-    // V tile is free
-    const auto stage = [&]() {
-        if (prev_len > 0) flush_outputs<D>(p, sm, t, prev_tok0, prev_len, h);
+    // every wave is past the previous chunk's recurrence (the barrier that
+    // ended it): its outputs leave the tile and the V tile is free
+    if (prev_len > 0) flush_outputs<D>(p, sm, t, prev_tok0, prev_len, h);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            *reinterpret_cast<bf16x8*>(&sm.vt[16 * R + n16][32 * (2 * hf + kk) + 8 * g]) = rows.v[kk];
-    };
-    if constexpr (NHALF == 1) stage();
+    for (int kk = 0; kk < 2; ++kk)
+        *reinterpret_cast<bf16x8*>(&sm.vt[16 * R + n16][32 * kk + 8 * g]) = rows.v[kk];
 
     // in-block cumulative log2-decay: a scan over the 16 lanes of each row
     float gam[2][8], tau[2][8];
@@ -313,19 +312,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
     sq += xor_shfl(sq, 32);
     sk += xor_shfl(sk, 16);
     sk += xor_shfl(sk, 32);
-    int ex = __builtin_amdgcn_readfirstlane(__ballot(big) != 0ull ? 1 : 0);
-    if constexpr (NHALF == 2) {
-        if (g == 0) {
-            sm.sumsq[0][hf][16 * R + n16] = sq;
-            sm.sumsq[1][hf][16 * R + n16] = sk;
-        }
-        if (lane == 0) sm.exact[R][hf] = ex;
-        __syncthreads();  // B1
-        sq += sm.sumsq[0][hf ^ 1][16 * R + n16];
-        sk += sm.sumsq[1][hf ^ 1][16 * R + n16];
-        ex = __builtin_amdgcn_readfirstlane(sm.exact[R][0] | sm.exact[R][1]);
-        stage();
-    }
+    const int ex = __builtin_amdgcn_readfirstlane(__ballot(big) != 0ull ? 1 : 0);
     const float rqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f) * p.scale;
     const float rks = p.l2norm ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
 
@@ -343,7 +330,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
     f32x4 Aa = {0.f, 0.f, 0.f, 0.f}, Ata = Aa, Mta = Aa;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const int ks = 2 * hf + kk;
+        const int ks = kk;
         float ke[8], qe[8], kf[8], kfs[8], T[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -411,7 +398,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         // K' from its own exponent: 2^tau may be far below 2^-64 here
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const int ks = 2 * hf + kk;
+            const int ks = kk;
             float kf[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) kf[i] = kh[kk][i] * exp2_hw(tau[kk][i] - gam[kk][i]);
@@ -427,23 +414,10 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
             }
         }
     }
-    if constexpr (NHALF == 2) {
-        if (hf == 1) {
-            sm.part[R][0][lane] = Aa;
-            sm.part[R][1][lane] = Ata;
-            sm.part[R][2][lane] = Mta;
-        }
-        __syncthreads();  // B2
-    }
     // the rows are read: refill them with the next chunk's (q and k now, the
     // rest during the recurrence)
     load_chunk_rows<D, 0>(p, tok0 + 64, next_len, h, w, lane, rows);
-    if (hf == 0) {
-        if constexpr (NHALF == 2) {
-            Aa += sm.part[R][0][lane];
-            Ata += sm.part[R][1][lane];
-            Mta += sm.part[R][2][lane];
-        }
+    {
         f32x4 N, Nt, Mt, bi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -457,7 +431,7 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         sm.rec.tb[R][lane] = to_bf16x4(Tt * bi);
         sm.rec.m[R][lane] = to_bf16x4(Mt);
     }
-    __syncthreads();  // B3: the record is complete
+    __syncthreads();  // the record is complete
 
 
     // ---- recurrence over the four blocks, value columns of this wave
@@ -491,15 +465,16 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
         if (Rb == 0) load_chunk_rows<D, 1>(p, tok0 + 64, next_len, h, w, lane, rows);
         if (Rb == 1) load_chunk_rows<D, 2>(p, tok0 + 64, next_len, h, w, lane, rows);
     }
-    // (d = 128: the next chunk writes the record only after its B1)
-    if constexpr (NHALF == 1) __syncthreads();
+    // every wave is past its recurrence before the next chunk writes the record
+    __syncthreads();
 }
 
-// A workgroup of d/16 waves works on one chain at a time; persistent, chains
-// handed out through `counter` in `order`.  Every workgroup takes chains until
-// the counter passes the last one, so all of them finish.
+// A workgroup of four waves (d = 64) works on one chain at a time; persistent,
+// chains handed out through `counter` in `order`.  Every workgroup takes
+// chains until the counter passes the last one, so all of them finish.
 template <int D>
 __global__ __launch_bounds__(D * 4, 2) void fused_kernel(FusedParams p) {
+    static_assert(D == 64, "d = 128 takes fused_ws_kernel");
     constexpr int NCT = D / 16;
     __shared__ FusedSmem<D> sm;
     const int t = threadIdx.x, lane = t & 63;
@@ -566,6 +541,442 @@ __global__ __launch_bounds__(D * 4, 2) void fused_kernel(FusedParams p) {
     }
 }
 
+// ------------------------------------------------------------ specialised waves
+//
+// At d = 128 the workgroup holds two kinds of waves.  Four preparation waves,
+// one per 16-token block and each over all the block's channels, write the
+// record of chunk i while four recurrence waves, 32 value columns each, run
+// chunk i - 1 from the other record buffer.  One of each shares a SIMD, so
+// the hardware fills one's waits with the other's work, and they meet once per
+// chunk, at the barrier after which record i is complete and record i - 1 is
+// free.  A recurrence wave loads its own V columns, runs its two 16-column
+// tiles through each block together (one read of each record operand serves
+// both), writes the outputs over the V rows they replace and sends them out
+// with 16-byte stores.
+
+template <int D>
+struct WsSmem {
+    static constexpr int TPV = 8;  // V rows 4 banks apart
+    SubRecord<D> rec[2];
+    bf16 vt[64][D + TPV];          // V of the chunk under recurrence, then its outputs
+    int next;
+};
+
+// Waves per workgroup: preparation (one per block), recurrence.
+template <int D>
+constexpr int kWsPrep = 4;
+template <int D>
+constexpr int kWsRec = D / 32;
+
+// A preparation wave's inputs: q, k, g of token 16 R + lane % 16 over the
+// lane's 8 channels of each of the D / 32 slices (channels 32 ks + 8 (lane /
+// 16) ..), and beta (zero-extended, as in ChunkRows).
+template <int D>
+struct BlockRows {
+    bf16x8 q[D / 32], k[D / 32], g[D / 32];
+    uint32_t beta;
+};
+
+// PART 0: q and k, 1: g and beta, -1 all; rows past Lc read zero.
+template <int D, int PART = -1>
+__device__ __forceinline__ void ws_load_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
+                                             int R, int lane, BlockRows<D>& r) {
+    constexpr bool QK = PART < 0 || PART == 0, GB = PART < 0 || PART == 1;
+    const int n16 = lane & 15, g = lane >> 4;
+    const int64_t H = p.n_heads;
+    const ChunkRange<D> c(tok0, Lc, H, h);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + c.ebase, c.nbytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+        p.beta + tok0 * H + h, Lc > 0 ? (uint32_t)(((int64_t)(Lc - 1) * H + 1) * 2) : 0u);
+    const uint32_t roff = (uint32_t)(16 * R + n16) * c.rowb;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const uint32_t off = roff + (uint32_t)(32 * ks + 8 * g) * 2;
+        if constexpr (QK) {
+            r.q[ks] = buffer_load<bf16x8>(rq, off);
+            r.k[ks] = buffer_load<bf16x8>(rk, off);
+        }
+        if constexpr (GB) r.g[ks] = buffer_load<bf16x8>(rg, off);
+    }
+    if constexpr (GB) r.beta = buffer_load<uint16_t>(rb, (uint32_t)(16 * R + n16) * (uint32_t)H * 2);
+}
+
+// Preparation of block R of one chunk (first token tok0) into `rec`, by one
+// wave over all the block's channels; the same arithmetic as fused_chunk, the
+// two channel halves' partial products summed in the same order.  `rows` holds
+// the block's inputs and is refilled with the next chunk's (next_len tokens)
+// once read.
+template <int D>
+__device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec, int R, int lane,
+                                        int64_t tok0, int h, BlockRows<D>& rows, int next_len) {
+    static_assert(D == 128, "two channel halves of two slices");
+    const int n16 = lane & 15, g = lane >> 4;
+    const float bt = bf16_bits_f32(rows.beta);
+
+    // in-block cumulative log2-decay: a scan over the 16 lanes of each row;
+    // [half][slice in half][channel]
+    float gam[2][2][8];
+    float sq[2] = {0.f, 0.f}, sk[2] = {0.f, 0.f};
+    bool big = false;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float x = fmaxf(to_f32(rows.g[2 * hf + kk][i]) * kLog2e, kSubMinLog2);
+                x += dpp<0x111>(x);  // row_shr:1
+                x += dpp<0x112>(x);  // row_shr:2
+                x += dpp<0x114>(x);  // row_shr:4
+                x += dpp<0x118>(x);  // row_shr:8
+                gam[hf][kk][i] = x;
+                // the block's total decay sits in its last lane
+                big |= n16 == 15 && -x > kSubFactoredMax;
+            }
+    // g and beta are read: request the next chunk's
+    ws_load_rows<D, 1>(p, tok0 + 64, next_len, h, R, lane, rows);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float qx = to_f32(rows.q[2 * hf + kk][i]), kx = to_f32(rows.k[2 * hf + kk][i]);
+                sq[hf] += qx * qx;
+                sk[hf] += kx * kx;
+            }
+        sq[hf] += xor_shfl(sq[hf], 16);
+        sq[hf] += xor_shfl(sq[hf], 32);
+        sk[hf] += xor_shfl(sk[hf], 16);
+        sk[hf] += xor_shfl(sk[hf], 32);
+    }
+    const int ex = __builtin_amdgcn_readfirstlane(__ballot(big) != 0ull ? 1 : 0);
+    const float rqs = (p.l2norm ? __builtin_amdgcn_rsqf(sq[0] + sq[1] + kL2Eps) : 1.f) * p.scale;
+    const float rks = p.l2norm ? __builtin_amdgcn_rsqf(sk[0] + sk[1] + kL2Eps) : 1.f;
+
+    bf16x8 sel_lo, sel_hi;  // 0/1 selectors for the K'^T tiles (as in fused_chunk)
+    {
+        const uint32_t one = (g == (n16 >> 2)) ? 0x3F80u : 0u;  // bf16 1.0
+        const uint32_t w0 = (n16 & 2) ? 0u : one << (16 * (n16 & 1));
+        const uint32_t w1 = (n16 & 2) ? one << (16 * (n16 & 1)) : 0u;
+        sel_lo = __builtin_bit_cast(bf16x8, u32x4{w0, w1, 0u, 0u});
+        sel_hi = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, w0, w1});
+    }
+    f32x4 Aa[2], Ata[2], Mta[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        Aa[hf] = Ata[hf] = Mta[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ks = 2 * hf + kk;
+            float ke[8], qe[8], kf[8], kfs[8], T[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float kh = to_f32(rows.k[ks][i]) * rks;
+                const float qh = to_f32(rows.q[ks][i]) * rqs;
+                const float E = exp2_hw(gam[hf][kk][i]);
+                // (clamped: then unused, but finite, when the block is past the range)
+                const float G = exp2_hw(fminf(-gam[hf][kk][i], kSubFactoredMax));
+                T[i] = __shfl(E, lane | 15, kWave);  // 2^tau, from the block's last token
+                ke[i] = kh * E;
+                qe[i] = qh * E;
+                kfs[i] = kh * G;
+                // K' = khat 2^(tau - Gamma); past the factored range it is redone below
+                kf[i] = kfs[i] * T[i];
+            }
+            const bf16x8 KE = to_bf16x8(ke), QE = to_bf16x8(qe), KF = to_bf16x8(kf);
+            rec.ke[R][ks][lane] = KE;
+            rec.qe[R][ks][lane] = QE;
+            if (!ex) {
+                const bf16x8 KS = to_bf16x8(kfs);
+                Aa[hf] = mfma32(KE, KS, Aa[hf]);    // A[i][j] / beta_i
+                Ata[hf] = mfma32(KS, KE, Ata[hf]);  // its transpose
+                Mta[hf] = mfma32(KS, QE, Mta[hf]);  // M^T
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
+            rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
+            if (n16 == 0) {
+                rec.gend[R][8 * ks + 2 * g] = f32x4{T[0], T[1], T[2], T[3]};
+                rec.gend[R][8 * ks + 2 * g + 1] = f32x4{T[4], T[5], T[6], T[7]};
+            }
+        }
+    }
+    if (ex) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float kh[2][8], qh[2][8], tau[2][8];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    kh[kk][i] = to_f32(rows.k[2 * hf + kk][i]) * rks;
+                    qh[kk][i] = to_f32(rows.q[2 * hf + kk][i]) * rqs;
+                    tau[kk][i] = __shfl(gam[hf][kk][i], lane | 15, kWave);
+                }
+            Aa[hf] = Ata[hf] = Mta[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // every pair (i, j) belongs to exactly one level: select, not add
+#pragma unroll 1
+            for (int L = 0; L <= 4; ++L) {
+                f32x4 P, Q;
+                exact_level(L, n16, g, kh, qh, gam[hf], P, Q);
+                const int sh = 5 - L, m2 = (32 >> L) - 1, hh = 16 >> L;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    if (L == 0) {
+                        Mta[hf][e] = r == n16 ? Q[e] : Mta[hf][e];
+                    } else {
+                        const bool same = (r >> sh) == (n16 >> sh);
+                        // (i, j) = (r, n16) and (n16, r): i in the right half, j in the left
+                        const bool a_rn = same && (r & m2) >= hh && (n16 & m2) < hh;
+                        const bool a_nr = same && (n16 & m2) >= hh && (r & m2) < hh;
+                        Aa[hf][e] = a_rn ? P[e] : Aa[hf][e];
+                        Ata[hf][e] = a_nr ? P[e] : Ata[hf][e];
+                        Mta[hf][e] = a_nr ? Q[e] : Mta[hf][e];
+                    }
+                }
+            }
+            // K' from its own exponent: 2^tau may be far below 2^-64 here
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ks = 2 * hf + kk;
+                float kf[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kf[i] = kh[kk][i] * exp2_hw(tau[kk][i] - gam[hf][kk][i]);
+                const bf16x8 KF = to_bf16x8(kf);
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
+                rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
+                if (n16 == 0) {
+                    rec.gend[R][8 * ks + 2 * g] = f32x4{exp2_hw(tau[kk][0]), exp2_hw(tau[kk][1]),
+                                                        exp2_hw(tau[kk][2]), exp2_hw(tau[kk][3])};
+                    rec.gend[R][8 * ks + 2 * g + 1] = f32x4{exp2_hw(tau[kk][4]), exp2_hw(tau[kk][5]),
+                                                            exp2_hw(tau[kk][6]), exp2_hw(tau[kk][7])};
+                }
+            }
+        }
+    }
+    // q and k are read: request the next chunk's
+    ws_load_rows<D, 0>(p, tok0 + 64, next_len, h, R, lane, rows);
+    {
+        const f32x4 As = Aa[0] + Aa[1], Ats = Ata[0] + Ata[1], Ms = Mta[0] + Mta[1];
+        f32x4 N, Nt, Mt, bi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            bi[e] = __shfl(bt, r, kWave);  // beta of token r
+            N[e] = n16 < r ? As[e] * bi[e] : 0.f;
+            Nt[e] = r < n16 ? Ats[e] * bt : 0.f;
+            Mt[e] = r <= n16 ? Ms[e] : 0.f;
+        }
+        const f32x4 Tt = unit_lower_inverse_t(N, Nt, n16, g);
+        rec.tb[R][lane] = to_bf16x4(Tt * bi);
+        rec.m[R][lane] = to_bf16x4(Mt);
+    }
+}
+
+// One 16-token block of the recurrence on a recurrence wave's two 16-column
+// tiles (value columns 32 wr + 16 c + lane % 16): operands from `rec`, V from
+// `vt`, whose rows of the block then take the block's outputs.
+template <int D, int TPV>
+__device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64][D + TPV],
+                                         f32x4 (&S)[2][D / 16], int wr, int lane, int Rb) {
+    constexpr int NKS = D / 32, NCT = D / 16;
+    const int n16 = lane & 15, g = lane >> 4;
+    bf16x8 Sb[2][NKS];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Sb[c][ks][e] = (bf16)S[c][2 * ks][e];
+                Sb[c][ks][4 + e] = (bf16)S[c][2 * ks + 1][e];
+            }
+    f32x4 X[2], O[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) X[c] = O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = rec.ke[Rb][ks][lane], b = rec.qe[Rb][ks][lane];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            X[c] = mfma32(a, Sb[c][ks], X[c]);
+            O[c] = mfma32(b, Sb[c][ks], O[c]);
+        }
+    }
+    const bf16x4 tb = rec.tb[Rb][lane], m = rec.m[Rb][lane];
+    bf16x4 u[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int col = 32 * wr + 16 * c + n16;
+        bf16x4 Y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(to_f32(vt[16 * Rb + 4 * g + e][col]) - X[c][e]);
+        u[c] = to_bf16x4(mfma16(tb, Y, f32x4{0.f, 0.f, 0.f, 0.f}));
+        O[c] = mfma16(m, u[c], O[c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[16 * Rb + 4 * g + e][col] = (bf16)O[c][e];
+    }
+#pragma unroll
+    for (int rt = 0; rt < NCT; ++rt) {
+        const bf16x4 a = rec.kt[Rb][rt][lane];
+        const f32x4 gd = rec.gend[Rb][state_channel(rt, g, 0) / 4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) S[c][rt] = mfma16(a, u[c], S[c][rt] * gd);
+    }
+}
+
+// A recurrence wave's V columns of one chunk (Lc rows): lane piece j is row
+// 16 j + lane / 4, columns 32 wr + 8 (lane % 4) ..; rows past Lc read zero.
+template <int D>
+__device__ __forceinline__ void ws_load_v(const FusedParams& p, int64_t tok0, int Lc, int h,
+                                          int wr, int lane, bf16x8 (&v)[4]) {
+    const ChunkRange<D> c(tok0, Lc, p.n_heads, h);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + c.ebase, c.nbytes);
+    const uint32_t cb = (uint32_t)(32 * wr + 8 * (lane & 3)) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = buffer_load<bf16x8>(rv, (uint32_t)(16 * j + (lane >> 2)) * c.rowb + cb);
+}
+
+// The same pieces of the outputs from `vt` to HBM; rows past Lc are dropped
+// by the range check of the stores.
+template <int D, int TPV>
+__device__ __forceinline__ void ws_flush(const FusedParams& p, const bf16 (&vt)[64][D + TPV],
+                                         int64_t tok0, int Lc, int h, int wr, int lane) {
+    const ChunkRange<D> c(tok0, Lc, p.n_heads, h);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + c.ebase, c.nbytes);
+    const int c8 = 32 * wr + 8 * (lane & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * j + (lane >> 2);
+        const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(&vt[r][c8]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o8), ro,
+                                               (int)((uint32_t)r * c.rowb + (uint32_t)c8 * 2), 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
+    constexpr int NCT = D / 16, TPV = WsSmem<D>::TPV;
+    __shared__ WsSmem<D> sm;
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t H = p.n_heads;
+    const int64_t chains = (int64_t)p.n_seqs * H;
+    for (;;) {
+        if (t == 0) sm.next = atomicAdd(p.counter, 1);
+        __syncthreads();
+        const int64_t ci = sm.next;
+        __syncthreads();  // every thread has read `next` before it is written again
+        if (ci >= chains) break;
+        const int64_t si = ci / H;
+        const int h = (int)(ci - si * H);
+        const int64_t n = p.order ? (int64_t)p.order[si] : si;
+        int64_t s_begin, s_len;
+        if (p.cu) {
+            s_begin = p.cu[n];
+            s_len = (int64_t)p.cu[n + 1] - s_begin;
+        } else {
+            s_len = p.total_tokens / p.n_seqs;
+            s_begin = n * s_len;
+        }
+        const int64_t nch = (s_len + 63) / 64;
+        const auto len_of = [&](int64_t kc) {
+            return (int)max((int64_t)0, min((int64_t)64, s_len - 64 * kc));
+        };
+        if (w < kWsPrep<D>) {
+            // block w of chunk kc into record kc % 2, a barrier after each,
+            // then one for the last chunk's recurrence
+            if (nch > 0) {
+                BlockRows<D> rows;
+                ws_load_rows<D>(p, s_begin, len_of(0), h, w, lane, rows);
+                for (int64_t kc = 0; kc < nch; ++kc) {
+                    // a copy of the lane index the compiler cannot see
+                    // through: the chunk's index arithmetic is redone per
+                    // chunk instead of held in registers across the loop
+                    int lane_c = lane;
+                    asm volatile("" : "+v"(lane_c));
+                    ws_prep<D>(p, sm.rec[kc & 1], w, lane_c, s_begin + 64 * kc, h, rows,
+                               len_of(kc + 1));
+                    __syncthreads();
+                }
+                __syncthreads();
+            }
+        } else {
+            const int wr = w - kWsPrep<D>;
+            const int n16 = lane & 15, g = lane >> 4;
+            // this lane's state: key channels state_channel(rt, g, e), value
+            // column 32 wr + 16 c + n16 of tile c
+            const int64_t sbase = (n * H + h) * D * D;
+            f32x4 S[2][NCT];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int rt = 0; rt < NCT; ++rt) S[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p.init) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            S[c][rt][e] = p.init[sbase + (int64_t)state_channel(rt, g, e) * D +
+                                                 32 * wr + 16 * c + n16];
+            }
+            // the state's loads complete here, once per chain
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[c][rt]));
+            if (nch > 0) {
+                bf16x8 v[4];
+                ws_load_v<D>(p, s_begin, len_of(0), h, wr, lane, v);
+                // step 0: nothing to run; V of chunk 0 to the tile
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<bf16x8*>(&sm.vt[16 * j + (lane >> 2)][32 * wr + 8 * (lane & 3)]) = v[j];
+                ws_load_v<D>(p, s_begin + 64, len_of(1), h, wr, lane, v);
+                __syncthreads();
+                // step kc: the recurrence of chunk kc - 1 from record (kc - 1) % 2
+                for (int64_t kc = 1; kc <= nch; ++kc) {
+                    int lane_c = lane;
+                    asm volatile("" : "+v"(lane_c));
+                    const SubRecord<D>& rec = sm.rec[(kc - 1) & 1];
+#pragma unroll
+                    for (int Rb = 0; Rb < 4; ++Rb) ws_block<D, TPV>(rec, sm.vt, S, wr, lane_c, Rb);
+                    ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
+                    if (kc < nch) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<bf16x8*>(
+                                &sm.vt[16 * j + (lane_c >> 2)][32 * wr + 8 * (lane_c & 3)]) = v[j];
+                        ws_load_v<D>(p, s_begin + 64 * (kc + 1), len_of(kc + 1), h, wr, lane_c, v);
+                    }
+                    __syncthreads();
+                }
+            }
+            if (p.fin) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            p.fin[sbase + (int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * c + n16] =
+                                S[c][rt][e];
+            }
+        }
+    }
+}
+
+// Whether the launcher takes the specialised-wave kernel.
+template <int D>
+constexpr bool kSpecialised = D == 128;
+
 // Largest number of sequences the order kernel sorts (in LDS); past it the
 // chains go in their natural order.
 constexpr int kOrderSortMax = 2048;
@@ -613,15 +1024,19 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
     for (int i = t; i < n_seqs; i += 1024) order[i] = (int32_t)(key[i] & 0xffffffffu);
 }
 
-// Resident workgroups per CU of fused_kernel<D> (queried once per process; the
+// Resident workgroups per CU of the fused kernel for D (queried once per process; the
 // answer depends only on the kernel's resources and the gfx950 CU).
 template <int D>
 hipError_t fused_blocks_per_cu(int* out) {
     static std::atomic<int> cached{0};
     int c = cached.load(std::memory_order_relaxed);
     if (c <= 0) {
-        const hipError_t e =
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_kernel<D>, D * 4, 0);
+        hipError_t e;
+        if constexpr (kSpecialised<D>)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_ws_kernel<D>,
+                                                             64 * (kWsPrep<D> + kWsRec<D>), 0);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_kernel<D>, D * 4, 0);
         if (e != hipSuccess) return e;
         if (c <= 0) c = 1;
         cached.store(c, std::memory_order_relaxed);
@@ -663,7 +1078,11 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
     const int grid = (int)std::min<int64_t>(chains, cus * per_cu);
-    hipLaunchKernelGGL((fused_kernel<D>), dim3(grid), dim3(D * 4), 0, stream, fp);
+    if constexpr (kSpecialised<D>)
+        hipLaunchKernelGGL((fused_ws_kernel<D>), dim3(grid), dim3(64 * (kWsPrep<D> + kWsRec<D>)), 0,
+                           stream, fp);
+    else
+        hipLaunchKernelGGL((fused_kernel<D>), dim3(grid), dim3(D * 4), 0, stream, fp);
     return hipGetLastError();
 }
 
