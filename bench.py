@@ -492,7 +492,7 @@ def main():
                    "num_seqs": VN, "total_tokens": VT, "min_len": min(v_lens),
                    "max_len": max(v_lens), "heads": VH, "d_k": D, "d_v": D, "chunk": 64,
                    "io": "bf16", "state": "fp32"},
-        "roofline": roofline("kda_chunk_prefill call (chain_order_kernel + fused_kernel<128>)",
+        "roofline": roofline("kda_chunk_prefill call (chain_order_kernel + fused_ws_kernel<128>)",
                              v_bytes, v_avg, p_traffic, copy_GBps,
                              flops=fused_executed_flops(VT, VH, D),
                              median_call_ms=float(np.median(v_ms)),

@@ -141,8 +141,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // A prefill takes the fused kernel (persistent workgroups working through
 // whole (sequence, head) chains) instead of the preparation and recurrence
 // kernels once it has at least one chain per kFusedCUsPerChain compute units.
-// Measured at d = 128, 8,192-token sequences: 64 chains 1.36x the two-kernel
-// time, 128 chains 0.86x, 256 chains 0.47x (256 CUs).
+// Measured at d = 128, 8,192-token sequences: 64 chains 1.15x the two-kernel
+// time, 128 chains 0.73x, 256 chains 0.42x (256 CUs).
 constexpr int64_t kFusedCUsPerChain = 2;
 
 // Whether launch_prefill takes the fused kernel for these arguments.  The
