@@ -393,7 +393,7 @@ def main():
                               workspace=l_ws, stream=stream)
 
     l_wall, l_avg, l_ms = timed(long_call, 2 if args.profile else 4, 1)
-    long_segs = kda.kda_prefill_pipeline_segments(l_dims)
+    long_path, long_segs = kda.kda_prefill_path(l_dims)
     l_bytes = prefill_algorithmic_bytes(LT, LH, D)
     l_heads = seeded_heads(LH, 2, 104)
     L_SAMPLE = 131072
@@ -522,7 +522,9 @@ def main():
                           "algorithmic_bytes_per_call": fe_bytes},
         },
         "prefill_long": {
-            "workload": CONFIGS[4].name, "pipeline_segments": long_segs,
+            "workload": CONFIGS[4].name,
+            "path": {0: "split", 1: "pipelined", 2: "fused", 3: "segmented"}.get(long_path, "?"),
+            "segments": long_segs,
             "tokens_per_s": LT / l_avg,
             "roofline": roofline("kda_chunk_prefill call", l_bytes, l_avg,
                                  counter_traffic("prefill_long"), copy_GBps,

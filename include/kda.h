@@ -162,13 +162,25 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * fused kernel: persistent workgroups take whole chains, longest sequences
  * first, and step through each 64-token chunk as four 16-token sub-chunks with
  * the chunk's operands in LDS, so only the inputs, the outputs and the states
- * touch HBM; it uses only the first two index areas of the workspace.  Every other call runs the
- * preparation and recurrence kernels, which hand per-chunk records through the
- * workspace.  The two compute the same recurrence with the same operand
- * precision but round in a different order, so their results agree to the
- * accuracy below, not bit for bit.  The environment variable KDA_PREFILL_PATH
- * (read at each call) set to "split" or "fused" overrides the choice where the
- * fused kernel applies.
+ * touch HBM; it uses only the first two index areas of the workspace.  A
+ * call with few chains -- at most one per 16 compute units -- over long
+ * sequences (one sequence, or equal lengths without cu_seqlens), d = 128 and
+ * otherwise the fused kernel's conditions, is segmented: each sequence is cut
+ * into P segments of at least 256 chunks, with P chosen so that the
+ * (segment, head) chains give every two compute units one.  The fused kernel
+ * forms each segment's state map S_end = M S_start + b twice over (b from the
+ * zero state, M from the identity with v taken as zero, neither writing
+ * outputs), a scan kernel composes the maps in order into every segment's
+ * start state and the final state, and the fused kernel runs the segments
+ * again from those states for the outputs (three [N P, H, d, d] fp32 arrays in
+ * the workspace's record area).  Every other call runs the preparation and
+ * recurrence kernels, which hand per-chunk records through the workspace.  The
+ * paths compute the same recurrence with the same operand precision but round
+ * in a different order, so their results agree to the accuracy below, not bit
+ * for bit.  The environment variable KDA_PREFILL_PATH (read at each call) set
+ * to "split", "fused" or "segmented" overrides the choice where that path
+ * applies, and KDA_PREFILL_SEGMENTS=<P> (1 to 64) sets the segment count of a
+ * segmented call.
  *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Any g <= 0 is handled:
@@ -185,11 +197,27 @@ kda_status kda_chunk_prefill(const kda_dims* dims, const void* q, const void* k,
                              void* out, float* final_state, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Segments a kda_chunk_prefill with these sizes is pipelined into on the
- * current device, outside stream capture (see Streams at kda_chunk_prefill): 0 for one launch of each
- * kernel, S >= 4 for S segments, -1 for a descriptor the library would reject
- * or a device that cannot be queried.  Reads no device memory. */
+/* Segments a kda_chunk_prefill with these sizes (cu_seqlens NULL) is
+ * pipelined into on the current device, outside stream capture (see Streams
+ * at kda_chunk_prefill): 0 for one launch of each kernel or another path
+ * (kda_prefill_path), S >= 4 for S segments, -1 for a descriptor the library
+ * would reject or a device that cannot be queried.  Reads no device memory. */
 int32_t kda_prefill_pipeline_segments(const kda_dims* dims);
+
+/* The kernels a plain kda_chunk_prefill with these sizes runs on the current
+ * device (see Kernels at kda_chunk_prefill), outside stream capture, with
+ * cu_seqlens given (packed != 0) or NULL and out aligned to 16 bytes; the
+ * environment overrides of that paragraph apply.  *segments (when not NULL)
+ * receives the pipeline or segment count (0 for the other paths).  Returns -1
+ * for a descriptor the library would reject or a device that cannot be
+ * queried.  Reads no device memory.  A diagnostic, for benchmarks and tests. */
+typedef enum {
+    KDA_PATH_SPLIT = 0,      /* preparation + recurrence kernels, one launch each */
+    KDA_PATH_PIPELINED = 1,  /* the same, pipelined over segments of one sequence */
+    KDA_PATH_FUSED = 2,      /* the fused kernel, whole chains */
+    KDA_PATH_SEGMENTED = 3   /* segment maps, their scan, then the segments again */
+} kda_prefill_path_kind;
+int32_t kda_prefill_path(const kda_dims* dims, int32_t packed, int32_t* segments);
 
 /* Number of intermediate states kda_chunk_prefill_checkpoints writes: for each
  * sequence of c = ceil(len / 64) chunks, floor((c - 1) / checkpoint_interval)

@@ -136,9 +136,45 @@ bool fused_path(const PrefillArgs& a) {
     return a.compute_units > 0 && chains * kFusedCUsPerChain >= (int64_t)a.compute_units;
 }
 
+int segmented_segments(const PrefillArgs& a) {
+    // the fused kernel's plain recurrence at d = 128, whole call, and segment
+    // bounds the host knows: one sequence, or equal lengths
+    if (!a.bf16 || a.d != 128 || a.scalar_g || a.out_gate != 0 || a.fe.active() ||
+        a.ckpt_interval > 0)
+        return 0;
+    if ((reinterpret_cast<uintptr_t>(a.out) & 15) != 0) return 0;
+    if (a.total_tokens <= 0 || a.n_seqs < 1 || a.slot_begin != 0 || a.slot_end != -1 ||
+        a.chunk_begin != 0 || a.chunk_end != INT64_MAX)
+        return 0;
+    if (a.cu_seqlens && a.n_seqs != 1) return 0;
+    if (fused_path(a)) return 0;
+    const char* env = std::getenv("KDA_PREFILL_PATH");
+    const bool forced = env && std::strcmp(env, "segmented") == 0;
+    if (env && (std::strcmp(env, "split") == 0 || std::strcmp(env, "fused") == 0)) return 0;
+    const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
+    const int64_t seq_chunks = (a.total_tokens / a.n_seqs + 63) / 64;
+    const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
+    int64_t P = std::min<int64_t>(kSegMaxSegments, std::max<int64_t>(1, cus / chains));
+    P = std::min<int64_t>(P, seq_chunks / kSegMinChunks);
+    if (const char* ps = std::getenv("KDA_PREFILL_SEGMENTS")) {
+        const long v = std::strtol(ps, nullptr, 10);
+        if (v >= 1 && v <= kSegMaxSegments) P = std::min<int64_t>(v, seq_chunks);
+    }
+    if (P < 2) return 0;
+    // automatically: few chains, and enough segments to give every two
+    // compute units a chain
+    if (!forced && (a.compute_units <= 0 || chains * kSegCUsPerChain > a.compute_units ||
+                    chains * P * kFusedCUsPerChain < a.compute_units))
+        return 0;
+    // its arrays fit in the record area the split path would use
+    if (segmented_scratch_bytes(a, (int)P) > a.layout.records_bytes()) return 0;
+    return (int)P;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if (fused_path(a))
         return a.d == 128 ? launch_fused<128>(a, s) : launch_fused<64>(a, s);
+    if (const int P = segmented_segments(a)) return launch_segmented(a, P, s);
     // under stream capture the call stays on the caller's stream: no library
     // stream or events enter the caller's graph (the results are the same)
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -241,15 +277,45 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
         .total();
 }
 
-int32_t kda_prefill_pipeline_segments(const kda_dims* d) {
+int32_t kda_prefill_path(const kda_dims* d, int32_t packed, int32_t* segments) {
     if (check_dims(d, true) != KDA_OK) return -1;
-    kda::PrefillArgs a;
+    kda::PrefillArgs a{};  // (no options, no checkpoints: zero)
     a.total_tokens = d->total_tokens;
     a.n_seqs = d->num_seqs;
     a.n_heads = d->num_heads;
     a.d = d->d_k;
+    a.bf16 = d->io_dtype == KDA_BF16;
+    a.scalar_g = d->gate == KDA_GATE_HEAD;
+    a.scale = d->scale;
+    a.l2norm = d->qk_l2norm;
+    a.fe = kda::FrontEnd{};
+    // stand-ins the choice looks at only for being null or 16-byte aligned
+    a.out = reinterpret_cast<void*>(uintptr_t{256});
+    a.cu_seqlens = packed ? reinterpret_cast<const int32_t*>(uintptr_t{256}) : nullptr;
+    a.layout = kda::make_layout(d->d_k, (int)elt_bytes(d), d->total_tokens, d->num_seqs,
+                                d->num_heads, true);
     if (compute_units(&a.compute_units) != hipSuccess) return -1;
-    return kda::pipeline_segments(a);
+    int32_t seg = 0, path = KDA_PATH_SPLIT;
+    if (d->num_seqs > 0 && d->total_tokens > 0) {
+        if (kda::fused_path(a)) {
+            path = KDA_PATH_FUSED;
+        } else if ((seg = kda::segmented_segments(a)) > 0) {
+            path = KDA_PATH_SEGMENTED;
+        } else if ((seg = kda::pipeline_segments(a)) >= 2) {
+            path = KDA_PATH_PIPELINED;
+        } else {
+            seg = 0;
+        }
+    }
+    if (segments) *segments = seg;
+    return path;
+}
+
+int32_t kda_prefill_pipeline_segments(const kda_dims* d) {
+    int32_t seg = 0;
+    const int32_t path = kda_prefill_path(d, 0, &seg);
+    if (path < 0) return -1;
+    return path == KDA_PATH_PIPELINED ? seg : 0;
 }
 
 }  // extern "C"
@@ -430,7 +496,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
         if (overlap(r_fin, fr.state_out) || overlap(fr.state_out, r_s0)) return KDA_ERR_INVALID_ARG;
     }
 
-    kda::PrefillArgs a;
+    kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.initial_state = initial_state;
     a.cu_seqlens = cu_seqlens;
@@ -473,9 +539,13 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(hs, &cap) != hipSuccess) return KDA_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone) return KDA_ERR_WORKSPACE;
-    // (the fused path keeps its records in LDS and needs only the index areas)
+    // (the fused path keeps its records in LDS and needs only the index areas;
+    // the segmented path adds its state maps)
     void* ws = nullptr;
-    const size_t ws_alloc = kda::fused_path(a) ? a.layout.records_offset() : ws_need;
+    const int seg = kda::segmented_segments(a);
+    const size_t ws_alloc = kda::fused_path(a) ? a.layout.records_offset()
+                            : seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg)
+                                      : ws_need;
     if (hipMallocAsync(&ws, ws_alloc, hs) != hipSuccess) return KDA_ERR_HIP;
     a.workspace = static_cast<unsigned char*>(ws);
     const hipError_t e = kda::launch_prefill(a, hs);

@@ -105,6 +105,12 @@ struct FusedParams {
     int32_t n_seqs, n_heads;
     float scale;
     int l2norm;
+    // segmented kernels: the n_seqs / seg_per_seq sequences (equal lengths,
+    // no cu) are cut into seg_per_seq segments of seg_len tokens (the last of
+    // each shorter), and each (segment, head) is a chain; n_seqs counts the
+    // segments
+    int64_t seg_len = 0;
+    int32_t seg_per_seq = 1;
 };
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -577,8 +583,9 @@ struct BlockRows {
     uint32_t beta;
 };
 
-// PART 0: q and k, 1: g and beta, -1 all; rows past Lc read zero.
-template <int D, int PART = -1>
+// PART 0: q and k, 1: g and beta, -1 all; rows past Lc read zero.  QROWS false:
+// no q (a pass that writes no outputs).
+template <int D, int PART = -1, bool QROWS = true>
 __device__ __forceinline__ void ws_load_rows(const FusedParams& p, int64_t tok0, int Lc, int h,
                                              int R, int lane, BlockRows<D>& r) {
     constexpr bool QK = PART < 0 || PART == 0, GB = PART < 0 || PART == 1;
@@ -595,7 +602,7 @@ __device__ __forceinline__ void ws_load_rows(const FusedParams& p, int64_t tok0,
     for (int ks = 0; ks < D / 32; ++ks) {
         const uint32_t off = roff + (uint32_t)(32 * ks + 8 * g) * 2;
         if constexpr (QK) {
-            r.q[ks] = buffer_load<bf16x8>(rq, off);
+            if constexpr (QROWS) r.q[ks] = buffer_load<bf16x8>(rq, off);
             r.k[ks] = buffer_load<bf16x8>(rk, off);
         }
         if constexpr (GB) r.g[ks] = buffer_load<bf16x8>(rg, off);
@@ -607,8 +614,8 @@ __device__ __forceinline__ void ws_load_rows(const FusedParams& p, int64_t tok0,
 // wave over all the block's channels; the same arithmetic as fused_chunk, the
 // two channel halves' partial products summed in the same order.  `rows` holds
 // the block's inputs and is refilled with the next chunk's (next_len tokens)
-// once read.
-template <int D>
+// once read.  QROWS false: the record's Qe and M are not formed (no outputs).
+template <int D, bool QROWS = true>
 __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec, int R, int lane,
                                         int64_t tok0, int h, BlockRows<D>& rows, int next_len) {
     static_assert(D == 128, "two channel halves of two slices");
@@ -636,14 +643,15 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
                 big |= n16 == 15 && -x > kSubFactoredMax;
             }
     // g and beta are read: request the next chunk's
-    ws_load_rows<D, 1>(p, tok0 + 64, next_len, h, R, lane, rows);
+    ws_load_rows<D, 1, QROWS>(p, tok0 + 64, next_len, h, R, lane, rows);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float qx = to_f32(rows.q[2 * hf + kk][i]), kx = to_f32(rows.k[2 * hf + kk][i]);
+                const float qx = QROWS ? to_f32(rows.q[2 * hf + kk][i]) : 0.f;
+                const float kx = to_f32(rows.k[2 * hf + kk][i]);
                 sq[hf] += qx * qx;
                 sk[hf] += kx * kx;
             }
@@ -675,7 +683,7 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float kh = to_f32(rows.k[ks][i]) * rks;
-                const float qh = to_f32(rows.q[ks][i]) * rqs;
+                const float qh = QROWS ? to_f32(rows.q[ks][i]) * rqs : 0.f;
                 const float E = exp2_hw(gam[hf][kk][i]);
                 // (clamped: then unused, but finite, when the block is past the range)
                 const float G = exp2_hw(fminf(-gam[hf][kk][i], kSubFactoredMax));
@@ -688,12 +696,12 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
             }
             const bf16x8 KE = to_bf16x8(ke), QE = to_bf16x8(qe), KF = to_bf16x8(kf);
             rec.ke[R][ks][lane] = KE;
-            rec.qe[R][ks][lane] = QE;
+            if constexpr (QROWS) rec.qe[R][ks][lane] = QE;
             if (!ex) {
                 const bf16x8 KS = to_bf16x8(kfs);
                 Aa[hf] = mfma32(KE, KS, Aa[hf]);    // A[i][j] / beta_i
                 Ata[hf] = mfma32(KS, KE, Ata[hf]);  // its transpose
-                Mta[hf] = mfma32(KS, QE, Mta[hf]);  // M^T
+                if constexpr (QROWS) Mta[hf] = mfma32(KS, QE, Mta[hf]);  // M^T
             }
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
@@ -713,7 +721,7 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     kh[kk][i] = to_f32(rows.k[2 * hf + kk][i]) * rks;
-                    qh[kk][i] = to_f32(rows.q[2 * hf + kk][i]) * rqs;
+                    qh[kk][i] = QROWS ? to_f32(rows.q[2 * hf + kk][i]) * rqs : 0.f;
                     tau[kk][i] = __shfl(gam[hf][kk][i], lane | 15, kWave);
                 }
             Aa[hf] = Ata[hf] = Mta[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -760,7 +768,7 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
         }
     }
     // q and k are read: request the next chunk's
-    ws_load_rows<D, 0>(p, tok0 + 64, next_len, h, R, lane, rows);
+    ws_load_rows<D, 0, QROWS>(p, tok0 + 64, next_len, h, R, lane, rows);
     {
         const f32x4 As = Aa[0] + Aa[1], Ats = Ata[0] + Ata[1], Ms = Mta[0] + Mta[1];
         f32x4 N, Nt, Mt, bi;
@@ -774,14 +782,15 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
         }
         const f32x4 Tt = unit_lower_inverse_t(N, Nt, n16, g);
         rec.tb[R][lane] = to_bf16x4(Tt * bi);
-        rec.m[R][lane] = to_bf16x4(Mt);
+        if constexpr (QROWS) rec.m[R][lane] = to_bf16x4(Mt);
     }
 }
 
 // One 16-token block of the recurrence on a recurrence wave's two 16-column
 // tiles (value columns 32 wr + 16 c + lane % 16): operands from `rec`, V from
-// `vt`, whose rows of the block then take the block's outputs.
-template <int D, int TPV>
+// `vt`, whose rows of the block then take the block's outputs.  OUT false:
+// no outputs; ZERO_V: V is zero (the state map's linear part), vt unread.
+template <int D, int TPV, bool OUT = true, bool ZERO_V = false>
 __device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64][D + TPV],
                                          f32x4 (&S)[2][D / 16], int wr, int lane, int Rb) {
     constexpr int NKS = D / 32, NCT = D / 16;
@@ -801,25 +810,31 @@ __device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64]
     for (int c = 0; c < 2; ++c) X[c] = O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = rec.ke[Rb][ks][lane], b = rec.qe[Rb][ks][lane];
+        const bf16x8 a = rec.ke[Rb][ks][lane];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            X[c] = mfma32(a, Sb[c][ks], X[c]);
-            O[c] = mfma32(b, Sb[c][ks], O[c]);
+        for (int c = 0; c < 2; ++c) X[c] = mfma32(a, Sb[c][ks], X[c]);
+        if constexpr (OUT) {
+            const bf16x8 b = rec.qe[Rb][ks][lane];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) O[c] = mfma32(b, Sb[c][ks], O[c]);
         }
     }
-    const bf16x4 tb = rec.tb[Rb][lane], m = rec.m[Rb][lane];
+    const bf16x4 tb = rec.tb[Rb][lane];
+    const bf16x4 m = OUT ? rec.m[Rb][lane] : bf16x4{};
     bf16x4 u[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int col = 32 * wr + 16 * c + n16;
         bf16x4 Y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(to_f32(vt[16 * Rb + 4 * g + e][col]) - X[c][e]);
+        for (int e = 0; e < 4; ++e)
+            Y[e] = (bf16)((ZERO_V ? 0.f : to_f32(vt[16 * Rb + 4 * g + e][col])) - X[c][e]);
         u[c] = to_bf16x4(mfma16(tb, Y, f32x4{0.f, 0.f, 0.f, 0.f}));
-        O[c] = mfma16(m, u[c], O[c]);
+        if constexpr (OUT) {
+            O[c] = mfma16(m, u[c], O[c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vt[16 * Rb + 4 * g + e][col] = (bf16)O[c][e];
+            for (int e = 0; e < 4; ++e) vt[16 * Rb + 4 * g + e][col] = (bf16)O[c][e];
+        }
     }
 #pragma unroll
     for (int rt = 0; rt < NCT; ++rt) {
@@ -859,7 +874,11 @@ __device__ __forceinline__ void ws_flush(const FusedParams& p, const bf16 (&vt)[
     }
 }
 
-template <int D>
+// The segmented prefill's kernels: SEG, chains are the segments of p.seg_len;
+// OUT false, no outputs (p.out unused, no q read); ZERO_V, V taken as zero
+// and every chain started from the identity (p.v and p.init unused: the
+// linear part of each segment's state map).
+template <int D, bool OUT = true, bool ZERO_V = false, bool SEG = false>
 __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
     constexpr int NCT = D / 16, TPV = WsSmem<D>::TPV;
     __shared__ WsSmem<D> sm;
@@ -877,7 +896,13 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
         const int h = (int)(ci - si * H);
         const int64_t n = p.order ? (int64_t)p.order[si] : si;
         int64_t s_begin, s_len;
-        if (p.cu) {
+        if constexpr (SEG) {
+            // segment n % seg_per_seq of sequence n / seg_per_seq
+            const int64_t seq_len = p.total_tokens / (p.n_seqs / p.seg_per_seq);
+            const int64_t part = n % p.seg_per_seq;
+            s_begin = (n / p.seg_per_seq) * seq_len + part * p.seg_len;
+            s_len = max((int64_t)0, min(p.seg_len, seq_len - part * p.seg_len));
+        } else if (p.cu) {
             s_begin = p.cu[n];
             s_len = (int64_t)p.cu[n + 1] - s_begin;
         } else {
@@ -893,15 +918,15 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
             // then one for the last chunk's recurrence
             if (nch > 0) {
                 BlockRows<D> rows;
-                ws_load_rows<D>(p, s_begin, len_of(0), h, w, lane, rows);
+                ws_load_rows<D, -1, OUT>(p, s_begin, len_of(0), h, w, lane, rows);
                 for (int64_t kc = 0; kc < nch; ++kc) {
                     // a copy of the lane index the compiler cannot see
                     // through: the chunk's index arithmetic is redone per
                     // chunk instead of held in registers across the loop
                     int lane_c = lane;
                     asm volatile("" : "+v"(lane_c));
-                    ws_prep<D>(p, sm.rec[kc & 1], w, lane_c, s_begin + 64 * kc, h, rows,
-                               len_of(kc + 1));
+                    ws_prep<D, OUT>(p, sm.rec[kc & 1], w, lane_c, s_begin + 64 * kc, h, rows,
+                                    len_of(kc + 1));
                     __syncthreads();
                 }
                 __syncthreads();
@@ -917,7 +942,15 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int rt = 0; rt < NCT; ++rt) S[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (p.init) {
+            if constexpr (ZERO_V) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            S[c][rt][e] = state_channel(rt, g, e) == 32 * wr + 16 * c + n16 ? 1.f : 0.f;
+            } else if (p.init) {
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -934,12 +967,15 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
                 for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[c][rt]));
             if (nch > 0) {
                 bf16x8 v[4];
-                ws_load_v<D>(p, s_begin, len_of(0), h, wr, lane, v);
-                // step 0: nothing to run; V of chunk 0 to the tile
+                if constexpr (!ZERO_V) {
+                    ws_load_v<D>(p, s_begin, len_of(0), h, wr, lane, v);
+                    // step 0: nothing to run; V of chunk 0 to the tile
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<bf16x8*>(&sm.vt[16 * j + (lane >> 2)][32 * wr + 8 * (lane & 3)]) = v[j];
-                ws_load_v<D>(p, s_begin + 64, len_of(1), h, wr, lane, v);
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<bf16x8*>(&sm.vt[16 * j + (lane >> 2)][32 * wr + 8 * (lane & 3)]) =
+                            v[j];
+                    ws_load_v<D>(p, s_begin + 64, len_of(1), h, wr, lane, v);
+                }
                 __syncthreads();
                 // step kc: the recurrence of chunk kc - 1 from record (kc - 1) % 2
                 for (int64_t kc = 1; kc <= nch; ++kc) {
@@ -947,9 +983,11 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
                     asm volatile("" : "+v"(lane_c));
                     const SubRecord<D>& rec = sm.rec[(kc - 1) & 1];
 #pragma unroll
-                    for (int Rb = 0; Rb < 4; ++Rb) ws_block<D, TPV>(rec, sm.vt, S, wr, lane_c, Rb);
-                    ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
-                    if (kc < nch) {
+                    for (int Rb = 0; Rb < 4; ++Rb)
+                        ws_block<D, TPV, OUT, ZERO_V>(rec, sm.vt, S, wr, lane_c, Rb);
+                    if constexpr (OUT)
+                        ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
+                    if (!ZERO_V && kc < nch) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             *reinterpret_cast<bf16x8*>(
@@ -1024,6 +1062,64 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
     for (int i = t; i < n_seqs; i += 1024) order[i] = (int32_t)(key[i] & 0xffffffffu);
 }
 
+// Composition of the segments' state maps (segmented prefill).  A segment p
+// of a sequence maps its start state to its end state as S_end = M_p S_start +
+// b_p (the recurrence is affine in the state, linear in its key rows); M_p is
+// the segment run from the identity with V = 0, b_p the segment run from the
+// zero state.  One workgroup per (16-column tile, head, sequence) walks the
+// segments in order, S <- M_p S + b_p from the initial state (zero when
+// `init` is null), storing the state before each segment to `start` and the
+// one after the last to `fin` (when not null).  fp32; each element a
+// sequential sum over k, so the result does not depend on the launch.
+// Maps and starts are [sequence * P + segment][H][D][D].
+template <int D>
+__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ init,
+                                                           const float* __restrict__ Mm,
+                                                           const float* __restrict__ bm,
+                                                           float* __restrict__ start,
+                                                           float* __restrict__ fin, int32_t H,
+                                                           int32_t P) {
+    static_assert(D == 128, "256 threads: 128 rows x two 8-column halves of a 16-column tile");
+    __shared__ float St[D][16];
+    const int t = threadIdx.x, row = t >> 1, c0 = (t & 1) * 8;
+    const int64_t h = blockIdx.y, n = blockIdx.z;
+    const int64_t col = 16 * (int64_t)blockIdx.x + c0;
+    {
+        const int64_t o = ((n * H + h) * D + row) * D + col;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) St[row][c0 + j] = init ? init[o + j] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p < P; ++p) {
+        const int64_t base = ((n * P + p) * H + h) * D * D;
+        const int64_t o = base + (int64_t)row * D + col;
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            start[o + j] = St[row][c0 + j];
+            acc[j] = bm[o + j];
+        }
+        const float4* mrow = reinterpret_cast<const float4*>(Mm + base + (int64_t)row * D);
+        for (int k4 = 0; k4 < D / 4; ++k4) {
+            const float4 m = mrow[k4];
+            const float mk[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] = fmaf(mk[kk], St[4 * k4 + kk][c0 + j], acc[j]);
+        }
+        __syncthreads();  // every thread has read the tile
+#pragma unroll
+        for (int j = 0; j < 8; ++j) St[row][c0 + j] = acc[j];
+        __syncthreads();
+    }
+    if (fin) {
+        const int64_t o = ((n * H + h) * D + row) * D + col;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fin[o + j] = St[row][c0 + j];
+    }
+}
+
 // Resident workgroups per CU of the fused kernel for D (queried once per process; the
 // answer depends only on the kernel's resources and the gfx950 CU).
 template <int D>
@@ -1088,5 +1184,73 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
 
 template hipError_t launch_fused<128>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_fused<64>(const PrefillArgs&, hipStream_t);
+
+size_t segmented_scratch_bytes(const PrefillArgs& a, int P) {
+    return 3 * (size_t)a.n_seqs * P * a.n_heads * a.d * a.d * sizeof(float);
+}
+
+hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
+    constexpr int D = 128;
+    if (!a.bf16 || a.d != D || (a.cu_seqlens && a.n_seqs != 1) || P < 1) return hipErrorInvalidValue;
+    const int64_t N = a.n_seqs, H = a.n_heads;
+    const int64_t seq_len = a.total_tokens / N;
+    // segments of whole chunks; the last of each sequence is shorter
+    const int64_t seg_len = ((seq_len + P - 1) / P + 63) / 64 * 64;
+    const int Pe = (int)((seq_len + seg_len - 1) / seg_len);
+    const size_t map_elems = (size_t)N * Pe * H * D * D;
+    float* Mm = reinterpret_cast<float*>(a.workspace + a.layout.records_offset());
+    float* bm = Mm + map_elems;
+    float* st = bm + map_elems;
+    FusedParams fp;
+    fp.q = static_cast<const bf16*>(a.q);
+    fp.k = static_cast<const bf16*>(a.k);
+    fp.v = static_cast<const bf16*>(a.v);
+    fp.g = static_cast<const bf16*>(a.g);
+    fp.beta = static_cast<const bf16*>(a.beta);
+    fp.cu = nullptr;
+    fp.order = nullptr;
+    fp.counter = reinterpret_cast<int32_t*>(a.workspace);
+    fp.total_tokens = N * seq_len;
+    fp.n_seqs = (int32_t)(N * Pe);
+    fp.n_heads = (int32_t)H;
+    fp.scale = a.scale;
+    fp.l2norm = a.l2norm;
+    fp.seg_len = seg_len;
+    fp.seg_per_seq = Pe;
+    int per_cu = 1;
+    hipError_t e = fused_blocks_per_cu<D>(&per_cu);
+    if (e != hipSuccess) return e;
+    const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
+    const int grid = (int)std::min<int64_t>(N * Pe * H, cus * per_cu);
+    const dim3 block(64 * (kWsPrep<D> + kWsRec<D>));
+    const auto reset = [&]() {
+        hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, nullptr, 0, nullptr,
+                           fp.counter);
+        return hipGetLastError();
+    };
+    // the maps' affine parts: every segment from the zero state, no outputs
+    fp.init = nullptr;
+    fp.fin = bm;
+    fp.out = nullptr;
+    if ((e = reset()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fused_ws_kernel<D, false, false, true>), dim3(grid), block, 0, stream, fp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // their linear parts: from the identity with V = 0
+    fp.fin = Mm;
+    if ((e = reset()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fused_ws_kernel<D, false, true, true>), dim3(grid), block, 0, stream, fp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // every segment's start state, and the final states
+    hipLaunchKernelGGL((segment_scan_kernel<D>), dim3(D / 16, (unsigned)H, (unsigned)N), dim3(256), 0,
+                       stream, a.initial_state, Mm, bm, st, a.final_state, (int32_t)H, (int32_t)Pe);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the outputs: every segment again from its start state
+    fp.init = st;
+    fp.fin = nullptr;
+    fp.out = static_cast<bf16*>(a.out);
+    if ((e = reset()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fused_ws_kernel<D, true, false, true>), dim3(grid), block, 0, stream, fp);
+    return hipGetLastError();
+}
 
 }  // namespace kda

@@ -149,6 +149,26 @@ constexpr int64_t kFusedCUsPerChain = 2;
 // environment variable KDA_PREFILL_PATH=split or =fused overrides the choice
 // where the fused kernel applies.
 bool fused_path(const PrefillArgs& a);
+
+// Segmented prefill of few long chains (d = 128, bf16, plain options, one
+// sequence or equal lengths): every sequence is cut into P segments, the
+// fused kernel forms each segment's state map from the zero state and from
+// the identity, a scan composes the maps into every segment's start state, and
+// the fused kernel runs the segments again from those states for the outputs.
+// segmented_segments gives P, or 0 where the path does not apply or would not
+// pay (KDA_PREFILL_PATH=segmented forces it where it applies, and
+// KDA_PREFILL_SEGMENTS=<P> sets P).  Its three [N P, H, d, d] fp32 arrays take
+// segmented_scratch_bytes of the workspace's record area.
+int segmented_segments(const PrefillArgs& a);
+size_t segmented_scratch_bytes(const PrefillArgs& a, int P);
+hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream);
+// Chains per compute unit below which the segmented path is taken
+// automatically: one chain per kSegCUsPerChain units or fewer.
+constexpr int64_t kSegCUsPerChain = 16;
+// Fewest chunks per segment, and most segments per sequence.
+constexpr int64_t kSegMinChunks = 256;
+constexpr int kSegMaxSegments = 64;
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kda

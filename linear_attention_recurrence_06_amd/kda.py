@@ -28,12 +28,13 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_MISALIGNED, \
     KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(6)
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_GATE_CHANNEL, KDA_GATE_HEAD = 0, 1
+KDA_PATH_SPLIT, KDA_PATH_PIPELINED, KDA_PATH_FUSED, KDA_PATH_SEGMENTED = range(4)
 
 #: every symbol include/kda.h declares
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
             "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_decode_step",
             "kda_decode_step_ex", "kda_status_string", "kda_version",
-            "kda_prefill_pipeline_segments", "kda_chunk_prefill_noalloc")
+            "kda_prefill_pipeline_segments", "kda_chunk_prefill_noalloc", "kda_prefill_path")
 
 #: bytes of the per-device array kda_chunk_prefill_noalloc uses as its workspace
 KDA_NOALLOC_SCRATCH_BYTES = 320 << 20
@@ -136,6 +137,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_version.restype = ctypes.c_int
     lib.kda_prefill_pipeline_segments.argtypes = [D]
     lib.kda_prefill_pipeline_segments.restype = ctypes.c_int32
+    lib.kda_prefill_path.argtypes = [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_prefill_path.restype = ctypes.c_int32
     lib.kda_chunk_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
     _lib = lib
@@ -200,8 +203,18 @@ def kda_prefill_workspace_bytes(dims: kda_dims) -> int:
 
 def kda_prefill_pipeline_segments(dims: kda_dims) -> int:
     """Segments a prefill of these sizes is pipelined into on the current
-    device (0: one launch of each kernel; -1: rejected descriptor)."""
+    device (0: one launch of each kernel or another path; -1: rejected
+    descriptor)."""
     return int(load_library().kda_prefill_pipeline_segments(ctypes.byref(dims)))
+
+
+def kda_prefill_path(dims: kda_dims, packed: bool = False):
+    """(path, segments) a plain prefill of these sizes takes on the current
+    device: path one of KDA_PATH_*, or -1 for a rejected descriptor."""
+    seg = ctypes.c_int32(0)
+    path = int(load_library().kda_prefill_path(ctypes.byref(dims), int(bool(packed)),
+                                               ctypes.byref(seg)))
+    return path, int(seg.value)
 
 
 def _check_tensor(name, t, shape, dtype, device):

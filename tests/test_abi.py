@@ -63,8 +63,9 @@ def test_workspace_bytes(kda):
     slots2 = 8192 // 64 + 2
     desc2 = -(-slots2 * 8 // 256) * 256
     assert kda.kda_prefill_workspace_bytes(d2) == 2 * 256 + desc2 + rec * slots2 * 32
-    # a rejected descriptor has no pipeline segment count
+    # a rejected descriptor has no pipeline segment count and no path
     assert kda.kda_prefill_pipeline_segments(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == -1
+    assert kda.kda_prefill_path(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16))[0] == -1
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     # fp32 I/O at d = 128: the same record with 4-byte elements

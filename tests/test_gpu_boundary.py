@@ -103,7 +103,7 @@ def test_fp32_d128_strong_decay_and_decode(lib, oracle):
 def test_library_workspace_equals_caller_workspace(lib, lens, heads):
     """workspace NULL: the library allocates it on the stream (hipMallocAsync /
     hipFreeAsync).  Results are bitwise those of a caller workspace; the second
-    shape is pipelined over two streams."""
+    shape (one 262,144-token sequence, 16 heads) takes the segmented path."""
     from kda_inputs import make_prefill
     inp = make_prefill(lens, heads, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=405,
                        device="cuda", packed_cu=len(lens) > 1)
@@ -112,6 +112,9 @@ def test_library_workspace_equals_caller_workspace(lib, lens, heads):
     o1, f1 = lib.kda_chunk_prefill(*args, num_seqs=len(lens))
     o2, f2 = lib.kda_chunk_prefill(*args, num_seqs=len(lens), library_workspace=True)
     s = torch.cuda.Stream()
+    # the side stream starts after the inputs exist (torch made them on the
+    # current stream)
+    s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         o3, f3 = lib.kda_chunk_prefill(*args, num_seqs=len(lens), library_workspace=True,
                                        stream=s)

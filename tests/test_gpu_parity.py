@@ -182,12 +182,13 @@ def test_prefill_config4(lib, oracle):
     from kda_inputs import make_config_prefill, seeded_heads
     inp = make_config_prefill(4, device="cuda")
     say("config4: inputs ready")
-    # 16 heads x 8 recurrence tiles leave half the CUs idle: the call is
-    # pipelined in 16 segments, so this parity covers that path
+    # 16 chains on a 256-CU device: the call is segmented (16 segments of
+    # 1,024 chunks), so this parity covers that path at full size
     import linear_attention_recurrence_06_amd as kda
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    segs = kda.kda_prefill_pipeline_segments(kda.make_dims(1 << 20, 1, 16, 128, 128, kda.kda.KDA_BF16))
-    assert segs == (16 if 16 * 8 < cus else 0)
+    path, segs = kda.kda_prefill_path(kda.make_dims(1 << 20, 1, 16, 128, 128, kda.kda.KDA_BF16))
+    if cus == 256:
+        assert (path, segs) == (kda.kda.KDA_PATH_SEGMENTED, 16)
     hs = seeded_heads(16, 2, 104)
     out, fin, o_ref, f_ref = run_prefill_case(lib, oracle, inp, heads=hs, label="config4")
     o_gpu = host(out[:, hs])

@@ -114,16 +114,21 @@ def test_pipelined_all_options(lib):
 
 def test_pipeline_segment_rule(lib):
     """Segments as documented: min(16, chunks / 1024) when that is at least 4,
-    for one sequence whose H * d / 16 recurrence workgroups leave CUs idle."""
+    for one sequence whose H * d / 16 recurrence workgroups leave CUs idle and
+    that neither the fused nor the segmented path takes."""
     K = lib.kda
-    seg = lambda T, N, H, d=128: lib.kda_prefill_pipeline_segments(
-        lib.make_dims(T, N, H, d, d, K.KDA_BF16))
+    seg = lambda T, N, H, d=128, io=K.KDA_BF16: lib.kda_prefill_pipeline_segments(
+        lib.make_dims(T, N, H, d, d, io))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert seg(4095 * 64, 1, 2) == 0                  # 4,095 chunks
     assert seg(4095 * 64 + 1, 1, 2) == 4              # 4,096 chunks (the last one partial)
     assert seg(8191 * 64, 1, 2) == 7                  # 8,191 chunks: 7 whole 1,024-chunk segments
-    assert seg(1 << 20, 1, 16) == (16 if 16 * 8 < cus else 0)   # the million-token workload
-    assert seg(1 << 22, 1, 2) == 16                   # at most 16 segments
+    # the million-token workload: segmented instead (bf16, on 256 CUs), so
+    # not pipelined; with fp32 I/O it is
+    if cus == 256:
+        assert seg(1 << 20, 1, 16) == 0
+    assert seg(1 << 20, 1, 16, io=K.KDA_FP32) == (16 if 16 * 8 < cus else 0)
+    assert seg(1 << 22, 1, 2, io=K.KDA_FP32) == 16    # at most 16 segments
     assert seg(8192, 1, 32) == 0                      # the 8,192-token workload: too short
     assert seg(1 << 20, 1, cus // 8) == 0             # the recurrence fills every CU
     assert seg(1 << 20, 2, 2) == 0                    # more than one sequence

@@ -1,0 +1,216 @@
+"""GPU tests of the segmented prefill: a long sequence with few heads is cut
+into segments; the fused kernel forms every segment's state map S_end = M S_start
++ b (b from the zero state, M from the identity with V = 0), a scan composes the
+maps into each segment's start state, and the fused kernel runs the segments
+again from those states for the outputs.
+
+* Parity with the fp64 oracle at the bf16 bar (max abs error 2e-2, every
+  output finite): one ragged sequence cut into 4 segments (the last shorter,
+  ending in a partial chunk), equal lengths without cu_seqlens, decay strong
+  enough for the exact diagonal products, channels of all three decay
+  regimes, no initial and no final state.
+* Agreement with the two-kernel path within twice that bar where the oracle
+  would be slow: the automatic choice on a 262,144-token sequence with 8 heads.
+* Bitwise: two runs of the same call, and the library-allocated workspace.
+
+KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS the
+segment count.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+def maxerr(a, b):
+    a = np.asarray(a, np.float64)
+    return float(np.max(np.abs(a - np.asarray(b, np.float64)))) if a.size else 0.0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_recurrence_06_amd as kda
+    kda.load_library()
+    return kda
+
+
+def args_of(inp):
+    return (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+            inp["cu_seqlens"])
+
+
+def run(lib, monkeypatch, inp, path, segments=None, **kw):
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    if segments is None:
+        monkeypatch.delenv("KDA_PREFILL_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("KDA_PREFILL_SEGMENTS", str(segments))
+    out, fin = lib.kda_chunk_prefill(*args_of(inp), num_seqs=len(inp["lens"]), **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def near_split(lib, monkeypatch, inp, label, segments=None, **kw):
+    """The segmented path, checked against the two-kernel path within 2 TOL."""
+    o_s, f_s = run(lib, monkeypatch, inp, "split", **kw)
+    o_g, f_g = run(lib, monkeypatch, inp, "segmented", segments, **kw)
+    eo = maxerr(host(o_g), host(o_s))
+    ef = maxerr(host(f_g), host(f_s)) if f_g is not None else 0.0
+    say(f"[{label}] segmented vs split: out {eo:.3e} state {ef:.3e}")
+    assert torch.isfinite(o_g.float()).all()
+    assert (f_g is None) == (f_s is None)
+    assert f_g is None or torch.isfinite(f_g).all()
+    assert eo <= 2 * TOL and ef <= 2 * TOL
+    return o_g, f_g
+
+
+def oracle_check(oracle, inp, out, fin, label):
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].cpu().numpy()
+    o_ref, f_ref = oracle.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]),
+                                  host(inp["beta"]), cu_seqlens=cu,
+                                  initial_state=host(inp["initial_state"]),
+                                  n_seqs=len(inp["lens"]))
+    eo = maxerr(host(out), o_ref)
+    ef = maxerr(host(fin), f_ref) if fin is not None else 0.0
+    say(f"[{label}] oracle err_out={eo:.3e} err_state={ef:.3e} tol={TOL}")
+    assert eo <= TOL and ef <= TOL
+
+
+def test_ragged_sequence(lib, oracle, monkeypatch):
+    """16,421 tokens (257 chunks, the last partial) x 2 heads in 4 segments of
+    4,160 tokens; the last segment is 3,941."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([16421], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=601,
+                       device="cuda")
+    out, fin = near_split(lib, monkeypatch, inp, "ragged", segments=4)
+    oracle_check(oracle, inp, out, fin, "ragged")
+
+
+def test_equal_lengths_without_cu(lib, oracle, monkeypatch):
+    """Three 8,192-token sequences without cu_seqlens, 3 segments each."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([8192] * 3, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=602,
+                       device="cuda", packed_cu=False)
+    assert inp["cu_seqlens"] is None
+    out, fin = near_split(lib, monkeypatch, inp, "equal lengths", segments=3)
+    oracle_check(oracle, inp, out, fin, "equal lengths")
+
+
+@pytest.mark.parametrize("g_value", [-8.0, -30.0])
+def test_strong_decay(lib, oracle, monkeypatch, g_value):
+    """Blocks past the factored range in every channel, plus 1% of gates at
+    -100: the maps' linear parts then decay to zero within a segment."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([6000], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=603,
+                       device="cuda")
+    g = torch.full_like(inp["g"], g_value)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(604)
+    g[torch.rand(g.shape, generator=gen, device="cuda") < 0.01] = -100.0
+    inp["g"] = g
+    out, fin = near_split(lib, monkeypatch, inp, f"g={g_value}", segments=4)
+    oracle_check(oracle, inp, out, fin, f"g={g_value}")
+
+
+def test_mixed_decay_forms(lib, oracle, monkeypatch):
+    """Key channels in the three decay regimes side by side, and long-retention
+    channels (g near zero) whose state carries across every segment."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([12800], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=605,
+                       device="cuda")
+    g = inp["g"].float().clone()
+    g[:, :, 32:64] = -2.0
+    g[:, :, 64:96] = -8.0
+    g[:, :, 96:128] = -0.001
+    inp["g"] = g.to(inp["g"].dtype)
+    out, fin = near_split(lib, monkeypatch, inp, "mixed decay", segments=5)
+    oracle_check(oracle, inp, out, fin, "mixed decay")
+
+
+def test_no_initial_no_final_state(lib, oracle, monkeypatch):
+    from kda_inputs import make_prefill
+    inp = make_prefill([9000], 2, 128, "bf16", g_scale=0.5, s0_std=None, seed=606,
+                       device="cuda")
+    assert inp["initial_state"] is None
+    out, fin = near_split(lib, monkeypatch, inp, "no states", segments=4,
+                          output_final_state=False)
+    assert fin is None
+    oracle_check(oracle, inp, out, None, "no states")
+
+
+def test_auto_choice_long_sequence(lib, monkeypatch):
+    """262,144 tokens x 8 heads: 8 chains, so on a 256-CU device the automatic
+    choice cuts the sequence into 16 segments of 256 chunks (128 chains);
+    checked against the two-kernel path, bitwise against the forced path with
+    the same count, and bitwise from run to run."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([262144], 8, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=607,
+                       device="cuda")
+    o_a, f_a = run(lib, monkeypatch, inp, "auto")
+    o_s, f_s = run(lib, monkeypatch, inp, "split")
+    eo, ef = maxerr(host(o_a), host(o_s)), maxerr(host(f_a), host(f_s))
+    say(f"[auto 262,144 x 8] vs split: out {eo:.3e} state {ef:.3e}")
+    assert torch.isfinite(o_a.float()).all() and torch.isfinite(f_a).all()
+    assert eo <= 2 * TOL and ef <= 2 * TOL
+    o_g, f_g = run(lib, monkeypatch, inp, "segmented", 16)
+    assert torch.equal(o_g, o_a) and torch.equal(f_g, f_a)
+    o_2, f_2 = run(lib, monkeypatch, inp, "segmented", 16)
+    assert torch.equal(o_2, o_g) and torch.equal(f_2, f_g)
+
+
+def test_path_choice(lib, monkeypatch):
+    """The rule on a 256-CU device: few chains over long sequences, enough
+    segments of at least 256 chunks to give every two CUs a chain."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the thresholds below are for 256 compute units")
+    monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
+    monkeypatch.delenv("KDA_PREFILL_SEGMENTS", raising=False)
+    K = lib.kda
+    path = lambda T, N, H, packed=False, io=K.KDA_BF16, d=128: lib.kda_prefill_path(
+        lib.make_dims(T, N, H, d, d, io), packed)
+    assert path(1 << 20, 1, 16) == (K.KDA_PATH_SEGMENTED, 16)      # the million-token workload
+    assert path(1 << 19, 1, 8) == (K.KDA_PATH_SEGMENTED, 32)
+    assert path(1 << 18, 1, 8) == (K.KDA_PATH_SEGMENTED, 16)       # 128 chains
+    assert path(1 << 18, 1, 4)[0] == K.KDA_PATH_PIPELINED           # 64 chains: too few
+    assert path(1 << 20, 1, 32)[0] == K.KDA_PATH_SPLIT              # 32 chains: too many
+    assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # 64 segments of 256 chunks
+    assert path(1 << 20, 1, 16, packed=True) == (K.KDA_PATH_SEGMENTED, 16)  # cu = [0, T]
+    assert path(1 << 20, 2, 8)[0] == K.KDA_PATH_SEGMENTED           # equal lengths, no cu
+    assert path(1 << 20, 2, 8, packed=True)[0] == K.KDA_PATH_SPLIT  # packed: bounds unknown
+    assert path(1 << 20, 1, 16, io=K.KDA_FP32)[0] == K.KDA_PATH_PIPELINED  # bf16 only
+    assert path(1 << 20, 1, 16, d=64)[0] == K.KDA_PATH_PIPELINED    # d = 128 only
+    assert path(8192, 1, 32)[0] == K.KDA_PATH_SPLIT                 # the 8,192-token workload
+    assert path(1007721, 64, 32, packed=True)[0] == K.KDA_PATH_FUSED
+    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+    assert path(1 << 20, 1, 16)[0] == K.KDA_PATH_PIPELINED
+    monkeypatch.setenv("KDA_PREFILL_PATH", "segmented")
+    monkeypatch.setenv("KDA_PREFILL_SEGMENTS", "4")
+    assert path(16421, 1, 2) == (K.KDA_PATH_SEGMENTED, 4)
+
+
+def test_library_workspace(lib, monkeypatch):
+    """No workspace given: the library allocates the index areas and the maps."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([16421], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=608,
+                       device="cuda")
+    o_w, f_w = run(lib, monkeypatch, inp, "segmented", 4)
+    o_l, f_l = run(lib, monkeypatch, inp, "segmented", 4, library_workspace=True)
+    assert torch.equal(o_l, o_w) and torch.equal(f_l, f_w)
