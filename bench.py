@@ -20,7 +20,8 @@ Secondary figures in the same run, each with its own roofline object:
 * the 8,192-token single-sequence prefill (H=32), four input copies rotated so
   a call never finds its inputs in the MALL, plus its checkpoint, per-head
   gate, output-gate and front-end variants;
-* the 2^20-token single-sequence prefill (H=16);
+* the 2^20-token single-sequence prefill (H=16; its 16 chains take the
+  segmented path: 16 segments per head);
 * the decode step on 256 sequences x 32 heads (512 MiB fp32 state advanced in
   place), plus its output-gate and front-end variants.
 
@@ -71,6 +72,14 @@ def fused_executed_flops(T, H, d, C=16):
     and M u 2 C d each, the diagonal A, A^T, M^T 6 C d, the K'^T selector
     products 4 C d (the inverse's fp32 products, 16 C^2, are not counted)."""
     return (6 * d * d + 14 * C * d) * T * H
+
+
+def segmented_executed_flops(T, H, d, C=16):
+    """bf16 MFMA work per token-head of the segmented prefill: the two map
+    passes without outputs (Ke S, the state update, T Diag(beta) Y, A, A^T and
+    the selector products: 4 d^2 + 10 C d each) and the output pass (the fused
+    kernel's 6 d^2 + 14 C d); the scan's fp32 products are not counted."""
+    return (14 * d * d + 34 * C * d) * T * H
 
 
 def decode_state_bytes(n, h, d):
@@ -528,7 +537,8 @@ def main():
             "tokens_per_s": LT / l_avg,
             "roofline": roofline("kda_chunk_prefill call", l_bytes, l_avg,
                                  counter_traffic("prefill_long"), copy_GBps,
-                                 flops=prefill_executed_flops(LT, LH, D),
+                                 flops=(segmented_executed_flops(LT, LH, D) if long_path == 3
+                                        else prefill_executed_flops(LT, LH, D)),
                                  median_call_ms=float(np.median(l_ms))),
             "cpu_baseline": cpu_long,
         },
