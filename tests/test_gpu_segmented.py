@@ -11,7 +11,8 @@ again from those states for the outputs.
   regimes, no initial and no final state.
 * Agreement with the two-kernel path within twice that bar where the oracle
   would be slow: the automatic choice on a 262,144-token sequence with 8 heads.
-* Bitwise: two runs of the same call, and the library-allocated workspace.
+* Bitwise: two runs of the same call, the library-allocated workspace, and
+  graph replays of the segmented and the fused path.
 
 KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS the
 segment count.
@@ -214,3 +215,38 @@ def test_library_workspace(lib, monkeypatch):
     o_w, f_w = run(lib, monkeypatch, inp, "segmented", 4)
     o_l, f_l = run(lib, monkeypatch, inp, "segmented", 4, library_workspace=True)
     assert torch.equal(o_l, o_w) and torch.equal(f_l, f_w)
+
+
+@pytest.mark.parametrize("path,lens,heads,segments", [("segmented", [16421], 2, 4),
+                                                      ("fused", [300, 64, 1000, 5], 4, None)])
+def test_replayed_from_a_graph(lib, monkeypatch, path, lens, heads, segments):
+    """The segmented and fused paths captured into a graph (every launch on
+    the capturing stream, the chain counter zeroed by a kernel, not a memset)
+    and replayed three times with eager work in between: every replay equals
+    the eager call bit for bit."""
+    from kda_inputs import make_prefill
+    inp = make_prefill(lens, heads, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=609,
+                       device="cuda")
+    o_ref, f_ref = run(lib, monkeypatch, inp, path, segments)
+    dims = lib.make_dims(sum(lens), len(lens), heads, 128, 128, lib.kda.KDA_BF16)
+    ws = torch.empty(lib.kda_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out, fin = torch.empty_like(o_ref), torch.empty_like(f_ref)
+    call = lambda: lib.kda_chunk_prefill(*args_of(inp), out, fin, num_seqs=len(lens), workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(fin, f_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        fin.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[{path}] graph replay {rep}")
+        assert torch.equal(out, o_ref) and torch.equal(fin, f_ref)
