@@ -38,19 +38,26 @@
 // lane (t, g) = (lane % 16, lane / 16) holding token t of the block and
 // channels 32 ks + 8 g + {0..7} of each 32-channel slice ks (one 16-byte load
 // per row and slice), which is the K order of every 16 x 16 x 32 product over
-// channels.  The state's key
-// channels are placed in its 16-row tiles to match: row 4 g + e of tile 2 ks
-// holds channel 32 ks + 8 g + e, of tile 2 ks + 1 channel 32 ks + 8 g + 4 + e,
-// so the state rows a lane holds as accumulator are, as they stand, its B
-// operand: no state data moves between lanes.  K'^T is transposed into that
+// channels.  The state's key channels are placed in its 16-row tiles to match:
+// row 4 g + e of tile 2 ks holds channel 32 ks + 8 g + e, of tile 2 ks + 1
+// channel 32 ks + 8 g + 4 + e, so the state rows a lane holds as accumulator
+// are, as they stand, its B operand: no state data moves between lanes.  K'^T is transposed into that
 // row order by a product with a 0/1 selector operand.  A recurrence wave owns
 // 16 (d = 64) or 32 (d = 128) value columns of the fp32 state and needs no
 // other wave's state; the block's operands come from the record in LDS.
 //
-// Two kernels.  At d = 64 (fused_kernel) the four waves of a workgroup prepare
-// a chunk's four blocks, meet at a barrier, then run its recurrence on 16
-// value columns each.  At d = 128 (fused_ws_kernel) four waves only prepare
-// and four only run the recurrence, one chunk behind, on the same SIMDs.
+// Kernels.  At d = 64 (fused_kernel) the four waves of a workgroup prepare a
+// chunk's four blocks, meet at a barrier, then run its recurrence on 16 value
+// columns each.  At d = 128 (fused_ws_kernel) four waves only prepare and four
+// only run the recurrence, one chunk behind, on the same SIMDs.
+//
+// Segmented prefill (launch_segmented).  For few long chains the sequences are
+// cut into segments whose (segment, head) chains fill the device.  The
+// recurrence is affine in the state, so over a segment S_end = M S_start + b:
+// variants of fused_ws_kernel form b (from the zero state) and M (from the
+// identity, v taken as zero) without writing outputs, segment_scan_kernel
+// composes them in order into every segment's start state, and
+// fused_ws_kernel runs the segments again from those states for the outputs.
 #include <algorithm>
 #include <atomic>
 
