@@ -164,10 +164,11 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * the chunk's operands in LDS, so only the inputs, the outputs and the states
  * touch HBM; it uses only the first two index areas of the workspace.  A
  * call with few chains -- at most one per 16 compute units -- over long
- * sequences (one sequence, or equal lengths without cu_seqlens), d = 128 and
- * otherwise the fused kernel's conditions, is segmented: each sequence is cut
- * into P segments of at least 256 chunks, with P chosen so that the
- * (segment, head) chains give every two compute units one.  The fused kernel
+ * sequences, d = 128 and otherwise the fused kernel's conditions, is
+ * segmented: each sequence is cut into P segments of whole chunks (at least
+ * 256 chunks for sequences of the average length; a short sequence may leave
+ * segments empty), with P chosen so that the (segment, head) chains give
+ * every two compute units one.  The fused kernel
  * forms each segment's state map S_end = M S_start + b twice over (b from the
  * zero state, M from the identity with v taken as zero, neither writing
  * outputs), a scan kernel composes the maps in order into every segment's

@@ -137,8 +137,7 @@ bool fused_path(const PrefillArgs& a) {
 }
 
 int segmented_segments(const PrefillArgs& a) {
-    // the fused kernel's plain recurrence at d = 128, whole call, and segment
-    // bounds the host knows: one sequence, or equal lengths
+    // the fused kernel's plain recurrence at d = 128, the whole call
     if (!a.bf16 || a.d != 128 || a.scalar_g || a.out_gate != 0 || a.fe.active() ||
         a.ckpt_interval > 0)
         return 0;
@@ -146,7 +145,6 @@ int segmented_segments(const PrefillArgs& a) {
     if (a.total_tokens <= 0 || a.n_seqs < 1 || a.slot_begin != 0 || a.slot_end != -1 ||
         a.chunk_begin != 0 || a.chunk_end != INT64_MAX)
         return 0;
-    if (a.cu_seqlens && a.n_seqs != 1) return 0;
     if (fused_path(a)) return 0;
     const char* env = std::getenv("KDA_PREFILL_PATH");
     const bool forced = env && std::strcmp(env, "segmented") == 0;

@@ -112,10 +112,12 @@ struct FusedParams {
     int32_t n_seqs, n_heads;
     float scale;
     int l2norm;
-    // segmented kernels: the n_seqs / seg_per_seq sequences (equal lengths,
-    // no cu) are cut into seg_per_seq segments of seg_len tokens (the last of
-    // each shorter), and each (segment, head) is a chain; n_seqs counts the
-    // segments
+    // segmented kernels: each of the n_seqs / seg_per_seq sequences is cut
+    // into seg_per_seq segments of whole chunks, and each (segment, head) is a
+    // chain; n_seqs counts the segments.  With cu, a sequence's segments are
+    // ceil(len / seg_per_seq) tokens rounded up to whole chunks (those past
+    // its end empty); without, equal lengths and segments of seg_len tokens
+    // (the last shorter)
     int64_t seg_len = 0;
     int32_t seg_per_seq = 1;
 };
@@ -905,10 +907,18 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
         int64_t s_begin, s_len;
         if constexpr (SEG) {
             // segment n % seg_per_seq of sequence n / seg_per_seq
-            const int64_t seq_len = p.total_tokens / (p.n_seqs / p.seg_per_seq);
-            const int64_t part = n % p.seg_per_seq;
-            s_begin = (n / p.seg_per_seq) * seq_len + part * p.seg_len;
-            s_len = max((int64_t)0, min(p.seg_len, seq_len - part * p.seg_len));
+            const int64_t seq = n / p.seg_per_seq, part = n % p.seg_per_seq;
+            int64_t seq_begin, seq_len, seg_len = p.seg_len;
+            if (p.cu) {
+                seq_begin = p.cu[seq];
+                seq_len = (int64_t)p.cu[seq + 1] - seq_begin;
+                seg_len = ((seq_len + p.seg_per_seq - 1) / p.seg_per_seq + 63) / 64 * 64;
+            } else {
+                seq_len = p.total_tokens / (p.n_seqs / p.seg_per_seq);
+                seq_begin = seq * seq_len;
+            }
+            s_begin = seq_begin + part * seg_len;
+            s_len = max((int64_t)0, min(seg_len, seq_len - part * seg_len));
         } else if (p.cu) {
             s_begin = p.cu[n];
             s_len = (int64_t)p.cu[n + 1] - s_begin;
@@ -1198,12 +1208,14 @@ size_t segmented_scratch_bytes(const PrefillArgs& a, int P) {
 
 hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     constexpr int D = 128;
-    if (!a.bf16 || a.d != D || (a.cu_seqlens && a.n_seqs != 1) || P < 1) return hipErrorInvalidValue;
+    if (!a.bf16 || a.d != D || P < 1) return hipErrorInvalidValue;
     const int64_t N = a.n_seqs, H = a.n_heads;
-    const int64_t seq_len = a.total_tokens / N;
-    // segments of whole chunks; the last of each sequence is shorter
-    const int64_t seg_len = ((seq_len + P - 1) / P + 63) / 64 * 64;
-    const int Pe = (int)((seq_len + seg_len - 1) / seg_len);
+    // segments of whole chunks; the last of each sequence is shorter.  With
+    // cu_seqlens the kernel cuts each sequence into P itself (segments past a
+    // short sequence's end are empty: M = I, b = 0)
+    const int64_t seq_len = a.cu_seqlens ? 0 : a.total_tokens / N;
+    const int64_t seg_len = a.cu_seqlens ? 0 : ((seq_len + P - 1) / P + 63) / 64 * 64;
+    const int Pe = a.cu_seqlens ? P : (int)((seq_len + seg_len - 1) / seg_len);
     const size_t map_elems = (size_t)N * Pe * H * D * D;
     float* Mm = reinterpret_cast<float*>(a.workspace + a.layout.records_offset());
     float* bm = Mm + map_elems;
@@ -1214,10 +1226,10 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     fp.v = static_cast<const bf16*>(a.v);
     fp.g = static_cast<const bf16*>(a.g);
     fp.beta = static_cast<const bf16*>(a.beta);
-    fp.cu = nullptr;
+    fp.cu = a.cu_seqlens;
     fp.order = nullptr;
     fp.counter = reinterpret_cast<int32_t*>(a.workspace);
-    fp.total_tokens = N * seq_len;
+    fp.total_tokens = a.cu_seqlens ? a.total_tokens : N * seq_len;
     fp.n_seqs = (int32_t)(N * Pe);
     fp.n_heads = (int32_t)H;
     fp.scale = a.scale;

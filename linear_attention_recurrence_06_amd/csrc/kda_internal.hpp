@@ -150,8 +150,8 @@ constexpr int64_t kFusedCUsPerChain = 2;
 // where the fused kernel applies.
 bool fused_path(const PrefillArgs& a);
 
-// Segmented prefill of few long chains (d = 128, bf16, plain options, one
-// sequence or equal lengths): every sequence is cut into P segments, the
+// Segmented prefill of few long chains (d = 128, bf16, plain options): every
+// sequence is cut into P segments (by the kernel, from cu_seqlens), the
 // fused kernel forms each segment's state map from the zero state and from
 // the identity, a scan composes the maps into every segment's start state, and
 // the fused kernel runs the segments again from those states for the outputs.

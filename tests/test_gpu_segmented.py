@@ -6,7 +6,8 @@ again from those states for the outputs.
 
 * Parity with the fp64 oracle at the bf16 bar (max abs error 2e-2, every
   output finite): one ragged sequence cut into 4 segments (the last shorter,
-  ending in a partial chunk), equal lengths without cu_seqlens, decay strong
+  ending in a partial chunk), packed sequences with empty segments and an
+  empty sequence, equal lengths without cu_seqlens, decay strong
   enough for the exact diagonal products, channels of all three decay
   regimes, no initial and no final state.
 * Agreement with the two-kernel path within twice that bar where the oracle
@@ -105,6 +106,19 @@ def test_ragged_sequence(lib, oracle, monkeypatch):
     oracle_check(oracle, inp, out, fin, "ragged")
 
 
+def test_packed_sequences(lib, oracle, monkeypatch):
+    """Four packed sequences of 200, 20,000, 0 and 9,000 tokens cut into 8
+    segments each on the device: the short one leaves four segments empty
+    (their maps M = I, b = 0) and the empty one keeps its initial state."""
+    from kda_inputs import make_prefill
+    lens = [200, 20000, 0, 9000]
+    inp = make_prefill(lens, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=610, device="cuda")
+    assert inp["cu_seqlens"] is not None
+    out, fin = near_split(lib, monkeypatch, inp, "packed", segments=8)
+    oracle_check(oracle, inp, out, fin, "packed")
+    assert torch.equal(fin[2], inp["initial_state"][2])
+
+
 def test_equal_lengths_without_cu(lib, oracle, monkeypatch):
     """Three 8,192-token sequences without cu_seqlens, 3 segments each."""
     from kda_inputs import make_prefill
@@ -195,7 +209,7 @@ def test_path_choice(lib, monkeypatch):
     assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # 64 segments of 256 chunks
     assert path(1 << 20, 1, 16, packed=True) == (K.KDA_PATH_SEGMENTED, 16)  # cu = [0, T]
     assert path(1 << 20, 2, 8)[0] == K.KDA_PATH_SEGMENTED           # equal lengths, no cu
-    assert path(1 << 20, 2, 8, packed=True)[0] == K.KDA_PATH_SPLIT  # packed: bounds unknown
+    assert path(1 << 20, 2, 8, packed=True)[0] == K.KDA_PATH_SEGMENTED  # cut on the device
     assert path(1 << 20, 1, 16, io=K.KDA_FP32)[0] == K.KDA_PATH_PIPELINED  # bf16 only
     assert path(1 << 20, 1, 16, d=64)[0] == K.KDA_PATH_PIPELINED    # d = 128 only
     assert path(8192, 1, 32)[0] == K.KDA_PATH_SPLIT                 # the 8,192-token workload
