@@ -145,6 +145,8 @@ int segmented_segments(const PrefillArgs& a) {
     if (a.total_tokens <= 0 || a.n_seqs < 1 || a.slot_begin != 0 || a.slot_end != -1 ||
         a.chunk_begin != 0 || a.chunk_end != INT64_MAX)
         return 0;
+    // (the scan's grid is tiles x heads x sequences)
+    if (a.n_seqs > 65535 || a.n_heads > 65535) return 0;
     if (fused_path(a)) return 0;
     const char* env = std::getenv("KDA_PREFILL_PATH");
     const bool forced = env && std::strcmp(env, "segmented") == 0;
