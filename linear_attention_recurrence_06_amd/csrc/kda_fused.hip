@@ -883,10 +883,11 @@ __device__ __forceinline__ void ws_flush(const FusedParams& p, const bf16 (&vt)[
     }
 }
 
-// The segmented prefill's kernels: SEG, chains are the segments of p.seg_len;
-// OUT false, no outputs (p.out unused, no q read); ZERO_V, V taken as zero
-// and every chain started from the identity (p.v and p.init unused: the
-// linear part of each segment's state map).
+// The segmented prefill's kernels: SEG, chains are (segment, head) pairs
+// (p.seg_per_seq segments per sequence, placed from p.seg_len or p.cu); OUT
+// false, no outputs (p.out unused, no q read); ZERO_V, V taken as zero and
+// every chain started from the identity (p.v and p.init unused: the linear
+// part of each segment's state map).
 template <int D, bool OUT = true, bool ZERO_V = false, bool SEG = false>
 __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
     constexpr int NCT = D / 16, TPV = WsSmem<D>::TPV;
