@@ -75,11 +75,12 @@ def fused_executed_flops(T, H, d, C=16):
 
 
 def segmented_executed_flops(T, H, d, C=16):
-    """bf16 MFMA work per token-head of the segmented prefill: the two map
-    passes without outputs (Ke S, the state update, T Diag(beta) Y, A, A^T and
-    the selector products: 4 d^2 + 10 C d each) and the output pass (the fused
-    kernel's 6 d^2 + 14 C d); the scan's fp32 products are not counted."""
-    return (14 * d * d + 34 * C * d) * T * H
+    """bf16 MFMA work per token-head of the segmented prefill: the map pass
+    without outputs (Ke S, the state update and T Diag(beta) Y for the b and
+    the M tiles, 8 d^2 + 4 C d, and the A, A^T and selector products once, 8 C
+    d) and the output pass (the fused kernel's 6 d^2 + 14 C d); the scan's
+    fp32 products are not counted."""
+    return (14 * d * d + 26 * C * d) * T * H
 
 
 def decode_state_bytes(n, h, d):

@@ -161,10 +161,11 @@ int segmented_segments(const PrefillArgs& a) {
         if (v >= 1 && v <= kSegMaxSegments) P = std::min<int64_t>(v, seq_chunks);
     }
     if (P < 2) return 0;
-    // automatically: few chains, and enough segments to give every two
-    // compute units a chain
-    if (!forced && (a.compute_units <= 0 || chains * kSegCUsPerChain > a.compute_units ||
-                    chains * P * kFusedCUsPerChain < a.compute_units))
+    // automatically: at least kSegMinSegments segments, and either enough
+    // that the segment chains fill three quarters of the device or at least
+    // kSegManySegments
+    if (!forced && (a.compute_units <= 0 || P < kSegMinSegments ||
+                    (chains * P * 4 < (int64_t)a.compute_units * 3 && P < kSegManySegments)))
         return 0;
     // its arrays fit in the record area the split path would use
     if (segmented_scratch_bytes(a, (int)P) > a.layout.records_bytes()) return 0;

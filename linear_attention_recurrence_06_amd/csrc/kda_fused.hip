@@ -54,10 +54,11 @@
 // Segmented prefill (launch_segmented).  For few long chains the sequences are
 // cut into segments whose (segment, head) chains fill the device.  The
 // recurrence is affine in the state, so over a segment S_end = M S_start + b:
-// variants of fused_ws_kernel form b (from the zero state) and M (from the
-// identity, v taken as zero) without writing outputs, segment_scan_kernel
-// composes them in order into every segment's start state, and
-// fused_ws_kernel runs the segments again from those states for the outputs.
+// one variant of fused_ws_kernel forms b (from the zero state) and M (from the
+// identity, v taken as zero) together, each recurrence wave carrying four
+// state tiles and no outputs, segment_scan_kernel composes the maps in order
+// into every segment's start state, and fused_ws_kernel runs the segments
+// again from those states for the outputs.
 #include <algorithm>
 #include <atomic>
 
@@ -120,6 +121,7 @@ struct FusedParams {
     // (the last shorter)
     int64_t seg_len = 0;
     int32_t seg_per_seq = 1;
+    float* fin2 = nullptr;  // MAPS kernels: the linear parts M (fin takes b)
 };
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -795,49 +797,71 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
     }
 }
 
-// One 16-token block of the recurrence on a recurrence wave's two 16-column
-// tiles (value columns 32 wr + 16 c + lane % 16): operands from `rec`, V from
-// `vt`, whose rows of the block then take the block's outputs.  OUT false:
-// no outputs; ZERO_V: V is zero (the state map's linear part), vt unread.
-template <int D, int TPV, bool OUT = true, bool ZERO_V = false>
+// One 16-token block of the recurrence on NT 16-column tiles of a recurrence
+// wave (tile c: value column 32 wr + 16 (c % 2) + lane % 16 of its state):
+// operands from `rec`; tiles c < NV take V from `vt`, the others V = 0 (the
+// linear part of a state map).  OUT: the outputs of tiles 0 and 1 replace the
+// block's V rows in `vt`.  Every record operand read serves all NT tiles.
+template <int D, int TPV, bool OUT, int NT, int NV>
 __device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64][D + TPV],
-                                         f32x4 (&S)[2][D / 16], int wr, int lane, int Rb) {
+                                         f32x4 (&S)[NT][D / 16], int wr, int lane, int Rb) {
+    static_assert(!OUT || (NT == 2 && NV == 2), "outputs only for two V tiles");
     constexpr int NKS = D / 32, NCT = D / 16;
     const int n16 = lane & 15, g = lane >> 4;
-    bf16x8 Sb[2][NKS];
+    // X = Ke S (and O = Qe S): the state as B operands (tile c, rows 32 ks ..
+    // 32 ks + 31), two tiles converted up front, four step by step (fewer
+    // registers live)
+    f32x4 X[NT], O[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NT; ++c) X[c] = O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NT == 2) {
+        bf16x8 Sb[NT][NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int c = 0; c < NT; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Sb[c][ks][e] = (bf16)S[c][2 * ks][e];
-                Sb[c][ks][4 + e] = (bf16)S[c][2 * ks + 1][e];
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Sb[c][ks][e] = (bf16)S[c][2 * ks][e];
+                    Sb[c][ks][4 + e] = (bf16)S[c][2 * ks + 1][e];
+                }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 a = rec.ke[Rb][ks][lane];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) X[c] = mfma32(a, Sb[c][ks], X[c]);
+            if constexpr (OUT) {
+                const bf16x8 b = rec.qe[Rb][ks][lane];
+#pragma unroll
+                for (int c = 0; c < NT; ++c) O[c] = mfma32(b, Sb[c][ks], O[c]);
             }
-    f32x4 X[2], O[2];
+        }
+    } else {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) X[c] = O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < NKS; ++ks) {
+            bf16x8 Sb[NT];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = rec.ke[Rb][ks][lane];
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) X[c] = mfma32(a, Sb[c][ks], X[c]);
-        if constexpr (OUT) {
-            const bf16x8 b = rec.qe[Rb][ks][lane];
+                for (int e = 0; e < 4; ++e) {
+                    Sb[c][e] = (bf16)S[c][2 * ks][e];
+                    Sb[c][4 + e] = (bf16)S[c][2 * ks + 1][e];
+                }
+            const bf16x8 a = rec.ke[Rb][ks][lane];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) O[c] = mfma32(b, Sb[c][ks], O[c]);
+            for (int c = 0; c < NT; ++c) X[c] = mfma32(a, Sb[c], X[c]);
         }
     }
     const bf16x4 tb = rec.tb[Rb][lane];
     const bf16x4 m = OUT ? rec.m[Rb][lane] : bf16x4{};
-    bf16x4 u[2];
+    bf16x4 u[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int col = 32 * wr + 16 * c + n16;
+    for (int c = 0; c < NT; ++c) {
+        const int col = 32 * wr + 16 * (c % 2) + n16;
         bf16x4 Y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            Y[e] = (bf16)((ZERO_V ? 0.f : to_f32(vt[16 * Rb + 4 * g + e][col])) - X[c][e]);
+            Y[e] = (bf16)((c < NV ? to_f32(vt[16 * Rb + 4 * g + e][col]) : 0.f) - X[c][e]);
         u[c] = to_bf16x4(mfma16(tb, Y, f32x4{0.f, 0.f, 0.f, 0.f}));
         if constexpr (OUT) {
             O[c] = mfma16(m, u[c], O[c]);
@@ -850,7 +874,7 @@ __device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64]
         const bf16x4 a = rec.kt[Rb][rt][lane];
         const f32x4 gd = rec.gend[Rb][state_channel(rt, g, 0) / 4];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) S[c][rt] = mfma16(a, u[c], S[c][rt] * gd);
+        for (int c = 0; c < NT; ++c) S[c][rt] = mfma16(a, u[c], S[c][rt] * gd);
     }
 }
 
@@ -887,10 +911,15 @@ __device__ __forceinline__ void ws_flush(const FusedParams& p, const bf16 (&vt)[
 // (p.seg_per_seq segments per sequence, placed from p.seg_len or p.cu); OUT
 // false, no outputs (p.out unused, no q read); ZERO_V, V taken as zero and
 // every chain started from the identity (p.v and p.init unused: the linear
-// part of each segment's state map).
-template <int D, bool OUT = true, bool ZERO_V = false, bool SEG = false>
+// part of each segment's state map); MAPS (with SEG, without OUT), both parts
+// at once: each recurrence wave carries two tiles of b, from the zero state
+// with V, and two of M, from the identity with V = 0, to p.fin and p.fin2.
+template <int D, bool OUT = true, bool ZERO_V = false, bool SEG = false, bool MAPS = false>
 __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
+    static_assert(!MAPS || (SEG && !OUT && !ZERO_V), "the maps of a segmented call");
     constexpr int NCT = D / 16, TPV = WsSmem<D>::TPV;
+    constexpr int NT = MAPS ? 4 : 2;            // 16-column state tiles per recurrence wave
+    constexpr int NV = ZERO_V ? 0 : 2;          // of which the first NV see V
     __shared__ WsSmem<D> sm;
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -953,22 +982,22 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
             const int wr = w - kWsPrep<D>;
             const int n16 = lane & 15, g = lane >> 4;
             // this lane's state: key channels state_channel(rt, g, e), value
-            // column 32 wr + 16 c + n16 of tile c
+            // column 32 wr + 16 (c % 2) + n16 of tile c
             const int64_t sbase = (n * H + h) * D * D;
-            f32x4 S[2][NCT];
+            f32x4 S[NT][NCT];
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
                 for (int rt = 0; rt < NCT; ++rt) S[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (ZERO_V) {
+            // tiles from the identity: all of them (ZERO_V), or the M tiles (MAPS)
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+            for (int c = NV; c < NT; ++c)
 #pragma unroll
-                    for (int rt = 0; rt < NCT; ++rt)
+                for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[c][rt][e] = state_channel(rt, g, e) == 32 * wr + 16 * c + n16 ? 1.f : 0.f;
-            } else if (p.init) {
+                    for (int e = 0; e < 4; ++e)
+                        S[c][rt][e] = state_channel(rt, g, e) == 32 * wr + 16 * (c % 2) + n16 ? 1.f : 0.f;
+            if (!ZERO_V && !MAPS && p.init) {
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -980,7 +1009,7 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
             }
             // the state's loads complete here, once per chain
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < NT; ++c)
 #pragma unroll
                 for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[c][rt]));
             if (nch > 0) {
@@ -1002,7 +1031,7 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
                     const SubRecord<D>& rec = sm.rec[(kc - 1) & 1];
 #pragma unroll
                     for (int Rb = 0; Rb < 4; ++Rb)
-                        ws_block<D, TPV, OUT, ZERO_V>(rec, sm.vt, S, wr, lane_c, Rb);
+                        ws_block<D, TPV, OUT, NT, NV>(rec, sm.vt, S, wr, lane_c, Rb);
                     if constexpr (OUT)
                         ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
                     if (!ZERO_V && kc < nch) {
@@ -1017,13 +1046,15 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
             }
             if (p.fin) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < NT; ++c) {
+                    float* f = c < 2 ? p.fin : p.fin2;
 #pragma unroll
                     for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            p.fin[sbase + (int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * c + n16] =
+                            f[sbase + (int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * (c % 2) + n16] =
                                 S[c][rt][e];
+                }
             }
         }
     }
@@ -1087,9 +1118,16 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
 // zero state.  One workgroup per (16-column tile, head, sequence) walks the
 // segments in order, S <- M_p S + b_p from the initial state (zero when
 // `init` is null), storing the state before each segment to `start` and the
-// one after the last to `fin` (when not null).  fp32; each element a
-// sequential sum over k, so the result does not depend on the launch.
-// Maps and starts are [sequence * P + segment][H][D][D].
+// one after the last to `fin` (when not null).  Maps and starts are
+// [sequence * P + segment][H][D][D], fp32.
+//
+// Each step is a 128 x 128 by 128 x 16 product on fp32 MFMA (16x16x4): wave w
+// takes rows 32 w .. 32 w + 31 (two row tiles); lane (r, kg) = (lane % 16,
+// lane / 16) feeds, at product step s, A = M[row r][32 kg + s] and B =
+// S[32 kg + s][column r], so the 32 steps cover every k.  The tile's state
+// sits transposed in LDS (St[column][k]) for the B operands; the A operands
+// of the next segment's M are loaded while the current one is multiplied.
+// The summation order is fixed, so the result does not depend on the launch.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ init,
                                                            const float* __restrict__ Mm,
@@ -1097,44 +1135,78 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
                                                            float* __restrict__ start,
                                                            float* __restrict__ fin, int32_t H,
                                                            int32_t P) {
-    static_assert(D == 128, "256 threads: 128 rows x two 8-column halves of a 16-column tile");
-    __shared__ float St[D][16];
-    const int t = threadIdx.x, row = t >> 1, c0 = (t & 1) * 8;
+    static_assert(D == 128, "four waves of two 16-row tiles");
+    constexpr int SP = D + 4;  // row pitch of the transposed tile (floats)
+    __shared__ __align__(16) float St[16][SP];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, r = lane & 15, kg = lane >> 4;
     const int64_t h = blockIdx.y, n = blockIdx.z;
-    const int64_t col = 16 * (int64_t)blockIdx.x + c0;
-    {
-        const int64_t o = ((n * H + h) * D + row) * D + col;
+    const int col0 = 16 * blockIdx.x;
+    // this lane's output elements: rows 32 w + 16 j + 4 kg + v, column col0 + r
+    const auto out_off = [&](int j, int v) { return (int64_t)(32 * w + 16 * j + 4 * kg + v) * D + col0 + r; };
+    const int64_t sbase = (n * H + h) * D * D;
+    f32x4 acc[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) St[row][c0 + j] = init ? init[o + j] : 0.f;
-    }
-    __syncthreads();
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[j][v] = init ? init[sbase + out_off(j, v)] : 0.f;
+    // A operands of segment p: M_p[32 w + 16 j + r][32 kg .. 32 kg + 31]
+    float4 Ma[2][8];
+    const auto load_m = [&](int p, float4 (&m)[2][8]) {
+        const float* base = Mm + ((n * P + p) * H + h) * D * D;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float4* row = reinterpret_cast<const float4*>(base + (int64_t)(32 * w + 16 * j + r) * D + 32 * kg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m[j][i] = row[i];
+        }
+    };
+    if (P > 0) load_m(0, Ma);
     for (int p = 0; p < P; ++p) {
-        const int64_t base = ((n * P + p) * H + h) * D * D;
-        const int64_t o = base + (int64_t)row * D + col;
-        float acc[8];
+        const int64_t mb = ((n * P + p) * H + h) * D * D;
+        // the state before segment p: to `start`, and transposed into LDS
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            start[o + j] = St[row][c0 + j];
-            acc[j] = bm[o + j];
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) start[mb + out_off(j, v)] = acc[j][v];
+            *reinterpret_cast<f32x4*>(&St[r][32 * w + 16 * j + 4 * kg]) = acc[j];
         }
-        const float4* mrow = reinterpret_cast<const float4*>(Mm + base + (int64_t)row * D);
-        for (int k4 = 0; k4 < D / 4; ++k4) {
-            const float4 m = mrow[k4];
-            const float mk[4] = {m.x, m.y, m.z, m.w};
+        f32x4 bv[2];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = fmaf(mk[kk], St[4 * k4 + kk][c0 + j], acc[j]);
-        }
-        __syncthreads();  // every thread has read the tile
-#pragma unroll
-        for (int j = 0; j < 8; ++j) St[row][c0 + j] = acc[j];
+            for (int v = 0; v < 4; ++v) bv[j][v] = bm[mb + out_off(j, v)];
+        float4 Mn[2][8];
+        if (p + 1 < P) load_m(p + 1, Mn);
         __syncthreads();
+        // B operands: S[32 kg .. 32 kg + 31][column r]
+        float4 Sb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Sb[i] = *reinterpret_cast<const float4*>(&St[r][32 * kg + 4 * i]);
+        __syncthreads();  // every wave has its B operands; St is free for the next step
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 c = bv[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].x, Sb[i].x, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].y, Sb[i].y, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].z, Sb[i].z, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].w, Sb[i].w, c, 0, 0, 0);
+            }
+            acc[j] = c;
+        }
+        if (p + 1 < P) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) Ma[j][i] = Mn[j][i];
+        }
     }
     if (fin) {
-        const int64_t o = ((n * H + h) * D + row) * D + col;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fin[o + j] = St[row][c0 + j];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) fin[sbase + out_off(j, v)] = acc[j][v];
     }
 }
 
@@ -1248,18 +1320,16 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
                            fp.counter);
         return hipGetLastError();
     };
-    // the maps' affine parts: every segment from the zero state, no outputs
+    // every segment's map in one pass, no outputs: the affine parts b from
+    // the zero state, the linear parts M from the identity with V = 0
     fp.init = nullptr;
     fp.fin = bm;
+    fp.fin2 = Mm;
     fp.out = nullptr;
     if ((e = reset()) != hipSuccess) return e;
-    hipLaunchKernelGGL((fused_ws_kernel<D, false, false, true>), dim3(grid), block, 0, stream, fp);
+    hipLaunchKernelGGL((fused_ws_kernel<D, false, false, true, true>), dim3(grid), block, 0, stream, fp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // their linear parts: from the identity with V = 0
-    fp.fin = Mm;
-    if ((e = reset()) != hipSuccess) return e;
-    hipLaunchKernelGGL((fused_ws_kernel<D, false, true, true>), dim3(grid), block, 0, stream, fp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    fp.fin2 = nullptr;
     // every segment's start state, and the final states
     hipLaunchKernelGGL((segment_scan_kernel<D>), dim3(D / 16, (unsigned)H, (unsigned)N), dim3(256), 0,
                        stream, a.initial_state, Mm, bm, st, a.final_state, (int32_t)H, (int32_t)Pe);

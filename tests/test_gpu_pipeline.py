@@ -11,8 +11,10 @@ is empty: with more than one sequence the library never pipelines.
 Also checked: the call's results are ordered on the caller's stream (a side
 stream, synchronised alone), the state handed between segments goes through
 the workspace when no final state is asked for, and final_state may alias
-initial_state.  Parity with the oracle through this path is covered by the
-million-token workload in test_gpu_parity.py (16 heads, 16 segments).
+initial_state.  Its parity with the oracle follows from that bitwise equality
+and the single-launch path's parity tests.  The bf16 d = 128 sequences here
+would otherwise take the segmented path, so each test sets
+KDA_PREFILL_PATH=split.
 """
 
 import sys
@@ -32,6 +34,15 @@ T_PIPE = 4 * 1024 * 64 + 37
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def two_kernel_path(monkeypatch):
+    """The bf16 d = 128 sequences below would otherwise be segmented: these
+    tests are about the two-kernel path (set per test; the rule test below
+    clears it)."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+    monkeypatch.delenv("KDA_PREFILL_SEGMENTS", raising=False)
 
 
 @pytest.fixture(scope="module")
@@ -112,12 +123,14 @@ def test_pipelined_all_options(lib):
     assert torch.equal(cs_p, cs_r[:1])
 
 
-def test_pipeline_segment_rule(lib):
+def test_pipeline_segment_rule(lib, monkeypatch):
     """Segments as documented: min(16, chunks / 1024) when that is at least 4,
     for one sequence whose H * d / 16 recurrence workgroups leave CUs idle and
-    that neither the fused nor the segmented path takes."""
+    that neither the fused nor the segmented path takes (fp32 I/O below, which
+    neither takes)."""
+    monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
     K = lib.kda
-    seg = lambda T, N, H, d=128, io=K.KDA_BF16: lib.kda_prefill_pipeline_segments(
+    seg = lambda T, N, H, d=128, io=K.KDA_FP32: lib.kda_prefill_pipeline_segments(
         lib.make_dims(T, N, H, d, d, io))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert seg(4095 * 64, 1, 2) == 0                  # 4,095 chunks
@@ -126,9 +139,9 @@ def test_pipeline_segment_rule(lib):
     # the million-token workload: segmented instead (bf16, on 256 CUs), so
     # not pipelined; with fp32 I/O it is
     if cus == 256:
-        assert seg(1 << 20, 1, 16) == 0
-    assert seg(1 << 20, 1, 16, io=K.KDA_FP32) == (16 if 16 * 8 < cus else 0)
-    assert seg(1 << 22, 1, 2, io=K.KDA_FP32) == 16    # at most 16 segments
+        assert seg(1 << 20, 1, 16, io=K.KDA_BF16) == 0
+    assert seg(1 << 20, 1, 16) == (16 if 16 * 8 < cus else 0)
+    assert seg(1 << 22, 1, 2) == 16                   # at most 16 segments
     assert seg(8192, 1, 32) == 0                      # the 8,192-token workload: too short
     assert seg(1 << 20, 1, cus // 8) == 0             # the recurrence fills every CU
     assert seg(1 << 20, 2, 2) == 0                    # more than one sequence

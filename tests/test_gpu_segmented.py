@@ -9,11 +9,12 @@ again from those states for the outputs.
   ending in a partial chunk), packed sequences with empty segments and an
   empty sequence, equal lengths without cu_seqlens, decay strong
   enough for the exact diagonal products, channels of all three decay
-  regimes, no initial and no final state.
+  regimes, no initial and no final state, 64 segments (the most).
 * Agreement with the two-kernel path within twice that bar where the oracle
   would be slow: the automatic choice on a 262,144-token sequence with 8 heads.
-* Bitwise: two runs of the same call, the library-allocated workspace, and
-  graph replays of the segmented and the fused path.
+* Bitwise: two runs of the same call, the library-allocated workspace, the
+  final state written over the initial state on a side stream, and graph
+  replays of the segmented and the fused path.
 
 KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS the
 segment count.
@@ -171,9 +172,37 @@ def test_no_initial_no_final_state(lib, oracle, monkeypatch):
     oracle_check(oracle, inp, out, None, "no states")
 
 
+def test_sixty_four_segments(lib, oracle, monkeypatch):
+    """32,768 tokens x 2 heads in 64 segments of 8 chunks: the scan composes
+    the most maps a call can have."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([32768], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=611,
+                       device="cuda")
+    out, fin = near_split(lib, monkeypatch, inp, "64 segments", segments=64)
+    oracle_check(oracle, inp, out, fin, "64 segments")
+
+
+def test_in_place_on_a_side_stream(lib, monkeypatch):
+    """final_state aliasing initial_state, called on a side stream that alone
+    is synchronised: the same results as the call with separate states."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([16421], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=612,
+                       device="cuda")
+    o_ref, f_ref = run(lib, monkeypatch, inp, "segmented", 4)
+    st = inp["initial_state"].clone()
+    out = torch.empty_like(o_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.kda_chunk_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], st, None,
+                              out, st, stream=side)
+    side.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(st, f_ref)
+
+
 def test_auto_choice_long_sequence(lib, monkeypatch):
     """262,144 tokens x 8 heads: 8 chains, so on a 256-CU device the automatic
-    choice cuts the sequence into 16 segments of 256 chunks (128 chains);
+    choice cuts the sequence into 32 segments of 128 chunks (256 chains);
     checked against the two-kernel path, bitwise against the forced path with
     the same count, and bitwise from run to run."""
     from kda_inputs import make_prefill
@@ -185,15 +214,17 @@ def test_auto_choice_long_sequence(lib, monkeypatch):
     say(f"[auto 262,144 x 8] vs split: out {eo:.3e} state {ef:.3e}")
     assert torch.isfinite(o_a.float()).all() and torch.isfinite(f_a).all()
     assert eo <= 2 * TOL and ef <= 2 * TOL
-    o_g, f_g = run(lib, monkeypatch, inp, "segmented", 16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    o_g, f_g = run(lib, monkeypatch, inp, "segmented", min(64, cus // 8))
     assert torch.equal(o_g, o_a) and torch.equal(f_g, f_a)
-    o_2, f_2 = run(lib, monkeypatch, inp, "segmented", 16)
+    o_2, f_2 = run(lib, monkeypatch, inp, "segmented", min(64, cus // 8))
     assert torch.equal(o_2, o_g) and torch.equal(f_2, f_g)
 
 
 def test_path_choice(lib, monkeypatch):
-    """The rule on a 256-CU device: few chains over long sequences, enough
-    segments of at least 256 chunks to give every two CUs a chain."""
+    """The rule on a 256-CU device, where the fused kernel does not apply: P =
+    one segment chain per CU (at most 64), segments of at least 32 chunks;
+    taken with P >= 4 whose chains fill 3/4 of the CUs, or with P >= 16."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the thresholds below are for 256 compute units")
     monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
@@ -203,10 +234,16 @@ def test_path_choice(lib, monkeypatch):
         lib.make_dims(T, N, H, d, d, io), packed)
     assert path(1 << 20, 1, 16) == (K.KDA_PATH_SEGMENTED, 16)      # the million-token workload
     assert path(1 << 19, 1, 8) == (K.KDA_PATH_SEGMENTED, 32)
-    assert path(1 << 18, 1, 8) == (K.KDA_PATH_SEGMENTED, 16)       # 128 chains
-    assert path(1 << 18, 1, 4)[0] == K.KDA_PATH_PIPELINED           # 64 chains: too few
-    assert path(1 << 20, 1, 32)[0] == K.KDA_PATH_SPLIT              # 32 chains: too many
-    assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # 64 segments of 256 chunks
+    assert path(1 << 18, 1, 8) == (K.KDA_PATH_SEGMENTED, 32)       # 32 segments of 128 chunks
+    assert path(1 << 18, 1, 4) == (K.KDA_PATH_SEGMENTED, 64)       # 64 of 64 chunks
+    assert path(1 << 20, 1, 32) == (K.KDA_PATH_SEGMENTED, 8)
+    assert path(1 << 20, 1, 64) == (K.KDA_PATH_SEGMENTED, 4)
+    assert path(1 << 16, 1, 48) == (K.KDA_PATH_SEGMENTED, 5)       # 240 chains
+    assert path(1 << 20, 1, 96)[0] == K.KDA_PATH_SPLIT              # P = 2: too few
+    assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # at most 64 segments
+    assert path(1 << 16, 1, 1) == (K.KDA_PATH_SEGMENTED, 32)       # 32 of 32 chunks
+    assert path(1 << 14, 1, 16)[0] == K.KDA_PATH_SPLIT              # P = 8: 128 chains, too few
+    assert path(8192, 1, 4)[0] == K.KDA_PATH_SPLIT                  # P = 4: too few
     assert path(1 << 20, 1, 16, packed=True) == (K.KDA_PATH_SEGMENTED, 16)  # cu = [0, T]
     assert path(1 << 20, 2, 8)[0] == K.KDA_PATH_SEGMENTED           # equal lengths, no cu
     assert path(1 << 20, 2, 8, packed=True)[0] == K.KDA_PATH_SEGMENTED  # cut on the device
