@@ -156,10 +156,10 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * device share the second stream; each call's own events keep its launches
  * ordered.
  *
- * Kernels.  A call with many (sequence, head) chains -- at least half the
- * device's compute units -- with bf16 I/O, a per-channel gate, out aligned to
- * 16 bytes and no options of kda_chunk_prefill_ex or checkpoints runs one
- * fused kernel: persistent workgroups take whole chains, longest sequences
+ * Kernels.  A call with many (sequence, head) chains -- at least a third of
+ * the device's compute units at d = 128, half at d = 64 -- with bf16 I/O, a
+ * per-channel gate, out aligned to 16 bytes and no options of
+ * kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent workgroups take whole chains, longest sequences
  * first, and step through each 64-token chunk as four 16-token sub-chunks with
  * the chunk's operands in LDS, so only the inputs, the outputs and the states
  * touch HBM; it uses only the first two index areas of the workspace.  A
@@ -167,7 +167,7 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * is segmented where that pays: each sequence is cut into P segments of whole
  * chunks, P being one (segment, head) chain per compute unit, at most 64, with
  * segments of at least 32 chunks for sequences of the average length (a short
- * sequence may leave segments empty); the path is taken with P of at least 4
+ * sequence may leave segments empty); the path is taken with P of at least 3
  * whose chains fill three quarters of the compute units, or with P of 16 or
  * more.  One pass of the fused kernel forms each segment's state map S_end =
  * M S_start + b (b from the zero state, M from the identity with v taken as

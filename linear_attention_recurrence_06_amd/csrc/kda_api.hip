@@ -133,7 +133,8 @@ bool fused_path(const PrefillArgs& a) {
     if (env && std::strcmp(env, "split") == 0) return false;
     if (env && std::strcmp(env, "fused") == 0) return true;
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
-    return a.compute_units > 0 && chains * kFusedCUsPerChain >= (int64_t)a.compute_units;
+    const int64_t per = a.d == 128 ? kFusedCUsPerChain : kFusedCUsPerChain64;
+    return a.compute_units > 0 && chains * per >= (int64_t)a.compute_units;
 }
 
 int segmented_segments(const PrefillArgs& a) {

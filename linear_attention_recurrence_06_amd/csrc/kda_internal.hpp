@@ -140,10 +140,13 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // A prefill takes the fused kernel (persistent workgroups working through
 // whole (sequence, head) chains) instead of the preparation and recurrence
-// kernels once it has at least one chain per kFusedCUsPerChain compute units.
-// Measured at d = 128, 8,192-token sequences: 64 chains 1.15x the two-kernel
-// time, 128 chains 0.73x, 256 chains 0.42x (256 CUs).
-constexpr int64_t kFusedCUsPerChain = 2;
+// kernels once it has at least one chain per kFusedCUsPerChain compute units
+// (d = 128; per two at d = 64).  Measured at d = 128 against the two-kernel
+// time (256 CUs): 8,192-token sequences, 64 chains 1.15x, 86 chains 0.86x,
+// 128 chains 0.73x, 256 chains 0.42x; 65,536-token sequences, 80 chains 0.95x,
+// 96 chains 0.86x, 112 chains 0.68x.  At d = 64, 128 chains 0.94x.
+constexpr int64_t kFusedCUsPerChain = 3;
+constexpr int64_t kFusedCUsPerChain64 = 2;
 
 // Whether launch_prefill takes the fused kernel for these arguments.  The
 // environment variable KDA_PREFILL_PATH=split or =fused overrides the choice
@@ -168,11 +171,12 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream);
 // chains fill three quarters of the device, or with kSegManySegments or more.
 // Measured at d = 128 on 256 CUs, time against the two-kernel path:
 // 2^20 tokens x 16 heads 0.61x, x 32 heads 0.82x; 2^16 x 64 heads 0.80x;
-// 2^16 x 8 heads (32 segments of 32 chunks) 0.65x; 8,192 tokens x 32 heads
-// with 4 segments 1.6x (not taken).
+// 2^16 x 8 heads (32 segments of 32 chunks) 0.65x; 2^16 x 80 heads (3
+// segments) 0.78x; 8,192 tokens x 80 heads (3 segments) 0.80x; 8,192 tokens x
+// 32 heads with 4 segments 1.6x (not taken).
 constexpr int64_t kSegMinChunks = 32;
 constexpr int kSegMaxSegments = 64;
-constexpr int64_t kSegMinSegments = 4;
+constexpr int64_t kSegMinSegments = 3;
 constexpr int64_t kSegManySegments = 16;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -222,9 +222,10 @@ def test_auto_choice_long_sequence(lib, monkeypatch):
 
 
 def test_path_choice(lib, monkeypatch):
-    """The rule on a 256-CU device, where the fused kernel does not apply: P =
-    one segment chain per CU (at most 64), segments of at least 32 chunks;
-    taken with P >= 4 whose chains fill 3/4 of the CUs, or with P >= 16."""
+    """The rule on a 256-CU device, where the fused kernel does not apply (it
+    takes a chain per 3 CUs at d = 128): P = one segment chain per CU (at most
+    64), segments of at least 32 chunks; taken with P >= 3 whose chains fill
+    3/4 of the CUs, or with P >= 16."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the thresholds below are for 256 compute units")
     monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
@@ -239,7 +240,11 @@ def test_path_choice(lib, monkeypatch):
     assert path(1 << 20, 1, 32) == (K.KDA_PATH_SEGMENTED, 8)
     assert path(1 << 20, 1, 64) == (K.KDA_PATH_SEGMENTED, 4)
     assert path(1 << 16, 1, 48) == (K.KDA_PATH_SEGMENTED, 5)       # 240 chains
-    assert path(1 << 20, 1, 96)[0] == K.KDA_PATH_SPLIT              # P = 2: too few
+    assert path(1 << 16, 1, 80) == (K.KDA_PATH_SEGMENTED, 3)       # 240 chains
+    assert path(8192, 1, 80) == (K.KDA_PATH_SEGMENTED, 3)          # 3 of 42 chunks
+    assert path(4 * 4096, 4, 20)[0] == K.KDA_PATH_SPLIT             # P = 2: too few
+    assert path(1 << 16, 1, 86)[0] == K.KDA_PATH_FUSED              # a chain per 3 CUs
+    assert path(1 << 16, 1, 86, d=64)[0] == K.KDA_PATH_SPLIT        # d = 64: per 2 CUs
     assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # at most 64 segments
     assert path(1 << 16, 1, 1) == (K.KDA_PATH_SEGMENTED, 32)       # 32 of 32 chunks
     assert path(1 << 14, 1, 16)[0] == K.KDA_PATH_SPLIT              # P = 8: 128 chains, too few
