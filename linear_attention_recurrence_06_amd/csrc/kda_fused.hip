@@ -77,6 +77,10 @@ __device__ __forceinline__ int state_channel(int rt, int g, int e) {
     return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + e;
 }
 
+// The value of lane 15 of this lane's 16-lane row (DPP row_newbcast:15).
+__device__ __forceinline__ float row_last(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));
+}
 // Operands of one 64-token chunk (four 16-token blocks), in MFMA lane order.
 template <int D>
 struct SubRecord {
@@ -354,8 +358,9 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
             const float kh = to_f32(kv[kk][i]) * rks;
             const float qh = to_f32(qv[kk][i]) * rqs;
             const float E = exp2_hw(gam[kk][i]);
-            // (clamped: then unused, but finite, when the block is past the range)
-            const float G = exp2_hw(fminf(-gam[kk][i], kSubFactoredMax));
+            // (past the factored range G may overflow; the products that use it
+            // are then skipped and K' is redone below)
+            const float G = exp2_hw(-gam[kk][i]);
             T[i] = __shfl(E, lane | 15, kWave);  // 2^tau, from the block's last token
             ke[i] = kh * E;
             qe[i] = qh * E;
@@ -690,20 +695,20 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int ks = 2 * hf + kk;
-            float ke[8], qe[8], kf[8], kfs[8], T[8];
+            float ke[8], qe[8], kf[8], kfs[8], E[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float kh = to_f32(rows.k[ks][i]) * rks;
                 const float qh = QROWS ? to_f32(rows.q[ks][i]) * rqs : 0.f;
-                const float E = exp2_hw(gam[hf][kk][i]);
-                // (clamped: then unused, but finite, when the block is past the range)
-                const float G = exp2_hw(fminf(-gam[hf][kk][i], kSubFactoredMax));
-                T[i] = __shfl(E, lane | 15, kWave);  // 2^tau, from the block's last token
-                ke[i] = kh * E;
-                qe[i] = qh * E;
+                E[i] = exp2_hw(gam[hf][kk][i]);
+                // (past the factored range G may overflow; the products that use
+                // it are then skipped and K' is redone below)
+                const float G = exp2_hw(-gam[hf][kk][i]);
+                ke[i] = kh * E[i];
+                qe[i] = qh * E[i];
                 kfs[i] = kh * G;
-                // K' = khat 2^(tau - Gamma); past the factored range it is redone below
-                kf[i] = kfs[i] * T[i];
+                // K' = khat 2^(tau - Gamma), 2^tau from the block's last token
+                kf[i] = kfs[i] * __shfl(E[i], lane | 15, kWave);
             }
             const bf16x8 KE = to_bf16x8(ke), QE = to_bf16x8(qe), KF = to_bf16x8(kf);
             rec.ke[R][ks][lane] = KE;
@@ -717,9 +722,9 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             rec.kt[R][2 * ks][lane] = to_bf16x4(mfma32(KF, sel_lo, z));
             rec.kt[R][2 * ks + 1][lane] = to_bf16x4(mfma32(KF, sel_hi, z));
-            if (n16 == 0) {
-                rec.gend[R][8 * ks + 2 * g] = f32x4{T[0], T[1], T[2], T[3]};
-                rec.gend[R][8 * ks + 2 * g + 1] = f32x4{T[4], T[5], T[6], T[7]};
+            if (n16 == 15) {  // the block's last token: E = 2^tau
+                rec.gend[R][8 * ks + 2 * g] = f32x4{E[0], E[1], E[2], E[3]};
+                rec.gend[R][8 * ks + 2 * g + 1] = f32x4{E[4], E[5], E[6], E[7]};
             }
         }
     }
@@ -733,7 +738,7 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
                 for (int i = 0; i < 8; ++i) {
                     kh[kk][i] = to_f32(rows.k[2 * hf + kk][i]) * rks;
                     qh[kk][i] = QROWS ? to_f32(rows.q[2 * hf + kk][i]) * rqs : 0.f;
-                    tau[kk][i] = __shfl(gam[hf][kk][i], lane | 15, kWave);
+                    tau[kk][i] = row_last(gam[hf][kk][i]);
                 }
             Aa[hf] = Ata[hf] = Mta[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
             // every pair (i, j) belongs to exactly one level: select, not add
