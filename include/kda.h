@@ -159,22 +159,23 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * Kernels.  A call with many (sequence, head) chains -- at least a third of
  * the device's compute units at d = 128, half at d = 64 -- with bf16 I/O, a
  * per-channel gate, out aligned to 16 bytes and no options of
- * kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent workgroups take whole chains, longest sequences
- * first, and step through each 64-token chunk as four 16-token sub-chunks with
- * the chunk's operands in LDS, so only the inputs, the outputs and the states
- * touch HBM; it uses only the first two index areas of the workspace.  A
- * call with fewer chains, d = 128 and otherwise the fused kernel's conditions
- * is segmented where that pays: each sequence is cut into P segments of whole
- * chunks, P being one (segment, head) chain per compute unit, at most 64, with
- * segments of at least 32 chunks for sequences of the average length (a short
- * sequence may leave segments empty); the path is taken with P of at least 3
- * whose chains fill three quarters of the compute units, or with P of 16 or
- * more.  One pass of the fused kernel forms each segment's state map S_end =
- * M S_start + b (b from the zero state, M from the identity with v taken as
- * zero, no outputs), a scan kernel composes the maps in order into every
- * segment's start state and the final state, and the fused kernel runs the
- * segments again from those states for the outputs (three [N P, H, d, d] fp32
- * arrays in the workspace's record area).  Every other call runs the preparation and
+ * kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent
+ * workgroups take whole chains, longest sequences first, and step through
+ * each 64-token chunk as four 16-token sub-chunks with the chunk's operands in
+ * LDS, so only the inputs, the outputs and the states touch HBM; it uses only
+ * the first two index areas of the workspace.  A call with fewer chains, d =
+ * 128 and otherwise the fused kernel's conditions is segmented where that
+ * pays: each sequence is cut into P segments of whole chunks, P being one
+ * (segment, head) chain per compute unit, at most 64, with segments of at
+ * least 32 chunks for sequences of the average length (a short sequence may
+ * leave segments empty); the path is taken with P of at least 3 whose chains
+ * fill three quarters of the compute units, or with P of 16 or more.  One
+ * pass of the fused kernel forms each segment's state map S_end = M S_start +
+ * b (b from the zero state, M from the identity with v taken as zero, no
+ * outputs), a scan kernel composes the maps in order into every segment's
+ * start state and the final state, and the fused kernel runs the segments
+ * again from those states for the outputs (three [N P, H, d, d] fp32 arrays in
+ * the workspace's record area).  Every other call runs the preparation and
  * recurrence kernels, which hand per-chunk records through the workspace.  The
  * paths compute the same recurrence with the same operand precision but round
  * in a different order, so their results agree to the accuracy below, not bit
