@@ -383,8 +383,12 @@ kda_status kda_decode_step(const kda_dims* dims, const void* q, const void* k,
  * looked up once per device on the first call there.  The call never uses the
  * second stream of the pipelined prefill (no library stream or event) and
  * calls no allocating routine.
- * Errors: as kda_chunk_prefill, plus KDA_ERR_WORKSPACE when
- * kda_prefill_workspace_bytes(dims) exceeds KDA_NOALLOC_SCRATCH_BYTES.
+ * Errors: as kda_chunk_prefill, plus KDA_ERR_WORKSPACE when the path the
+ * call takes (kda_prefill_path) needs more than KDA_NOALLOC_SCRATCH_BYTES:
+ * the fused path only its index areas (4 (N + 1) bytes twice and 8 bytes
+ * per 64-token chunk of every sequence, each area rounded up to 256 bytes),
+ * the segmented path those and its 3 N P H d^2 fp32 state maps, any other
+ * path kda_prefill_workspace_bytes(dims).
  * Every call on one device shares that device's array: calls that may run at
  * the same time on one device (different streams without ordering between
  * them) race and corrupt each other's results; order them on one stream.  The

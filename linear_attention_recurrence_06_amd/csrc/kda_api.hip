@@ -408,6 +408,15 @@ hipError_t scratch_address(void** out) {
     return hipSuccess;
 }
 
+// Workspace bytes the path this call takes uses: the index areas (fused
+// kernel), those and the state maps (segmented), or all of ws_need, the
+// two-kernel path's records and pipeline state.
+size_t path_workspace_bytes(const kda::PrefillArgs& a, size_t ws_need) {
+    if (kda::fused_path(a)) return a.layout.records_offset();
+    const int seg = kda::segmented_segments(a);
+    return seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg) : ws_need;
+}
+
 // Shared body of the prefill entry points.
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
@@ -519,11 +528,16 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.out_gate_z = out_gate_z;
     a.fe = fe;
     a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
+    // a call that can only take the two-kernel path (fp32 I/O, or the per-head
+    // gate) is sized without asking the device
+    if (noalloc && (!a.bf16 || a.scalar_g) && ws_need > KDA_NOALLOC_SCRATCH_BYTES)
+        return KDA_ERR_WORKSPACE;
     if (compute_units(&a.compute_units) != hipSuccess) return KDA_ERR_HIP;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (noalloc) {
         // the library's per-device array (its address is found only now, after
         // every argument has been checked); one stream, no library events
+        if (path_workspace_bytes(a, ws_need) > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
         void* ws = nullptr;
         if (scratch_address(&ws) != hipSuccess) return KDA_ERR_HIP;
         a.workspace = static_cast<unsigned char*>(ws);
@@ -544,11 +558,7 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     // (the fused path keeps its records in LDS and needs only the index areas;
     // the segmented path adds its state maps)
     void* ws = nullptr;
-    const int seg = kda::segmented_segments(a);
-    const size_t ws_alloc = kda::fused_path(a) ? a.layout.records_offset()
-                            : seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg)
-                                      : ws_need;
-    if (hipMallocAsync(&ws, ws_alloc, hs) != hipSuccess) return KDA_ERR_HIP;
+    if (hipMallocAsync(&ws, path_workspace_bytes(a, ws_need), hs) != hipSuccess) return KDA_ERR_HIP;
     a.workspace = static_cast<unsigned char*>(ws);
     const hipError_t e = kda::launch_prefill(a, hs);
     const hipError_t f = hipFreeAsync(ws, hs);
@@ -619,9 +629,6 @@ extern "C" kda_status kda_chunk_prefill_noalloc(const kda_dims* d, const void* q
                                                 const float* initial_state,
                                                 const int32_t* cu_seqlens, void* out,
                                                 float* final_state, void* stream) {
-    const kda_status st = check_dims(d, true);
-    if (st != KDA_OK) return st;
-    if (kda_prefill_workspace_bytes(d) > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
     return prefill_impl(d, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                         kNoPrefillOptions, nullptr, 0, stream, /*noalloc=*/true);
 }

@@ -375,15 +375,17 @@ def test_decode_front_end_validation(kda):
 def test_noalloc_validation(kda):
     """The no-allocation prefill rejects sizes past its per-device array and bad
     arguments before touching the device (every call here is rejected: a call
-    that passed validation would launch on these fake addresses)."""
+    that passed validation would launch on these fake addresses).  The size
+    check needs no device where only the two-kernel path applies (fp32 I/O);
+    a bf16 call is sized by the path the device's CU count picks."""
     lib = kda.load_library()
     cap = 320 << 20
     fits = kda.make_dims(8192, 1, 32, 128, 128, kda.KDA_BF16)
     assert kda.kda_prefill_workspace_bytes(fits) <= cap
-    too_big = kda.make_dims(16384, 1, 32, 128, 128, kda.KDA_BF16)
+    too_big = kda.make_dims(16384, 1, 32, 128, 128, kda.KDA_FP32)
     assert kda.kda_prefill_workspace_bytes(too_big) > cap
     T, H, D = 16384, 32, 128
-    big = T * H * D * 2 + 4096
+    big = T * H * D * 4 + 4096
     p = [FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, FAKE + 4 * big, None, None,
          FAKE + 5 * big, None]
     call = lambda dd, a: lib.kda_chunk_prefill_noalloc(ctypes.byref(dd), *a, None)

@@ -40,11 +40,19 @@ def run_pair(lib, inp):
     return o_ref, f_ref, out, fin
 
 
-@pytest.mark.parametrize("io,d", [("bf16", 128), ("fp32", 64)])
-def test_noalloc_equals_prefill_twice(lib, io, d):
+@pytest.mark.parametrize("io,d,lens,heads", [
+    ("bf16", 128, [8192], 32),          # the two-kernel path
+    ("fp32", 64, [8192], 8),
+    ("bf16", 128, [4096] * 16, 32),     # the fused kernel: 512 chains
+    ("bf16", 128, [16384], 32),         # segmented: 8 segments per head
+])
+def test_noalloc_equals_prefill_twice(lib, io, d, lens, heads):
+    """The last two need far less of the array than kda_prefill_workspace_bytes
+    (2.3 GiB and 0.6 GiB, past the array): the fused path uses only the
+    index areas, the segmented path those and its state maps."""
     from kda_inputs import make_prefill
-    big = make_prefill([8192], 32 if d == 128 else 8, d, io, g_scale=0.5, s0_std=0.02,
-                       seed=501, device="cuda", packed_cu=False)
+    big = make_prefill(lens, heads, d, io, g_scale=0.5, s0_std=0.02, seed=501, device="cuda",
+                       packed_cu=len(lens) > 1)
     small = make_prefill([65, 1, 300], 3, d, io, g_scale=0.5, s0_std=0.02, seed=502,
                          device="cuda")
     for label, inp in (("first call", big), ("second, smaller call", small)):
@@ -55,8 +63,12 @@ def test_noalloc_equals_prefill_twice(lib, io, d):
 
 
 def test_noalloc_rejects_past_its_array(lib):
+    """fp32 I/O takes the two-kernel path, whose records for 16,384 tokens x 32
+    heads at d = 128 do not fit the array."""
     from kda_inputs import make_prefill
-    inp = make_prefill([16384], 32, 128, "bf16", seed=503, device="cuda", packed_cu=False)
+    inp = make_prefill([16384], 32, 128, "fp32", seed=503, device="cuda", packed_cu=False)
+    dims = lib.make_dims(16384, 1, 32, 128, 128, lib.kda.KDA_FP32)
+    assert lib.kda_prefill_workspace_bytes(dims) > lib.kda.KDA_NOALLOC_SCRATCH_BYTES
     out = torch.empty_like(inp["v"])
     with pytest.raises(lib.KDAError) as e:
         lib.kda_chunk_prefill_noalloc(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
