@@ -235,7 +235,9 @@ def main():
     VT, VH = var_in["q"].shape[0], var_in["q"].shape[1]
     VN = var_in["cu_seqlens"].numel() - 1
     v_dims = kda.make_dims(VT, VN, VH, D, D, 0)
-    v_ws = torch.empty(kda.kda_prefill_workspace_bytes(v_dims), dtype=torch.uint8, device=dev)
+    # the workspace the call's path uses (the fused kernel: its index areas)
+    v_ws = torch.empty(kda.kda_prefill_path_workspace_bytes(v_dims, True), dtype=torch.uint8,
+                       device=dev)
     v_out = torch.empty((VT, VH, D), dtype=torch.bfloat16, device=dev)
     v_fin = torch.empty((VN, VH, D, D), dtype=torch.float32, device=dev)
 
@@ -393,7 +395,9 @@ def main():
     long_in = make_config_prefill(4, device=dev)
     LT, LH = long_in["q"].shape[0], long_in["q"].shape[1]
     l_dims = kda.make_dims(LT, 1, LH, D, D, 0)
-    l_ws = torch.empty(kda.kda_prefill_workspace_bytes(l_dims), dtype=torch.uint8, device=dev)
+    # (segmented: the index areas and the segments' state maps)
+    l_ws = torch.empty(kda.kda_prefill_path_workspace_bytes(l_dims), dtype=torch.uint8,
+                       device=dev)
     l_out = torch.empty((LT, LH, D), dtype=torch.bfloat16, device=dev)
     l_fin = torch.empty((1, LH, D, D), dtype=torch.float32, device=dev)
 

@@ -129,8 +129,11 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  *   final_state      : device fp32 [N,H,d_k,d_v] or NULL; may be the very same
  *                      pointer as initial_state (each sequence-head reads its
  *                      slot before writing it), any other overlap is rejected
- *   workspace        : device, at least kda_prefill_workspace_bytes(dims) bytes,
- *                      16-byte aligned; must not overlap any other buffer;
+ *   workspace        : device, 16-byte aligned, at least the bytes the call's
+ *                      path uses (kda_prefill_path_workspace_bytes; the
+ *                      options of kda_chunk_prefill_ex and checkpoints take
+ *                      the two-kernel path), and kda_prefill_workspace_bytes(dims)
+ *                      is enough for every path; must not overlap any other buffer;
  *                      contents on entry are ignored and on return are
  *                      unspecified.  NULL: the library allocates it with
  *                      hipMallocAsync on stream and frees it there with
@@ -220,6 +223,16 @@ typedef enum {
     KDA_PATH_SEGMENTED = 3   /* segment maps, their scan, then the segments again */
 } kda_prefill_path_kind;
 int32_t kda_prefill_path(const kda_dims* dims, int32_t packed, int32_t* segments);
+
+/* Bytes of workspace a plain kda_chunk_prefill with these sizes uses on the
+ * current device, for the path kda_prefill_path reports with the same
+ * arguments: the fused kernel only the index areas (4 (N + 1) bytes twice and
+ * 8 bytes per 64-token chunk of every sequence, each area rounded up to 256
+ * bytes), a segmented call those and its 3 N P H d^2 fp32 state maps, the
+ * other paths kda_prefill_workspace_bytes(dims).  Never more than
+ * kda_prefill_workspace_bytes(dims); 0 where kda_prefill_path returns -1.
+ * Reads no device memory. */
+size_t kda_prefill_path_workspace_bytes(const kda_dims* dims, int32_t packed);
 
 /* Number of intermediate states kda_chunk_prefill_checkpoints writes: for each
  * sequence of c = ceil(len / 64) chunks, floor((c - 1) / checkpoint_interval)
@@ -384,11 +397,8 @@ kda_status kda_decode_step(const kda_dims* dims, const void* q, const void* k,
  * second stream of the pipelined prefill (no library stream or event) and
  * calls no allocating routine.
  * Errors: as kda_chunk_prefill, plus KDA_ERR_WORKSPACE when the path the
- * call takes (kda_prefill_path) needs more than KDA_NOALLOC_SCRATCH_BYTES:
- * the fused path only its index areas (4 (N + 1) bytes twice and 8 bytes
- * per 64-token chunk of every sequence, each area rounded up to 256 bytes),
- * the segmented path those and its 3 N P H d^2 fp32 state maps, any other
- * path kda_prefill_workspace_bytes(dims).
+ * call takes needs more than KDA_NOALLOC_SCRATCH_BYTES
+ * (kda_prefill_path_workspace_bytes).
  * Every call on one device shares that device's array: calls that may run at
  * the same time on one device (different streams without ordering between
  * them) race and corrupt each other's results; order them on one stream.  The

@@ -8,11 +8,13 @@ ctypes binding whose functions carry the C ABI's names.
 from .kda import (KDA_NOALLOC_SCRATCH_BYTES, KDAError, kda_checkpoint_count, kda_chunk_prefill,
                   kda_chunk_prefill_checkpoints, kda_chunk_prefill_ex,
                   kda_chunk_prefill_noalloc, kda_decode_step,
-                  kda_decode_step_ex, kda_dims, kda_prefill_path, kda_prefill_pipeline_segments,
-                  kda_prefill_workspace_bytes, load_library, make_dims, status_string)
+                  kda_decode_step_ex, kda_dims, kda_prefill_path, kda_prefill_path_workspace_bytes,
+                  kda_prefill_pipeline_segments, kda_prefill_workspace_bytes, load_library,
+                  make_dims, status_string)
 
 __all__ = ["KDA_NOALLOC_SCRATCH_BYTES", "KDAError", "kda_checkpoint_count", "kda_chunk_prefill",
            "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_chunk_prefill_noalloc",
            "kda_decode_step",
-           "kda_decode_step_ex", "kda_dims", "kda_prefill_path", "kda_prefill_pipeline_segments",
+           "kda_decode_step_ex", "kda_dims", "kda_prefill_path", "kda_prefill_path_workspace_bytes",
+           "kda_prefill_pipeline_segments",
            "kda_prefill_workspace_bytes", "load_library", "make_dims", "status_string"]

@@ -279,9 +279,16 @@ size_t kda_prefill_workspace_bytes(const kda_dims* d) {
         .total();
 }
 
-int32_t kda_prefill_path(const kda_dims* d, int32_t packed, int32_t* segments) {
-    if (check_dims(d, true) != KDA_OK) return -1;
-    kda::PrefillArgs a{};  // (no options, no checkpoints: zero)
+}  // extern "C"
+
+namespace {
+
+// Arguments of a plain call with these sizes on the current device, as far
+// as the path choice reads them (false: a descriptor the library rejects, or
+// a device that cannot be queried).
+bool plain_call_args(const kda_dims* d, int32_t packed, kda::PrefillArgs& a) {
+    if (check_dims(d, true) != KDA_OK) return false;
+    a = kda::PrefillArgs{};  // (no options, no checkpoints: zero)
     a.total_tokens = d->total_tokens;
     a.n_seqs = d->num_seqs;
     a.n_heads = d->num_heads;
@@ -296,7 +303,32 @@ int32_t kda_prefill_path(const kda_dims* d, int32_t packed, int32_t* segments) {
     a.cu_seqlens = packed ? reinterpret_cast<const int32_t*>(uintptr_t{256}) : nullptr;
     a.layout = kda::make_layout(d->d_k, (int)elt_bytes(d), d->total_tokens, d->num_seqs,
                                 d->num_heads, true);
-    if (compute_units(&a.compute_units) != hipSuccess) return -1;
+    return compute_units(&a.compute_units) == hipSuccess;
+}
+
+// Workspace bytes the path of a call uses: the index areas (fused kernel),
+// those and the state maps (segmented), or all of ws_need, the two-kernel
+// path's records and pipeline state.
+size_t path_workspace_bytes(const kda::PrefillArgs& a, size_t ws_need) {
+    if (a.n_seqs == 0 || a.total_tokens == 0) return ws_need;
+    if (kda::fused_path(a)) return a.layout.records_offset();
+    const int seg = kda::segmented_segments(a);
+    return seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg) : ws_need;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_path_workspace_bytes(const kda_dims* d, int32_t packed) {
+    kda::PrefillArgs a;
+    if (!plain_call_args(d, packed, a)) return 0;
+    return path_workspace_bytes(a, kda_prefill_workspace_bytes(d));
+}
+
+int32_t kda_prefill_path(const kda_dims* d, int32_t packed, int32_t* segments) {
+    kda::PrefillArgs a;
+    if (!plain_call_args(d, packed, a)) return -1;
     int32_t seg = 0, path = KDA_PATH_SPLIT;
     if (d->num_seqs > 0 && d->total_tokens > 0) {
         if (kda::fused_path(a)) {
@@ -408,15 +440,6 @@ hipError_t scratch_address(void** out) {
     return hipSuccess;
 }
 
-// Workspace bytes the path this call takes uses: the index areas (fused
-// kernel), those and the state maps (segmented), or all of ws_need, the
-// two-kernel path's records and pipeline state.
-size_t path_workspace_bytes(const kda::PrefillArgs& a, size_t ws_need) {
-    if (kda::fused_path(a)) return a.layout.records_offset();
-    const int seg = kda::segmented_segments(a);
-    return seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg) : ws_need;
-}
-
 // Shared body of the prefill entry points.
 kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* initial_state,
@@ -452,8 +475,16 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     const void* f32_ptrs[] = {initial_state, final_state, cu_seqlens, checkpoints};
     for (const void* p : f32_ptrs)
         if (p && !aligned_to(p, 4)) return KDA_ERR_MISALIGNED;
+    // the workspace: too small for any path, or for the two-kernel path where
+    // that is the only one the call can take, is rejected without asking the
+    // device; the path-specific size is checked once the path is known
     const size_t ws_need = kda_prefill_workspace_bytes(d);
-    if (workspace && workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    const bool two_kernel_only = d->io_dtype != KDA_BF16 || sg || interval > 0 ||
+                                 out_gate != KDA_OUT_GATE_NONE || fe.active();
+    const kda::PrefillLayout lay = kda::make_layout((int)D, (int)elt_bytes(d), T, N, H, true);
+    if (workspace && (workspace_bytes < lay.records_offset() ||
+                      (two_kernel_only && workspace_bytes < ws_need)))
+        return KDA_ERR_WORKSPACE;
 
     // overlaps: no output may touch an input or another output; final_state
     // may equal initial_state exactly
@@ -527,12 +558,12 @@ kda_status prefill_impl(const kda_dims* d, const void* q, const void* k, const v
     a.out_gate = out_gate;
     a.out_gate_z = out_gate_z;
     a.fe = fe;
-    a.layout = kda::make_layout((int)D, (int)E, T, N, H, true);
+    a.layout = lay;
     // a call that can only take the two-kernel path (fp32 I/O, or the per-head
     // gate) is sized without asking the device
-    if (noalloc && (!a.bf16 || a.scalar_g) && ws_need > KDA_NOALLOC_SCRATCH_BYTES)
-        return KDA_ERR_WORKSPACE;
+    if (noalloc && two_kernel_only && ws_need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
     if (compute_units(&a.compute_units) != hipSuccess) return KDA_ERR_HIP;
+    if (workspace && workspace_bytes < path_workspace_bytes(a, ws_need)) return KDA_ERR_WORKSPACE;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (noalloc) {
         // the library's per-device array (its address is found only now, after

@@ -34,7 +34,8 @@ KDA_PATH_SPLIT, KDA_PATH_PIPELINED, KDA_PATH_FUSED, KDA_PATH_SEGMENTED = range(4
 EXPORTED = ("kda_prefill_workspace_bytes", "kda_chunk_prefill", "kda_checkpoint_count",
             "kda_chunk_prefill_checkpoints", "kda_chunk_prefill_ex", "kda_decode_step",
             "kda_decode_step_ex", "kda_status_string", "kda_version",
-            "kda_prefill_pipeline_segments", "kda_chunk_prefill_noalloc", "kda_prefill_path")
+            "kda_prefill_pipeline_segments", "kda_chunk_prefill_noalloc", "kda_prefill_path",
+            "kda_prefill_path_workspace_bytes")
 
 #: bytes of the per-device array kda_chunk_prefill_noalloc uses as its workspace
 KDA_NOALLOC_SCRATCH_BYTES = 320 << 20
@@ -139,6 +140,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_prefill_pipeline_segments.restype = ctypes.c_int32
     lib.kda_prefill_path.argtypes = [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.kda_prefill_path.restype = ctypes.c_int32
+    lib.kda_prefill_path_workspace_bytes.argtypes = [D, ctypes.c_int32]
+    lib.kda_prefill_path_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_prefill_noalloc.restype = ctypes.c_int
     _lib = lib
@@ -199,6 +202,13 @@ def _gate(g: torch.Tensor, lead) -> int:
 
 def kda_prefill_workspace_bytes(dims: kda_dims) -> int:
     return int(load_library().kda_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def kda_prefill_path_workspace_bytes(dims: kda_dims, packed: bool = False) -> int:
+    """Bytes of workspace a plain prefill of these sizes uses on the current
+    device (the path's own need; 0 for a rejected descriptor)."""
+    return int(load_library().kda_prefill_path_workspace_bytes(ctypes.byref(dims),
+                                                               int(bool(packed))))
 
 
 def kda_prefill_pipeline_segments(dims: kda_dims) -> int:
@@ -272,8 +282,14 @@ def kda_chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     elif final_state is not None:
         _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
     dims = make_dims(T, N, H, dk, dv, _io_dtype(q), scale, qk_l2norm, gate=gate)
-    need = kda_prefill_workspace_bytes(dims)
     if workspace is None and not library_workspace:
+        # what this call's path uses (the fused and segmented paths need out
+        # aligned to 16 bytes; otherwise the two-kernel workspace)
+        if out.data_ptr() % 16 == 0:
+            with torch.cuda.device(dev):
+                need = kda_prefill_path_workspace_bytes(dims, cu_seqlens is not None)
+        else:
+            need = kda_prefill_workspace_bytes(dims)
         workspace = _workspace(need, dev, stream)
     rc = lib.kda_chunk_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(out),

@@ -101,7 +101,10 @@ def test_prefill_validation(kda):
     # passed validation would launch on these fake addresses)
     assert prefill_call(kda, d, ws=None, q=None) == kda.KDA_ERR_INVALID_ARG
     assert prefill_call(kda, d, ws=None, q=FAKE + 8) == kda.KDA_ERR_MISALIGNED
-    assert prefill_call(kda, d, ws_bytes=1024) == kda.KDA_ERR_WORKSPACE
+    # smaller than any path uses (the fused kernel's index areas, 768 bytes
+    # here): rejected without asking the device; a plain bf16 call is otherwise
+    # sized by its path, which needs the device
+    assert prefill_call(kda, d, ws_bytes=512) == kda.KDA_ERR_WORKSPACE
     # the workspace must not overlap an input (the kernels write it)
     big = 256 * 4 * 128 * 2 + 4096
     assert prefill_call(kda, d, ws=FAKE + 3 * big + 256) == kda.KDA_ERR_INVALID_ARG   # over g
@@ -259,9 +262,11 @@ def test_output_gate_validation(kda):
         kda.KDA_ERR_INVALID_ARG
     # nor the final state
     assert call(kda.KDA_OUT_GATE_CHANNEL, fin=FAKE + 30 * big + 256) == kda.KDA_ERR_INVALID_ARG
-    # with no gate, z is ignored (NULL options mean "no options")
-    assert call(kda.KDA_OUT_GATE_NONE, z=None, wsb=1024) == kda.KDA_ERR_WORKSPACE
-    assert call(0, null_opts=True, wsb=1024) == kda.KDA_ERR_WORKSPACE
+    # with no gate, z is ignored (NULL options mean "no options"); such a call
+    # may take the fused path, so only a workspace below its 768 bytes is
+    # rejected without the device
+    assert call(kda.KDA_OUT_GATE_NONE, z=None, wsb=512) == kda.KDA_ERR_WORKSPACE
+    assert call(0, null_opts=True, wsb=512) == kda.KDA_ERR_WORKSPACE
     # an empty batch is a no-op even with a gate and no z
     e = kda.make_dims(0, 0, 4, 128, 128, kda.KDA_BF16)
     o = kda.kda_prefill_options(0, kda.KDA_OUT_GATE_CHANNEL, None, None)

@@ -12,9 +12,10 @@ again from those states for the outputs.
   regimes, no initial and no final state, 64 segments (the most).
 * Agreement with the two-kernel path within twice that bar where the oracle
   would be slow: the automatic choice on a 262,144-token sequence with 8 heads.
-* Bitwise: two runs of the same call, the library-allocated workspace, the
-  final state written over the initial state on a side stream, and graph
-  replays of the segmented and the fused path.
+* Bitwise: two runs of the same call, the library-allocated workspace, a
+  workspace of just the bytes the call's path uses (segmented, fused and
+  two-kernel), the final state written over the initial state on a side
+  stream, and graph replays of the segmented and the fused path.
 
 KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS the
 segment count.
@@ -271,6 +272,41 @@ def test_library_workspace(lib, monkeypatch):
     o_w, f_w = run(lib, monkeypatch, inp, "segmented", 4)
     o_l, f_l = run(lib, monkeypatch, inp, "segmented", 4, library_workspace=True)
     assert torch.equal(o_l, o_w) and torch.equal(f_l, f_w)
+
+
+@pytest.mark.parametrize("lens,heads,path", [([16384], 32, 3), ([4096] * 16, 32, 2),
+                                             ([300, 65], 3, 0)])
+def test_path_workspace(lib, monkeypatch, lens, heads, path):
+    """A workspace of exactly kda_prefill_path_workspace_bytes (the segmented
+    path: index areas and maps; the fused kernel: index areas; the two-kernel
+    path: everything) gives the results of the full-size workspace bitwise; a
+    byte less is rejected."""
+    from kda_inputs import make_prefill
+    monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
+    monkeypatch.delenv("KDA_PREFILL_SEGMENTS", raising=False)
+    K = lib.kda
+    n, T = len(lens), sum(lens)
+    dims = lib.make_dims(T, n, heads, 128, 128, K.KDA_BF16)
+    full = lib.kda_prefill_workspace_bytes(dims)
+    need = lib.kda_prefill_path_workspace_bytes(dims, n > 1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        assert lib.kda_prefill_path(dims, n > 1)[0] == path
+    assert 0 < need <= full and (need == full) == (path == 0)
+    say(f"[path workspace {n} x {lens[0]} x {heads}] {need} of {full} bytes")
+    inp = make_prefill(lens, heads, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=613,
+                       device="cuda", packed_cu=n > 1)
+    ws_full = torch.empty(full, dtype=torch.uint8, device="cuda")
+    o_f, f_f = lib.kda_chunk_prefill(*args_of(inp), num_seqs=n, workspace=ws_full)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o_p, f_p = lib.kda_chunk_prefill(*args_of(inp), num_seqs=n, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_f) and torch.equal(f_p, f_f)
+    with pytest.raises(lib.KDAError) as e:
+        lib.kda_chunk_prefill(*args_of(inp), num_seqs=n, workspace=ws[:need - 1])
+    assert e.value.status == K.KDA_ERR_WORKSPACE
+    fp32 = lib.make_dims(T, n, heads, 128, 128, K.KDA_FP32)
+    assert lib.kda_prefill_path_workspace_bytes(fp32, n > 1) == lib.kda_prefill_workspace_bytes(fp32)
 
 
 @pytest.mark.parametrize("path,lens,heads,segments", [("segmented", [16421], 2, 4),
