@@ -8,8 +8,8 @@ its seed), H=32, d_k=d_v=128, bf16 I/O, fp32 per-sequence initial and final
 states; seeded synthetic inputs resident in HBM (33 GB of q, k, v, g per call,
 far past the 256 MB MALL).  Its 2,048 (sequence, head) chains take the fused
 kernel (chain order + one persistent kernel); the single-sequence workloads
-below take the preparation and recurrence kernels.  This is the
-largest single-GPU workload.  Untimed calls run first until --ramp-ms of GPU
+below take the segmented path (two passes of the same kernel around a scan of
+the segments' state maps).  This is the largest single-GPU workload.  Untimed calls run first until --ramp-ms of GPU
 time has passed (the shader clock rises over the first ~25 ms of load), then
 W warm-up steps, then K back-to-back steps timed between device
 synchronisations, with two HIP events on the launch stream around them giving
@@ -17,11 +17,12 @@ the average call duration behind the roofline figure; a separate loop with
 events around each call gives the per-call spread.
 
 Secondary figures in the same run, each with its own roofline object:
-* the 8,192-token single-sequence prefill (H=32), four input copies rotated so
-  a call never finds its inputs in the MALL, plus its checkpoint, per-head
-  gate, output-gate and front-end variants;
-* the 2^20-token single-sequence prefill (H=16; its 16 chains take the
-  segmented path: 16 segments per head);
+* the 8,192-token single-sequence prefill (H=32; 8 chains per head in each
+  segmented pass), four input copies rotated so a call never finds its inputs
+  in the MALL, plus its checkpoint, per-head gate, output-gate and front-end
+  variants (these take the preparation and recurrence kernels);
+* the 2^20-token single-sequence prefill (H=16; 16 chains per head in each
+  segmented pass, 17 segments);
 * the decode step on 256 sequences x 32 heads (512 MiB fp32 state advanced in
   place), plus its output-gate and front-end variants.
 
@@ -74,13 +75,20 @@ def fused_executed_flops(T, H, d, C=16):
     return (6 * d * d + 14 * C * d) * T * H
 
 
-def segmented_executed_flops(T, H, d, C=16):
-    """bf16 MFMA work per token-head of the segmented prefill: the map pass
-    without outputs (Ke S, the state update and T Diag(beta) Y for the b and
-    the M tiles, 8 d^2 + 4 C d, and the A, A^T and selector products once, 8 C
-    d) and the output pass (the fused kernel's 6 d^2 + 14 C d); the scan's
-    fp32 products are not counted."""
-    return (14 * d * d + 26 * C * d) * T * H
+def segmented_executed_flops(T, H, d, P, C=16):
+    """bf16 MFMA work of the segmented prefill of one T-token sequence with P
+    chains per head: every token-head runs the fused kernel with its outputs
+    (6 d^2 + 14 C d), and those of segments 1..P-1 are first run for their
+    maps (Ke S, the state update and T Diag(beta) Y for the b and the M tiles,
+    8 d^2 + 4 C d, and the A, A^T and selector products once, 8 C d).  The
+    segments as the kernel places them: of n chunks, P of l = ceil(7 n /
+    (7 P + 8)) after a first segment of n - P l; the scan's fp32 products are
+    not counted."""
+    n = (T + 63) // 64
+    l = (7 * n + 7 * P + 7) // (7 * P + 8)
+    a = max(0, n - P * l)
+    mapped = max(0, min(n, a + (P - 1) * l) - a) * 64
+    return (6 * d * d + 14 * C * d) * T * H + (8 * d * d + 12 * C * d) * min(mapped, T) * H
 
 
 def decode_state_bytes(n, h, d):
@@ -268,7 +276,9 @@ def main():
     out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
     dims = kda.make_dims(T, 1, H, D, D, 0)
+    # (the full workspace: the option variants below take the two-kernel path)
     ws = torch.empty(kda.kda_prefill_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    single_path, single_segs = kda.kda_prefill_path(dims)
 
     def single(i=0):
         s = sets[i % len(sets)]
@@ -513,11 +523,15 @@ def main():
                              min_call_ms=float(np.min(v_ms))),
         "cpu_baseline": cpu,
         "prefill_single": {
-            "workload": CONFIGS[1].name, "tokens_per_s": T / s_wall,
+            "workload": CONFIGS[1].name,
+            "path": {0: "split", 1: "pipelined", 2: "fused", 3: "segmented"}.get(single_path, "?"),
+            "segments": single_segs,
+            "tokens_per_s": T / s_wall,
             "ms_per_step": s_wall * 1e3,
             "roofline": roofline("kda_chunk_prefill call", s_bytes, s_avg,
                                  counter_traffic("prefill_single"), copy_GBps,
-                                 flops=prefill_executed_flops(T, H, D),
+                                 flops=(segmented_executed_flops(T, H, D, single_segs)
+                                        if single_path == 3 else prefill_executed_flops(T, H, D)),
                                  median_call_us=s_med_us,
                                  min_call_us=float(np.min(s_ms)) * 1e3),
             "cpu_baseline": cpu_single,
@@ -542,7 +556,7 @@ def main():
             "tokens_per_s": LT / l_avg,
             "roofline": roofline("kda_chunk_prefill call", l_bytes, l_avg,
                                  counter_traffic("prefill_long"), copy_GBps,
-                                 flops=(segmented_executed_flops(LT, LH, D) if long_path == 3
+                                 flops=(segmented_executed_flops(LT, LH, D, long_segs) if long_path == 3
                                         else prefill_executed_flops(LT, LH, D)),
                                  median_call_ms=float(np.median(l_ms))),
             "cpu_baseline": cpu_long,

@@ -159,33 +159,33 @@ size_t kda_prefill_workspace_bytes(const kda_dims* dims);
  * device share the second stream; each call's own events keep its launches
  * ordered.
  *
- * Kernels.  A call with many (sequence, head) chains -- at least a third of
- * the device's compute units at d = 128, half at d = 64 -- with bf16 I/O, a
- * per-channel gate, out aligned to 16 bytes and no options of
- * kda_chunk_prefill_ex or checkpoints runs one fused kernel: persistent
- * workgroups take whole chains, longest sequences first, and step through
- * each 64-token chunk as four 16-token sub-chunks with the chunk's operands in
- * LDS, so only the inputs, the outputs and the states touch HBM; it uses only
- * the first two index areas of the workspace.  A call with fewer chains, d =
- * 128 and otherwise the fused kernel's conditions is segmented where that
- * pays: each sequence is cut into P segments of whole chunks, P being one
- * (segment, head) chain per compute unit, at most 64, with segments of at
- * least 32 chunks for sequences of the average length (a short sequence may
- * leave segments empty); the path is taken with P of at least 3 whose chains
- * fill three quarters of the compute units, or with P of 16 or more.  One
- * pass of the fused kernel forms each segment's state map S_end = M S_start +
- * b (b from the zero state, M from the identity with v taken as zero, no
- * outputs), a scan kernel composes the maps in order into every segment's
- * start state and the final state, and the fused kernel runs the segments
- * again from those states for the outputs (three [N P, H, d, d] fp32 arrays in
- * the workspace's record area).  Every other call runs the preparation and
- * recurrence kernels, which hand per-chunk records through the workspace.  The
- * paths compute the same recurrence with the same operand precision but round
- * in a different order, so their results agree to the accuracy below, not bit
- * for bit.  The environment variable KDA_PREFILL_PATH (read at each call) set
- * to "split", "fused" or "segmented" overrides the choice where that path
- * applies, and KDA_PREFILL_SEGMENTS=<P> (1 to 64) sets the segment count of a
- * segmented call.
+ * Kernels.  A call with bf16 I/O, d = 128, a per-channel gate, out aligned to
+ * 16 bytes and no options of kda_chunk_prefill_ex or checkpoints is
+ * segmented where that pays.  With P (sequence, head) chains per compute unit
+ * in each pass -- CUs / chains, at most 64, lowered until the segments hold at
+ * least 12 chunks for sequences of the average length -- each sequence is cut
+ * into P + 1 segments of whole chunks (a short sequence may leave segments
+ * empty): a first pass of the fused kernel below runs segment 0 with its
+ * outputs and forms the state maps S_end = M S_start + b of segments 1..P-1 (b
+ * from the zero state, M from the identity with v taken as zero), a scan
+ * kernel composes the maps in order into the start states of segments 2..P,
+ * and a second pass runs segments 1..P with their outputs (three [N (P + 1),
+ * H, d, d] fp32 arrays in the workspace's record area).  It is taken with P of
+ * at least 2 whose chains fill three quarters of the compute units, with P of
+ * 16 or more, or where the fused kernel would take the call.  Otherwise a
+ * call with many chains -- at least a third of the device's compute units at
+ * d = 128, half at d = 64 -- under the same conditions (bf16 also at d = 64)
+ * runs one fused kernel: persistent workgroups take whole chains, longest
+ * sequences first, and step through each 64-token chunk as four 16-token
+ * sub-chunks with the chunk's operands in LDS, so only the inputs, the outputs
+ * and the states touch HBM; it uses only the first two index areas of the
+ * workspace.  Every other call runs the preparation and recurrence kernels,
+ * which hand per-chunk records through the workspace.  The paths compute the
+ * same recurrence with the same operand precision but round in a different
+ * order, so their results agree to the accuracy below, not bit for bit.  The
+ * environment variable KDA_PREFILL_PATH (read at each call) set to "split",
+ * "fused" or "segmented" overrides the choice where that path applies, and
+ * KDA_PREFILL_SEGMENTS=<P> (2 to 64) sets P for a segmented call.
  *
  * Accuracy: bf16 I/O uses bf16 MFMA operands with fp32 accumulation and an
  * fp32 state; fp32 I/O uses fp32 MFMA throughout.  Any g <= 0 is handled:
@@ -228,7 +228,7 @@ int32_t kda_prefill_path(const kda_dims* dims, int32_t packed, int32_t* segments
  * current device, for the path kda_prefill_path reports with the same
  * arguments: the fused kernel only the index areas (4 (N + 1) bytes twice and
  * 8 bytes per 64-token chunk of every sequence, each area rounded up to 256
- * bytes), a segmented call those and its 3 N P H d^2 fp32 state maps, the
+ * bytes), a segmented call those and its 3 N (P + 1) H d^2 fp32 state maps, the
  * other paths kda_prefill_workspace_bytes(dims).  Never more than
  * kda_prefill_workspace_bytes(dims); 0 where kda_prefill_path returns -1.
  * Reads no device memory. */

@@ -130,7 +130,7 @@ bool fused_path(const PrefillArgs& a) {
         a.chunk_end != INT64_MAX)
         return false;
     const char* env = std::getenv("KDA_PREFILL_PATH");
-    if (env && std::strcmp(env, "split") == 0) return false;
+    if (env && (std::strcmp(env, "split") == 0 || std::strcmp(env, "segmented") == 0)) return false;
     if (env && std::strcmp(env, "fused") == 0) return true;
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t per = a.d == 128 ? kFusedCUsPerChain : kFusedCUsPerChain64;
@@ -146,27 +146,29 @@ int segmented_segments(const PrefillArgs& a) {
     if (a.total_tokens <= 0 || a.n_seqs < 1 || a.slot_begin != 0 || a.slot_end != -1 ||
         a.chunk_begin != 0 || a.chunk_end != INT64_MAX)
         return 0;
-    // (the scan's grid is tiles x heads x sequences)
-    if (a.n_seqs > 65535 || a.n_heads > 65535) return 0;
-    if (fused_path(a)) return 0;
+    // (the scan's grid: eight workgroups per chain)
+    if ((int64_t)a.n_seqs * a.n_heads > (int64_t{1} << 24)) return 0;
     const char* env = std::getenv("KDA_PREFILL_PATH");
     const bool forced = env && std::strcmp(env, "segmented") == 0;
     if (env && (std::strcmp(env, "split") == 0 || std::strcmp(env, "fused") == 0)) return 0;
     const int64_t chains = (int64_t)a.n_seqs * a.n_heads;
     const int64_t seq_chunks = (a.total_tokens / a.n_seqs + 63) / 64;
     const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
+    // one chain per CU in each pass, with segments of at least kSegMinChunks
+    // (the kernel's placement: P of ceil(7 C / (7 P + 8)) chunks after the first)
     int64_t P = std::min<int64_t>(kSegMaxSegments, std::max<int64_t>(1, cus / chains));
-    P = std::min<int64_t>(P, seq_chunks / kSegMinChunks);
+    while (P >= 2 && (7 * seq_chunks + 7 * P + 7) / (7 * P + 8) < kSegMinChunks) --P;
     if (const char* ps = std::getenv("KDA_PREFILL_SEGMENTS")) {
         const long v = std::strtol(ps, nullptr, 10);
         if (v >= 1 && v <= kSegMaxSegments) P = std::min<int64_t>(v, seq_chunks);
     }
     if (P < 2) return 0;
-    // automatically: at least kSegMinSegments segments, and either enough
-    // that the segment chains fill three quarters of the device or at least
-    // kSegManySegments
-    if (!forced && (a.compute_units <= 0 || P < kSegMinSegments ||
-                    (chains * P * 4 < (int64_t)a.compute_units * 3 && P < kSegManySegments)))
+    // automatically: the segment chains fill three quarters of the device,
+    // or there are at least kSegManySegments, or the fused kernel would take
+    // the call with a chain per CU at most (a third of the device or more)
+    if (!forced && (a.compute_units <= 0 ||
+                    (chains * P * 4 < (int64_t)a.compute_units * 3 && P < kSegManySegments &&
+                     chains * kFusedCUsPerChain < (int64_t)a.compute_units)))
         return 0;
     // its arrays fit in the record area the split path would use
     if (segmented_scratch_bytes(a, (int)P) > a.layout.records_bytes()) return 0;
@@ -174,9 +176,9 @@ int segmented_segments(const PrefillArgs& a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    if (const int P = segmented_segments(a)) return launch_segmented(a, P, s);
     if (fused_path(a))
         return a.d == 128 ? launch_fused<128>(a, s) : launch_fused<64>(a, s);
-    if (const int P = segmented_segments(a)) return launch_segmented(a, P, s);
     // under stream capture the call stays on the caller's stream: no library
     // stream or events enter the caller's graph (the results are the same)
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -311,9 +313,9 @@ bool plain_call_args(const kda_dims* d, int32_t packed, kda::PrefillArgs& a) {
 // path's records and pipeline state.
 size_t path_workspace_bytes(const kda::PrefillArgs& a, size_t ws_need) {
     if (a.n_seqs == 0 || a.total_tokens == 0) return ws_need;
-    if (kda::fused_path(a)) return a.layout.records_offset();
-    const int seg = kda::segmented_segments(a);
-    return seg > 0 ? a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg) : ws_need;
+    if (const int seg = kda::segmented_segments(a))
+        return a.layout.records_offset() + kda::segmented_scratch_bytes(a, seg);
+    return kda::fused_path(a) ? a.layout.records_offset() : ws_need;
 }
 
 }  // namespace
@@ -331,10 +333,10 @@ int32_t kda_prefill_path(const kda_dims* d, int32_t packed, int32_t* segments) {
     if (!plain_call_args(d, packed, a)) return -1;
     int32_t seg = 0, path = KDA_PATH_SPLIT;
     if (d->num_seqs > 0 && d->total_tokens > 0) {
-        if (kda::fused_path(a)) {
-            path = KDA_PATH_FUSED;
-        } else if ((seg = kda::segmented_segments(a)) > 0) {
+        if ((seg = kda::segmented_segments(a)) > 0) {
             path = KDA_PATH_SEGMENTED;
+        } else if (kda::fused_path(a)) {
+            path = KDA_PATH_FUSED;
         } else if ((seg = kda::pipeline_segments(a)) >= 2) {
             path = KDA_PATH_PIPELINED;
         } else {

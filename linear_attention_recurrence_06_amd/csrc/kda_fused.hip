@@ -117,15 +117,12 @@ struct FusedParams {
     int32_t n_seqs, n_heads;
     float scale;
     int l2norm;
-    // segmented kernels: each of the n_seqs / seg_per_seq sequences is cut
-    // into seg_per_seq segments of whole chunks, and each (segment, head) is a
-    // chain; n_seqs counts the segments.  With cu, a sequence's segments are
-    // ceil(len / seg_per_seq) tokens rounded up to whole chunks (those past
-    // its end empty); without, equal lengths and segments of seg_len tokens
-    // (the last shorter)
-    int64_t seg_len = 0;
+    // segmented passes: seg_per_seq chains (parts) per sequence and head,
+    // n_seqs counting parts; the segments are placed by seg_bounds from each
+    // sequence's length (cu, or equal lengths)
     int32_t seg_per_seq = 1;
-    float* fin2 = nullptr;  // MAPS kernels: the linear parts M (fin takes b)
+    float* fin2 = nullptr;  // the first pass's linear parts M (fin takes b)
+    float* st = nullptr;    // segment start states
 };
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -912,24 +909,154 @@ __device__ __forceinline__ void ws_flush(const FusedParams& p, const bf16 (&vt)[
     }
 }
 
-// The segmented prefill's kernels: SEG, chains are (segment, head) pairs
-// (p.seg_per_seq segments per sequence, placed from p.seg_len or p.cu); OUT
-// false, no outputs (p.out unused, no q read); ZERO_V, V taken as zero and
-// every chain started from the identity (p.v and p.init unused: the linear
-// part of each segment's state map); MAPS (with SEG, without OUT), both parts
-// at once: each recurrence wave carries two tiles of b, from the zero state
-// with V, and two of M, from the identity with V = 0, to p.fin and p.fin2.
-template <int D, bool OUT = true, bool ZERO_V = false, bool SEG = false, bool MAPS = false>
-__global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
-    static_assert(!MAPS || (SEG && !OUT && !ZERO_V), "the maps of a segmented call");
+// Placement of a sequence's segments in a segmented call with Q chains per
+// sequence and head in each pass (Q + 1 segments): of its C chunks, segments
+// 1..Q take l = ceil(7 C / (7 Q + 8)) each (the last ones shorter or empty)
+// and segment 0 the a = max(0, C - Q l) before them, about 8/7 of l.
+// Segment 0 runs with its outputs in the first pass beside the maps of
+// segments 1..Q-1, whose chains take about 8/7 as long per chunk.
+__device__ __forceinline__ void seg_bounds(int64_t seq_len, int Q, int s, int64_t& begin,
+                                           int64_t& len) {
+    const int64_t C = (seq_len + 63) / 64;
+    const int64_t l = (7 * C + 7 * Q + 7) / (7 * Q + 8);
+    const int64_t a = max((int64_t)0, C - Q * l);
+    const int64_t c0 = s == 0 ? 0 : min(C, a + (int64_t)(s - 1) * l);
+    const int64_t c1 = s == 0 ? a : min(C, a + (int64_t)s * l);
+    begin = 64 * c0;
+    len = max((int64_t)0, min(64 * c1, seq_len) - 64 * c0);
+}
+
+// One chain through fused_ws_kernel: tokens [s_begin, s_begin + s_len) of
+// head h, from the state `init` (null: zero) to `fin` (null: not written),
+// each the chain's [D, D] fp32 state.  OUT: the outputs are written.  MAPS
+// (without OUT): the chain's state map instead, each recurrence wave carrying
+// two tiles of b, from the zero state with V, to `fin` and two of M, from the
+// identity with V = 0, to `fin2` (init unused).
+template <int D, bool OUT, bool MAPS>
+__device__ __forceinline__ void ws_chain(const FusedParams& p, WsSmem<D>& sm, int w, int lane,
+                                         int h, int64_t s_begin, int64_t s_len,
+                                         const float* __restrict__ init, float* __restrict__ fin,
+                                         float* __restrict__ fin2) {
+    static_assert(!(OUT && MAPS), "a map pass writes no outputs");
     constexpr int NCT = D / 16, TPV = WsSmem<D>::TPV;
-    constexpr int NT = MAPS ? 4 : 2;            // 16-column state tiles per recurrence wave
-    constexpr int NV = ZERO_V ? 0 : 2;          // of which the first NV see V
+    constexpr int NT = MAPS ? 4 : 2;  // 16-column state tiles per recurrence wave
+    constexpr int NV = 2;             // of which the first NV see V
+    const int64_t nch = (s_len + 63) / 64;
+    const auto len_of = [&](int64_t kc) {
+        return (int)max((int64_t)0, min((int64_t)64, s_len - 64 * kc));
+    };
+    if (w < kWsPrep<D>) {
+        // block w of chunk kc into record kc % 2, a barrier after each,
+        // then one for the last chunk's recurrence
+        if (nch > 0) {
+            BlockRows<D> rows;
+            ws_load_rows<D, -1, OUT>(p, s_begin, len_of(0), h, w, lane, rows);
+            for (int64_t kc = 0; kc < nch; ++kc) {
+                // a copy of the lane index the compiler cannot see
+                // through: the chunk's index arithmetic is redone per
+                // chunk instead of held in registers across the loop
+                int lane_c = lane;
+                asm volatile("" : "+v"(lane_c));
+                ws_prep<D, OUT>(p, sm.rec[kc & 1], w, lane_c, s_begin + 64 * kc, h, rows,
+                                len_of(kc + 1));
+                __syncthreads();
+            }
+            __syncthreads();
+        }
+    } else {
+        const int wr = w - kWsPrep<D>;
+        const int n16 = lane & 15, g = lane >> 4;
+        // this lane's state: key channels state_channel(rt, g, e), value
+        // column 32 wr + 16 (c % 2) + n16 of tile c
+        f32x4 S[NT][NCT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int rt = 0; rt < NCT; ++rt) S[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the M tiles start from the identity
+#pragma unroll
+        for (int c = NV; c < NT; ++c)
+#pragma unroll
+            for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[c][rt][e] = state_channel(rt, g, e) == 32 * wr + 16 * (c % 2) + n16 ? 1.f : 0.f;
+        if (!MAPS && init) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[c][rt][e] = init[(int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * c + n16];
+        }
+        // the state's loads complete here, once per chain
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[c][rt]));
+        if (nch > 0) {
+            bf16x8 v[4];
+            ws_load_v<D>(p, s_begin, len_of(0), h, wr, lane, v);
+            // step 0: nothing to run; V of chunk 0 to the tile
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<bf16x8*>(&sm.vt[16 * j + (lane >> 2)][32 * wr + 8 * (lane & 3)]) = v[j];
+            ws_load_v<D>(p, s_begin + 64, len_of(1), h, wr, lane, v);
+            __syncthreads();
+            // step kc: the recurrence of chunk kc - 1 from record (kc - 1) % 2
+            for (int64_t kc = 1; kc <= nch; ++kc) {
+                int lane_c = lane;
+                asm volatile("" : "+v"(lane_c));
+                const SubRecord<D>& rec = sm.rec[(kc - 1) & 1];
+#pragma unroll
+                for (int Rb = 0; Rb < 4; ++Rb)
+                    ws_block<D, TPV, OUT, NT, NV>(rec, sm.vt, S, wr, lane_c, Rb);
+                if constexpr (OUT)
+                    ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
+                if (kc < nch) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<bf16x8*>(
+                            &sm.vt[16 * j + (lane_c >> 2)][32 * wr + 8 * (lane_c & 3)]) = v[j];
+                    ws_load_v<D>(p, s_begin + 64 * (kc + 1), len_of(kc + 1), h, wr, lane_c, v);
+                }
+                __syncthreads();
+            }
+        }
+        if (fin) {
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                float* f = c < 2 ? fin : fin2;
+#pragma unroll
+                for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        f[(int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * (c % 2) + n16] = S[c][rt][e];
+            }
+        }
+    }
+}
+
+// Chains of fused_ws_kernel.  kWsPlain: (sequence, head) pairs, states p.init
+// and p.fin [N, H, D, D].  The segmented prefill's two passes, chains (part,
+// head) with p.seg_per_seq = Q parts per sequence (p.n_seqs counts parts):
+// kWsSegFirst, part 0 runs segment 0 with its outputs from p.init to start
+// state slot 1 of p.st, and part k >= 1 forms the map of segment k, b to p.fin
+// and M to p.fin2; kWsSegOut, part k runs segment k + 1 with its outputs from
+// start slot k + 1 of p.st, and the last part writes the final state to p.fin
+// [N, H, D, D].  p.st, p.fin and p.fin2 of the first pass are [N (Q + 1), H,
+// D, D], slot s of sequence n at n (Q + 1) + s.
+enum WsKind { kWsPlain = 0, kWsSegFirst = 1, kWsSegOut = 2 };
+
+template <int D, int KIND = kWsPlain>
+__global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_kernel(FusedParams p) {
     __shared__ WsSmem<D> sm;
-    const int t = threadIdx.x, lane = t & 63;
+    const int t = threadIdx.x, lane0 = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t H = p.n_heads;
     const int64_t chains = (int64_t)p.n_seqs * H;
+    constexpr int64_t DD = (int64_t)D * D;
     for (;;) {
         if (t == 0) sm.next = atomicAdd(p.counter, 1);
         __syncthreads();
@@ -938,128 +1065,50 @@ __global__ __launch_bounds__(64 * (kWsPrep<D> + kWsRec<D>), 1) void fused_ws_ker
         if (ci >= chains) break;
         const int64_t si = ci / H;
         const int h = (int)(ci - si * H);
-        const int64_t n = p.order ? (int64_t)p.order[si] : si;
-        int64_t s_begin, s_len;
-        if constexpr (SEG) {
-            // segment n % seg_per_seq of sequence n / seg_per_seq
-            const int64_t seq = n / p.seg_per_seq, part = n % p.seg_per_seq;
-            int64_t seq_begin, seq_len, seg_len = p.seg_len;
+        // a copy of the lane index the compiler cannot see through: what the
+        // chain derives from it is computed per chain, not hoisted out of the
+        // chain loop and held (or spilled) for the whole kernel
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
+        if constexpr (KIND == kWsPlain) {
+            const int64_t n = p.order ? (int64_t)p.order[si] : si;
+            int64_t s_begin, s_len;
+            if (p.cu) {
+                s_begin = p.cu[n];
+                s_len = (int64_t)p.cu[n + 1] - s_begin;
+            } else {
+                s_len = p.total_tokens / p.n_seqs;
+                s_begin = n * s_len;
+            }
+            const int64_t sb = (n * H + h) * DD;
+            ws_chain<D, true, false>(p, sm, w, lane, h, s_begin, s_len, p.init ? p.init + sb : nullptr,
+                                     p.fin ? p.fin + sb : nullptr, nullptr);
+        } else {
+            const int Q = p.seg_per_seq;
+            const int64_t seq = si / Q;
+            const int s = (int)(si - seq * Q) + (KIND == kWsSegOut ? 1 : 0);
+            int64_t seq_begin, seq_len;
             if (p.cu) {
                 seq_begin = p.cu[seq];
                 seq_len = (int64_t)p.cu[seq + 1] - seq_begin;
-                seg_len = ((seq_len + p.seg_per_seq - 1) / p.seg_per_seq + 63) / 64 * 64;
             } else {
-                seq_len = p.total_tokens / (p.n_seqs / p.seg_per_seq);
+                seq_len = p.total_tokens / (p.n_seqs / Q);
                 seq_begin = seq * seq_len;
             }
-            s_begin = seq_begin + part * seg_len;
-            s_len = max((int64_t)0, min(seg_len, seq_len - part * seg_len));
-        } else if (p.cu) {
-            s_begin = p.cu[n];
-            s_len = (int64_t)p.cu[n + 1] - s_begin;
-        } else {
-            s_len = p.total_tokens / p.n_seqs;
-            s_begin = n * s_len;
-        }
-        const int64_t nch = (s_len + 63) / 64;
-        const auto len_of = [&](int64_t kc) {
-            return (int)max((int64_t)0, min((int64_t)64, s_len - 64 * kc));
-        };
-        if (w < kWsPrep<D>) {
-            // block w of chunk kc into record kc % 2, a barrier after each,
-            // then one for the last chunk's recurrence
-            if (nch > 0) {
-                BlockRows<D> rows;
-                ws_load_rows<D, -1, OUT>(p, s_begin, len_of(0), h, w, lane, rows);
-                for (int64_t kc = 0; kc < nch; ++kc) {
-                    // a copy of the lane index the compiler cannot see
-                    // through: the chunk's index arithmetic is redone per
-                    // chunk instead of held in registers across the loop
-                    int lane_c = lane;
-                    asm volatile("" : "+v"(lane_c));
-                    ws_prep<D, OUT>(p, sm.rec[kc & 1], w, lane_c, s_begin + 64 * kc, h, rows,
-                                    len_of(kc + 1));
-                    __syncthreads();
-                }
-                __syncthreads();
-            }
-        } else {
-            const int wr = w - kWsPrep<D>;
-            const int n16 = lane & 15, g = lane >> 4;
-            // this lane's state: key channels state_channel(rt, g, e), value
-            // column 32 wr + 16 (c % 2) + n16 of tile c
-            const int64_t sbase = (n * H + h) * D * D;
-            f32x4 S[NT][NCT];
-#pragma unroll
-            for (int c = 0; c < NT; ++c)
-#pragma unroll
-                for (int rt = 0; rt < NCT; ++rt) S[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // tiles from the identity: all of them (ZERO_V), or the M tiles (MAPS)
-#pragma unroll
-            for (int c = NV; c < NT; ++c)
-#pragma unroll
-                for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        S[c][rt][e] = state_channel(rt, g, e) == 32 * wr + 16 * (c % 2) + n16 ? 1.f : 0.f;
-            if (!ZERO_V && !MAPS && p.init) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[c][rt][e] = p.init[sbase + (int64_t)state_channel(rt, g, e) * D +
-                                                 32 * wr + 16 * c + n16];
-            }
-            // the state's loads complete here, once per chain
-#pragma unroll
-            for (int c = 0; c < NT; ++c)
-#pragma unroll
-                for (int rt = 0; rt < NCT; ++rt) asm volatile("" : "+v"(S[c][rt]));
-            if (nch > 0) {
-                bf16x8 v[4];
-                if constexpr (!ZERO_V) {
-                    ws_load_v<D>(p, s_begin, len_of(0), h, wr, lane, v);
-                    // step 0: nothing to run; V of chunk 0 to the tile
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        *reinterpret_cast<bf16x8*>(&sm.vt[16 * j + (lane >> 2)][32 * wr + 8 * (lane & 3)]) =
-                            v[j];
-                    ws_load_v<D>(p, s_begin + 64, len_of(1), h, wr, lane, v);
-                }
-                __syncthreads();
-                // step kc: the recurrence of chunk kc - 1 from record (kc - 1) % 2
-                for (int64_t kc = 1; kc <= nch; ++kc) {
-                    int lane_c = lane;
-                    asm volatile("" : "+v"(lane_c));
-                    const SubRecord<D>& rec = sm.rec[(kc - 1) & 1];
-#pragma unroll
-                    for (int Rb = 0; Rb < 4; ++Rb)
-                        ws_block<D, TPV, OUT, NT, NV>(rec, sm.vt, S, wr, lane_c, Rb);
-                    if constexpr (OUT)
-                        ws_flush<D, TPV>(p, sm.vt, s_begin + 64 * (kc - 1), len_of(kc - 1), h, wr, lane_c);
-                    if (!ZERO_V && kc < nch) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            *reinterpret_cast<bf16x8*>(
-                                &sm.vt[16 * j + (lane_c >> 2)][32 * wr + 8 * (lane_c & 3)]) = v[j];
-                        ws_load_v<D>(p, s_begin + 64 * (kc + 1), len_of(kc + 1), h, wr, lane_c, v);
-                    }
-                    __syncthreads();
-                }
-            }
-            if (p.fin) {
-#pragma unroll
-                for (int c = 0; c < NT; ++c) {
-                    float* f = c < 2 ? p.fin : p.fin2;
-#pragma unroll
-                    for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            f[sbase + (int64_t)state_channel(rt, g, e) * D + 32 * wr + 16 * (c % 2) + n16] =
-                                S[c][rt][e];
-                }
+            int64_t b, len;
+            seg_bounds(seq_len, Q, s, b, len);
+            const int64_t sb = (seq * H + h) * DD;                      // [N, H, D, D]
+            const auto slot = [&](int k) { return ((seq * (Q + 1) + k) * H + h) * DD; };
+            if constexpr (KIND == kWsSegFirst) {
+                if (s == 0)
+                    ws_chain<D, true, false>(p, sm, w, lane, h, seq_begin + b, len,
+                                             p.init ? p.init + sb : nullptr, p.st + slot(1), nullptr);
+                else
+                    ws_chain<D, false, true>(p, sm, w, lane, h, seq_begin + b, len, nullptr,
+                                             p.fin + slot(s), p.fin2 + slot(s));
+            } else {
+                ws_chain<D, true, false>(p, sm, w, lane, h, seq_begin + b, len, p.st + slot(s),
+                                         (s == Q && p.fin) ? p.fin + sb : nullptr, nullptr);
             }
         }
     }
@@ -1120,11 +1169,14 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
 // of a sequence maps its start state to its end state as S_end = M_p S_start +
 // b_p (the recurrence is affine in the state, linear in its key rows); M_p is
 // the segment run from the identity with V = 0, b_p the segment run from the
-// zero state.  One workgroup per (16-column tile, head, sequence) walks the
-// segments in order, S <- M_p S + b_p from the initial state (zero when
-// `init` is null), storing the state before each segment to `start` and the
-// one after the last to `fin` (when not null).  Maps and starts are
-// [sequence * P + segment][H][D][D], fp32.
+// zero state.  One workgroup per (16-column tile, head, sequence), the eight
+// tiles of a (sequence, head) on one XCD so that they read M_p from one L2
+// (workgroup b: chain 8 (b / 64) + b % 8, tile (b / 8) % 8), walks
+// segments p0 .. p0 + cnt - 1 in order, S <- M_p S + b_p from the state
+// `init` (zero when null), storing the state before each segment to `start`
+// and the one after the last to `fin` (when not null).  Maps and starts are
+// [sequence * slots + p][H][D][D] fp32; init and fin hold a [H][D][D] block
+// every init_stride and fin_stride elements.
 //
 // Each step is a 128 x 128 by 128 x 16 product on fp32 MFMA (16x16x4): wave w
 // takes rows 32 w .. 32 w + 31 (two row tiles); lane (r, kg) = (lane % 16,
@@ -1134,30 +1186,32 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
 // of the next segment's M are loaded while the current one is multiplied.
 // The summation order is fixed, so the result does not depend on the launch.
 template <int D>
-__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ init,
-                                                           const float* __restrict__ Mm,
-                                                           const float* __restrict__ bm,
-                                                           float* __restrict__ start,
-                                                           float* __restrict__ fin, int32_t H,
-                                                           int32_t P) {
-    static_assert(D == 128, "four waves of two 16-row tiles");
+__global__ __launch_bounds__(256) void segment_scan_kernel(
+    const float* __restrict__ init, int64_t init_stride, const float* __restrict__ Mm,
+    const float* __restrict__ bm, float* __restrict__ start, float* __restrict__ fin,
+    int64_t fin_stride, int32_t n_seqs, int32_t H, int32_t slots, int32_t p0, int32_t cnt) {
+    static_assert(D == 128, "four waves of two 16-row tiles; eight column tiles");
     constexpr int SP = D + 4;  // row pitch of the transposed tile (floats)
     __shared__ __align__(16) float St[16][SP];
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, r = lane & 15, kg = lane >> 4;
-    const int64_t h = blockIdx.y, n = blockIdx.z;
-    const int col0 = 16 * blockIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t chain = 8 * (b / 64) + b % 8;
+    if (chain >= (int64_t)n_seqs * H) return;  // (the whole workgroup: no barrier is skipped)
+    const int64_t n = chain / H, h = chain % H;
+    const int col0 = 16 * (int)((b / 8) % 8);
     // this lane's output elements: rows 32 w + 16 j + 4 kg + v, column col0 + r
     const auto out_off = [&](int j, int v) { return (int64_t)(32 * w + 16 * j + 4 * kg + v) * D + col0 + r; };
-    const int64_t sbase = (n * H + h) * D * D;
+    const auto map_base = [&](int p) { return ((n * slots + p) * H + h) * D * D; };
     f32x4 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[j][v] = init ? init[sbase + out_off(j, v)] : 0.f;
+        for (int v = 0; v < 4; ++v)
+            acc[j][v] = init ? init[n * init_stride + h * D * D + out_off(j, v)] : 0.f;
     // A operands of segment p: M_p[32 w + 16 j + r][32 kg .. 32 kg + 31]
     float4 Ma[2][8];
     const auto load_m = [&](int p, float4 (&m)[2][8]) {
-        const float* base = Mm + ((n * P + p) * H + h) * D * D;
+        const float* base = Mm + map_base(p);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float4* row = reinterpret_cast<const float4*>(base + (int64_t)(32 * w + 16 * j + r) * D + 32 * kg);
@@ -1165,9 +1219,9 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
             for (int i = 0; i < 8; ++i) m[j][i] = row[i];
         }
     };
-    if (P > 0) load_m(0, Ma);
-    for (int p = 0; p < P; ++p) {
-        const int64_t mb = ((n * P + p) * H + h) * D * D;
+    if (cnt > 0) load_m(p0, Ma);
+    for (int p = p0; p < p0 + cnt; ++p) {
+        const int64_t mb = map_base(p);
         // the state before segment p: to `start`, and transposed into LDS
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1181,7 +1235,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
 #pragma unroll
             for (int v = 0; v < 4; ++v) bv[j][v] = bm[mb + out_off(j, v)];
         float4 Mn[2][8];
-        if (p + 1 < P) load_m(p + 1, Mn);
+        if (p + 1 < p0 + cnt) load_m(p + 1, Mn);
         __syncthreads();
         // B operands: S[32 kg .. 32 kg + 31][column r]
         float4 Sb[8];
@@ -1200,7 +1254,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
             }
             acc[j] = c;
         }
-        if (p + 1 < P) {
+        if (p + 1 < p0 + cnt) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1211,7 +1265,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) fin[sbase + out_off(j, v)] = acc[j][v];
+            for (int v = 0; v < 4; ++v) fin[n * fin_stride + h * D * D + out_off(j, v)] = acc[j][v];
     }
 }
 
@@ -1224,7 +1278,7 @@ hipError_t fused_blocks_per_cu(int* out) {
     if (c <= 0) {
         hipError_t e;
         if constexpr (kSpecialised<D>)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_ws_kernel<D>,
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_ws_kernel<D, kWsPlain>,
                                                              64 * (kWsPrep<D> + kWsRec<D>), 0);
         else
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, fused_kernel<D>, D * 4, 0);
@@ -1270,7 +1324,7 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
     const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
     const int grid = (int)std::min<int64_t>(chains, cus * per_cu);
     if constexpr (kSpecialised<D>)
-        hipLaunchKernelGGL((fused_ws_kernel<D>), dim3(grid), dim3(64 * (kWsPrep<D> + kWsRec<D>)), 0,
+        hipLaunchKernelGGL((fused_ws_kernel<D, kWsPlain>), dim3(grid), dim3(64 * (kWsPrep<D> + kWsRec<D>)), 0,
                            stream, fp);
     else
         hipLaunchKernelGGL((fused_kernel<D>), dim3(grid), dim3(D * 4), 0, stream, fp);
@@ -1281,20 +1335,18 @@ template hipError_t launch_fused<128>(const PrefillArgs&, hipStream_t);
 template hipError_t launch_fused<64>(const PrefillArgs&, hipStream_t);
 
 size_t segmented_scratch_bytes(const PrefillArgs& a, int P) {
-    return 3 * (size_t)a.n_seqs * P * a.n_heads * a.d * a.d * sizeof(float);
+    // b, M and the start states of P + 1 segments per sequence and head
+    return 3 * (size_t)a.n_seqs * (P + 1) * a.n_heads * a.d * a.d * sizeof(float);
 }
 
 hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     constexpr int D = 128;
-    if (!a.bf16 || a.d != D || P < 1) return hipErrorInvalidValue;
+    if (!a.bf16 || a.d != D || P < 2) return hipErrorInvalidValue;
     const int64_t N = a.n_seqs, H = a.n_heads;
-    // segments of whole chunks; the last of each sequence is shorter.  With
-    // cu_seqlens the kernel cuts each sequence into P itself (segments past a
-    // short sequence's end are empty: M = I, b = 0)
-    const int64_t seq_len = a.cu_seqlens ? 0 : a.total_tokens / N;
-    const int64_t seg_len = a.cu_seqlens ? 0 : ((seq_len + P - 1) / P + 63) / 64 * 64;
-    const int Pe = a.cu_seqlens ? P : (int)((seq_len + seg_len - 1) / seg_len);
-    const size_t map_elems = (size_t)N * Pe * H * D * D;
+    // P chains per sequence and head in each pass, P + 1 segments (placed by
+    // seg_bounds in the kernel, from each sequence's length)
+    const int64_t slots = P + 1;
+    const size_t map_elems = (size_t)N * slots * H * D * D;
     float* Mm = reinterpret_cast<float*>(a.workspace + a.layout.records_offset());
     float* bm = Mm + map_elems;
     float* st = bm + map_elems;
@@ -1307,44 +1359,46 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     fp.cu = a.cu_seqlens;
     fp.order = nullptr;
     fp.counter = reinterpret_cast<int32_t*>(a.workspace);
-    fp.total_tokens = a.cu_seqlens ? a.total_tokens : N * seq_len;
-    fp.n_seqs = (int32_t)(N * Pe);
+    fp.total_tokens = a.total_tokens;
+    fp.n_seqs = (int32_t)(N * P);
     fp.n_heads = (int32_t)H;
     fp.scale = a.scale;
     fp.l2norm = a.l2norm;
-    fp.seg_len = seg_len;
-    fp.seg_per_seq = Pe;
+    fp.seg_per_seq = P;
+    fp.st = st;
+    fp.out = static_cast<bf16*>(a.out);
     int per_cu = 1;
     hipError_t e = fused_blocks_per_cu<D>(&per_cu);
     if (e != hipSuccess) return e;
     const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
-    const int grid = (int)std::min<int64_t>(N * Pe * H, cus * per_cu);
+    const int grid = (int)std::min<int64_t>(N * P * H, cus * per_cu);
     const dim3 block(64 * (kWsPrep<D> + kWsRec<D>));
     const auto reset = [&]() {
         hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, nullptr, 0, nullptr,
                            fp.counter);
         return hipGetLastError();
     };
-    // every segment's map in one pass, no outputs: the affine parts b from
-    // the zero state, the linear parts M from the identity with V = 0
-    fp.init = nullptr;
+    // segment 0 with its outputs, from the initial state to start slot 1,
+    // beside the maps of segments 1..P-1 (b from the zero state, M from the
+    // identity with V = 0)
+    fp.init = a.initial_state;
     fp.fin = bm;
     fp.fin2 = Mm;
-    fp.out = nullptr;
     if ((e = reset()) != hipSuccess) return e;
-    hipLaunchKernelGGL((fused_ws_kernel<D, false, false, true, true>), dim3(grid), block, 0, stream, fp);
+    hipLaunchKernelGGL((fused_ws_kernel<D, kWsSegFirst>), dim3(grid), block, 0, stream, fp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the start states of segments 2..P from that of segment 1
+    const int64_t scan_blocks = 64 * ((N * H + 7) / 8);
+    hipLaunchKernelGGL((segment_scan_kernel<D>), dim3((unsigned)scan_blocks), dim3(256), 0, stream,
+                       st + H * D * D, slots * H * D * D, Mm, bm, st, st + P * H * D * D,
+                       slots * H * D * D, (int32_t)N, (int32_t)H, (int32_t)slots, 1, P - 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // segments 1..P with their outputs; the last writes the final state
+    fp.init = nullptr;
+    fp.fin = a.final_state;
     fp.fin2 = nullptr;
-    // every segment's start state, and the final states
-    hipLaunchKernelGGL((segment_scan_kernel<D>), dim3(D / 16, (unsigned)H, (unsigned)N), dim3(256), 0,
-                       stream, a.initial_state, Mm, bm, st, a.final_state, (int32_t)H, (int32_t)Pe);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // the outputs: every segment again from its start state
-    fp.init = st;
-    fp.fin = nullptr;
-    fp.out = static_cast<bf16*>(a.out);
     if ((e = reset()) != hipSuccess) return e;
-    hipLaunchKernelGGL((fused_ws_kernel<D, true, false, true>), dim3(grid), block, 0, stream, fp);
+    hipLaunchKernelGGL((fused_ws_kernel<D, kWsSegOut>), dim3(grid), block, 0, stream, fp);
     return hipGetLastError();
 }
 

@@ -138,45 +138,47 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// A prefill takes the fused kernel (persistent workgroups working through
-// whole (sequence, head) chains) instead of the preparation and recurrence
-// kernels once it has at least one chain per kFusedCUsPerChain compute units
-// (d = 128; per two at d = 64).  Measured at d = 128 against the two-kernel
-// time (256 CUs): 8,192-token sequences, 64 chains 1.15x, 86 chains 0.86x,
-// 128 chains 0.73x, 256 chains 0.42x; 65,536-token sequences, 80 chains 0.95x,
-// 96 chains 0.86x, 112 chains 0.68x.  At d = 64, 128 chains 0.94x.
+// A prefill the segmented path does not take runs the fused kernel
+// (persistent workgroups working through whole (sequence, head) chains)
+// instead of the preparation and recurrence kernels once it has at least one
+// chain per kFusedCUsPerChain compute units (d = 128; per two at d = 64).
+// Measured at d = 128 against the two-kernel time (256 CUs): 8,192-token
+// sequences, 64 chains 1.15x, 86 chains 0.86x, 128 chains 0.73x, 256 chains
+// 0.42x; 65,536-token sequences, 80 chains 0.95x, 96 chains 0.86x, 112 chains
+// 0.68x.  At d = 64, 128 chains 0.94x.
 constexpr int64_t kFusedCUsPerChain = 3;
 constexpr int64_t kFusedCUsPerChain64 = 2;
 
-// Whether launch_prefill takes the fused kernel for these arguments.  The
+// Whether the fused kernel takes a call the segmented path does not.  The
 // environment variable KDA_PREFILL_PATH=split or =fused overrides the choice
-// where the fused kernel applies.
+// where the fused kernel applies (=segmented rules it out).
 bool fused_path(const PrefillArgs& a);
 
-// Segmented prefill of few long chains (d = 128, bf16, plain options): every
-// sequence is cut into P segments (by the kernel, from cu_seqlens), the
-// fused kernel forms each segment's state map from the zero state and from
-// the identity, a scan composes the maps into every segment's start state, and
-// the fused kernel runs the segments again from those states for the outputs.
+// Segmented prefill of long chains (d = 128, bf16, plain options): with P
+// chains per sequence and head in each pass, every sequence is cut (by the
+// kernel, from cu_seqlens) into P + 1 segments; a first pass runs segment 0
+// with its outputs and forms the state maps of segments 1..P-1 from the zero
+// state and from the identity, a scan composes the maps into the start states
+// of segments 2..P, and a second pass runs segments 1..P with their outputs.
 // segmented_segments gives P, or 0 where the path does not apply or would not
 // pay (KDA_PREFILL_PATH=segmented forces it where it applies, and
-// KDA_PREFILL_SEGMENTS=<P> sets P).  Its three [N P, H, d, d] fp32 arrays take
-// segmented_scratch_bytes of the workspace's record area.
+// KDA_PREFILL_SEGMENTS=<P> sets P).  Its three [N (P + 1), H, d, d] fp32
+// arrays take segmented_scratch_bytes of the workspace's record area.
 int segmented_segments(const PrefillArgs& a);
 size_t segmented_scratch_bytes(const PrefillArgs& a, int P);
 hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream);
-// P is one segment chain per compute unit, at most kSegMaxSegments, with
-// segments of at least kSegMinChunks chunks.  The path is taken automatically
-// (where the fused kernel is not) with at least kSegMinSegments segments whose
-// chains fill three quarters of the device, or with kSegManySegments or more.
-// Measured at d = 128 on 256 CUs, time against the two-kernel path:
-// 2^20 tokens x 16 heads 0.61x, x 32 heads 0.82x; 2^16 x 64 heads 0.80x;
-// 2^16 x 8 heads (32 segments of 32 chunks) 0.65x; 2^16 x 80 heads (3
-// segments) 0.78x; 8,192 tokens x 80 heads (3 segments) 0.80x; 8,192 tokens x
-// 32 heads with 4 segments 1.6x (not taken).
-constexpr int64_t kSegMinChunks = 32;
+// P is one chain per compute unit in each pass, at most kSegMaxSegments,
+// lowered until segments 1..P hold at least kSegMinChunks chunks.  The path is
+// taken automatically with P >= 2 whose chains fill three quarters of the
+// device, or with kSegManySegments or more, or where the fused kernel would
+// take the call (it then runs a chain per CU at most).  Measured at d = 128 on
+// 256 CUs, time against the best other path: 2^20 tokens x 16 heads 0.53x
+// (two-kernel); 8,192 tokens x 96 heads (P = 2) 0.83x and 2^16 x 96 heads
+// 0.73x (fused); 8,192 x 32 heads (P = 8, 14-chunk segments) 0.87x and x 64
+// heads (P = 4) 0.70x (two-kernel); 4,096 x 32 heads (P = 8, 7-chunk
+// segments) 1.16x and 2,048 x 128 heads (P = 2, 11 chunks) 1.16x (not taken).
+constexpr int64_t kSegMinChunks = 12;
 constexpr int kSegMaxSegments = 64;
-constexpr int64_t kSegMinSegments = 3;
 constexpr int64_t kSegManySegments = 16;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -4,8 +4,9 @@
 * a prefill given no workspace (the library allocates one on the stream),
   bitwise equal to the same call with a caller workspace;
 * launches split along the grid's y dimension: a prefill with more than 65,535
-  chunk slots and a decode step over more than 65,535 sequences, against the
-  oracle.
+  chunk slots (on the two-kernel path, forced, and on the fused kernel its
+  chain count picks) and a decode step over more than 65,535 sequences,
+  against the oracle.
 """
 
 import sys
@@ -124,13 +125,20 @@ def test_library_workspace_equals_caller_workspace(lib, lens, heads):
     assert torch.equal(o1, o3) and torch.equal(f1, f3)
 
 
-def test_prefill_more_than_65535_chunk_slots(lib, oracle):
+@pytest.mark.parametrize("path", ["split", "auto"])
+def test_prefill_more_than_65535_chunk_slots(lib, oracle, monkeypatch, path):
     """65,600 one-token sequences plus one of 1,000 tokens: 66,641 chunk slots,
-    so the preparation is launched in two grid ranges."""
+    so the preparation is launched in two grid ranges (the two-kernel path,
+    forced: its 131,202 chains would take the fused kernel, which the second
+    case runs)."""
     from kda_inputs import make_prefill
+    if path == "split":
+        monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+    else:
+        monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
     lens = [1] * 65600 + [1000]
     inp = make_prefill(lens, 2, 64, "bf16", g_scale=0.5, s0_std=0.02, seed=406, device="cuda")
-    check(lib, oracle, inp, "66,641 chunk slots")
+    check(lib, oracle, inp, f"66,641 chunk slots, {path}")
 
 
 def test_decode_more_than_65535_sequences(lib, oracle):

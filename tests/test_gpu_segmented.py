@@ -1,15 +1,16 @@
 """GPU tests of the segmented prefill: a long sequence with few heads is cut
-into segments; the fused kernel forms every segment's state map S_end = M S_start
-+ b (b from the zero state, M from the identity with V = 0), a scan composes the
-maps into each segment's start state, and the fused kernel runs the segments
-again from those states for the outputs.
+into P + 1 segments.  A first pass of the fused kernel runs segment 0 with its
+outputs from the initial state and forms the state maps S_end = M S_start + b
+of segments 1..P-1 (b from the zero state, M from the identity with V = 0); a
+scan composes them into the start states of segments 2..P; a second pass runs
+segments 1..P from their start states with their outputs.
 
 * Parity with the fp64 oracle at the bf16 bar (max abs error 2e-2, every
-  output finite): one ragged sequence cut into 4 segments (the last shorter,
-  ending in a partial chunk), packed sequences with empty segments and an
+  output finite): one ragged sequence (P = 4, the last segment ending in a
+  partial chunk), packed sequences with empty segments and an
   empty sequence, equal lengths without cu_seqlens, decay strong
   enough for the exact diagonal products, channels of all three decay
-  regimes, no initial and no final state, 64 segments (the most).
+  regimes, no initial and no final state, P = 64 (the most).
 * Agreement with the two-kernel path within twice that bar where the oracle
   would be slow: the automatic choice on a 262,144-token sequence with 8 heads.
 * Bitwise: two runs of the same call, the library-allocated workspace, a
@@ -17,8 +18,7 @@ again from those states for the outputs.
   two-kernel), the final state written over the initial state on a side
   stream, and graph replays of the segmented and the fused path.
 
-KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS the
-segment count.
+KDA_PREFILL_PATH=segmented forces the path and KDA_PREFILL_SEGMENTS sets P.
 """
 
 import sys
@@ -99,8 +99,8 @@ def oracle_check(oracle, inp, out, fin, label):
 
 
 def test_ragged_sequence(lib, oracle, monkeypatch):
-    """16,421 tokens (257 chunks, the last partial) x 2 heads in 4 segments of
-    4,160 tokens; the last segment is 3,941."""
+    """16,421 tokens (257 chunks, the last partial) x 2 heads, P = 4: segment
+    0 of 57 chunks, then four of 50 (the last ending in the partial chunk)."""
     from kda_inputs import make_prefill
     inp = make_prefill([16421], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=601,
                        device="cuda")
@@ -109,9 +109,10 @@ def test_ragged_sequence(lib, oracle, monkeypatch):
 
 
 def test_packed_sequences(lib, oracle, monkeypatch):
-    """Four packed sequences of 200, 20,000, 0 and 9,000 tokens cut into 8
-    segments each on the device: the short one leaves four segments empty
-    (their maps M = I, b = 0) and the empty one keeps its initial state."""
+    """Four packed sequences of 200, 20,000, 0 and 9,000 tokens, P = 8, cut
+    into 9 segments each on the device: the short one leaves segment 0 and
+    four others empty (their maps M = I, b = 0) and the empty one keeps its
+    initial state."""
     from kda_inputs import make_prefill
     lens = [200, 20000, 0, 9000]
     inp = make_prefill(lens, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=610, device="cuda")
@@ -122,7 +123,7 @@ def test_packed_sequences(lib, oracle, monkeypatch):
 
 
 def test_equal_lengths_without_cu(lib, oracle, monkeypatch):
-    """Three 8,192-token sequences without cu_seqlens, 3 segments each."""
+    """Three 8,192-token sequences without cu_seqlens, P = 3."""
     from kda_inputs import make_prefill
     inp = make_prefill([8192] * 3, 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=602,
                        device="cuda", packed_cu=False)
@@ -174,8 +175,8 @@ def test_no_initial_no_final_state(lib, oracle, monkeypatch):
 
 
 def test_sixty_four_segments(lib, oracle, monkeypatch):
-    """32,768 tokens x 2 heads in 64 segments of 8 chunks: the scan composes
-    the most maps a call can have."""
+    """32,768 tokens x 2 heads with P = 64: an empty segment 0 and 64 of 8
+    chunks; the scan composes the most maps a call can have."""
     from kda_inputs import make_prefill
     inp = make_prefill([32768], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=611,
                        device="cuda")
@@ -223,10 +224,10 @@ def test_auto_choice_long_sequence(lib, monkeypatch):
 
 
 def test_path_choice(lib, monkeypatch):
-    """The rule on a 256-CU device, where the fused kernel does not apply (it
-    takes a chain per 3 CUs at d = 128): P = one segment chain per CU (at most
-    64), segments of at least 32 chunks; taken with P >= 3 whose chains fill
-    3/4 of the CUs, or with P >= 16."""
+    """The rule on a 256-CU device: P = one chain per CU in each pass (at most
+    64), lowered until segments hold at least 12 chunks; taken with P >= 2
+    whose chains fill 3/4 of the CUs, or with P >= 16, or where the fused
+    kernel (a chain per 3 CUs at d = 128) would take the call."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the thresholds below are for 256 compute units")
     monkeypatch.delenv("KDA_PREFILL_PATH", raising=False)
@@ -234,29 +235,31 @@ def test_path_choice(lib, monkeypatch):
     K = lib.kda
     path = lambda T, N, H, packed=False, io=K.KDA_BF16, d=128: lib.kda_prefill_path(
         lib.make_dims(T, N, H, d, d, io), packed)
-    assert path(1 << 20, 1, 16) == (K.KDA_PATH_SEGMENTED, 16)      # the million-token workload
-    assert path(1 << 19, 1, 8) == (K.KDA_PATH_SEGMENTED, 32)
-    assert path(1 << 18, 1, 8) == (K.KDA_PATH_SEGMENTED, 32)       # 32 segments of 128 chunks
-    assert path(1 << 18, 1, 4) == (K.KDA_PATH_SEGMENTED, 64)       # 64 of 64 chunks
-    assert path(1 << 20, 1, 32) == (K.KDA_PATH_SEGMENTED, 8)
-    assert path(1 << 20, 1, 64) == (K.KDA_PATH_SEGMENTED, 4)
-    assert path(1 << 16, 1, 48) == (K.KDA_PATH_SEGMENTED, 5)       # 240 chains
-    assert path(1 << 16, 1, 80) == (K.KDA_PATH_SEGMENTED, 3)       # 240 chains
-    assert path(8192, 1, 80) == (K.KDA_PATH_SEGMENTED, 3)          # 3 of 42 chunks
-    assert path(4 * 4096, 4, 20)[0] == K.KDA_PATH_SPLIT             # P = 2: too few
-    assert path(1 << 16, 1, 86)[0] == K.KDA_PATH_FUSED              # a chain per 3 CUs
-    assert path(1 << 16, 1, 86, d=64)[0] == K.KDA_PATH_SPLIT        # d = 64: per 2 CUs
-    assert path(1 << 20, 1, 2) == (K.KDA_PATH_SEGMENTED, 64)       # at most 64 segments
-    assert path(1 << 16, 1, 1) == (K.KDA_PATH_SEGMENTED, 32)       # 32 of 32 chunks
-    assert path(1 << 14, 1, 16)[0] == K.KDA_PATH_SPLIT              # P = 8: 128 chains, too few
-    assert path(8192, 1, 4)[0] == K.KDA_PATH_SPLIT                  # P = 4: too few
-    assert path(1 << 20, 1, 16, packed=True) == (K.KDA_PATH_SEGMENTED, 16)  # cu = [0, T]
-    assert path(1 << 20, 2, 8)[0] == K.KDA_PATH_SEGMENTED           # equal lengths, no cu
-    assert path(1 << 20, 2, 8, packed=True)[0] == K.KDA_PATH_SEGMENTED  # cut on the device
+    SEG, FUSED, SPLIT = K.KDA_PATH_SEGMENTED, K.KDA_PATH_FUSED, K.KDA_PATH_SPLIT
+    assert path(1 << 20, 1, 16) == (SEG, 16)         # the million-token workload
+    assert path(8192, 1, 32) == (SEG, 8)             # the 8,192-token workload: 14-chunk segments
+    assert path(1007721, 64, 32, packed=True)[0] == FUSED   # the packed headline: 2,048 chains
+    assert path(1 << 19, 1, 8) == (SEG, 32)
+    assert path(1 << 18, 1, 4) == (SEG, 64)          # at most 64
+    assert path(1 << 20, 1, 64) == (SEG, 4)
+    assert path(1 << 16, 1, 48) == (SEG, 5)          # 240 chains
+    assert path(1 << 16, 1, 80) == (SEG, 3)
+    assert path(4 * 4096, 4, 20, packed=True) == (SEG, 3)   # 16-chunk segments
+    assert path(1 << 16, 1, 86) == (SEG, 2)          # where the fused kernel would run
+    assert path(1 << 20, 1, 128) == (SEG, 2)
+    assert path(1 << 16, 1, 160)[0] == FUSED         # P = 1
+    assert path(2048, 1, 128)[0] == FUSED            # P = 2 would leave 11-chunk segments
+    assert path(1 << 16, 1, 1) == (SEG, 64)          # 16-chunk segments
+    assert path(1 << 14, 1, 16) == (SEG, 16)
+    assert path(4096, 1, 32)[0] == SPLIT             # P = 4 at most: 128 chains
+    assert path(8192, 1, 16)[0] == SPLIT             # P = 8 at most: 128 chains
+    assert path(8192, 1, 4)[0] == SPLIT
+    assert path(1 << 20, 2, 8)[0] == SEG             # equal lengths, no cu
+    assert path(1 << 20, 2, 8, packed=True)[0] == SEG  # cut on the device
+    assert path(1 << 20, 1, 16, packed=True) == (SEG, 16)   # cu = [0, T]
     assert path(1 << 20, 1, 16, io=K.KDA_FP32)[0] == K.KDA_PATH_PIPELINED  # bf16 only
     assert path(1 << 20, 1, 16, d=64)[0] == K.KDA_PATH_PIPELINED    # d = 128 only
-    assert path(8192, 1, 32)[0] == K.KDA_PATH_SPLIT                 # the 8,192-token workload
-    assert path(1007721, 64, 32, packed=True)[0] == K.KDA_PATH_FUSED
+    assert path(1 << 16, 1, 86, d=64)[0] == SPLIT    # d = 64: the fused kernel from 128
     monkeypatch.setenv("KDA_PREFILL_PATH", "split")
     assert path(1 << 20, 1, 16)[0] == K.KDA_PATH_PIPELINED
     monkeypatch.setenv("KDA_PREFILL_PATH", "segmented")

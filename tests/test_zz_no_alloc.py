@@ -41,10 +41,10 @@ def run_pair(lib, inp):
 
 
 @pytest.mark.parametrize("io,d,lens,heads", [
-    ("bf16", 128, [8192], 32),          # the two-kernel path
-    ("fp32", 64, [8192], 8),
+    ("bf16", 128, [8192], 32),          # segmented: 8 chains per head in each pass
+    ("fp32", 64, [8192], 8),            # the two-kernel path
     ("bf16", 128, [4096] * 16, 32),     # the fused kernel: 512 chains
-    ("bf16", 128, [16384], 32),         # segmented: 8 segments per head
+    ("bf16", 128, [16384], 32),         # segmented, 28-chunk segments
 ])
 def test_noalloc_equals_prefill_twice(lib, io, d, lens, heads):
     """The last two need far less of the array than kda_prefill_workspace_bytes
