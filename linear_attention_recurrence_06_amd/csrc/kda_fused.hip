@@ -1183,8 +1183,9 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
 // lane / 16) feeds, at product step s, A = M[row r][32 kg + s] and B =
 // S[32 kg + s][column r], so the 32 steps cover every k.  The tile's state
 // sits transposed in LDS (St[column][k]) for the B operands; the A operands
-// of the next segment's M are loaded while the current one is multiplied.
-// The summation order is fixed, so the result does not depend on the launch.
+// of the next segment's M, and its b, are loaded while the current one is
+// multiplied.  The summation order is fixed, so the result does not depend
+// on the launch.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(
     const float* __restrict__ init, int64_t init_stride, const float* __restrict__ Mm,
@@ -1208,9 +1209,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             acc[j][v] = init ? init[n * init_stride + h * D * D + out_off(j, v)] : 0.f;
-    // A operands of segment p: M_p[32 w + 16 j + r][32 kg .. 32 kg + 31]
+    // A operands of segment p, M_p[32 w + 16 j + r][32 kg .. 32 kg + 31], and
+    // this lane's elements of b_p
     float4 Ma[2][8];
-    const auto load_m = [&](int p, float4 (&m)[2][8]) {
+    f32x4 bv[2];
+    const auto load_m = [&](int p, float4 (&m)[2][8], f32x4 (&bb)[2]) {
         const float* base = Mm + map_base(p);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1218,8 +1221,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) m[j][i] = row[i];
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bb[j][v] = bm[map_base(p) + out_off(j, v)];
     };
-    if (cnt > 0) load_m(p0, Ma);
+    if (cnt > 0) load_m(p0, Ma, bv);
     for (int p = p0; p < p0 + cnt; ++p) {
         const int64_t mb = map_base(p);
         // the state before segment p: to `start`, and transposed into LDS
@@ -1229,36 +1236,42 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
             for (int v = 0; v < 4; ++v) start[mb + out_off(j, v)] = acc[j][v];
             *reinterpret_cast<f32x4*>(&St[r][32 * w + 16 * j + 4 * kg]) = acc[j];
         }
-        f32x4 bv[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) bv[j][v] = bm[mb + out_off(j, v)];
         float4 Mn[2][8];
-        if (p + 1 < p0 + cnt) load_m(p + 1, Mn);
+        f32x4 bn[2];
+        if (p + 1 < p0 + cnt) load_m(p + 1, Mn, bn);
         __syncthreads();
         // B operands: S[32 kg .. 32 kg + 31][column r]
         float4 Sb[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) Sb[i] = *reinterpret_cast<const float4*>(&St[r][32 * kg + 4 * i]);
         __syncthreads();  // every wave has its B operands; St is free for the next step
+        // four independent accumulators per row tile (k in 32 kg + 8 q ..
+        // 32 kg + 8 q + 7, q = 0..3), so the products do not wait on one
+        // another; summed in a fixed order
+        f32x4 c[2][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 c = bv[j];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].x, Sb[i].x, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].y, Sb[i].y, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].z, Sb[i].z, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].w, Sb[i].w, c, 0, 0, 0);
+            for (int q = 0; q < 4; ++q) c[j][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4& cq = c[j][i / 2];
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].x, Sb[i].x, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].y, Sb[i].y, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].z, Sb[i].z, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].w, Sb[i].w, cq, 0, 0, 0);
             }
-            acc[j] = c;
-        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = bv[j] + ((c[j][0] + c[j][1]) + (c[j][2] + c[j][3]));
         if (p + 1 < p0 + cnt) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) Ma[j][i] = Mn[j][i];
+                bv[j] = bn[j];
+            }
         }
     }
     if (fin) {
