@@ -66,6 +66,7 @@ def test_workspace_bytes(kda):
     # a rejected descriptor has no pipeline segment count and no path
     assert kda.kda_prefill_pipeline_segments(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == -1
     assert kda.kda_prefill_path(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16))[0] == -1
+    assert kda.kda_prefill_path_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     # unsupported descriptors size to 0
     assert kda.kda_prefill_workspace_bytes(kda.make_dims(64, 1, 1, 96, 96, kda.KDA_BF16)) == 0
     # fp32 I/O at d = 128: the same record with 4-byte elements

@@ -158,9 +158,14 @@ def test_prefill_no_decay(lib, oracle):
 
 # ----------------------------------------------------------------------------- prefill, full sizes
 def test_prefill_config1(lib, oracle):
-    """T=8192, H=32, d=128, bf16: every head against the oracle."""
+    """T=8192, H=32, d=128, bf16: every head against the oracle, on the path
+    the library picks (segmented, 8 chains per head in each pass, on 256
+    CUs)."""
     from kda_inputs import make_config_prefill
     inp = make_config_prefill(1, device="cuda")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        path = lib.kda_prefill_path(lib.make_dims(8192, 1, 32, 128, 128, lib.kda.KDA_BF16))
+        assert path == (lib.kda.KDA_PATH_SEGMENTED, 8)
     say("config1: inputs ready")
     run_prefill_case(lib, oracle, inp, label="config1")
 
