@@ -213,7 +213,8 @@ int32_t kda_prefill_pipeline_segments(const kda_dims* dims);
  * device (see Kernels at kda_chunk_prefill), outside stream capture, with
  * cu_seqlens given (packed != 0) or NULL and out aligned to 16 bytes; the
  * environment overrides of that paragraph apply.  *segments (when not NULL)
- * receives the pipeline or segment count (0 for the other paths).  Returns -1
+ * receives the pipeline's segment count, or P of a segmented call (P + 1
+ * segments; 0 for the other paths).  Returns -1
  * for a descriptor the library would reject or a device that cannot be
  * queried.  Reads no device memory.  A diagnostic, for benchmarks and tests. */
 typedef enum {
