@@ -174,6 +174,34 @@ def test_no_initial_no_final_state(lib, oracle, monkeypatch):
     oracle_check(oracle, inp, out, None, "no states")
 
 
+def test_two_chains_per_pass(lib, oracle, monkeypatch):
+    """9,000 tokens x 2 heads with P = 2: segment 0 beside a single map in the
+    first pass, a one-step scan, segments 1 and 2 in the second."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([9000], 2, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=614,
+                       device="cuda")
+    out, fin = near_split(lib, monkeypatch, inp, "P = 2", segments=2)
+    oracle_check(oracle, inp, out, fin, "P = 2")
+
+
+def test_auto_choice_many_heads(lib, monkeypatch):
+    """8,192 tokens x 96 heads: where the fused kernel would run a chain per CU,
+    the automatic choice on a 256-CU device is P = 2; checked against the
+    two-kernel path and bitwise against the forced path."""
+    from kda_inputs import make_prefill
+    inp = make_prefill([8192], 96, 128, "bf16", g_scale=0.5, s0_std=0.02, seed=615,
+                       device="cuda")
+    o_a, f_a = run(lib, monkeypatch, inp, "auto")
+    o_s, f_s = run(lib, monkeypatch, inp, "split")
+    eo, ef = maxerr(host(o_a), host(o_s)), maxerr(host(f_a), host(f_s))
+    say(f"[auto 8,192 x 96] vs split: out {eo:.3e} state {ef:.3e}")
+    assert torch.isfinite(o_a.float()).all() and torch.isfinite(f_a).all()
+    assert eo <= 2 * TOL and ef <= 2 * TOL
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        o_g, f_g = run(lib, monkeypatch, inp, "segmented", 2)
+        assert torch.equal(o_g, o_a) and torch.equal(f_g, f_a)
+
+
 def test_sixty_four_segments(lib, oracle, monkeypatch):
     """32,768 tokens x 2 heads with P = 64: an empty segment 0 and 64 of 8
     chunks; the scan composes the most maps a call can have."""
