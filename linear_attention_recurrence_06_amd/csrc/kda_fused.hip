@@ -590,6 +590,8 @@ constexpr int kWsRec = D / 32;
 // A preparation wave's inputs: q, k, g of token 16 R + lane % 16 over the
 // lane's 8 channels of each of the D / 32 slices (channels 32 ks + 8 (lane /
 // 16) ..), and beta (zero-extended, as in ChunkRows).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct BlockRows {
     bf16x8 q[D / 32], k[D / 32], g[D / 32];
@@ -657,16 +659,19 @@ __device__ __forceinline__ void ws_prep(const FusedParams& p, SubRecord<D>& rec,
             }
     // g and beta are read: request the next chunk's
     ws_load_rows<D, 1, QROWS>(p, tok0 + 64, next_len, h, R, lane, rows);
+    // the norms' sums of squares, two channels per step (bf16 pairs)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float qx = QROWS ? to_f32(rows.q[2 * hf + kk][i]) : 0.f;
-                const float kx = to_f32(rows.k[2 * hf + kk][i]);
-                sq[hf] += qx * qx;
-                sk[hf] += kx * kx;
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (QROWS) {
+                    const bf16x2 qx = {rows.q[2 * hf + kk][2 * i], rows.q[2 * hf + kk][2 * i + 1]};
+                    sq[hf] = __builtin_amdgcn_fdot2_f32_bf16(qx, qx, sq[hf], false);
+                }
+                const bf16x2 kx = {rows.k[2 * hf + kk][2 * i], rows.k[2 * hf + kk][2 * i + 1]};
+                sk[hf] = __builtin_amdgcn_fdot2_f32_bf16(kx, kx, sk[hf], false);
             }
         sq[hf] += xor_shfl(sq[hf], 16);
         sq[hf] += xor_shfl(sq[hf], 32);
@@ -1180,8 +1185,8 @@ __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __rest
 //
 // Each step is a 128 x 128 by 128 x 16 product on fp32 MFMA (16x16x4): wave w
 // takes rows 32 w .. 32 w + 31 (two row tiles); lane (r, kg) = (lane % 16,
-// lane / 16) feeds, at product step s, A = M[row r][32 kg + s] and B =
-// S[32 kg + s][column r], so the 32 steps cover every k.  The tile's state
+// lane / 16) feeds, at product step 4 i + e, A = M[row r][16 i + 4 kg + e]
+// and B = S[16 i + 4 kg + e][column r], so the 32 steps cover every k.  The tile's state
 // sits transposed in LDS (St[column][k]) for the B operands; the A operands
 // of the next segment's M, and its b, are loaded while the current one is
 // multiplied.  The summation order is fixed, so the result does not depend
@@ -1209,25 +1214,27 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             acc[j][v] = init ? init[n * init_stride + h * D * D + out_off(j, v)] : 0.f;
-    // A operands of segment p, M_p[32 w + 16 j + r][32 kg .. 32 kg + 31], and
-    // this lane's elements of b_p
-    float4 Ma[2][8];
-    f32x4 bv[2];
+    // A operands of segment p: M_p[32 w + 16 j + r][16 i + 4 kg .. 16 i + 4 kg + 3]
+    // for i = 0..7 (the four lanes of a row read 64 contiguous bytes per load),
+    // and this lane's elements of b_p
     const auto load_m = [&](int p, float4 (&m)[2][8], f32x4 (&bb)[2]) {
         const float* base = Mm + map_base(p);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float4* row = reinterpret_cast<const float4*>(base + (int64_t)(32 * w + 16 * j + r) * D + 32 * kg);
+            const float4* row = reinterpret_cast<const float4*>(base + (int64_t)(32 * w + 16 * j + r) * D);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m[j][i] = row[i];
+            for (int i = 0; i < 8; ++i) m[j][i] = row[4 * i + kg];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) bb[j][v] = bm[map_base(p) + out_off(j, v)];
     };
-    if (cnt > 0) load_m(p0, Ma, bv);
-    for (int p = p0; p < p0 + cnt; ++p) {
+    // segment p with its operands in (m, bb), the next segment's loaded into
+    // (mn, bn) meanwhile; the two sets alternate, so no loaded value is
+    // copied (a copy would wait for the load in the middle of the products)
+    const auto step = [&](int p, const float4 (&m)[2][8], const f32x4 (&bb)[2], float4 (&mn)[2][8],
+                          f32x4 (&bn)[2]) {
         const int64_t mb = map_base(p);
         // the state before segment p: to `start`, and transposed into LDS
 #pragma unroll
@@ -1236,17 +1243,15 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
             for (int v = 0; v < 4; ++v) start[mb + out_off(j, v)] = acc[j][v];
             *reinterpret_cast<f32x4*>(&St[r][32 * w + 16 * j + 4 * kg]) = acc[j];
         }
-        float4 Mn[2][8];
-        f32x4 bn[2];
-        if (p + 1 < p0 + cnt) load_m(p + 1, Mn, bn);
+        if (p + 1 < p0 + cnt) load_m(p + 1, mn, bn);
         __syncthreads();
-        // B operands: S[32 kg .. 32 kg + 31][column r]
+        // B operands: S[16 i + 4 kg .. 16 i + 4 kg + 3][column r]
         float4 Sb[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Sb[i] = *reinterpret_cast<const float4*>(&St[r][32 * kg + 4 * i]);
+        for (int i = 0; i < 8; ++i) Sb[i] = *reinterpret_cast<const float4*>(&St[r][16 * i + 4 * kg]);
         __syncthreads();  // every wave has its B operands; St is free for the next step
-        // four independent accumulators per row tile (k in 32 kg + 8 q ..
-        // 32 kg + 8 q + 7, q = 0..3), so the products do not wait on one
+        // four independent accumulators per row tile (accumulator q takes the
+        // k of steps i = 2 q and 2 q + 1), so the products do not wait on one
         // another; summed in a fixed order
         f32x4 c[2][4];
 #pragma unroll
@@ -1258,22 +1263,23 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 f32x4& cq = c[j][i / 2];
-                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].x, Sb[i].x, cq, 0, 0, 0);
-                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].y, Sb[i].y, cq, 0, 0, 0);
-                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].z, Sb[i].z, cq, 0, 0, 0);
-                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(Ma[j][i].w, Sb[i].w, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(m[j][i].x, Sb[i].x, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(m[j][i].y, Sb[i].y, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(m[j][i].z, Sb[i].z, cq, 0, 0, 0);
+                cq = __builtin_amdgcn_mfma_f32_16x16x4f32(m[j][i].w, Sb[i].w, cq, 0, 0, 0);
             }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = bv[j] + ((c[j][0] + c[j][1]) + (c[j][2] + c[j][3]));
-        if (p + 1 < p0 + cnt) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) Ma[j][i] = Mn[j][i];
-                bv[j] = bn[j];
-            }
-        }
+        for (int j = 0; j < 2; ++j) acc[j] = bb[j] + ((c[j][0] + c[j][1]) + (c[j][2] + c[j][3]));
+    };
+    float4 Ma[2][8], Mb[2][8];
+    f32x4 ba[2], bb2[2];
+    if (cnt > 0) load_m(p0, Ma, ba);
+    int p = p0;
+    for (; p + 1 < p0 + cnt; p += 2) {
+        step(p, Ma, ba, Mb, bb2);
+        step(p + 1, Mb, bb2, Ma, ba);
     }
+    if (p < p0 + cnt) step(p, Ma, ba, Mb, bb2);
     if (fin) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
