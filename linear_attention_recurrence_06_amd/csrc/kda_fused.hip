@@ -1127,16 +1127,18 @@ constexpr bool kSpecialised = D == 128;
 // chains go in their natural order.
 constexpr int kOrderSortMax = 2048;
 
-// Zeroes the chain counter and writes the sequences in order of decreasing
-// length (ties by index): a bitonic sort of (length, index) keys in LDS by one
-// workgroup of 1024 threads, two keys each.
+// Zeroes the chain counter (and a second one when not null) and writes the
+// sequences in order of decreasing length (ties by index): a bitonic sort of
+// (length, index) keys in LDS by one workgroup of 1024 threads, two keys each.
 __global__ __launch_bounds__(1024) void chain_order_kernel(const int32_t* __restrict__ cu,
                                                            int32_t n_seqs,
                                                            int32_t* __restrict__ order,
-                                                           int32_t* __restrict__ counter) {
+                                                           int32_t* __restrict__ counter,
+                                                           int32_t* __restrict__ counter2) {
     __shared__ uint64_t key[kOrderSortMax];
     const int t = threadIdx.x;
     if (t == 0) *counter = 0;
+    if (t == 1 && counter2) *counter2 = 0;
     if (!cu || n_seqs > kOrderSortMax) {
         for (int i = t; i < n_seqs; i += 1024) order[i] = i;
         return;
@@ -1334,7 +1336,7 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
     fp.counter = reinterpret_cast<int32_t*>(a.workspace);
     fp.order = a.cu_seqlens ? order : nullptr;
     hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens,
-                       a.n_seqs, order, fp.counter);
+                       a.n_seqs, order, fp.counter, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int per_cu = 1;
@@ -1377,7 +1379,6 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     fp.beta = static_cast<const bf16*>(a.beta);
     fp.cu = a.cu_seqlens;
     fp.order = nullptr;
-    fp.counter = reinterpret_cast<int32_t*>(a.workspace);
     fp.total_tokens = a.total_tokens;
     fp.n_seqs = (int32_t)(N * P);
     fp.n_heads = (int32_t)H;
@@ -1392,18 +1393,19 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     const int64_t cus = a.compute_units > 0 ? a.compute_units : 256;
     const int grid = (int)std::min<int64_t>(N * P * H, cus * per_cu);
     const dim3 block(64 * (kWsPrep<D> + kWsRec<D>));
-    const auto reset = [&]() {
-        hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, nullptr, 0, nullptr,
-                           fp.counter);
-        return hipGetLastError();
-    };
+    // one chain counter per pass (the first two ints of the index area),
+    // both zeroed by one launch
+    int32_t* const counters = reinterpret_cast<int32_t*>(a.workspace);
+    hipLaunchKernelGGL(chain_order_kernel, dim3(1), dim3(1024), 0, stream, nullptr, 0, nullptr,
+                       counters, counters + 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     // segment 0 with its outputs, from the initial state to start slot 1,
     // beside the maps of segments 1..P-1 (b from the zero state, M from the
     // identity with V = 0)
     fp.init = a.initial_state;
     fp.fin = bm;
     fp.fin2 = Mm;
-    if ((e = reset()) != hipSuccess) return e;
+    fp.counter = counters;
     hipLaunchKernelGGL((fused_ws_kernel<D, kWsSegFirst>), dim3(grid), block, 0, stream, fp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the start states of segments 2..P from that of segment 1
@@ -1416,7 +1418,7 @@ hipError_t launch_segmented(const PrefillArgs& a, int P, hipStream_t stream) {
     fp.init = nullptr;
     fp.fin = a.final_state;
     fp.fin2 = nullptr;
-    if ((e = reset()) != hipSuccess) return e;
+    fp.counter = counters + 1;
     hipLaunchKernelGGL((fused_ws_kernel<D, kWsSegOut>), dim3(grid), block, 0, stream, fp);
     return hipGetLastError();
 }
