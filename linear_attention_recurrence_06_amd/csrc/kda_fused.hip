@@ -131,11 +131,14 @@ __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const 
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Two packed conversions (the element-wise form became four single ones and
+// two permutes where the result feeds a 16x16x16 product).
 __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
-    bf16x4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = (bf16)x[e];
-    return r;
+    const bf16x2v lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2v);
+    const bf16x2v hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2v);
+    return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
 }
 __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
     bf16x8 r;
@@ -865,15 +868,15 @@ __device__ __forceinline__ void ws_block(const SubRecord<D>& rec, bf16 (&vt)[64]
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         const int col = 32 * wr + 16 * (c % 2) + n16;
-        bf16x4 Y;
+        f32x4 Yf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Y[e] = (bf16)((c < NV ? to_f32(vt[16 * Rb + 4 * g + e][col]) : 0.f) - X[c][e]);
-        u[c] = to_bf16x4(mfma16(tb, Y, f32x4{0.f, 0.f, 0.f, 0.f}));
+        for (int e = 0; e < 4; ++e) Yf[e] = (c < NV ? to_f32(vt[16 * Rb + 4 * g + e][col]) : 0.f) - X[c][e];
+        u[c] = to_bf16x4(mfma16(tb, to_bf16x4(Yf), f32x4{0.f, 0.f, 0.f, 0.f}));
         if constexpr (OUT) {
             O[c] = mfma16(m, u[c], O[c]);
+            const bf16x4 ob = to_bf16x4(O[c]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vt[16 * Rb + 4 * g + e][col] = (bf16)O[c][e];
+            for (int e = 0; e < 4; ++e) vt[16 * Rb + 4 * g + e][col] = ob[e];
         }
     }
 #pragma unroll
