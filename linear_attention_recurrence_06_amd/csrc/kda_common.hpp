@@ -27,6 +27,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kChunk = 64;   // tokens per chunk
@@ -39,6 +41,21 @@ __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Two floats as one word of two bf16 (one packed conversion; element-wise
+// conversions into a vector can become single conversions and permutes).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+template <typename T> struct Vec4 { typedef T type __attribute__((ext_vector_type(4))); };
+// Four floats as a 4-vector of T (bf16: two packed conversions).
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type from_f32x4(const f32x4& x) {
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(typename Vec4<T>::type, u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
+    else
+        return x;
+}
 
 // ---------------------------------------------------------------- 8-element vectors
 // Frag<T>: 8 consecutive elements of T held by one lane (16 B for bf16, 32 B for fp32).

@@ -131,15 +131,9 @@ __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const 
 __device__ __forceinline__ f32x4 mfma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-// Two packed conversions (the element-wise form became four single ones and
-// two permutes where the result feeds a 16x16x16 product).
-__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
-    const bf16x2v lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2v);
-    const bf16x2v hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2v);
-    return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
-}
+// Two packed conversions (element-wise ones became four single conversions
+// and two permutes where the result feeds a 16x16x16 product).
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) { return from_f32x4<bf16>(x); }
 __device__ __forceinline__ bf16x8 to_bf16x8(const float (&x)[8]) {
     bf16x8 r;
 #pragma unroll
@@ -473,13 +467,14 @@ __device__ __forceinline__ void fused_chunk(const FusedParams& p, FusedSmem<D>& 
             X = mfma32(sm.rec.ke[Rb][ks][lane], Sb[ks], X);
             O = mfma32(sm.rec.qe[Rb][ks][lane], Sb[ks], O);
         }
-        bf16x4 Y;
+        f32x4 Yf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Y[e] = (bf16)(to_f32(sm.vt[16 * Rb + 4 * g + e][col]) - X[e]);
-        const bf16x4 u = to_bf16x4(mfma16(sm.rec.tb[Rb][lane], Y, f32x4{0.f, 0.f, 0.f, 0.f}));
+        for (int e = 0; e < 4; ++e) Yf[e] = to_f32(sm.vt[16 * Rb + 4 * g + e][col]) - X[e];
+        const bf16x4 u = to_bf16x4(mfma16(sm.rec.tb[Rb][lane], to_bf16x4(Yf), f32x4{0.f, 0.f, 0.f, 0.f}));
         O = mfma16(sm.rec.m[Rb][lane], u, O);
+        const bf16x4 ob = to_bf16x4(O);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.ot[16 * Rb + 4 * g + e][col] = (bf16)O[e];
+        for (int e = 0; e < 4; ++e) sm.ot[16 * Rb + 4 * g + e][col] = ob[e];
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt)
             S[rt] = mfma16(sm.rec.kt[Rb][rt][lane], u,
@@ -593,8 +588,6 @@ constexpr int kWsRec = D / 32;
 // A preparation wave's inputs: q, k, g of token 16 R + lane % 16 over the
 // lane's 8 channels of each of the D / 32 slices (channels 32 ks + 8 (lane /
 // 16) ..), and beta (zero-extended, as in ChunkRows).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 template <int D>
 struct BlockRows {
     bf16x8 q[D / 32], k[D / 32], g[D / 32];
